@@ -1,0 +1,158 @@
+/*
+ * libssd -- Mamba-2 selective state-space (SSD) chunked scan, forward and
+ * backward, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the Mamba-2 layer's state-space recurrence, the kernel that
+ * the Zyphra/AMD post "Training Transformers and Hybrid models on AMD Instinct
+ * MI300X Accelerators" (section "Mamba-2") writes forward and backward GPU
+ * kernels for.  The post gives no formula; the layer it names computes, for
+ * every batch b and head h (group g = h / (nheads / ngroups)):
+ *
+ *     S_{-1} = 0                                        state, dstate x headdim
+ *     S_t    = exp(dt_t A_h) S_{t-1} + dt_t B_t x_t^T
+ *     y_t    = S_t^T C_t + D_h x_t
+ *
+ * with a scalar A_h and D_h per head.  ssd_bwd returns the exact reverse-mode
+ * gradients of the scalar sum_t <dy_t, y_t> (the cotangent of final_state is
+ * zero): dx, ddt, dA, dB, dC, dD.
+ *
+ * Preconditions (not checked on the device): A_h <= 0 and dt >= 0, so every
+ * per-step decay lies in [0, 1]; dt is the step after any softplus.
+ *
+ * Layouts (dense, row-major, element strides implied by the shape):
+ *     x, y, dx, dy     [batch][seqlen][nheads][headdim]    dtype
+ *     dt, ddt          [batch][seqlen][nheads]             dtype
+ *     B, C, dB, dC     [batch][seqlen][ngroups][dstate]    dtype
+ *     A, D, dA, dD     [nheads]                            float32
+ *     final_state      [batch][nheads][headdim][dstate]    float32
+ *                      (element [p][n] is S_{L-1}[n][p])
+ * "dtype" is float32 (SSD_F32) or bfloat16 (SSD_BF16); accumulation is
+ * always float32.  Every pointer is a device pointer aligned to 16 bytes.
+ *
+ * Ownership: the caller allocates every buffer (inputs, outputs, the saved
+ * workspace and the scratch workspaces); the library never allocates or frees
+ * device memory and keeps no global mutable state, so calls are reentrant.
+ * All work is enqueued on `stream`; the calls return without synchronising.
+ *
+ * Errors: argument checks run on the host before anything is enqueued; on
+ * failure nothing is launched and an error code is returned.  A HIP launch
+ * error after the checks is reported as SSD_ERR_HIP.  No C++ exception
+ * crosses this interface.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, seqlen % chunk, nheads % ngroups, misalignment */
+    SSD_ERR_UNSUPPORTED = 2,      /* (dtype, chunk, headdim, dstate) combination not compiled in */
+    SSD_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than the *_bytes query */
+    SSD_ERR_HIP = 4               /* a HIP call or kernel launch failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Problem size.  chunk is the chunk length Q of the chunked scan; seqlen must
+ * be a multiple of it.  dtype is an ssd_dtype. */
+typedef struct {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} ssd_shape;
+
+/* Forward-to-backward context, filled by ssd_fwd.  It borrows the input
+ * pointers and the saved workspace: x, dt, A, B, C, D and saved_ws must stay
+ * alive and unmodified until the ssd_bwd that consumes this context has
+ * finished on its stream. */
+typedef struct {
+    ssd_shape shape;
+    const void *x, *dt, *B, *C;
+    const float *A, *D;
+    const void *saved_ws;
+    size_t saved_ws_bytes;
+} ssd_saved;
+
+/* Kernel identifiers, for timing one kernel with an ssd_probe. */
+typedef enum {
+    SSD_K_CHUNK_CUMSUM = 0,      /* per-chunk inclusive cumsum of dt*A */
+    SSD_K_BMM_FWD = 1,           /* C.B^T per chunk and group (forward tile order) */
+    SSD_K_CHUNK_STATE = 2,       /* decay-weighted B^T x per chunk and head */
+    SSD_K_STATE_PASSING = 3,     /* sequential inter-chunk state scan */
+    SSD_K_CHUNK_SCAN = 4,        /* intra-chunk masked product + state-to-output + D x */
+    SSD_K_BMM_BWD = 5,           /* C.B^T per chunk and group (backward tile order) */
+    SSD_K_CHUNK_STATE_BWD = 6,   /* exp(cs) C^T dy per chunk and head */
+    SSD_K_STATE_PASSING_BWD = 7, /* reverse inter-chunk state scan */
+    SSD_K_CHUNK_SCAN_BWD = 8,    /* dx, ddt and per-chunk dA/dD partials */
+    SSD_K_DW = 9,                /* head-summed masked dY.X^T per chunk and group */
+    SSD_K_DC = 10,               /* dC */
+    SSD_K_DB = 11,               /* dB */
+    SSD_K_DA_DD = 12,            /* fixed-order dA / dD reduction */
+    SSD_NUM_KERNELS = 13
+} ssd_kernel_id;
+
+/* Optional timing hook: when passed to ssd_fwd/ssd_bwd and `kernel` names a
+ * kernel that call launches, `start` is recorded on the stream right before
+ * that launch and `stop` right after it.  Both events are created by the
+ * caller (hipEventCreate).  Pass NULL for no timing. */
+typedef struct {
+    int32_t kernel;
+    int32_t reserved;
+    hipEvent_t start;
+    hipEvent_t stop;
+} ssd_probe;
+
+/* Workspace sizes in bytes for a shape; 0 if the shape is invalid or
+ * unsupported.  saved: kept from ssd_fwd to ssd_bwd (per-chunk cumsums and
+ * the chunk-entry states).  fwd/bwd scratch: only used during the call. */
+size_t ssd_saved_bytes(const ssd_shape *shape);
+size_t ssd_fwd_scratch_bytes(const ssd_shape *shape);
+size_t ssd_bwd_scratch_bytes(const ssd_shape *shape);
+
+/* SSD_OK if the shape is valid and its (dtype, chunk, headdim, dstate) is
+ * compiled in; otherwise the error ssd_fwd would return for it. */
+ssd_status ssd_check_shape(const ssd_shape *shape);
+
+/* Forward pass: y and final_state from x, dt, A, B, C, D.
+ * y is written; final_state is written if non-NULL.  saved_ws (>=
+ * ssd_saved_bytes) receives what ssd_bwd needs; saved_out, if non-NULL, is
+ * filled with the context ssd_bwd consumes.  scratch (>= ssd_fwd_scratch_bytes)
+ * is free to reuse once the call's work has finished on the stream.
+ * probe may be NULL. */
+ssd_status ssd_fwd(const ssd_shape *shape,
+                   const void *x, const void *dt, const float *A,
+                   const void *B, const void *C, const float *D,
+                   void *y, float *final_state,
+                   void *saved_ws, size_t saved_ws_bytes, ssd_saved *saved_out,
+                   void *scratch, size_t scratch_bytes,
+                   hipStream_t stream, const ssd_probe *probe);
+
+/* Backward pass: gradients of sum <dy, y> for the forward that filled
+ * `saved`.  dx, ddt, dA, dB, dC, dD are overwritten (not accumulated).
+ * scratch must hold ssd_bwd_scratch_bytes(&saved->shape). probe may be NULL. */
+ssd_status ssd_bwd(const ssd_saved *saved, const void *dy,
+                   void *dx, void *ddt, float *dA, void *dB, void *dC, float *dD,
+                   void *scratch, size_t scratch_bytes,
+                   hipStream_t stream, const ssd_probe *probe);
+
+/* Static description of a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* Static name of a kernel id (NULL if out of range). */
+const char *ssd_kernel_name(int32_t kernel);
+
+/* Library version, "major.minor.patch". */
+const char *ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

@@ -1,0 +1,200 @@
+// Shared device helpers for the SSD kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix-core conventions used by every kernel
+// --------------------------------------------
+// All products go through 16x16 output tiles of v_mfma_f32_16x16x32_bf16
+// (bf16 operands) or eight chained v_mfma_f32_16x16x4_f32 (fp32 operands).
+// A "fragment" is the 8 K-values one lane contributes to a 16x16x32 step:
+//   A fragment : row  m = lane % 16 of the A tile,  K-slots s = 0..7
+//   B fragment : col  n = lane % 16 of the B tile,  K-slots s = 0..7
+// Lane group q = lane / 16 and slot s together name one logical k.  The sum
+// over k does not care which logical k sits in which (q, s) as long as the A
+// and B fragments agree, so two mappings are used:
+//   contiguous : k = 8q + s                         (one 16-byte load in bf16)
+//   chained    : k = 4q + s (s < 4), 16 + 4q + s-4   (matches the rows a lane
+//                holds in a 16x16 accumulator, so an accumulator tile pair can
+//                be fed straight back in as the next product's A/B fragment)
+// Accumulator tile: lane holds col n = lane % 16, rows m = 4q + r, r = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16;
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }
+
+// 16-byte vector of T: 8 bf16 or 4 floats.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef f4 type; static constexpr int n = 4; };
+
+// ---- fragments --------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void mma(f4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ void frag_set(Frag<T>& f, int s, float v);
+template <> __device__ __forceinline__ void frag_set<bf16>(Frag<bf16>& f, int s, float v) { f.v[s] = (bf16)v; }
+template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int s, float v) { f.v[s] = v; }
+template <typename T> __device__ __forceinline__ float frag_get(const Frag<T>& f, int s) { return (float)f.v[s]; }
+
+// 8 contiguous elements (16-byte aligned for bf16, 32-byte pair for fp32).
+__device__ __forceinline__ void frag_load(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void frag_load(Frag<float>& f, const float* p) {
+  f4 a = *reinterpret_cast<const f4*>(p);
+  f4 b = *reinterpret_cast<const f4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+// Two runs of 4 contiguous elements (chained mapping).
+__device__ __forceinline__ void frag_load2(Frag<bf16>& f, const bf16* p0, const bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void frag_load2(Frag<float>& f, const float* p0, const float* p1) {
+  f4 a = *reinterpret_cast<const f4*>(p0);
+  f4 b = *reinterpret_cast<const f4*>(p1);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// ---- LDS staging --------------------------------------------------------------
+// 4 consecutive storage elements (one lane's share of an accumulator tile).
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f4 type; };
+
+// Copy `rows` x COLS of a global tile (COLS contiguous, row stride gstride
+// source elements) into LDS transposed, converting to TD:
+//   dst[c * dpitch + r] = src[r][c] * scale[r]          (scale may be null)
+// Work unit: 4 rows x one 16-byte column vector, written as 4-row runs.
+// rows must be a multiple of 4.
+template <typename TD, typename TS, int COLS, int NTHREADS>
+__device__ __forceinline__ void stage_transposed(TD* __restrict__ dst, int dpitch, const TS* __restrict__ src,
+                                                 int64_t gstride, int rows, const float* __restrict__ scale) {
+  constexpr int VN = Vec16<TS>::n;
+  constexpr int CU = COLS / VN;
+  typedef typename Vec16<TS>::type V;
+  const int units = (rows / 4) * CU;
+  for (int u = threadIdx.x; u < units; u += NTHREADS) {
+    const int cu = u % CU, r0 = (u / CU) * 4, c0 = cu * VN;
+    V v[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) v[rr] = *reinterpret_cast<const V*>(src + (int64_t)(r0 + rr) * gstride + c0);
+    float sc[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) sc[rr] = scale ? scale[r0 + rr] : 1.0f;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      typename Vec4<TD>::type w;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) w[rr] = from_f<TD>(to_f(v[rr][e]) * sc[rr]);
+      *reinterpret_cast<typename Vec4<TD>::type*>(dst + (c0 + e) * dpitch + r0) = w;
+    }
+  }
+}
+
+// Copy `rows` x COLS into LDS without transposing, converting to TD:
+//   dst[r * dpitch + c] = src[r][c] * scale[r]          (scale may be null)
+template <typename TD, typename TS, int COLS, int NTHREADS>
+__device__ __forceinline__ void stage_rows(TD* __restrict__ dst, int dpitch, const TS* __restrict__ src,
+                                           int64_t gstride, int rows, const float* __restrict__ scale) {
+  constexpr int VN = Vec16<TS>::n;
+  constexpr int CU = COLS / VN;
+  typedef typename Vec16<TS>::type V;
+  const int units = rows * CU;
+  for (int u = threadIdx.x; u < units; u += NTHREADS) {
+    const int cu = u % CU, r = u / CU;
+    const V v = *reinterpret_cast<const V*>(src + (int64_t)r * gstride + cu * VN);
+    const float sc = scale ? scale[r] : 1.0f;
+    TD* d = dst + r * dpitch + cu * VN;
+    if constexpr (sizeof(TD) == sizeof(TS) && VN == 8) {
+      if (!scale) { *reinterpret_cast<V*>(d) = v; continue; }
+    }
+    if constexpr (sizeof(TD) == sizeof(TS) && VN == 4) {
+      if (!scale) { *reinterpret_cast<V*>(d) = v; continue; }
+    }
+#pragma unroll
+    for (int e0 = 0; e0 < VN; e0 += 4) {
+      typename Vec4<TD>::type w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = from_f<TD>(to_f(v[e0 + e]) * sc);
+      *reinterpret_cast<typename Vec4<TD>::type*>(d + e0) = w;
+    }
+  }
+}
+
+// ---- wave-level scans and reductions (wave64) -------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Inclusive prefix sum across the 64 lanes.
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    float o = __shfl_up(v, off, kWave);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+// Inclusive suffix sum across the 64 lanes (lane l gets sum over lanes >= l).
+__device__ __forceinline__ float wave_inclusive_suffix(float v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    float o = __shfl_down(v, off, kWave);
+    if (l + off < kWave) v += o;
+  }
+  return v;
+}
+// Sum over the 16 lanes sharing lane / 16 (result valid in every lane).
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+// Sum over the 4 lanes sharing lane % 16 (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_q(float v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Balanced ownership of 16-row tiles across NW waves: tiles are dealt in a
+// zig-zag (0..NW-1, NW-1..0, ...) so triangular work evens out.
+template <int NW>
+__device__ __forceinline__ int zigzag_owner(int tile) {
+  const int m = tile % (2 * NW);
+  return m < NW ? m : 2 * NW - 1 - m;
+}
+
+}  // namespace ssd

@@ -1,0 +1,216 @@
+// Kernels used by both the forward and the backward pass:
+//   chunk cumsum, C.B^T tiles, chunk state (decay-weighted U^T V per chunk)
+//   and the forward / reverse inter-chunk state scans.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace ssd {
+
+template <typename T> __device__ __forceinline__ void frag_zero(Frag<T>& f);
+template <> __device__ __forceinline__ void frag_zero<bf16>(Frag<bf16>& f) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f.v[s] = (bf16)0.0f;
+}
+template <> __device__ __forceinline__ void frag_zero<float>(Frag<float>& f) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) f.v[s] = 0.0f;
+}
+
+// 8 contiguous K-values starting at k0 of a row whose K-extent is KD; zero
+// beyond KD (KD = 16 leaves the upper half of a 32-wide step empty).
+template <int KD, typename T>
+__device__ __forceinline__ void frag_load_k(Frag<T>& f, const T* row, int k0) {
+  if (KD % 32 == 0 || k0 < KD) frag_load(f, row + k0);
+  else frag_zero(f);
+}
+
+// Index of the lower-triangle 16x16 tile (I, J), J <= I.
+__device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// ---------------------------------------------------------------------------
+// Chunk cumsum: cs[b][h][k][i] = sum_{j <= i} dt[b][kQ + j][h] * A[h].
+// One wavefront per (b, h, k); each lane owns Q/64 consecutive tokens and the
+// chunk-wide prefix comes from a wave64 shuffle scan.
+template <typename T, int Q>
+__global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, const float* __restrict__ A,
+                                                     float* __restrict__ cs, int L, int H, int K) {
+  constexpr int TPL = Q / kWave;
+  const int bhk = blockIdx.x;
+  const int k = bhk % K, bh = bhk / K, h = bh % H, b = bh / H;
+  const int l = threadIdx.x;
+  const float a = A[h];
+  float v[TPL];
+#pragma unroll
+  for (int j = 0; j < TPL; ++j) {
+    const int64_t t = (int64_t)k * Q + l * TPL + j;
+    v[j] = to_f(dt[((int64_t)b * L + t) * H + h]) * a;
+  }
+#pragma unroll
+  for (int j = 1; j < TPL; ++j) v[j] += v[j - 1];
+  const float incl = wave_inclusive_scan(v[TPL - 1]);
+  float excl = __shfl_up(incl, 1, kWave);
+  if (l == 0) excl = 0.0f;
+  float* out = cs + (int64_t)bhk * Q + l * TPL;
+#pragma unroll
+  for (int j = 0; j < TPL; ++j) out[j] = v[j] + excl;
+}
+
+// ---------------------------------------------------------------------------
+// W = C.B^T per (b, k, g), stored as lower-triangle 16x16 accumulator tiles in
+// the lane order the consumer reads them (4 elements per lane, 256 per tile):
+//   FWD_ORDER : tile (I, J) lane l holds W[16I + l%16][16J + 4q + r]
+//               (the consumer walks source tokens j inside a lane)
+//   BWD_ORDER : tile (I, J) lane l holds W[16I + 4q + r][16J + l%16]
+// K-dimension of every product is dstate.
+template <typename T, int Q, int N, bool FWD_ORDER>
+__global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, const T* __restrict__ C,
+                                                   T* __restrict__ Wt, int L, int G, int K, int nsplit) {
+  constexpr int NT = Q / 16;
+  constexpr int TILES = NT * (NT + 1) / 2;
+  const int bkg = blockIdx.x;
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  T* out = Wt + (int64_t)bkg * TILES * 256;
+  const int slot = blockIdx.y * 4 + wave, nslots = nsplit * 4;
+  int idx = 0;
+  for (int I = 0; I < NT; ++I) {
+    for (int J = 0; J <= I; ++J, ++idx) {
+      if (idx % nslots != slot) continue;
+      // FWD_ORDER: D[row j][col i] = B_j . C_i  (A operand = B rows, B operand = C rows)
+      // BWD_ORDER: D[row i][col j] = C_i . B_j
+      const T* arow = FWD_ORDER ? B + ((row0 + 16 * J + c) * G + g) * N : C + ((row0 + 16 * I + c) * G + g) * N;
+      const T* brow = FWD_ORDER ? C + ((row0 + 16 * I + c) * G + g) * N : B + ((row0 + 16 * J + c) * G + g) * N;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < (N + 31) / 32; ++ks) {
+        Frag<T> fa, fb;
+        frag_load_k<N>(fa, arow, ks * 32 + 8 * q);
+        frag_load_k<N>(fb, brow, ks * 32 + 8 * q);
+        mma(acc, fa, fb);
+      }
+      typename Vec4<T>::type v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = from_f<T>(acc[r]);
+      *reinterpret_cast<typename Vec4<T>::type*>(out + (int64_t)idx * 256 + l * 4) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk state: out[b][k][h][p][n] = sum_i w_i U[kQ+i][h][p] V[kQ+i][g][n]
+//   forward  (BWD = false): U = x,  V = B, w_i = dt_i exp(cs_{Q-1} - cs_i)
+//   backward (BWD = true) : U = dy, V = C, w_i = exp(cs_i)
+// An (P x Q)(Q x N) product on the matrix cores, K = tokens, staged through
+// LDS 64 tokens at a time with both operands transposed so K is contiguous.
+template <typename T, int Q, int P, int N, bool BWD>
+__global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, const T* __restrict__ V,
+                                                     const T* __restrict__ dt, const float* __restrict__ cs,
+                                                     float* __restrict__ out, int L, int H, int G, int K) {
+  constexpr int KB = 64;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int TM = P / 16, TN = N / 16, NT = TM * TN, TPW = (NT + 3) / 4;
+  __shared__ __attribute__((aligned(16))) T Ut[P][KB + PAD];
+  __shared__ __attribute__((aligned(16))) T Vt[N][KB + PAD];
+  __shared__ float w[Q];
+
+  const int bkh = blockIdx.x;
+  const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
+  const int g = h / (H / G);
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const float* csc = cs + (((int64_t)b * H + h) * K + k) * Q;
+  const float cs_last = csc[Q - 1];
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+    if (BWD) w[i] = __expf(csc[i]);
+    else w[i] = to_f(dt[(row0 + i) * H + h]) * __expf(cs_last - csc[i]);
+  }
+  __syncthreads();
+
+  f4 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < Q / KB; ++kb) {
+    stage_transposed<T, T, P, 256>(&Ut[0][0], KB + PAD, U + ((row0 + kb * KB) * H + h) * P, (int64_t)H * P, KB, w + kb * KB);
+    stage_transposed<T, T, N, 256>(&Vt[0][0], KB + PAD, V + ((row0 + kb * KB) * G + g) * N, (int64_t)G * N, KB, nullptr);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KB / 32; ++ks) {
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const int j = wave + 4 * u;
+        if (j < NT) {
+          const int tm = j / TN, tn = j % TN;
+          Frag<T> fa, fb;
+          frag_load(fa, &Ut[tm * 16 + c][ks * 32 + 8 * q]);
+          frag_load(fb, &Vt[tn * 16 + c][ks * 32 + 8 * q]);
+          mma(acc[u], fa, fb);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* o = out + (int64_t)bkh * P * N;
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int j = wave + 4 * u;
+    if (j < NT) {
+      const int tm = j / TN, tn = j % TN;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[u][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward state passing, elementwise over the P*N state entries of each
+// (b, h) and sequential over chunks:
+//   hin[k] = h;  h = exp(cs_{Q-1}(k)) h + S[k];   final = h.
+// Each thread owns 4 consecutive entries (16-byte loads of S).
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restrict__ S, const float* __restrict__ cs,
+                                                           T* __restrict__ hin, float* __restrict__ final_state,
+                                                           int H, int K, int PN) {
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= PN) return;
+  const int bh = blockIdx.y, h = bh % H, b = bh / H;
+  const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
+  f4 st = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; ++k) {
+    const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
+    const f4 s = *reinterpret_cast<const f4*>(S + off);
+    const float alpha = __expf(csb[(int64_t)k * Q]);
+    typename Vec4<T>::type v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = from_f<T>(st[r]);
+    *reinterpret_cast<typename Vec4<T>::type*>(hin + off) = v;
+    st = alpha * st + s;
+  }
+  if (final_state) *reinterpret_cast<f4*>(final_state + (int64_t)bh * PN + e) = st;
+}
+
+// Reverse state passing: g = 0; for k = K-1..0: gout[k] = g; g = dhloc[k] + exp(cs_{Q-1}(k)) g.
+// gout[k] is the gradient w.r.t. the state leaving chunk k.
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_state_passing_bwd(const float* __restrict__ dhloc, const float* __restrict__ cs,
+                                                           T* __restrict__ gout, int H, int K, int PN) {
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= PN) return;
+  const int bh = blockIdx.y, h = bh % H, b = bh / H;
+  const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
+  f4 gs = {0.f, 0.f, 0.f, 0.f};
+  for (int k = K - 1; k >= 0; --k) {
+    const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
+    typename Vec4<T>::type v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = from_f<T>(gs[r]);
+    *reinterpret_cast<typename Vec4<T>::type*>(gout + off) = v;
+    const f4 d = *reinterpret_cast<const f4*>(dhloc + off);
+    const float alpha = __expf(csb[(int64_t)k * Q]);
+    gs = d + alpha * gs;
+  }
+}
+
+}  // namespace ssd

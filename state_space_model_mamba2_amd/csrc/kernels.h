@@ -1,0 +1,83 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Not part of the public header.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ssd.h"
+
+namespace ssd {
+
+typedef __bf16 bf16;
+
+// Workspace regions, all offsets in bytes from the workspace base and 256-byte aligned.
+struct Layout {
+  int64_t b, L, H, P, N, G, Q, K;
+  size_t esz;  // bytes per storage element (2 for bf16, 4 for fp32)
+  // saved workspace
+  size_t cs_off, hin_off, saved_bytes;
+  // forward scratch
+  size_t s_off, wt_off, fwd_bytes;
+  // backward scratch
+  size_t w_off, dhloc_off, g_off, dw_off, dapart_off, ddpart_off, bwd_bytes;
+  int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
+};
+
+struct FwdArgs {
+  const void *x, *dt, *B, *C;
+  const float *A, *D;
+  void* y;
+  float* final_state;
+  float* cs;    // [b][H][K][Q]
+  void* hin;    // [b][K][H][P][N]  storage dtype
+  float* S;     // [b][K][H][P][N]
+  void* wt;     // C.B^T tiles, forward order
+};
+
+struct BwdArgs {
+  const void *x, *dt, *B, *C, *dy;
+  const float *A, *D;
+  const float* cs;
+  const void* hin;
+  void *dx, *ddt, *dB, *dC;
+  float *dA, *dD;
+  void* w;         // C.B^T tiles, backward order
+  float* dhloc;    // [b][K][H][P][N]
+  void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
+  float* dw;       // [b][K][G][Q][Q]
+  float* dapart;   // [b][K][H]
+  float* ddpart;   // [b][K][H]
+};
+
+// Kernel timing hook (see ssd_probe in the public header).
+struct ProbeScope {
+  const ssd_probe* p;
+  int id;
+  hipStream_t s;
+  ProbeScope(const ssd_probe* p_, int id_, hipStream_t s_) : p(p_), id(id_), s(s_) {
+    if (p && p->kernel == id) (void)hipEventRecord(p->start, s);
+  }
+  ~ProbeScope() {
+    if (p && p->kernel == id) (void)hipEventRecord(p->stop, s);
+  }
+};
+
+template <typename T, int Q, int P, int N>
+void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);
+template <typename T, int Q, int P, int N>
+void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_probe* probe);
+
+}  // namespace ssd
+
+// Compiled (chunk, headdim, dstate) combinations, per storage dtype.  The
+// fp32 list stops at chunk 128 for headdim 64 because the backward kernel's
+// LDS staging of fp32 tiles would exceed the 160 KiB per workgroup.
+#define SSD_BF16_CONFIGS(X) \
+  X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
+  X(64, 64, 64) X(128, 64, 64) X(256, 64, 64) \
+  X(64, 64, 128) X(128, 64, 128) X(256, 64, 128)
+#define SSD_F32_CONFIGS(X) \
+  X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
+  X(64, 64, 64) X(128, 64, 64) \
+  X(64, 64, 128) X(128, 64, 128)

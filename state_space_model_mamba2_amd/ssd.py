@@ -1,0 +1,151 @@
+"""Python face of libssd: the Mamba-2 SSD chunked scan, forward and backward.
+
+    y, final_state, ctx = fwd(x, dt, A, B, C, D, chunk)
+    grads = bwd(dy, ctx)          # dict: dx, ddt, dA, dB, dC, dD
+
+Tensors are torch tensors on the GPU (torch supplies device memory and the
+stream).  Every step of the computation runs in libssd's HIP kernels; this
+module only checks dtypes/contiguity, allocates outputs and workspaces and
+passes pointers.  It raises if libssd.so has not been built.
+
+Layouts: x, y, dx, dy [b, L, H, P]; dt, ddt [b, L, H]; B, C, dB, dC [b, L, G, N];
+A, D, dA, dD [H] float32; final_state [b, H, P, N] float32.  x, dt, B, C, dy
+share one dtype (torch.bfloat16 or torch.float32).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.SSD_F32, torch.bfloat16: _lib.SSD_BF16}
+_ALIGN = 256
+
+
+def _check(code: int, what: str):
+    if code != _lib.SSD_OK:
+        raise RuntimeError(f"{what} failed: {_lib.status_string(code)} (status {code})")
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+@dataclasses.dataclass
+class Context:
+    """What the backward needs from the forward: the borrowed inputs, the
+    saved workspace (per-chunk cumsums and chunk-entry states) and the C
+    struct pointing at them.  Keeps every referenced tensor alive."""
+    saved: _lib.Saved
+    tensors: tuple
+    saved_ws: torch.Tensor
+    shape: _lib.Shape
+    dtype: torch.dtype
+
+    def intermediates(self):
+        """Views into the saved workspace: cs [b, H, K, Q] float32 and
+        hin [b, K, H, P, N] (entry state of each chunk, storage dtype)."""
+        s = self.shape
+        K = s.seqlen // s.chunk
+        ncs = s.batch * s.nheads * K * s.chunk
+        cs = self.saved_ws[: ncs * 4].view(torch.float32).view(s.batch, s.nheads, K, s.chunk)
+        off = (ncs * 4 + _ALIGN - 1) // _ALIGN * _ALIGN
+        esz = 2 if self.dtype == torch.bfloat16 else 4
+        nst = s.batch * K * s.nheads * s.headdim * s.dstate
+        hin = self.saved_ws[off: off + nst * esz].view(self.dtype).view(s.batch, K, s.nheads, s.headdim, s.dstate)
+        return cs, hin
+
+
+def shape_of(x, B, chunk, dtype_code) -> _lib.Shape:
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return _lib.make_shape(b, L, H, P, N, G, chunk, dtype_code)
+
+
+def _validate(x, dt, A, B, C, D):
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    for name, t in (("dt", dt), ("B", B), ("C", C)):
+        if t.dtype != x.dtype:
+            raise TypeError(f"{name} must have dtype {x.dtype}, got {t.dtype}")
+    for name, t in (("A", A), ("D", D)):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    for name, t in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    b, L, H, P = x.shape
+    if dt.shape != (b, L, H) or A.shape != (H,) or D.shape != (H,):
+        raise ValueError("shape mismatch among x, dt, A, D")
+    if B.shape[:2] != (b, L) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, B, C")
+
+
+def fwd(x, dt, A, B, C, D, chunk: int, *, stream=None, probe: _lib.Probe | None = None,
+        out: torch.Tensor | None = None, scratch: torch.Tensor | None = None, want_final_state: bool = True):
+    """Forward pass.  Returns (y, final_state or None, Context)."""
+    lib = _lib.load()
+    _validate(x, dt, A, B, C, D)
+    shape = shape_of(x, B, chunk, _DTYPES[x.dtype])
+    _check(lib.ssd_check_shape(ctypes.byref(shape)), "ssd_fwd")
+    dev = x.device
+    saved_bytes = lib.ssd_saved_bytes(ctypes.byref(shape))
+    scratch_bytes = lib.ssd_fwd_scratch_bytes(ctypes.byref(shape))
+    y = out if out is not None else torch.empty_like(x)
+    fs = torch.empty((shape.batch, shape.nheads, shape.headdim, shape.dstate), dtype=torch.float32,
+                     device=dev) if want_final_state else None
+    saved_ws = torch.empty(saved_bytes, dtype=torch.uint8, device=dev)
+    if scratch is None or scratch.numel() < scratch_bytes:
+        scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=dev)
+    saved = _lib.Saved()
+    code = lib.ssd_fwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(y), _ptr(fs) if fs is not None else None, _ptr(saved_ws), saved_bytes,
+                       ctypes.byref(saved), _ptr(scratch), scratch.numel(), _stream_handle(stream),
+                       ctypes.byref(probe) if probe is not None else None)
+    _check(code, "ssd_fwd")
+    ctx = Context(saved, (x, dt, A, B, C, D), saved_ws, shape, x.dtype)
+    return y, fs, ctx
+
+
+def bwd(dy, ctx: Context, *, stream=None, probe: _lib.Probe | None = None, scratch: torch.Tensor | None = None):
+    """Backward pass: gradients of sum(dy * y).  Returns a dict of tensors."""
+    lib = _lib.load()
+    x, dt, A, B, C, D = ctx.tensors
+    if dy.dtype != x.dtype or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
+        raise ValueError("dy must be a contiguous GPU tensor with x's shape and dtype")
+    scratch_bytes = lib.ssd_bwd_scratch_bytes(ctypes.byref(ctx.shape))
+    if scratch is None or scratch.numel() < scratch_bytes:
+        scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    ddt = torch.empty_like(dt)
+    dB = torch.empty_like(B)
+    dC = torch.empty_like(C)
+    dA = torch.empty_like(A)
+    dD = torch.empty_like(D)
+    code = lib.ssd_bwd(ctypes.byref(ctx.saved), _ptr(dy), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC),
+                       _ptr(dD), _ptr(scratch), scratch.numel(), _stream_handle(stream),
+                       ctypes.byref(probe) if probe is not None else None)
+    _check(code, "ssd_bwd")
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD)
+
+
+def to_device(inp, device="cuda"):
+    """Upload a seeded numpy draw (inputs.Inputs) as torch tensors of its storage dtype."""
+    import numpy as np
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return dict(x=t(inp.x), dt=t(inp.dt), A=t(inp.A), B=t(inp.B), C=t(inp.C), D=t(inp.D), dy=t(inp.dy))

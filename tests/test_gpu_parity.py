@@ -1,0 +1,57 @@
+"""Parity of libssd (HIP, gfx950) against the float64 oracle on seeded inputs.
+
+Tolerance: per tensor, max|gpu - oracle| / max|oracle| <= 1e-4 for fp32
+storage and <= 2e-2 for bf16 storage with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+
+from state_space_model_mamba2_amd import inputs
+from tests.util import GRADS, max_rel, run_gpu, run_oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _check(shape, seed=0, tol=None):
+    print(f"[parity] {shape}", flush=True)
+    inp = inputs.generate(shape, seed=seed)
+    got, _ = run_gpu(inp, shape.chunk)
+    ref = run_oracle(inp)
+    tol = TOL[shape.dtype] if tol is None else tol
+    errs = {k: max_rel(got[k], ref[k]) for k in ref}
+    print("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{shape}: over tolerance {tol}: {bad}"
+    return errs
+
+
+def test_tiny_fp32_workload():
+    _check(inputs.workload("tiny_fp32"))
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_tiny_shape_chunks_fp32(chunk):
+    _check(inputs.workload("tiny_fp32", chunk=chunk, seqlen=512, batch=2, nheads=4, ngroups=2))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mamba2_head_shape_small(dtype):
+    # headdim 64, dstate 128 as in the 370M / 2.7B workloads, few heads and tokens
+    chunk = 256 if dtype == "bf16" else 128
+    _check(inputs.workload("mamba2_370m", batch=2, seqlen=1024, nheads=4, chunk=chunk, dtype=dtype))
+
+
+def test_zamba_head_shape_small():
+    _check(inputs.workload("zamba2_7b", batch=1, seqlen=768, nheads=8, ngroups=2))
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bf16_smaller_chunks(chunk):
+    _check(inputs.workload("mamba2_2p7b", batch=1, seqlen=1024, nheads=4, ngroups=2, chunk=chunk))
+
+
+def test_long_context_decay_small():
+    _check(inputs.workload("long_context", seqlen=2048, nheads=8, ngroups=4))
