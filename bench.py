@@ -1,0 +1,346 @@
+"""Benchmark: Mamba-2 SSD chunked scan, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
+
+A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
+synthetic inputs (already resident in HBM).  Prints ONE JSON line on stdout;
+diagnostics (per-kernel times) go to stderr.
+
+The roofline object describes the kernel with the largest share of the step:
+its algorithmic bytes and flops per launch (formulas in kernel_model below)
+over its average launch duration, measured with HIP events that libssd records
+around that kernel on the launch stream during the timed steps.
+
+cpu_baseline: the float64 oracle on a bounded slice of the same workload
+(one batch row, a subset of heads), timed on this host's cores and scaled
+linearly in heads and batch to the workload's tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd+bwd tokens/s per GPU + % of bf16 MFMA peak / % HBM peak"
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic traffic and work per launch of each kernel.
+def kernel_model(s, esz):
+    b, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
+    K = L // Q
+    T = b * L
+    nt = Q // 16
+    tiles = nt * (nt + 1) // 2
+    X = T * H * P * esz              # one x-sized tensor
+    BC = T * G * N * esz             # one of B / C
+    DT = T * H * esz
+    CS = b * H * K * Q * 4
+    ST4 = b * K * H * P * N * 4      # chunk states, fp32
+    STe = b * K * H * P * N * esz    # chunk states, storage dtype
+    WT = b * K * G * tiles * 256 * esz
+    nbp = (Q // 64) * (Q // 64 + 1) // 2
+    DW = b * K * G * nbp * 64 * 64 * 4
+    tri = Q * (Q + 1) // 2
+    bkh, bkg = b * K * H, b * K * G
+    m = {
+        "chunk_cumsum": (DT + CS, 0),
+        "bmm_fwd": (2 * BC + WT, 2 * bkg * tri * N),
+        "chunk_state": (X + BC + DT + CS + ST4, 2 * bkh * Q * P * N),
+        "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
+        "chunk_scan": (2 * X + DT + CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
+        "bmm_bwd": (2 * BC + WT, 2 * bkg * tri * N),
+        "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
+        "state_passing_bwd": (ST4 + STe, 0),
+        "chunk_scan_bwd": (3 * X + 2 * DT + CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
+        "dw": (2 * X + DT + CS + DW, 2 * bkh * tri * P),
+        "dc": (X + CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
+        "db": (X + DT + CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
+        "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
+    }
+    return m
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "state_space_model_mamba2_amd", "csrc")
+    for f in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """The few HIP runtime calls bench needs for events (plumbing)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def make_probe(kernel_id, start, stop):
+    from state_space_model_mamba2_amd import _lib
+    return _lib.Probe(kernel_id, 0, start.value, stop.value)
+
+
+def run_step(ssd, dev, chunk, fscr, bscr, fprobe=None, bprobe=None):
+    y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk,
+                         scratch=fscr, probe=fprobe)
+    g = ssd.bwd(dev["dy"], ctx, scratch=bscr, probe=bprobe)
+    return y, fs, g
+
+
+def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
+    """Average duration of every kernel (probed one kernel per step)."""
+    from state_space_model_mamba2_amd import _lib
+    import torch
+    out = {}
+    fwd_ids = range(0, 5)
+    for kid, name in enumerate(_lib.KERNELS):
+        evs = [(hip.event(), hip.event()) for _ in range(reps)]
+        for a, b in evs:
+            p = make_probe(kid, a, b)
+            run_step(ssd, dev, chunk, fscr, bscr, fprobe=p if kid in fwd_ids else None,
+                     bprobe=None if kid in fwd_ids else p)
+        torch.cuda.synchronize()
+        out[name] = sum(hip.elapsed_ms(a, b) for a, b in evs) / reps
+        for a, b in evs:
+            hip.destroy(a)
+            hip.destroy(b)
+    return out
+
+
+def host_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
+def cpu_baseline(shape, inp_full, batch_rows: int, heads: int):
+    """Time the float64 oracle on the first `batch_rows` batch rows and the
+    first `heads` heads (rounded to whole groups) of the workload's inputs;
+    scale linearly in batch and heads to the workload's tokens/s."""
+    import numpy as np
+    from oracle import seq
+    from state_space_model_mamba2_amd.inputs import bf16_bits_to_f32
+
+    H, G = shape.nheads, shape.ngroups
+    hpg = H // G
+    heads = max(hpg, min(H, heads) // hpg * hpg)
+    gs = heads // hpg
+    nb = max(1, min(batch_rows, shape.batch))
+
+    def f64(a):
+        a = np.ascontiguousarray(a)
+        return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+    x = f64(inp_full.x[:nb, :, :heads])
+    dt = f64(inp_full.dt[:nb, :, :heads])
+    A, D = f64(inp_full.A[:heads]), f64(inp_full.D[:heads])
+    B = f64(inp_full.B[:nb, :, :gs])
+    C = f64(inp_full.C[:nb, :, :gs])
+    dy = f64(inp_full.dy[:nb, :, :heads])
+    threads = host_threads()
+    t0 = time.perf_counter()
+    seq.ssd_fwd(x, dt, A, B, C, D, nthreads=threads)
+    seq.ssd_bwd(x, dt, A, B, C, D, dy, nthreads=threads)
+    t = time.perf_counter() - t0
+    scale = (shape.batch / nb) * (H / heads)
+    tok_s = shape.batch * shape.seqlen / (t * scale)
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle fwd+bwd on batch rows 0..{nb - 1} of {shape.batch}, heads 0..{heads - 1} "
+                      f"of {H} ({gs} group(s)), seqlen {shape.seqlen}: {t:.1f} s wall on {threads} threads; "
+                      f"tokens/s scaled linearly by x{scale:g} (batch x heads) to the full workload"}
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("traffic_bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--cpu-heads", type=int, default=80, help="heads in the oracle CPU-baseline slice")
+    ap.add_argument("--cpu-batch", type=int, default=4, help="batch rows in the oracle CPU-baseline slice")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernel", default=None,
+                    help="only run warmup + steps (for rocprofv3); no breakdown, no CPU baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration mode: time a plain device copy of this many bytes and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the SSD scan here is a "
+              f"single-GPU build and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_model_mamba2_amd import _lib, inputs, ssd
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        dt_s = (time.perf_counter() - t0) / 10
+        print(json.dumps({"copy_bytes": n * 4, "ms": dt_s * 1e3, "GBps": 2 * n * 4 / dt_s / 1e9}))
+        return
+
+    _lib.load()  # fail loudly if the HIP library is missing
+    shape = inputs.workload(args.workload)
+    esz = 2 if shape.dtype == "bf16" else 4
+    log(f"[bench] workload {args.workload}: {shape}")
+    t0 = time.perf_counter()
+    inp = inputs.generate(shape, seed=0)
+    dev = ssd.to_device(inp, "cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+
+    shp = ssd.shape_of(dev["x"], dev["B"], shape.chunk, 1 if shape.dtype == "bf16" else 0)
+    lib = _lib.load()
+    fscr = torch.empty(lib.ssd_fwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
+    bscr = torch.empty(lib.ssd_bwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
+
+    hip = Hip()
+    model = kernel_model(shape, esz)
+
+    for _ in range(args.warmup):
+        run_step(ssd, dev, shape.chunk, fscr, bscr)
+    torch.cuda.synchronize()
+
+    if args.profile_kernel is None:
+        breakdown = per_kernel_times(ssd, dev, shape.chunk, fscr, bscr, hip)
+        dom = max(breakdown, key=breakdown.get)
+    else:
+        breakdown, dom = {}, args.profile_kernel
+    dom_id = _lib.KERNEL_ID[dom]
+    is_fwd = dom_id < 5
+
+    # Timed region: exactly `steps` steps; the dominant kernel is bracketed by events in each.
+    evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        p = make_probe(dom_id, a, b)
+        run_step(ssd, dev, shape.chunk, fscr, bscr, fprobe=p if is_fwd else None, bprobe=None if is_fwd else p)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dom_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / len(evs)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = shape.batch * shape.seqlen
+    value = tokens / (ms_per_step / 1e3)
+
+    nbytes, nflops = model[dom]
+    t_s = dom_ms / 1e3
+    mfma_frac = nflops / t_s / 1e12 / MFMA_PEAK_TFLOPS[shape.dtype] if nflops else 0.0
+    hbm_frac = nbytes / t_s / 1e9 / HBM_PEAK_GBS
+    ai = nflops / nbytes if nbytes else 0.0
+    ridge = MFMA_PEAK_TFLOPS[shape.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai > ridge:
+        roof = {"bound": "mfma", "achieved": nflops / t_s / 1e12, "peak": MFMA_PEAK_TFLOPS[shape.dtype],
+                "unit": "TFLOP/s", "frac": mfma_frac}
+    else:
+        roof = {"bound": "hbm", "achieved": nbytes / t_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": hbm_frac}
+    roof["traffic"] = load_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["kernel_ms"] = dom_ms
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = nflops
+    roof["mfma_frac"] = mfma_frac
+    roof["hbm_frac"] = hbm_frac
+
+    if breakdown:
+        log("[bench] per-kernel average duration (ms), algorithmic GB/s and TFLOP/s:")
+        tot = sum(breakdown.values())
+        for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1]):
+            nb, nf = model[k]
+            log(f"  {k:18s} {v:8.4f} ms {100 * v / tot:5.1f}%  {nb / v / 1e6:8.1f} GB/s ({100 * nb / v / 1e6 / HBM_PEAK_GBS:5.1f}%)"
+                f"  {nf / v / 1e9:7.1f} TFLOP/s ({100 * nf / v / 1e9 / MFMA_PEAK_TFLOPS[shape.dtype]:5.1f}%)")
+        log(f"  sum of kernels {tot:.4f} ms vs step {ms_per_step:.4f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline and args.profile_kernel is None:
+        log("[bench] timing the float64 oracle on a bounded sample ...")
+        cpu = cpu_baseline(shape, inp, args.cpu_batch, args.cpu_heads)
+        log(f"[bench] {cpu['sample']}")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": shape.batch, "seqlen": shape.seqlen,
+                   "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
+                   "ngroups": shape.ngroups, "chunk": shape.chunk, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernel_ms": breakdown or None,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
