@@ -48,10 +48,10 @@ Layout make_layout(const ssd_shape* s) {
   size_t o = 0;
   y.cs_off = o;   o += align_up((size_t)(y.b * y.H * y.K * y.Q) * 4);
   y.hin_off = o;  o += align_up(states * y.esz);
+  y.wt_off = o;   o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.saved_bytes = o;
   o = 0;
   y.s_off = o;    o += align_up(states * 4);
-  y.wt_off = o;   o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.fwd_bytes = o;
   o = 0;
   y.w_off = o;      o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
@@ -125,7 +125,7 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   a.cs = at<float>(saved_ws, lay.cs_off);
   a.hin = at<char>(saved_ws, lay.hin_off);
   a.S = at<float>(scratch, lay.s_off);
-  a.wt = at<char>(scratch, lay.wt_off);
+  a.wt = at<char>(saved_ws, lay.wt_off);
 
   bool dispatched = false;
 #define SSD_DISPATCH(TT, Q_, P_, N_)                                  \
@@ -169,6 +169,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, flo
   a.x = sv->x; a.dt = sv->dt; a.B = sv->B; a.C = sv->C; a.dy = dy; a.A = sv->A; a.D = sv->D;
   a.cs = at<float>(sv->saved_ws, lay.cs_off);
   a.hin = at<char>(sv->saved_ws, lay.hin_off);
+  a.wf = at<char>(sv->saved_ws, lay.wt_off);
   a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
   a.w = at<char>(scratch, lay.w_off);
   a.dhloc = at<float>(scratch, lay.dhloc_off);

@@ -6,7 +6,7 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 // Per-head chunk backward: one workgroup (4 waves) per (b, k, h).
 // With Gk = dL/d(state leaving chunk k), xt_j = dt_j x_j, W_ij = C_i . B_j,
-// Lam_ij = exp(cs_i - cs_j) (j <= i) and P = W o Lam, it computes
+// Lam_ij = exp(cs_i - cs_j) (j <= i) and P = W o Lam:
 //   dxt_j = e_j B_j^T Gk + sum_{i >= j} P_ij dy_i,        e_j = exp(cs_{Q-1} - cs_j)
 //   R_ij  = <dy_i, xt_j> P_ij
 //   dcs_i = sum_j R_ij - sum_i' R_i'i + exp(cs_i) <dy_i, Hin_k^T C_i> - q_i,
@@ -14,30 +14,38 @@ namespace ssd {
 //   dl    = reverse cumsum of dcs inside the chunk
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dx_j = dt_j dxt_j + D dy_j
 // plus the chunk's partial sums of dA (sum_j dt_j dl_j) and dD (sum <dy, x>).
-// Column tiles J (source tokens j) and row tiles I are both dealt to waves in
-// zig-zag order; row sums of R go to per-wave LDS rows and are added in a
-// fixed order, so the result does not depend on scheduling.
+// Each (row tile I, column tile J) pair is formed twice on the matrix cores:
+// as R (lanes own a column j; its rows are summed in-lane for the column sums
+// and it feeds dxt) and as R^T (lanes own a row i; summed in-lane for the row
+// sums).  Both come from the same operands and from C.B^T tiles holding
+// identical values in the two lane orders, so the row and column sums cancel
+// exactly where the exact gradient cancels.  Row tiles and column tiles are
+// dealt to waves in zig-zag order; per-wave partial row sums are added in a
+// fixed order.
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Ap,
     const float* __restrict__ Dp, const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin,
-    const T* __restrict__ gst, const T* __restrict__ wb, const T* __restrict__ dy, T* __restrict__ dx,
-    T* __restrict__ ddt, float* __restrict__ dapart, float* __restrict__ ddpart, int L, int H, int G, int K) {
+    const T* __restrict__ gst, const T* __restrict__ wf, const T* __restrict__ wb, const T* __restrict__ dy,
+    T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dapart, float* __restrict__ ddpart,
+    int L, int H, int G, int K) {
+  constexpr int NW = 4, NTH = NW * kWave;
   constexpr int PADQ = 16 / sizeof(T), PADN = 16 / sizeof(T);
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NKP = (P + 31) / 32;
   constexpr int TPL = Q / kWave;
+  typedef typename Vec4<T>::type V4;
   __shared__ __attribute__((aligned(16))) T DYt[P][Q + PADQ];
   __shared__ __attribute__((aligned(16))) T Xt[P][Q + PADQ];
   __shared__ __attribute__((aligned(16))) T Hs[P][N + PADN];
   __shared__ __attribute__((aligned(16))) T Gs[P][N + PADN];
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
-  __shared__ float rowacc[4][Q];
+  __shared__ float rowacc[NW][Q];
   __shared__ float colacc[Q];
   __shared__ float qv[Q];
   __shared__ float ddtd[Q];
-  __shared__ float red[8];
+  __shared__ float red[2 * NW];
 
   const int bkh = blockIdx.x;
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
@@ -45,26 +53,28 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
 
-  stage_transposed<T, T, P, 256>(&DYt[0][0], Q + PADQ, dy + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
-  stage_transposed<T, T, P, 256>(&Xt[0][0], Q + PADQ, x + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
-  stage_rows<T, T, N, 256>(&Hs[0][0], N + PADN, hin + (int64_t)bkh * P * N, N, P, nullptr);
-  stage_rows<T, T, N, 256>(&Gs[0][0], N + PADN, gst + (int64_t)bkh * P * N, N, P, nullptr);
+  stage_transposed<T, T, P, NTH>(&DYt[0][0], Q + PADQ, dy + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
+  stage_transposed<T, T, P, NTH>(&Xt[0][0], Q + PADQ, x + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
+  stage_rows<T, T, N, NTH>(&Hs[0][0], N + PADN, hin + (int64_t)bkh * P * N, N, P, nullptr);
+  stage_rows<T, T, N, NTH>(&Gs[0][0], N + PADN, gst + (int64_t)bkh * P * N, N, P, nullptr);
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+  for (int i = threadIdx.x; i < Q; i += NTH) {
     cs[i] = csc[i];
     dts[i] = to_f(dt[(row0 + i) * H + h]);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) rowacc[w][i] = 0.0f;
+    for (int w = 0; w < NW; ++w) rowacc[w][i] = 0.0f;
   }
   __syncthreads();
 
   const float cs_last = cs[Q - 1];
   const float Dh = Dp[h];
-  const T* wtb = wb + (int64_t)((b * K + k) * G + g) * TILES * 256;
+  const int64_t tbase = (int64_t)((b * K + k) * G + g) * TILES * 256;
+  const T* wfb = wf + tbase;
+  const T* wbb = wb + tbase;
 
   // (1) state -> output part of dcs: exp(cs_i) <dy_i, Hin^T C_i> for owned row tiles.
   for (int I = 0; I < NT; ++I) {
-    if (zigzag_owner<4>(I) != wave) continue;
+    if (zigzag_owner<NW>(I) != wave) continue;
     f4 acc[TP];
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
@@ -83,7 +93,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
-      const typename Vec4<T>::type dv = *reinterpret_cast<const typename Vec4<T>::type*>(&DYt[tp * 16 + c][16 * I + 4 * q]);
+      const V4 dv = *reinterpret_cast<const V4*>(&DYt[tp * 16 + c][16 * I + 4 * q]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[r] += acc[tp][r] * to_f(dv[r]);
     }
@@ -95,9 +105,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
     }
   }
 
-  // (2) owned column tiles J: dxt, q, R sums, ddt (direct part), dx.
+  // (2) owned column tiles J: dxt, q, row and column sums of R, ddt (direct part), dx.
+  float rowpart[NT];  // this lane's partial row sums, row i = 16 I + c
+#pragma unroll
+  for (int I = 0; I < NT; ++I) rowpart[I] = 0.0f;
   for (int J = 0; J < NT; ++J) {
-    if (zigzag_owner<4>(J) != wave) continue;
+    if (zigzag_owner<NW>(J) != wave) continue;
     f4 adx[TP];
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) adx[tp] = f4{0.f, 0.f, 0.f, 0.f};
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const typename Vec4<T>::type xv = *reinterpret_cast<const typename Vec4<T>::type*>(&Xt[tp * 16 + c][16 * J + 4 * q]);
+        const V4 xv = *reinterpret_cast<const V4*>(&Xt[tp * 16 + c][16 * J + 4 * q]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           adx[tp][r] *= __expf(cs_last - csr[r]);
@@ -133,42 +146,61 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
         if (c == 0) qv[j] = s;
       }
     }
-    // intra part: walk row tiles I >= J in pairs (32 tokens i per step)
-    const int cj = 16 * J + c;  // this lane's column j in the W / dP tiles
-    const float cs_j = cs[cj], dt_j = dts[cj];
+    // intra part: row tiles I >= J, two per step (32 tokens i); both tiles'
+    // operands (C.B^T tiles in both lane orders, dy fragments) are requested
+    // before either is used.
+    const int cj = 16 * J + c;  // this lane's column j in R
+    const float cs_cj = cs[cj], dt_cj = dts[cj];
+    const int rj0 = 16 * J + 4 * q;  // this lane's rows j in R^T
+    const f4 cs_rj = *reinterpret_cast<const f4*>(&cs[rj0]);
+    const f4 dt_rj = *reinterpret_cast<const f4*>(&dts[rj0]);
     Frag<T> xf[NKP];
     const T* xrow = x + ((row0 + cj) * H + h) * P;
 #pragma unroll
     for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(xf[kp], xrow, kp * 32 + 8 * q);
     float colsum = 0.0f;
-    for (int I2 = J / 2; I2 < NT / 2; ++I2) {
+#pragma unroll
+    for (int I2 = 0; I2 < NT / 2; ++I2) {
+      if (2 * I2 + 1 < J) continue;
+      V4 wv[2], wtv[2];
+      Frag<T> fd[2][NKP];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int I = 2 * I2 + half;
+        if (I >= J) {
+          wv[half] = *reinterpret_cast<const V4*>(wbb + (int64_t)tri_index(I, J) * 256 + l * 4);
+          wtv[half] = *reinterpret_cast<const V4*>(wfb + (int64_t)tri_index(I, J) * 256 + l * 4);
+          const T* dyrow = dy + ((row0 + 16 * I + c) * H + h) * P;
+#pragma unroll
+          for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(fd[half][kp], dyrow, kp * 32 + 8 * q);
+        }
+      }
       Frag<T> fa;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int I = 2 * I2 + half;
-        const int i0 = 16 * I + 4 * q;
         if (I >= J) {
-          const typename Vec4<T>::type wv =
-              *reinterpret_cast<const typename Vec4<T>::type*>(wtb + (int64_t)tri_index(I, J) * 256 + l * 4);
-          f4 dp = {0.f, 0.f, 0.f, 0.f};
-          const T* dyrow = dy + ((row0 + 16 * I + c) * H + h) * P;
+          f4 dp = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kp = 0; kp < NKP; ++kp) {
-            Frag<T> fd;
-            frag_load_k<P>(fd, dyrow, kp * 32 + 8 * q);
-            mma(dp, fd, xf[kp]);
+            mma(dp, fd[half][kp], xf[kp]);   // lane: column j = cj, rows i = 16I + 4q + r
+            mma(dpt, xf[kp], fd[half][kp]);  // lane: column i = 16I + c, rows j = rj0 + r
           }
+          const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
+          const int ci = 16 * I + c;
+          const float cs_ci = cs[ci];
+          float rsum = 0.0f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_j) : 0.0f;
-            const float pv = to_f(wv[r]) * lam;
-            const float R = dp[r] * dt_j * pv;
-            colsum += R;
-            const float rs = sum16(R);
-            if (c == 0) rowacc[wave][i0 + r] += rs;
+            const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
+            const float pv = to_f(wv[half][r]) * lam;
+            colsum += dp[r] * pv;
             frag_set<T>(fa, half * 4 + r, pv);
+            const float lamt = (ci >= rj0 + r) ? __expf(cs_ci - cs_rj[r]) : 0.0f;
+            rsum += dpt[r] * dt_rj[r] * (to_f(wtv[half][r]) * lamt);
           }
+          rowpart[I] += rsum;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, 0.0f);
@@ -181,15 +213,15 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
         mma(adx[tp], fa, fb);
       }
     }
-    colsum = sum_q(colsum);
+    colsum = sum_q(colsum) * dt_cj;
     if (q == 0) colacc[cj] = colsum;
     // ddt (direct part) and dx for rows j = 16J + 4q + r
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
       const int p = tp * 16 + c;
-      const typename Vec4<T>::type xv = *reinterpret_cast<const typename Vec4<T>::type*>(&Xt[p][16 * J + 4 * q]);
-      const typename Vec4<T>::type dv = *reinterpret_cast<const typename Vec4<T>::type*>(&DYt[p][16 * J + 4 * q]);
+      const V4 xv = *reinterpret_cast<const V4*>(&Xt[p][16 * J + 4 * q]);
+      const V4 dv = *reinterpret_cast<const V4*>(&DYt[p][16 * J + 4 * q]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * J + 4 * q + r;
@@ -203,20 +235,27 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
       if (c == 0) ddtd[16 * J + 4 * q + r] = s;
     }
   }
+  // this wave's row sums: combine the 4 lane groups, add to the wave's row
+#pragma unroll
+  for (int I = 0; I < NT; ++I) {
+    const float s = sum_q(rowpart[I]);
+    if (q == 0) rowacc[wave][16 * I + c] += s;
+  }
 
   // (3) <Gk, Hin_k> and sum <dy, x> over the chunk
   float gh = 0.0f, dd = 0.0f;
-  for (int e = threadIdx.x; e < P * N; e += blockDim.x) gh += to_f(Gs[e / N][e % N]) * to_f(Hs[e / N][e % N]);
-  for (int e = threadIdx.x; e < P * Q; e += blockDim.x) dd += to_f(DYt[e / Q][e % Q]) * to_f(Xt[e / Q][e % Q]);
+  for (int e = threadIdx.x; e < P * N; e += NTH) gh += to_f(Gs[e / N][e % N]) * to_f(Hs[e / N][e % N]);
+  for (int e = threadIdx.x; e < P * Q; e += NTH) dd += to_f(DYt[e / Q][e % Q]) * to_f(Xt[e / Q][e % Q]);
   gh = wave_sum(gh);
   dd = wave_sum(dd);
-  if (l == 0) { red[wave] = gh; red[4 + wave] = dd; }
+  if (l == 0) { red[wave] = gh; red[NW + wave] = dd; }
   __syncthreads();
 
   // (4) assemble dcs, reverse cumsum, ddt, partial dA / dD (wave 0)
   if (wave == 0) {
-    const float ghs = red[0] + red[1] + red[2] + red[3];
-    const float dds = red[4] + red[5] + red[6] + red[7];
+    float ghs = 0.0f, dds = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) { ghs += red[w]; dds += red[NW + w]; }
     float qs = 0.0f;
 #pragma unroll
     for (int t = 0; t < TPL; ++t) qs += qv[l * TPL + t];
@@ -225,7 +264,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = l * TPL + t;
-      v[t] = rowacc[0][i] + rowacc[1][i] + rowacc[2][i] + rowacc[3][i] - colacc[i] - qv[i];
+      float rsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) rsum += rowacc[w][i];
+      v[t] = rsum - colacc[i] - qv[i];
       if (i == Q - 1) v[t] += qs + __expf(cs_last) * ghs;
     }
     // local suffix sums, then across lanes
@@ -248,6 +290,31 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
       dapart[bkh] = da;
       ddpart[bkh] = dds;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward-order C.B^T tiles from the forward-order tiles the forward pass
+// saved: a per-tile lane transpose through LDS, so both orders hold the same
+// rounded values (tile (I, J): forward lane (q, c) holds W[16I + c][16J + 4q + r],
+// backward lane (q, c) holds W[16I + 4q + r][16J + c]).
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_tiles_to_bwd(const T* __restrict__ wf, T* __restrict__ wb, int nsplit) {
+  constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
+  __shared__ float tb[4][16][17];
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int64_t base = (int64_t)blockIdx.x * TILES * 256;
+  typedef typename Vec4<T>::type V4;
+  for (int idx = blockIdx.y * 4 + wave; idx < TILES; idx += nsplit * 4) {
+    const V4 v = *reinterpret_cast<const V4*>(wf + base + (int64_t)idx * 256 + l * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tb[wave][c][4 * q + r] = to_f(v[r]);  // tb[i_local][j_local]
+    __builtin_amdgcn_wave_barrier();
+    V4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[r] = from_f<T>(tb[wave][4 * q + r][c]);
+    *reinterpret_cast<V4*>(wb + base + (int64_t)idx * 256 + l * 4) = o;
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -415,18 +482,26 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
   }
 }
 
-// Fixed-order sums of the per-(b, k) partials: dA[h], dD[h].
+// Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
+// thread sums a strided slice, then a fixed tree combines the slices.
 __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart, const float* __restrict__ ddpart,
                                                float* __restrict__ dA, float* __restrict__ dD, int BK, int H) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+  __shared__ float ra[4], rd[4];
+  const int h = blockIdx.x;
   float sa = 0.0f, sd = 0.0f;
-  for (int i = 0; i < BK; ++i) {
+  for (int i = threadIdx.x; i < BK; i += 256) {
     sa += dapart[(int64_t)i * H + h];
     sd += ddpart[(int64_t)i * H + h];
   }
-  dA[h] = sa;
-  dD[h] = sd;
+  sa = wave_sum(sa);
+  sd = wave_sum(sd);
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) { ra[wave] = sa; rd[wave] = sd; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]);
+    dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]);
+  }
 }
 
 template <typename T, int Q, int P, int N>
@@ -442,8 +517,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_BMM_BWD, st);
-    const int nsplit = 8;
-    k_bmm_tiles<T, Q, N, false><<<dim3(b * K * G, nsplit), dim3(256), 0, st>>>(B, C, w, L, G, K, nsplit);
+    const int nsplit = 4;
+    k_tiles_to_bwd<T, Q><<<dim3(b * K * G, nsplit), dim3(256), 0, st>>>(static_cast<const T*>(a.wf), w, nsplit);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
@@ -457,7 +532,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.A, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), static_cast<T*>(a.ddt),
+        x, dt, a.cs, a.A, a.D, B, C, hin, gst, static_cast<const T*>(a.wf), w, dy, static_cast<T*>(a.dx),
+        static_cast<T*>(a.ddt),
         a.dapart, a.ddpart, L, H, G, K);
   }
   {
@@ -477,7 +553,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
-    k_da_dd<<<dim3((H + 255) / 256), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA, a.dD, b * K, H);
+    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA, a.dD, b * K, H);
   }
 }
 

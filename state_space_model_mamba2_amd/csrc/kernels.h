@@ -16,9 +16,9 @@ struct Layout {
   int64_t b, L, H, P, N, G, Q, K;
   size_t esz;  // bytes per storage element (2 for bf16, 4 for fp32)
   // saved workspace
-  size_t cs_off, hin_off, saved_bytes;
+  size_t cs_off, hin_off, wt_off, saved_bytes;
   // forward scratch
-  size_t s_off, wt_off, fwd_bytes;
+  size_t s_off, fwd_bytes;
   // backward scratch
   size_t w_off, dhloc_off, g_off, dw_off, dapart_off, ddpart_off, bwd_bytes;
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
@@ -32,7 +32,7 @@ struct FwdArgs {
   float* cs;    // [b][H][K][Q]
   void* hin;    // [b][K][H][P][N]  storage dtype
   float* S;     // [b][K][H][P][N]
-  void* wt;     // C.B^T tiles, forward order
+  void* wt;     // C.B^T tiles, forward order (kept in the saved workspace)
 };
 
 struct BwdArgs {
@@ -40,6 +40,7 @@ struct BwdArgs {
   const float *A, *D;
   const float* cs;
   const void* hin;
+  const void* wf;  // C.B^T tiles, forward order (saved by the forward pass)
   void *dx, *ddt, *dB, *dC;
   float *dA, *dD;
   void* w;         // C.B^T tiles, backward order

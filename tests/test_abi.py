@@ -1,0 +1,134 @@
+"""The C ABI of libssd on the host: the library loads, exports every function
+include/ssd.h declares, and rejects bad arguments before launching anything
+(these calls never reach the GPU, so they run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from state_space_model_mamba2_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = (_lib.SSD_OK, _lib.SSD_ERR_INVALID_ARGUMENT,
+                                       _lib.SSD_ERR_UNSUPPORTED, _lib.SSD_ERR_WORKSPACE)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ssd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"ssd_fwd", "ssd_bwd", "ssd_saved_bytes", "ssd_fwd_scratch_bytes", "ssd_bwd_scratch_bytes",
+            "ssd_check_shape", "ssd_status_string", "ssd_kernel_name", "ssd_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def shape(**kw):
+    d = dict(batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=2, chunk=256, dtype=_lib.SSD_BF16)
+    d.update(kw)
+    return _lib.make_shape(**d)
+
+
+def check(lib, s):
+    return lib.ssd_check_shape(ctypes.byref(s))
+
+
+def test_shape_checks(lib):
+    assert check(lib, shape()) == OK
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128)) == OK
+    assert check(lib, shape(seqlen=500)) == INVALID          # seqlen % chunk
+    assert check(lib, shape(nheads=5)) == INVALID            # nheads % ngroups
+    for k in ["batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"]:
+        assert check(lib, shape(**{k: 0})) == INVALID, k
+        assert check(lib, shape(**{k: -1})) == INVALID, k
+    assert check(lib, shape(dtype=7)) == INVALID
+    assert check(lib, shape(headdim=48)) == UNSUPPORTED
+    assert check(lib, shape(dstate=96)) == UNSUPPORTED
+    assert check(lib, shape(chunk=32, seqlen=512)) == UNSUPPORTED
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=256)) == UNSUPPORTED  # fp32 stops at chunk 128 for headdim 64
+    s = shape()
+    s.reserved = 1
+    assert check(lib, s) == INVALID
+
+
+def test_workspace_sizes(lib):
+    s = shape()
+    b, L, H, P, N, G, Q = 2, 512, 4, 64, 128, 2, 256
+    K = L // Q
+    saved = lib.ssd_saved_bytes(ctypes.byref(s))
+    assert saved >= b * H * K * Q * 4 + b * K * H * P * N * 2
+    assert lib.ssd_fwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * 4
+    assert lib.ssd_bwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * (4 + 2) + b * K * G * Q * Q * 4
+    assert lib.ssd_saved_bytes(ctypes.byref(shape(seqlen=500))) == 0
+    # sizes grow linearly with batch
+    assert lib.ssd_saved_bytes(ctypes.byref(shape(batch=4))) > saved
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(lib, s, **over):
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, y=FAKE, fs=FAKE, ws=FAKE, ws_bytes=0,
+                scratch=FAKE, scratch_bytes=0)
+    args.update(over)
+    return lib.ssd_fwd(ctypes.byref(s), args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"],
+                       args["y"], args["fs"], args["ws"], args["ws_bytes"], None, args["scratch"],
+                       args["scratch_bytes"], None, None)
+
+
+def test_fwd_rejects_before_launch(lib):
+    s = shape()
+    need_ws = lib.ssd_saved_bytes(ctypes.byref(s))
+    need_scr = lib.ssd_fwd_scratch_bytes(ctypes.byref(s))
+    assert fwd(lib, shape(seqlen=500)) == INVALID
+    assert fwd(lib, shape(headdim=48)) == UNSUPPORTED
+    for k in ["x", "dt", "A", "B", "C", "D", "y"]:
+        assert fwd(lib, s, **{k: None}, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID, k
+    assert fwd(lib, s, x=FAKE + 8, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID  # misaligned
+    assert fwd(lib, s, ws_bytes=need_ws - 1, scratch_bytes=need_scr) == WORKSPACE
+    assert fwd(lib, s, ws=None, ws_bytes=need_ws, scratch_bytes=need_scr) == WORKSPACE
+    assert fwd(lib, s, ws_bytes=need_ws, scratch_bytes=need_scr - 1) == WORKSPACE
+    assert fwd(lib, s, ws_bytes=need_ws, scratch=None, scratch_bytes=need_scr) == WORKSPACE
+    assert lib.ssd_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 0, None, None) == INVALID
+
+
+def test_bwd_rejects_before_launch(lib):
+    s = shape()
+    sv = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lib.ssd_saved_bytes(ctypes.byref(s)))
+    need = lib.ssd_bwd_scratch_bytes(ctypes.byref(s))
+
+    def bwd(saved, dy=FAKE, scratch=FAKE, nbytes=need, dx=FAKE):
+        return lib.ssd_bwd(ctypes.byref(saved) if saved is not None else None, dy, dx, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, scratch, nbytes, None, None)
+
+    assert bwd(None) == INVALID
+    assert bwd(sv, dy=None) == INVALID
+    assert bwd(sv, dx=None) == INVALID
+    assert bwd(sv, nbytes=need - 1) == WORKSPACE
+    assert bwd(sv, scratch=None) == WORKSPACE
+    small = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16)
+    assert bwd(small) == WORKSPACE
+    bad = _lib.Saved(shape(nheads=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
+    assert bwd(bad) == INVALID
+
+
+def test_strings(lib):
+    assert lib.ssd_version().decode().count(".") == 2
+    for code in range(5):
+        assert lib.ssd_status_string(code)
+    for i, n in enumerate(_lib.KERNELS):
+        assert lib.ssd_kernel_name(i).decode() == n
+    assert lib.ssd_kernel_name(len(_lib.KERNELS)) is None
+    assert lib.ssd_kernel_name(-1) is None
