@@ -14,16 +14,18 @@ namespace ssd {
 //   dl    = reverse cumsum of dcs inside the chunk
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dx_j = dt_j dxt_j + D dy_j
 // plus the chunk's partial sums of dA (sum_j dt_j dl_j) and dD (sum <dy, x>).
-// Each (row tile I, column tile J) pair is formed twice on the matrix cores:
-// as R (lanes own a column j; its rows are summed in-lane for the column sums
-// and it feeds dxt) and as R^T (lanes own a row i; summed in-lane for the row
-// sums).  Both come from the same operands and from C.B^T tiles holding
-// identical values in the two lane orders, so the row and column sums cancel
-// exactly where the exact gradient cancels.  Row tiles and column tiles are
-// dealt to waves in zig-zag order; per-wave partial row sums are added in a
-// fixed order.
+//
+// Each wave owns NT/4 column tiles J (16 source tokens each, zig-zag dealt)
+// and keeps their dxt accumulators and x fragments in registers.  dy streams
+// through LDS in 32-row slabs (natural and transposed copies, double-buffered:
+// the next slab is loaded into registers while the current one is used), and
+// the C.B^T tiles of each (I, J) pair are read from global memory (L2).  Each pair is formed twice on the matrix cores: as R
+// (lanes own a column j: column sums in-lane; feeds dxt through the chained
+// K mapping) and as R^T (lanes own a row i: row sums in-lane), from the same
+// operands and from C.B^T tiles holding identical values in both lane orders,
+// so the row and column sums cancel exactly where the exact gradient cancels.
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256) void k_chunk_scan_bwd(
+__global__ __launch_bounds__(256, 2) void k_chunk_scan_bwd(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Ap,
     const float* __restrict__ Dp, const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin,
     const T* __restrict__ gst, const T* __restrict__ wf, const T* __restrict__ wb, const T* __restrict__ dy,
@@ -31,14 +33,21 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
     int L, int H, int G, int K) {
   constexpr int NW = 4, NTH = NW * kWave;
   constexpr int PADQ = 16 / sizeof(T), PADN = 16 / sizeof(T);
-  constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
+  constexpr int NT = Q / 16, NS = NT / 2, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NKP = (P + 31) / 32;
+  constexpr int PP = P < 32 ? 32 : P;
+  constexpr int NSLOT = NT / NW;          // column tiles per wave
   constexpr int TPL = Q / kWave;
+  constexpr int SR = 32;                  // rows per slab
+  constexpr int VN = Vec16<T>::n, CUQ = P / VN;
+  constexpr int SPIECES = SR * CUQ;       // 16-byte pieces per slab
+  constexpr int SPT = (SPIECES + NTH - 1) / NTH;
   typedef typename Vec4<T>::type V4;
-  __shared__ __attribute__((aligned(16))) T DYt[P][Q + PADQ];
-  __shared__ __attribute__((aligned(16))) T Xt[P][Q + PADQ];
+  typedef typename Vec16<T>::type V;
   __shared__ __attribute__((aligned(16))) T Hs[P][N + PADN];
   __shared__ __attribute__((aligned(16))) T Gs[P][N + PADN];
+  __shared__ __attribute__((aligned(16))) T DYs[2][SR][PP + PADQ];   // slab rows, natural [i][p]
+  __shared__ __attribute__((aligned(16))) T DYts[2][P][SR + PADQ];   // slab rows, transposed [p][i]
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
   __shared__ float rowacc[NW][Q];
@@ -52,9 +61,15 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * H * P
+  const T* xh = x + (row0 * H + h) * P;
+  const int64_t rs = (int64_t)H * P;
 
-  stage_transposed<T, T, P, NTH>(&DYt[0][0], Q + PADQ, dy + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
-  stage_transposed<T, T, P, NTH>(&Xt[0][0], Q + PADQ, x + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
+  if (P < 32) {
+    T* z = &DYs[0][0][0];
+    for (int e = threadIdx.x; e < 2 * SR * (PP + PADQ); e += NTH) z[e] = from_f<T>(0.0f);
+    __syncthreads();
+  }
   stage_rows<T, T, N, NTH>(&Hs[0][0], N + PADN, hin + (int64_t)bkh * P * N, N, P, nullptr);
   stage_rows<T, T, N, NTH>(&Gs[0][0], N + PADN, gst + (int64_t)bkh * P * N, N, P, nullptr);
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
@@ -64,6 +79,29 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
 #pragma unroll
     for (int w = 0; w < NW; ++w) rowacc[w][i] = 0.0f;
   }
+  // slab registers and their LDS placement
+  V sv[SPT];
+  auto slab_load = [&](int sl) {
+#pragma unroll
+    for (int n = 0; n < SPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (u < SPIECES) sv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * sl + u / CUQ) * rs + (u % CUQ) * VN);
+    }
+  };
+  auto slab_store = [&](int bf) {
+#pragma unroll
+    for (int n = 0; n < SPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (u < SPIECES) {
+        const int r = u / CUQ, p0 = (u % CUQ) * VN;
+        *reinterpret_cast<V*>(&DYs[bf][r][p0]) = sv[n];
+#pragma unroll
+        for (int e = 0; e < VN; ++e) DYts[bf][p0 + e][r] = sv[n][e];
+      }
+    }
+  };
+  slab_load(0);
+  slab_store(0);
   __syncthreads();
 
   const float cs_last = cs[Q - 1];
@@ -72,49 +110,23 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
   const T* wfb = wf + tbase;
   const T* wbb = wb + tbase;
 
-  // (1) state -> output part of dcs: exp(cs_i) <dy_i, Hin^T C_i> for owned row tiles.
-  for (int I = 0; I < NT; ++I) {
-    if (zigzag_owner<NW>(I) != wave) continue;
-    f4 acc[TP];
+  // column tiles of this wave: J = 8 (s / 2) + (s even ? wave : 7 - wave)
+  int Js[NSLOT];
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
-    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      Frag<T> fa;
-      frag_load_k<N>(fa, crow, ks * 32 + 8 * q);
-#pragma unroll
-      for (int tp = 0; tp < TP; ++tp) {
-        Frag<T> fb;
-        frag_load_k<N>(fb, &Hs[tp * 16 + c][0], ks * 32 + 8 * q);
-        mma(acc[tp], fa, fb);
-      }
-    }
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
-      const V4 dv = *reinterpret_cast<const V4*>(&DYt[tp * 16 + c][16 * I + 4 * q]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) part[r] += acc[tp][r] * to_f(dv[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * q + r;
-      const float s = sum16(part[r]) * __expf(cs[i]);
-      if (c == 0) rowacc[wave][i] += s;
-    }
-  }
+  for (int sl = 0; sl < NSLOT; ++sl) Js[sl] = 8 * (sl / 2) + ((sl & 1) ? 7 - wave : wave);
 
-  // (2) owned column tiles J: dxt, q, row and column sums of R, ddt (direct part), dx.
-  float rowpart[NT];  // this lane's partial row sums, row i = 16 I + c
+  f4 adx[NSLOT][TP];
+  Frag<T> xf[NSLOT][NKP];
+  float colsum[NSLOT];
 #pragma unroll
-  for (int I = 0; I < NT; ++I) rowpart[I] = 0.0f;
-  for (int J = 0; J < NT; ++J) {
-    if (zigzag_owner<NW>(J) != wave) continue;
-    f4 adx[TP];
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int J = Js[sl];
+    colsum[sl] = 0.0f;
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) adx[tp] = f4{0.f, 0.f, 0.f, 0.f};
-    // state part: B_j^T Gk (K = dstate), scaled by e_j
+    for (int tp = 0; tp < TP; ++tp) adx[sl][tp] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(xf[sl][kp], xh + (int64_t)(16 * J + c) * rs, kp * 32 + 8 * q);
+    // state part: e_j B_j^T Gk (K = dstate)
     const T* brow = B + ((row0 + 16 * J + c) * G + g) * N;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
@@ -124,67 +136,98 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
       for (int tp = 0; tp < TP; ++tp) {
         Frag<T> fb;
         frag_load_k<N>(fb, &Gs[tp * 16 + c][0], ks * 32 + 8 * q);
-        mma(adx[tp], fa, fb);
+        mma(adx[sl][tp], fa, fb);
       }
     }
-    {
-      const f4 csr = *reinterpret_cast<const f4*>(&cs[16 * J + 4 * q]);
+    // q_j = dt_j <x_j, e_j B_j^T Gk>
+    const f4 csr = *reinterpret_cast<const f4*>(&cs[16 * J + 4 * q]);
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        adx[sl][tp][r] *= __expf(cs_last - csr[r]);
+        part[r] += adx[sl][tp][r] * to_f(xh[(int64_t)(16 * J + 4 * q + r) * rs + 16 * tp + c]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * J + 4 * q + r;
+      const float sq = sum16(part[r]) * dts[j];
+      if (c == 0) qv[j] = sq;
+    }
+  }
+
+  for (int s = 0; s < NS; ++s) {
+    const int bf = s & 1;
+    if (s + 1 < NS) slab_load(s + 1);
+    // state -> output part of dcs for the slab's two row tiles: exp(cs_i) <dy_i, Hin^T C_i>
+    if (wave == ((2 * s) & 3) || wave == ((2 * s + 1) & 3)) {
+      const int half = (wave == ((2 * s) & 3)) ? 0 : 1;
+      const int I = 2 * s + half;
+      f4 acc[TP];
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
+      const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        Frag<T> fa;
+        frag_load_k<N>(fa, crow, ks * 32 + 8 * q);
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          Frag<T> fb;
+          frag_load_k<N>(fb, &Hs[tp * 16 + c][0], ks * 32 + 8 * q);
+          mma(acc[tp], fa, fb);
+        }
+      }
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const V4 xv = *reinterpret_cast<const V4*>(&Xt[tp * 16 + c][16 * J + 4 * q]);
+        const V4 dv = *reinterpret_cast<const V4*>(&DYts[bf][tp * 16 + c][16 * half + 4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          adx[tp][r] *= __expf(cs_last - csr[r]);
-          part[r] += adx[tp][r] * to_f(xv[r]);
-        }
+        for (int r = 0; r < 4; ++r) part[r] += acc[tp][r] * to_f(dv[r]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * J + 4 * q + r;
-        const float s = sum16(part[r]) * dts[j];
-        if (c == 0) qv[j] = s;
+        const int i = 16 * I + 4 * q + r;
+        const float sq = sum16(part[r]) * __expf(cs[i]);
+        if (c == 0) rowacc[wave][i] += sq;
       }
     }
-    // intra part: row tiles I >= J, two per step (32 tokens i); both tiles'
-    // operands (C.B^T tiles in both lane orders, dy fragments) are requested
-    // before either is used.
-    const int cj = 16 * J + c;  // this lane's column j in R
-    const float cs_cj = cs[cj], dt_cj = dts[cj];
-    const int rj0 = 16 * J + 4 * q;  // this lane's rows j in R^T
-    const f4 cs_rj = *reinterpret_cast<const f4*>(&cs[rj0]);
-    const f4 dt_rj = *reinterpret_cast<const f4*>(&dts[rj0]);
-    Frag<T> xf[NKP];
-    const T* xrow = x + ((row0 + cj) * H + h) * P;
+    // intra pairs (I in this slab, J owned), I >= J
+    float rowpart[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(xf[kp], xrow, kp * 32 + 8 * q);
-    float colsum = 0.0f;
-#pragma unroll
-    for (int I2 = 0; I2 < NT / 2; ++I2) {
-      if (2 * I2 + 1 < J) continue;
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const int J = Js[sl];
+      if (J > 2 * s + 1) continue;
+      const int cj = 16 * J + c;             // lane's column j in R
+      const float cs_cj = cs[cj];
+      const int rj0 = 16 * J + 4 * q;        // lane's rows j in R^T
+      const f4 cs_rj = *reinterpret_cast<const f4*>(&cs[rj0]);
+      const f4 dt_rj = *reinterpret_cast<const f4*>(&dts[rj0]);
+      // C.B^T tiles of the pair (both lane orders)
       V4 wv[2], wtv[2];
-      Frag<T> fd[2][NKP];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int I = 2 * I2 + half;
+        const int I = 2 * s + half;
         if (I >= J) {
           wv[half] = *reinterpret_cast<const V4*>(wbb + (int64_t)tri_index(I, J) * 256 + l * 4);
           wtv[half] = *reinterpret_cast<const V4*>(wfb + (int64_t)tri_index(I, J) * 256 + l * 4);
-          const T* dyrow = dy + ((row0 + 16 * I + c) * H + h) * P;
-#pragma unroll
-          for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(fd[half][kp], dyrow, kp * 32 + 8 * q);
         }
       }
       Frag<T> fa;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int I = 2 * I2 + half;
+        const int I = 2 * s + half;
         if (I >= J) {
+          Frag<T> fd[NKP];
+#pragma unroll
+          for (int kp = 0; kp < NKP; ++kp) frag_load(fd[kp], &DYs[bf][16 * half + c][kp * 32 + 8 * q]);
           f4 dp = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kp = 0; kp < NKP; ++kp) {
-            mma(dp, fd[half][kp], xf[kp]);   // lane: column j = cj, rows i = 16I + 4q + r
-            mma(dpt, xf[kp], fd[half][kp]);  // lane: column i = 16I + c, rows j = rj0 + r
+            mma(dp, fd[kp], xf[sl][kp]);   // lane: column j = cj, rows i = 16I + 4q + r
+            mma(dpt, xf[sl][kp], fd[kp]);  // lane: column i = 16I + c, rows j = rj0 + r
           }
           const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
@@ -195,12 +238,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
           for (int r = 0; r < 4; ++r) {
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
             const float pv = to_f(wv[half][r]) * lam;
-            colsum += dp[r] * pv;
+            colsum[sl] += dp[r] * pv;
             frag_set<T>(fa, half * 4 + r, pv);
             const float lamt = (ci >= rj0 + r) ? __expf(cs_ci - cs_rj[r]) : 0.0f;
             rsum += dpt[r] * dt_rj[r] * (to_f(wtv[half][r]) * lamt);
           }
-          rowpart[I] += rsum;
+          rowpart[half] += rsum;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, 0.0f);
@@ -209,49 +252,57 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
         Frag<T> fb;
-        frag_load2(fb, &DYt[tp * 16 + c][32 * I2 + 4 * q], &DYt[tp * 16 + c][32 * I2 + 16 + 4 * q]);
-        mma(adx[tp], fa, fb);
+        frag_load2(fb, &DYts[bf][tp * 16 + c][4 * q], &DYts[bf][tp * 16 + c][16 + 4 * q]);
+        mma(adx[sl][tp], fa, fb);
       }
     }
-    colsum = sum_q(colsum) * dt_cj;
-    if (q == 0) colacc[cj] = colsum;
-    // ddt (direct part) and dx for rows j = 16J + 4q + r
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const float sq = sum_q(rowpart[half]);
+      if (q == 0) rowacc[wave][16 * (2 * s + half) + c] += sq;
+    }
+    if (s + 1 < NS) slab_store(bf ^ 1);
+    __syncthreads();
+  }
+
+  // per owned column tile: column sums, ddt (direct part), dx, and this wave's share of sum <dy, x>
+  float dd = 0.0f;
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int J = Js[sl];
+    const int cj = 16 * J + c;
+    const float cs_sum = sum_q(colsum[sl]) * dts[cj];
+    if (q == 0) colacc[cj] = cs_sum;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
       const int p = tp * 16 + c;
-      const V4 xv = *reinterpret_cast<const V4*>(&Xt[p][16 * J + 4 * q]);
-      const V4 dv = *reinterpret_cast<const V4*>(&DYt[p][16 * J + 4 * q]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * J + 4 * q + r;
-        part[r] += adx[tp][r] * to_f(xv[r]);
-        dx[((row0 + j) * H + h) * P + p] = from_f<T>(dts[j] * adx[tp][r] + Dh * to_f(dv[r]));
+        const float xv = to_f(xh[(int64_t)j * rs + p]);
+        const float dv = to_f(dyh[(int64_t)j * rs + p]);
+        part[r] += adx[sl][tp][r] * xv;
+        dd += dv * xv;
+        dx[((row0 + j) * H + h) * P + p] = from_f<T>(dts[j] * adx[sl][tp][r] + Dh * dv);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float s = sum16(part[r]);
-      if (c == 0) ddtd[16 * J + 4 * q + r] = s;
+      const float sq = sum16(part[r]);
+      if (c == 0) ddtd[16 * J + 4 * q + r] = sq;
     }
   }
-  // this wave's row sums: combine the 4 lane groups, add to the wave's row
-#pragma unroll
-  for (int I = 0; I < NT; ++I) {
-    const float s = sum_q(rowpart[I]);
-    if (q == 0) rowacc[wave][16 * I + c] += s;
-  }
 
-  // (3) <Gk, Hin_k> and sum <dy, x> over the chunk
-  float gh = 0.0f, dd = 0.0f;
+  // <Gk, Hin_k>
+  float gh = 0.0f;
   for (int e = threadIdx.x; e < P * N; e += NTH) gh += to_f(Gs[e / N][e % N]) * to_f(Hs[e / N][e % N]);
-  for (int e = threadIdx.x; e < P * Q; e += NTH) dd += to_f(DYt[e / Q][e % Q]) * to_f(Xt[e / Q][e % Q]);
   gh = wave_sum(gh);
   dd = wave_sum(dd);
   if (l == 0) { red[wave] = gh; red[NW + wave] = dd; }
   __syncthreads();
 
-  // (4) assemble dcs, reverse cumsum, ddt, partial dA / dD (wave 0)
+  // assemble dcs, reverse cumsum, ddt, partial dA / dD (wave 0)
   if (wave == 0) {
     float ghs = 0.0f, dds = 0.0f;
 #pragma unroll
@@ -270,7 +321,6 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bwd(
       v[t] = rsum - colacc[i] - qv[i];
       if (i == Q - 1) v[t] += qs + __expf(cs_last) * ghs;
     }
-    // local suffix sums, then across lanes
 #pragma unroll
     for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
     const float incl = wave_inclusive_suffix(v[0]);
@@ -322,61 +372,173 @@ __global__ __launch_bounds__(256) void k_tiles_to_bwd(const T* __restrict__ wf, 
 // Head-summed masked outer products for one (b, k, g) and one 64x64 block
 // (IB, JB), JB <= IB, of the chunk's Q x Q matrix:
 //   dW_ij = sum_{h in g} <dy_i, xt_j> exp(cs_i - cs_j)   (j <= i, else 0)
-// Wave w owns the block's 16-row tile w; heads are the reduction loop.
-template <typename T, int Q, int P>
+// Off-diagonal blocks (IB > JB): every i lies after every j, so with the
+// reference token r = 64 JB + 63 (last of block JB) the decay splits as
+// exp(cs_i - cs_r) exp(cs_r - cs_j), both factors <= 1.  The factors are
+// folded into the operands while they are staged in LDS, so dW_IJ is one
+// product with K = (head, headdim) accumulated on the matrix cores across
+// heads.  Diagonal blocks stage unscaled operands and apply the masked decay
+// per head.  Heads are staged HS at a time through two LDS buffers: each
+// thread loads its share of the next stage into registers, the products of
+// the current stage run, then the registers are written to the other buffer.
+// Wave w owns the block's 16-row tile w and all four 16-column tiles.
+template <typename T, int Q, int P, bool DIAG>
 __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __restrict__ dt,
                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
                                             float* __restrict__ dw, int L, int H, int G, int K) {
-  constexpr int NKP = (P + 31) / 32;
+  constexpr int HS = 2;                     // heads per stage
+  constexpr int PP = P < 32 ? 32 : P;       // K extent per head, padded to a 32-step
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int RP = PP + PAD;              // LDS row pitch
+  constexpr int VN = Vec16<T>::n, CU = P / VN;
+  constexpr int UNITS = HS * 2 * 64 * CU;   // 16-byte row pieces per stage
+  constexpr int UPT = (UNITS + 255) / 256;  // per thread
+  typedef typename Vec16<T>::type V;
+  __shared__ __attribute__((aligned(16))) T As[2][HS][64][RP];
+  __shared__ __attribute__((aligned(16))) T Bs[2][HS][64][RP];
+  __shared__ __attribute__((aligned(16))) float csI[2][HS][64];
+  __shared__ __attribute__((aligned(16))) float csJ[2][HS][64];
+  __shared__ __attribute__((aligned(16))) float dtJ[2][HS][64];
   const int bkg = blockIdx.x;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
-  int IB = 0;
-  while ((IB + 1) * (IB + 2) / 2 <= (int)blockIdx.y) ++IB;
-  const int JB = blockIdx.y - IB * (IB + 1) / 2;
+  int IB, JB;
+  if (DIAG) {
+    IB = JB = blockIdx.y;
+  } else {
+    IB = 1;  // enumerate pairs IB > JB: y = IB (IB - 1) / 2 + JB
+    while ((IB + 1) * IB / 2 <= (int)blockIdx.y) ++IB;
+    JB = blockIdx.y - IB * (IB - 1) / 2;
+  }
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const int hpg = H / G;
-  const int ib0 = 64 * IB + 16 * wave;  // first row of this wave's tile
+  const int nstage = (hpg + HS - 1) / HS;
+  const int i0 = 64 * IB, j0 = 64 * JB, ref = j0 + 63;
+
+  if (P < 32) {  // zero the padded K columns once; staging never writes them
+    T* a = &As[0][0][0][0];
+    for (int e = threadIdx.x; e < 2 * HS * 64 * RP; e += 256) a[e] = from_f<T>(0.0f);
+    T* bb = &Bs[0][0][0][0];
+    for (int e = threadIdx.x; e < 2 * HS * 64 * RP; e += 256) bb[e] = from_f<T>(0.0f);
+  }
+
+  // registers of the stage in flight
+  V rv[UPT];
+  float rs[UPT];
+  float fcs_i = 0.f, fcs_j = 0.f, fdt_j = 0.f;  // DIAG factors: thread t < 64*HS holds row t%64 of head t/64
+
+  auto load = [&](int st) {
+#pragma unroll
+    for (int n = 0; n < UPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      rs[n] = 0.0f;
+      if (u >= UNITS) continue;
+      const int hs = u / (2 * 64 * CU), rem = u % (2 * 64 * CU);
+      const int which = rem / (64 * CU), r = (rem % (64 * CU)) / CU, cu = rem % CU;
+      const int hh = st * HS + hs;
+      if (hh >= hpg) continue;
+      const int h = g * hpg + hh;
+      const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+      if (which == 0) {
+        rv[n] = *reinterpret_cast<const V*>(dy + ((row0 + i0 + r) * H + h) * P + cu * VN);
+        rs[n] = DIAG ? 1.0f : __expf(csb[i0 + r] - csb[ref]);
+      } else {
+        rv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + cu * VN);
+        rs[n] = DIAG ? 1.0f : to_f(dt[(row0 + j0 + r) * H + h]) * __expf(csb[ref] - csb[j0 + r]);
+      }
+    }
+    if (DIAG && threadIdx.x < 64 * HS) {
+      const int hs = threadIdx.x / 64, t = threadIdx.x % 64, hh = st * HS + hs;
+      if (hh < hpg) {
+        const int h = g * hpg + hh;
+        const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+        fcs_i = csb[i0 + t];
+        fcs_j = csb[j0 + t];
+        fdt_j = to_f(dt[(row0 + j0 + t) * H + h]);
+      }
+    }
+  };
+  auto store = [&](int bf) {
+#pragma unroll
+    for (int n = 0; n < UPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      if (u >= UNITS) continue;
+      const int hs = u / (2 * 64 * CU), rem = u % (2 * 64 * CU);
+      const int which = rem / (64 * CU), r = (rem % (64 * CU)) / CU, cu = rem % CU;
+      T* d = (which == 0 ? &As[bf][hs][r][0] : &Bs[bf][hs][r][0]) + cu * VN;
+      if (DIAG) {
+        *reinterpret_cast<V*>(d) = rv[n];
+      } else {
+#pragma unroll
+        for (int e0 = 0; e0 < VN; e0 += 4) {
+          typename Vec4<T>::type w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = from_f<T>(to_f(rv[n][e0 + e]) * rs[n]);
+          *reinterpret_cast<typename Vec4<T>::type*>(d + e0) = w;
+        }
+      }
+    }
+    if (DIAG && threadIdx.x < 64 * HS) {
+      const int hs = threadIdx.x / 64, t = threadIdx.x % 64;
+      csI[bf][hs][t] = fcs_i;
+      csJ[bf][hs][t] = fcs_j;
+      dtJ[bf][hs][t] = fdt_j;
+    }
+  };
 
   f4 acc[4];
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) acc[tj] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-    Frag<T> fa[NKP];
-    const T* dyrow = dy + ((row0 + ib0 + c) * H + h) * P;
+  load(0);
+  store(0);
+  for (int st = 0; st < nstage; ++st) {
+    const int bf = st & 1;
+    __syncthreads();  // stage st is in buffer bf; buffer bf ^ 1 is no longer read
+    if (st + 1 < nstage) load(st + 1);
+    for (int hs = 0; hs < HS; ++hs) {
+      if (st * HS + hs >= hpg) break;
+      Frag<T> fa[PP / 32];
 #pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(fa[kp], dyrow, kp * 32 + 8 * q);
-    const f4 csi = *reinterpret_cast<const f4*>(csb + ib0 + 4 * q);
+      for (int kp = 0; kp < PP / 32; ++kp) frag_load(fa[kp], &As[bf][hs][16 * wave + c][kp * 32 + 8 * q]);
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      if (IB == JB && tj > wave) continue;  // strictly above the diagonal: zero
-      const int j = 64 * JB + 16 * tj + c;
-      Frag<T> fb[NKP];
-      const T* xrow = x + ((row0 + j) * H + h) * P;
+      for (int tj = 0; tj < 4; ++tj) {
+        if (DIAG) {
+          if (tj > wave) continue;  // strictly above the diagonal: zero
+          f4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(fb[kp], xrow, kp * 32 + 8 * q);
-      f4 dp = {0.f, 0.f, 0.f, 0.f};
+          for (int kp = 0; kp < PP / 32; ++kp) {
+            Frag<T> fb;
+            frag_load(fb, &Bs[bf][hs][16 * tj + c][kp * 32 + 8 * q]);
+            mma(dp, fa[kp], fb);
+          }
+          const f4 csi = *reinterpret_cast<const f4*>(&csI[bf][hs][16 * wave + 4 * q]);
+          const int jl = 16 * tj + c;
+          const float csj = csJ[bf][hs][jl], dtj = dtJ[bf][hs][jl];
 #pragma unroll
-      for (int kp = 0; kp < NKP; ++kp) mma(dp, fa[kp], fb[kp]);
-      const float csj = csb[j];
-      const float dtj = to_f(dt[(row0 + j) * H + h]);
+          for (int r = 0; r < 4; ++r) {
+            const int il = 16 * wave + 4 * q + r;
+            const float lam = (il >= jl) ? __expf(csi[r] - csj) : 0.0f;
+            acc[tj][r] += dp[r] * dtj * lam;
+          }
+        } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = ib0 + 4 * q + r;
-        const float lam = (i >= j) ? __expf(csi[r] - csj) : 0.0f;
-        acc[tj][r] += dp[r] * dtj * lam;
+          for (int kp = 0; kp < PP / 32; ++kp) {
+            Frag<T> fb;
+            frag_load(fb, &Bs[bf][hs][16 * tj + c][kp * 32 + 8 * q]);
+            mma(acc[tj], fa[kp], fb);
+          }
+        }
       }
     }
+    if (st + 1 < nstage) store(bf ^ 1);
   }
   float* o = dw + (int64_t)bkg * Q * Q;
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
-    const int j = 64 * JB + 16 * tj + c;
+    const int j = j0 + 16 * tj + c;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[(int64_t)(ib0 + 4 * q + r) * Q + j] = acc[tj][r];
+    for (int r = 0; r < 4; ++r) o[(int64_t)(i0 + 16 * wave + 4 * q + r) * Q + j] = acc[tj][r];
   }
 }
 
@@ -384,27 +546,35 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
 // dC / dB for one (b, k, g) and one 64-row block RB of the chunk:
 //   dC_i = sum_{h in g} exp(cs_i) Hin_k^T dy_i + sum_{j <= i} dW_ij B_j
 //   dB_j = sum_{h in g} e_j dt_j Gk^T x_j      + sum_{i >= j} dW_ij C_i
-// The head sums are one product with K = (head, headdim): per head the rows
-// (dy or x, pre-scaled) and the transposed state are staged in LDS.  Then the
-// dW rows (or columns) and B (or C) are staged and multiplied with K = tokens.
+// The head sums are one product with K = (head, headdim): the rows (dy or x,
+// pre-scaled) and the transposed state of HS heads are staged per step
+// through two LDS buffers (each thread loads the next step into registers
+// while the current step's products run).  Then the dW rows (or columns)
+// and B (or C) are staged and multiplied with K = tokens.
 template <typename T, int Q, int P, int N, bool DB>
 __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* __restrict__ dt,
                                              const float* __restrict__ cs_g, const T* __restrict__ dy,
                                              const T* __restrict__ state, const float* __restrict__ dw,
                                              const T* __restrict__ M, T* __restrict__ out,
                                              int L, int H, int G, int K) {
+  constexpr int HS = sizeof(T) == 2 ? 2 : 1;  // heads per step (fp32 staging would not fit two)
   constexpr int PAD = 16 / sizeof(T);
-  constexpr int PP = P < 32 ? 32 : P;  // K extent of the head products, padded to a 32-step
+  constexpr int PP = P < 32 ? 32 : P;  // K extent per head, padded to a 32-step
+  constexpr int RP = PP + PAD;
   constexpr int TN = N / 16;
-  constexpr size_t PH1 = sizeof(T) * (64 * (PP + PAD) + N * (PP + PAD));
+  constexpr int VN = Vec16<T>::n;
+  typedef typename Vec16<T>::type V;
+  typedef typename Vec4<T>::type V4;
+  // phase 1 buffers: As[2][HS][64][RP], Ss[2][HS][N][RP]; phase 2: Ws[64][Q+PAD], Mt[N][Q+PAD]
+  constexpr size_t PH1 = sizeof(T) * 2 * HS * (64 + N) * RP;
   constexpr size_t PH2 = sizeof(T) * (64 * (Q + PAD) + N * (Q + PAD));
   constexpr size_t LDSB = PH1 > PH2 ? PH1 : PH2;
+  static_assert(LDSB <= 160 * 1024, "LDS exceeds 160 KiB");
   __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
-  __shared__ float fac[64];
-  T* As = reinterpret_cast<T*>(lds);                 // [64][PP + PAD]
-  T* Ss = As + 64 * (PP + PAD);                      // [N][PP + PAD]
-  T* Ws = reinterpret_cast<T*>(lds);                 // [64][Q + PAD]
-  T* Mt = Ws + 64 * (Q + PAD);                       // [N][Q + PAD]
+  T* As = reinterpret_cast<T*>(lds);
+  T* Ss = As + 2 * HS * 64 * RP;
+  auto A_at = [&](int bf, int hs, int r) { return As + ((bf * HS + hs) * 64 + r) * RP; };
+  auto S_at = [&](int bf, int hs, int n) { return Ss + ((bf * HS + hs) * N + n) * RP; };
 
   const int bkg = blockIdx.x, RB = blockIdx.y;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
@@ -412,43 +582,112 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const int r0 = 64 * RB;
   const int hpg = H / G;
+  const int nstage = (hpg + HS - 1) / HS;
 
   if (P < 32) {
-    for (int e = threadIdx.x; e < (64 + N) * (PP + PAD); e += blockDim.x) As[e] = from_f<T>(0.0f);
+    for (int e = threadIdx.x; e < (int)(PH1 / sizeof(T)); e += 256) As[e] = from_f<T>(0.0f);
   }
+
+  // per step: rows (64 x P, 16-byte pieces) and state units (4 state rows p x 16 bytes of n)
+  constexpr int RU = 64 * (P / VN);            // row pieces per head
+  constexpr int SU = (P / 4) * (N / VN);       // state units per head
+  constexpr int RPT = (HS * RU + 255) / 256;
+  constexpr int SPT = (HS * SU + 255) / 256;
+  V rv[RPT];
+  float rsc[RPT];
+  V sv[SPT][4];
+
+  auto load = [&](int st) {
+#pragma unroll
+    for (int n = 0; n < RPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      rsc[n] = 0.0f;
+      if (u >= HS * RU) continue;
+      const int hs = u / RU, rem = u % RU, r = rem / (P / VN), cu = rem % (P / VN);
+      const int hh = st * HS + hs;
+      if (hh >= hpg) continue;
+      const int h = g * hpg + hh;
+      const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+      const int i = r0 + r;
+      rv[n] = *reinterpret_cast<const V*>((DB ? x : dy) + ((row0 + i) * H + h) * P + cu * VN);
+      rsc[n] = DB ? __expf(csb[Q - 1] - csb[i]) * to_f(dt[(row0 + i) * H + h]) : __expf(csb[i]);
+    }
+#pragma unroll
+    for (int n = 0; n < SPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      if (u >= HS * SU) continue;
+      const int hs = u / SU, rem = u % SU, p4 = rem / (N / VN), cu = rem % (N / VN);
+      const int hh = st * HS + hs;
+      if (hh >= hpg) continue;
+      const int h = g * hpg + hh;
+      const T* sp = state + (((int64_t)b * K + k) * H + h) * P * N + (int64_t)(4 * p4) * N + cu * VN;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sv[n][rr] = *reinterpret_cast<const V*>(sp + rr * N);
+    }
+  };
+  auto store = [&](int bf) {
+#pragma unroll
+    for (int n = 0; n < RPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      if (u >= HS * RU) continue;
+      const int hs = u / RU, rem = u % RU, r = rem / (P / VN), cu = rem % (P / VN);
+      T* d = A_at(bf, hs, r) + cu * VN;
+#pragma unroll
+      for (int e0 = 0; e0 < VN; e0 += 4) {
+        V4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = from_f<T>(to_f(rv[n][e0 + e]) * rsc[n]);
+        *reinterpret_cast<V4*>(d + e0) = w;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < SPT; ++n) {
+      const int u = threadIdx.x + 256 * n;
+      if (u >= HS * SU) continue;
+      const int hs = u / SU, rem = u % SU, p4 = rem / (N / VN), cu = rem % (N / VN);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        V4 w;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) w[rr] = sv[n][rr][e];
+        *reinterpret_cast<V4*>(S_at(bf, hs, cu * VN + e) + 4 * p4) = w;
+      }
+    }
+  };
+
   f4 acc[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) acc[tn] = f4{0.f, 0.f, 0.f, 0.f};
 
   // phase 1: head sums (K = head x headdim)
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-    __syncthreads();  // previous head's products are done with As / Ss / fac
-    if (threadIdx.x < 64) {
-      const int i = r0 + threadIdx.x;
-      fac[threadIdx.x] = DB ? __expf(csb[Q - 1] - csb[i]) * to_f(dt[(row0 + i) * H + h]) : __expf(csb[i]);
-    }
+  if (P < 32) __syncthreads();
+  load(0);
+  store(0);
+  for (int st = 0; st < nstage; ++st) {
+    const int bf = st & 1;
     __syncthreads();
-    const T* rows = (DB ? x : dy) + ((row0 + r0) * H + h) * P;
-    stage_rows<T, T, P, 256>(As, PP + PAD, rows, (int64_t)H * P, 64, fac);
-    stage_transposed<T, T, N, 256>(Ss, PP + PAD, state + (((int64_t)b * K + k) * H + h) * P * N, N, P, nullptr);
-    __syncthreads();
+    if (st + 1 < nstage) load(st + 1);
+    for (int hs = 0; hs < HS; ++hs) {
+      if (st * HS + hs >= hpg) break;
 #pragma unroll
-    for (int kp = 0; kp < PP / 32; ++kp) {
-      Frag<T> fa;
-      frag_load(fa, As + (16 * wave + c) * (PP + PAD) + kp * 32 + 8 * q);
+      for (int kp = 0; kp < PP / 32; ++kp) {
+        Frag<T> fa;
+        frag_load(fa, A_at(bf, hs, 16 * wave + c) + kp * 32 + 8 * q);
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        Frag<T> fb;
-        frag_load(fb, Ss + (16 * tn + c) * (PP + PAD) + kp * 32 + 8 * q);
-        mma(acc[tn], fa, fb);
+        for (int tn = 0; tn < TN; ++tn) {
+          Frag<T> fb;
+          frag_load(fb, S_at(bf, hs, 16 * tn + c) + kp * 32 + 8 * q);
+          mma(acc[tn], fa, fb);
+        }
       }
     }
+    if (st + 1 < nstage) store(bf ^ 1);
   }
   __syncthreads();
 
   // phase 2: dW part (K = tokens)
+  T* Ws = reinterpret_cast<T*>(lds);   // [64][Q + PAD]
+  T* Mt = Ws + 64 * (Q + PAD);         // [N][Q + PAD]
   const float* dwb = dw + (int64_t)bkg * Q * Q;
   const int kb0 = DB ? r0 : 0;             // first token of the K range
   const int kr = DB ? Q - r0 : r0 + 64;    // K range length (multiple of 64)
@@ -461,10 +700,9 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
   }
   stage_transposed<T, T, N, 256>(Mt, Q + PAD, M + ((row0 + kb0) * G + g) * N, (int64_t)G * N, kr, nullptr);
   __syncthreads();
-  const int wofs = DB ? 0 : 0;
   for (int ks = 0; ks < kr / 32; ++ks) {
     Frag<T> fa;
-    frag_load(fa, Ws + (16 * wave + c) * (Q + PAD) + wofs + ks * 32 + 8 * q);
+    frag_load(fa, Ws + (16 * wave + c) * (Q + PAD) + ks * 32 + 8 * q);
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       Frag<T> fb;
@@ -539,7 +777,9 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_DW, st);
     const int nb = Q / 64;
-    k_dw<T, Q, P><<<dim3(b * K * G, nb * (nb + 1) / 2), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K);
+    k_dw<T, Q, P, true><<<dim3(b * K * G, nb), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K);
+    if (nb > 1)
+      k_dw<T, Q, P, false><<<dim3(b * K * G, nb * (nb - 1) / 2), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);

@@ -72,8 +72,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_
 }  // namespace ssd
 
 // Compiled (chunk, headdim, dstate) combinations, per storage dtype.  The
-// fp32 list stops at chunk 128 for headdim 64 because the backward kernel's
-// LDS staging of fp32 tiles would exceed the 160 KiB per workgroup.
+// fp32 list is shorter because the backward chunk kernel's LDS staging of
+// fp32 tiles must fit in 160 KiB per workgroup.
 #define SSD_BF16_CONFIGS(X) \
   X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
   X(64, 64, 64) X(128, 64, 64) X(256, 64, 64) \
@@ -81,4 +81,4 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_
 #define SSD_F32_CONFIGS(X) \
   X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
   X(64, 64, 64) X(128, 64, 64) \
-  X(64, 64, 128) X(128, 64, 128)
+  X(64, 64, 128)

@@ -47,7 +47,8 @@ def check(lib, s):
 
 def test_shape_checks(lib):
     assert check(lib, shape()) == OK
-    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128)) == OK
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=64)) == OK
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128, dstate=64)) == OK
     assert check(lib, shape(seqlen=500)) == INVALID          # seqlen % chunk
     assert check(lib, shape(nheads=5)) == INVALID            # nheads % ngroups
     for k in ["batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"]:
@@ -57,7 +58,8 @@ def test_shape_checks(lib):
     assert check(lib, shape(headdim=48)) == UNSUPPORTED
     assert check(lib, shape(dstate=96)) == UNSUPPORTED
     assert check(lib, shape(chunk=32, seqlen=512)) == UNSUPPORTED
-    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=256)) == UNSUPPORTED  # fp32 stops at chunk 128 for headdim 64
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=256)) == UNSUPPORTED  # fp32 LDS staging limit
+    assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128)) == UNSUPPORTED
     s = shape()
     s.reserved = 1
     assert check(lib, s) == INVALID

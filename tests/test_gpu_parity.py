@@ -40,7 +40,7 @@ def test_tiny_shape_chunks_fp32(chunk):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_mamba2_head_shape_small(dtype):
     # headdim 64, dstate 128 as in the 370M / 2.7B workloads, few heads and tokens
-    chunk = 256 if dtype == "bf16" else 128
+    chunk = 256 if dtype == "bf16" else 64
     _check(inputs.workload("mamba2_370m", batch=2, seqlen=1024, nheads=4, chunk=chunk, dtype=dtype))
 
 
