@@ -14,6 +14,10 @@ namespace ssd {
 //   dl    = reverse cumsum of dcs inside the chunk
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dx_j = dt_j dxt_j + D dy_j
 // plus the chunk's partial sums of dA (sum_j dt_j dl_j) and dD (sum <dy, x>).
+// dl is formed without cancelling large terms against each other: the
+// diagonal R_jj (which cancels exactly) is left out of both sums, and the q
+// terms enter as an exclusive prefix sum.  With strong decay dl is tiny next
+// to the individual R_jj, and forming it as a difference lost all accuracy.
 //
 // Each wave owns NT/4 column tiles J (16 source tokens each, zig-zag dealt)
 // and keeps their dxt accumulators and x fragments in registers.  dy streams
@@ -238,9 +242,11 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_bwd(
           for (int r = 0; r < 4; ++r) {
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
             const float pv = to_f(wv[half][r]) * lam;
-            colsum[sl] += dp[r] * pv;
+            // the diagonal R_jj enters a row sum and a column sum with opposite
+            // signs and cancels exactly, so it is left out of both
+            if (i0 + r > cj) colsum[sl] += dp[r] * pv;
             frag_set<T>(fa, half * 4 + r, pv);
-            const float lamt = (ci >= rj0 + r) ? __expf(cs_ci - cs_rj[r]) : 0.0f;
+            const float lamt = (ci > rj0 + r) ? __expf(cs_ci - cs_rj[r]) : 0.0f;
             rsum += dpt[r] * dt_rj[r] * (to_f(wtv[half][r]) * lamt);
           }
           rowpart[half] += rsum;
@@ -307,31 +313,42 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_bwd(
     float ghs = 0.0f, dds = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) { ghs += red[w]; dds += red[NW + w]; }
-    float qs = 0.0f;
-#pragma unroll
-    for (int t = 0; t < TPL; ++t) qs += qv[l * TPL + t];
-    qs = wave_sum(qs);
-    float v[TPL];
+    // dl_j = sum_{i >= j} (row sum_i - column sum_i)  [suffix sum]
+    //      + sum_{j' < j} q_j'                          [exclusive prefix sum]
+    //      + exp(cs_{Q-1}) <Gk, Hin_k>
+    // (the q terms, added at the chunk end and subtracted at each token, are
+    // summed directly as a prefix so no large terms cancel)
+    float v[TPL], qp[TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int i = l * TPL + t;
       float rsum = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) rsum += rowacc[w][i];
-      v[t] = rsum - colacc[i] - qv[i];
-      if (i == Q - 1) v[t] += qs + __expf(cs_last) * ghs;
+      v[t] = rsum - colacc[i];
+      qp[t] = qv[i];
     }
 #pragma unroll
     for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
+    float qrun = 0.0f;  // exclusive prefix of q inside this lane's tokens
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+      const float qt = qp[t];
+      qp[t] = qrun;
+      qrun += qt;
+    }
     const float incl = wave_inclusive_suffix(v[0]);
     float excl = __shfl_down(incl, 1, kWave);
     if (l == kWave - 1) excl = 0.0f;
+    const float qincl = wave_inclusive_scan(qrun);
+    const float qexcl = qincl - qrun;
+    const float tail = __expf(cs_last) * ghs;
     const float Ah = Ap[h];
     float da = 0.0f;
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
       const int j = l * TPL + t;
-      const float dl = v[t] + excl;
+      const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
       da += dts[j] * dl;
       ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + ddtd[j]);
     }
