@@ -57,7 +57,19 @@ Layout make_layout(const ssd_shape* s) {
   y.w_off = o;      o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.dhloc_off = o;  o += align_up(states * 4);
   y.g_off = o;      o += align_up(states * y.esz);
-  y.dw_off = o;     o += align_up((size_t)(y.b * y.K * y.G * y.Q * y.Q) * 4);
+  // Head slices for the group-level backward kernels: enough workgroups to
+  // fill the chip (about 1024 per launch) without slicing finer than a head.
+  {
+    const int64_t base = y.b * y.K * y.G * (y.Q / 64);
+    const int64_t hpg = y.H / y.G;
+    int64_t sl = (1024 + base - 1) / base;
+    if (sl > hpg) sl = hpg;
+    if (sl < 1) sl = 1;
+    y.nslice = sl;
+  }
+  y.dw_off = o;     o += align_up((size_t)(y.nslice * y.b * y.K * y.G * y.Q * y.Q) * 4);
+  y.dcpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.L * y.G * y.N) * 4);
+  y.dbpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.L * y.G * y.N) * 4);
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.bwd_bytes = o;
@@ -175,6 +187,8 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, flo
   a.dhloc = at<float>(scratch, lay.dhloc_off);
   a.gst = at<char>(scratch, lay.g_off);
   a.dw = at<float>(scratch, lay.dw_off);
+  a.dcpart = at<float>(scratch, lay.dcpart_off);
+  a.dbpart = at<float>(scratch, lay.dbpart_off);
   a.dapart = at<float>(scratch, lay.dapart_off);
   a.ddpart = at<float>(scratch, lay.ddpart_off);
 

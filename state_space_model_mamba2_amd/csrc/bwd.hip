@@ -399,10 +399,12 @@ __global__ __launch_bounds__(256) void k_tiles_to_bwd(const T* __restrict__ wf, 
 // thread loads its share of the next stage into registers, the products of
 // the current stage run, then the registers are written to the other buffer.
 // Wave w owns the block's 16-row tile w and all four 16-column tiles.
+// blockIdx.z selects a slice of hps heads of the group; each slice writes its
+// own partial dW (summed later in a fixed order).
 template <typename T, int Q, int P, bool DIAG>
 __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __restrict__ dt,
                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                            float* __restrict__ dw, int L, int H, int G, int K) {
+                                            float* __restrict__ dw, int L, int H, int G, int K, int hps) {
   constexpr int HS = 2;                     // heads per stage
   constexpr int PP = P < 32 ? 32 : P;       // K extent per head, padded to a 32-step
   constexpr int PAD = 16 / sizeof(T);
@@ -429,7 +431,9 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const int hpg = H / G;
-  const int nstage = (hpg + HS - 1) / HS;
+  const int h0 = g * hpg + blockIdx.z * hps;                  // first head of this slice
+  const int nh = min(hps, hpg - (int)blockIdx.z * hps);       // heads in this slice
+  const int nstage = (nh + HS - 1) / HS;
   const int i0 = 64 * IB, j0 = 64 * JB, ref = j0 + 63;
 
   if (P < 32) {  // zero the padded K columns once; staging never writes them
@@ -453,8 +457,8 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
       const int hs = u / (2 * 64 * CU), rem = u % (2 * 64 * CU);
       const int which = rem / (64 * CU), r = (rem % (64 * CU)) / CU, cu = rem % CU;
       const int hh = st * HS + hs;
-      if (hh >= hpg) continue;
-      const int h = g * hpg + hh;
+      if (hh >= nh) continue;
+      const int h = h0 + hh;
       const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
       if (which == 0) {
         rv[n] = *reinterpret_cast<const V*>(dy + ((row0 + i0 + r) * H + h) * P + cu * VN);
@@ -466,8 +470,8 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
     }
     if (DIAG && threadIdx.x < 64 * HS) {
       const int hs = threadIdx.x / 64, t = threadIdx.x % 64, hh = st * HS + hs;
-      if (hh < hpg) {
-        const int h = g * hpg + hh;
+      if (hh < nh) {
+        const int h = h0 + hh;
         const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
         fcs_i = csb[i0 + t];
         fcs_j = csb[j0 + t];
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
     __syncthreads();  // stage st is in buffer bf; buffer bf ^ 1 is no longer read
     if (st + 1 < nstage) load(st + 1);
     for (int hs = 0; hs < HS; ++hs) {
-      if (st * HS + hs >= hpg) break;
+      if (st * HS + hs >= nh) break;
       Frag<T> fa[PP / 32];
 #pragma unroll
       for (int kp = 0; kp < PP / 32; ++kp) frag_load(fa[kp], &As[bf][hs][16 * wave + c][kp * 32 + 8 * q]);
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
     }
     if (st + 1 < nstage) store(bf ^ 1);
   }
-  float* o = dw + (int64_t)bkg * Q * Q;
+  float* o = dw + ((int64_t)blockIdx.z * gridDim.x + bkg) * Q * Q;
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
     const int j = j0 + 16 * tj + c;
@@ -566,14 +570,16 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
 // The head sums are one product with K = (head, headdim): the rows (dy or x,
 // pre-scaled) and the transposed state of HS heads are staged per step
 // through two LDS buffers (each thread loads the next step into registers
-// while the current step's products run).  Then the dW rows (or columns)
-// and B (or C) are staged and multiplied with K = tokens.
+// while the current step's products run).  blockIdx.z selects a slice of hps
+// heads; every slice writes an fp32 partial, and slice 0 also adds the dW
+// part: the dW rows (or columns), summed over the dW slices in a fixed
+// order, and B (or C) are staged and multiplied with K = tokens.
 template <typename T, int Q, int P, int N, bool DB>
 __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* __restrict__ dt,
                                              const float* __restrict__ cs_g, const T* __restrict__ dy,
                                              const T* __restrict__ state, const float* __restrict__ dw,
-                                             const T* __restrict__ M, T* __restrict__ out,
-                                             int L, int H, int G, int K) {
+                                             const T* __restrict__ M, float* __restrict__ out,
+                                             int L, int H, int G, int K, int hps, int nslice_dw) {
   constexpr int HS = sizeof(T) == 2 ? 2 : 1;  // heads per step (fp32 staging would not fit two)
   constexpr int PAD = 16 / sizeof(T);
   constexpr int PP = P < 32 ? 32 : P;  // K extent per head, padded to a 32-step
@@ -599,7 +605,9 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const int r0 = 64 * RB;
   const int hpg = H / G;
-  const int nstage = (hpg + HS - 1) / HS;
+  const int h0 = g * hpg + blockIdx.z * hps;
+  const int nh = min(hps, hpg - (int)blockIdx.z * hps);
+  const int nstage = (nh + HS - 1) / HS;
 
   if (P < 32) {
     for (int e = threadIdx.x; e < (int)(PH1 / sizeof(T)); e += 256) As[e] = from_f<T>(0.0f);
@@ -622,8 +630,8 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
       if (u >= HS * RU) continue;
       const int hs = u / RU, rem = u % RU, r = rem / (P / VN), cu = rem % (P / VN);
       const int hh = st * HS + hs;
-      if (hh >= hpg) continue;
-      const int h = g * hpg + hh;
+      if (hh >= nh) continue;
+      const int h = h0 + hh;
       const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
       const int i = r0 + r;
       rv[n] = *reinterpret_cast<const V*>((DB ? x : dy) + ((row0 + i) * H + h) * P + cu * VN);
@@ -635,8 +643,8 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
       if (u >= HS * SU) continue;
       const int hs = u / SU, rem = u % SU, p4 = rem / (N / VN), cu = rem % (N / VN);
       const int hh = st * HS + hs;
-      if (hh >= hpg) continue;
-      const int h = g * hpg + hh;
+      if (hh >= nh) continue;
+      const int h = h0 + hh;
       const T* sp = state + (((int64_t)b * K + k) * H + h) * P * N + (int64_t)(4 * p4) * N + cu * VN;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) sv[n][rr] = *reinterpret_cast<const V*>(sp + rr * N);
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
     __syncthreads();
     if (st + 1 < nstage) load(st + 1);
     for (int hs = 0; hs < HS; ++hs) {
-      if (st * HS + hs >= hpg) break;
+      if (st * HS + hs >= nh) break;
 #pragma unroll
       for (int kp = 0; kp < PP / 32; ++kp) {
         Frag<T> fa;
@@ -702,39 +710,82 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
   }
   __syncthreads();
 
-  // phase 2: dW part (K = tokens)
-  T* Ws = reinterpret_cast<T*>(lds);   // [64][Q + PAD]
-  T* Mt = Ws + 64 * (Q + PAD);         // [N][Q + PAD]
-  const float* dwb = dw + (int64_t)bkg * Q * Q;
-  const int kb0 = DB ? r0 : 0;             // first token of the K range
-  const int kr = DB ? Q - r0 : r0 + 64;    // K range length (multiple of 64)
-  if (!DB) {
-    // Ws[r][j] = dW[r0 + r][j];  Mt[n][j] = B[j][n]
-    stage_rows<T, float, Q, 256>(Ws, Q + PAD, dwb + (int64_t)r0 * Q, Q, 64, nullptr);
-  } else {
-    // Ws[r][i - r0] = dW[i][r0 + r];  Mt[n][i - r0] = C[i][n]
-    stage_transposed<T, float, 64, 256>(Ws, Q + PAD, dwb + (int64_t)r0 * Q + r0, Q, kr, nullptr);
-  }
-  stage_transposed<T, T, N, 256>(Mt, Q + PAD, M + ((row0 + kb0) * G + g) * N, (int64_t)G * N, kr, nullptr);
-  __syncthreads();
-  for (int ks = 0; ks < kr / 32; ++ks) {
-    Frag<T> fa;
-    frag_load(fa, Ws + (16 * wave + c) * (Q + PAD) + ks * 32 + 8 * q);
+  // phase 2 (slice 0 only): dW part (K = tokens)
+  if (blockIdx.z == 0) {
+    T* Ws = reinterpret_cast<T*>(lds);   // [64][Q + PAD]
+    T* Mt = Ws + 64 * (Q + PAD);         // [N][Q + PAD]
+    const float* dwb = dw + (int64_t)bkg * Q * Q;
+    const int64_t dws = (int64_t)gridDim.x * Q * Q;  // stride between dW slices
+    const int kb0 = DB ? r0 : 0;             // first token of the K range
+    const int kr = DB ? Q - r0 : r0 + 64;    // K range length (multiple of 64)
+    if (!DB) {
+      // Ws[r][j] = sum_s dW_s[r0 + r][j], j < kr
+      for (int u = threadIdx.x; u < 64 * (kr / 4); u += 256) {
+        const int r = u / (kr / 4), j4 = (u % (kr / 4)) * 4;
+        f4 v = *reinterpret_cast<const f4*>(dwb + (int64_t)(r0 + r) * Q + j4);
+        for (int sl = 1; sl < nslice_dw; ++sl) v += *reinterpret_cast<const f4*>(dwb + sl * dws + (int64_t)(r0 + r) * Q + j4);
+        V4 w;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      Frag<T> fb;
-      frag_load(fb, Mt + (16 * tn + c) * (Q + PAD) + ks * 32 + 8 * q);
-      mma(acc[tn], fa, fb);
+        for (int e = 0; e < 4; ++e) w[e] = from_f<T>(v[e]);
+        *reinterpret_cast<V4*>(Ws + r * (Q + PAD) + j4) = w;
+      }
+    } else {
+      // Ws[j][i - r0] = sum_s dW_s[i][r0 + j], i in [r0, Q)
+      for (int u = threadIdx.x; u < (kr / 4) * 16; u += 256) {
+        const int i4 = (u / 16) * 4, j4 = (u % 16) * 4;
+        f4 v[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) v[rr] = *reinterpret_cast<const f4*>(dwb + (int64_t)(r0 + i4 + rr) * Q + r0 + j4);
+        for (int sl = 1; sl < nslice_dw; ++sl) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            v[rr] += *reinterpret_cast<const f4*>(dwb + sl * dws + (int64_t)(r0 + i4 + rr) * Q + r0 + j4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          V4 w;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f<T>(v[rr][e]);
+          *reinterpret_cast<V4*>(Ws + (j4 + e) * (Q + PAD) + i4) = w;
+        }
+      }
+    }
+    stage_transposed<T, T, N, 256>(Mt, Q + PAD, M + ((row0 + kb0) * G + g) * N, (int64_t)G * N, kr, nullptr);
+    __syncthreads();
+    for (int ks = 0; ks < kr / 32; ++ks) {
+      Frag<T> fa;
+      frag_load(fa, Ws + (16 * wave + c) * (Q + PAD) + ks * 32 + 8 * q);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        Frag<T> fb;
+        frag_load(fb, Mt + (16 * tn + c) * (Q + PAD) + ks * 32 + 8 * q);
+        mma(acc[tn], fa, fb);
+      }
     }
   }
+  float* o = out + (int64_t)blockIdx.z * gridDim.x * Q * N;  // slice stride b*K*G*Q*N = b*L*G*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = r0 + 16 * wave + 4 * q + r;
-      out[((row0 + row) * G + g) * N + 16 * tn + c] = from_f<T>(acc[tn][r]);
+      o[((row0 + row) * G + g) * N + 16 * tn + c] = acc[tn][r];
     }
   }
+}
+
+// out[e] = sum_s part[s][e] in slice order, converted to the storage dtype.
+template <typename T>
+__global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ part, T* __restrict__ out,
+                                                    int64_t n, int nslice) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  f4 v = *reinterpret_cast<const f4*>(part + e);
+  for (int sl = 1; sl < nslice; ++sl) v += *reinterpret_cast<const f4*>(part + sl * n + e);
+  typename Vec4<T>::type w;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
+  *reinterpret_cast<typename Vec4<T>::type*>(out + e) = w;
 }
 
 // Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
@@ -791,22 +842,27 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
         static_cast<T*>(a.ddt),
         a.dapart, a.ddpart, L, H, G, K);
   }
+  const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
+  const int64_t nbc = (int64_t)b * L * G * N;  // elements of dB / dC
   {
     ProbeScope ps(probe, SSD_K_DW, st);
     const int nb = Q / 64;
-    k_dw<T, Q, P, true><<<dim3(b * K * G, nb), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K);
+    k_dw<T, Q, P, true><<<dim3(b * K * G, nb, S), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K, hps);
     if (nb > 1)
-      k_dw<T, Q, P, false><<<dim3(b * K * G, nb * (nb - 1) / 2), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K);
+      k_dw<T, Q, P, false><<<dim3(b * K * G, nb * (nb - 1) / 2, S), dim3(256), 0, st>>>(
+          x, dt, a.cs, dy, a.dw, L, H, G, K, hps);
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);
-    k_dbc<T, Q, P, N, false><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, a.dw, B, static_cast<T*>(a.dC), L, H, G, K);
+    k_dbc<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, hin, a.dw, B, a.dcpart, L, H, G, K, hps, S);
+    k_sum_slices<T><<<dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0, st>>>(a.dcpart, static_cast<T*>(a.dC), nbc, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DB, st);
-    k_dbc<T, Q, P, N, true><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, gst, a.dw, C, static_cast<T*>(a.dB), L, H, G, K);
+    k_dbc<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, gst, a.dw, C, a.dbpart, L, H, G, K, hps, S);
+    k_sum_slices<T><<<dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0, st>>>(a.dbpart, static_cast<T*>(a.dB), nbc, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);

@@ -20,7 +20,8 @@ struct Layout {
   // forward scratch
   size_t s_off, fwd_bytes;
   // backward scratch
-  size_t w_off, dhloc_off, g_off, dw_off, dapart_off, ddpart_off, bwd_bytes;
+  size_t w_off, dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, bwd_bytes;
+  int64_t nslice;  // head slices of the group-level backward kernels
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
 };
 
@@ -46,7 +47,9 @@ struct BwdArgs {
   void* w;         // C.B^T tiles, backward order
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
-  float* dw;       // [b][K][G][Q][Q]
+  float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
+  float* dcpart;   // [nslice][b][L][G][N] fp32 partials of dC
+  float* dbpart;   // [nslice][b][L][G][N] fp32 partials of dB
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
 };
