@@ -72,6 +72,9 @@ Layout make_layout(const ssd_shape* s) {
   y.dbpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.L * y.G * y.N) * 4);
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
+  const int64_t nsp = scan_bwd_splits((int)y.Q);
+  y.dlpart_off = o; o += align_up((size_t)(y.b * y.K * y.H * (nsp + 3) * y.Q) * 4);
+  y.dlscal_off = o; o += align_up((size_t)(y.b * y.K * y.H * (nsp + 1)) * 4);
   y.bwd_bytes = o;
   return y;
 }
@@ -191,6 +194,8 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, flo
   a.dbpart = at<float>(scratch, lay.dbpart_off);
   a.dapart = at<float>(scratch, lay.dapart_off);
   a.ddpart = at<float>(scratch, lay.ddpart_off);
+  a.dlpart = at<float>(scratch, lay.dlpart_off);
+  a.dlscal = at<float>(scratch, lay.dlscal_off);
 
   bool dispatched = false;
 #define SSD_DISPATCH_B(TT, Q_, P_, N_)                                \

@@ -4,359 +4,432 @@
 namespace ssd {
 
 // ---------------------------------------------------------------------------
-// Per-head chunk backward: one workgroup (4 waves) per (b, k, h).
-// With Gk = dL/d(state leaving chunk k), xt_j = dt_j x_j, W_ij = C_i . B_j,
-// Lam_ij = exp(cs_i - cs_j) (j <= i) and P = W o Lam:
+// Per-head chunk backward.  With Gk = dL/d(state leaving chunk k),
+// xt_j = dt_j x_j, W_ij = C_i . B_j, Lam_ij = exp(cs_i - cs_j) (j <= i) and
+// P = W o Lam:
 //   dxt_j = e_j B_j^T Gk + sum_{i >= j} P_ij dy_i,        e_j = exp(cs_{Q-1} - cs_j)
 //   R_ij  = <dy_i, xt_j> P_ij
 //   dcs_i = sum_j R_ij - sum_i' R_i'i + exp(cs_i) <dy_i, Hin_k^T C_i> - q_i,
 //           q_j = <xt_j, e_j B_j^T Gk>;   dcs_{Q-1} += sum_j q_j + exp(cs_{Q-1}) <Gk, Hin_k>
 //   dl    = reverse cumsum of dcs inside the chunk
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dx_j = dt_j dxt_j + D dy_j
-// plus the chunk's partial sums of dA (sum_j dt_j dl_j) and dD (sum <dy, x>).
-// dl is formed without cancelling large terms against each other: the
-// diagonal R_jj (which cancels exactly) is left out of both sums, and the q
-// terms enter as an exclusive prefix sum.  With strong decay dl is tiny next
-// to the individual R_jj, and forming it as a difference lost all accuracy.
+// This kernel writes dx and, per token, the partial sums that dl is formed
+// from (row sums, column sums, q_j, <dxt_j, x_j>); k_dl_assemble finishes dl,
+// ddt and the chunk's dA / dD partials.
 //
-// Each wave owns NT/4 column tiles J (16 source tokens each, zig-zag dealt)
-// and keeps their dxt accumulators and x fragments in registers.  dy streams
-// through LDS in 32-row slabs (natural and transposed copies, double-buffered:
-// the next slab is loaded into registers while the current one is used), and
-// the C.B^T tiles of each (I, J) pair are read from global memory (L2).  Each pair is formed twice on the matrix cores: as R
-// (lanes own a column j: column sums in-lane; feeds dxt through the chained
-// K mapping) and as R^T (lanes own a row i: row sums in-lane), from the same
-// operands and from C.B^T tiles holding identical values in both lane orders,
-// so the row and column sums cancel exactly where the exact gradient cancels.
+// Layout of the work.  NSPLIT workgroups of 4 waves share one (b, k, h);
+// the chunk's 16-token column tiles J are dealt to the 4 NSPLIT waves in a
+// zig-zag (owner o gets J = o and 2 NO - 1 - o), so the triangular work is
+// even.  A wave keeps, per owned tile, x_J as chained-K fragments and dxt_J^T
+// as matrix-core accumulators (lane (q, c) holds dxt[16J + c][16tp + 4q + r]),
+// so every token's x and dxt values sit in the same lane and slot: <dxt_j, x_j>
+// and q_j need no second read of x.
+// The chunk's dy rows of this head are read once, all at the start, into LDS
+// (row-major; the dy^T operands are gathered from it).  C and the owned
+// C.B^T tiles stream through LDS in 32-row slabs from the chunk end backwards
+// (double-buffered: the next slab is loaded into registers while the current
+// one is used; these mostly hit in L2, which they share with the other heads
+// of the group).  A column tile's dxt is complete once the slab holding its
+// own rows has been used, so dx is written right there.
+// R is formed once per (I, J) tile pair on the matrix cores: lanes own a
+// column j, so column sums accumulate in-lane and row sums come from 16-lane
+// register (DPP) reductions over the very same values; the diagonal R_jj
+// (which cancels exactly between the two) is left out of both.
+// The workgroups of one (b, k, h) are 8 dispatch slots apart, so the
+// round-robin dispatch over the 8 XCDs runs them on one XCD (one L2) at
+// about the same time.
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256, 2) void k_chunk_scan_bwd(
-    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Ap,
-    const float* __restrict__ Dp, const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin,
-    const T* __restrict__ gst, const T* __restrict__ wf, const T* __restrict__ wb, const T* __restrict__ dy,
-    T* __restrict__ dx, T* __restrict__ ddt, float* __restrict__ dapart, float* __restrict__ ddpart,
-    int L, int H, int G, int K) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
+    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
+    const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin, const T* __restrict__ gst,
+    const T* __restrict__ wb, const T* __restrict__ dy, T* __restrict__ dx, float* __restrict__ dlpart,
+    float* __restrict__ dlscal, int nitems, int L, int H, int G, int K) {
   constexpr int NW = 4, NTH = NW * kWave;
-  constexpr int PADQ = 16 / sizeof(T), PADN = 16 / sizeof(T);
+  constexpr int NSPLIT = scan_bwd_splits(Q);
+  constexpr int PADR = 16 / sizeof(T);    // row padding: 16-byte aligned rows, spread banks
   constexpr int NT = Q / 16, NS = NT / 2, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NKP = (P + 31) / 32;
-  constexpr int PP = P < 32 ? 32 : P;
-  constexpr int NSLOT = NT / NW;          // column tiles per wave
-  constexpr int TPL = Q / kWave;
+  constexpr int NO = NSPLIT * NW;         // column-tile owners per (b, k, h)
+  constexpr int NSLOT = NT / NO;          // column tiles per wave
   constexpr int SR = 32;                  // rows per slab
-  constexpr int VN = Vec16<T>::n, CUQ = P / VN;
-  constexpr int SPIECES = SR * CUQ;       // 16-byte pieces per slab
-  constexpr int SPT = (SPIECES + NTH - 1) / NTH;
+  constexpr int VN = Vec16<T>::n;
+  constexpr int CUP = P / VN, CUN = N / VN;
+  constexpr int YPIECES = Q * CUP, CPIECES = SR * CUN;   // 16-byte pieces: dy chunk, C slab
+  constexpr int YPT = (YPIECES + NTH - 1) / NTH, CPT = (CPIECES + NTH - 1) / NTH;
+  // C.B^T tiles of a slab: rows I = 2s + half against every owned column tile
+  // of this workgroup, slot (half, wave, sl); tiles with J > I stay unused
+  constexpr int WT = 2 * NW * NSLOT;
+  constexpr int WPIECES = WT * 256 / VN;
+  constexpr int WPT = (WPIECES + NTH - 1) / NTH;
+  static_assert(P == 16 || P % 32 == 0, "headdim");
+  static_assert(N == 16 || N % 32 == 0, "dstate");
+  static_assert(NT % NO == 0 && NSLOT >= 1 && NS >= 1, "chunk");
+  static_assert(NSLOT == 1 || NSLOT == 2, "zig-zag dealing of two tiles per owner");
+  static_assert(TP <= NW, "each Hin row block needs a wave");
+  static_assert(NSPLIT == 1 || NSPLIT == 2, "a split owns one row tile of each slab");
   typedef typename Vec4<T>::type V4;
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T Hs[P][N + PADN];
-  __shared__ __attribute__((aligned(16))) T Gs[P][N + PADN];
-  __shared__ __attribute__((aligned(16))) T DYs[2][SR][PP + PADQ];   // slab rows, natural [i][p]
-  __shared__ __attribute__((aligned(16))) T DYts[2][P][SR + PADQ];   // slab rows, transposed [p][i]
+  __shared__ __attribute__((aligned(16))) T DY[Q][P + PADR];        // this head's dy rows of the chunk
+  __shared__ __attribute__((aligned(16))) T Cs[2][SR][N + PADR];    // slab rows of C
+  __shared__ __attribute__((aligned(16))) T Ws[2][WT * 256];        // slab C.B^T tiles (lane order)
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
   __shared__ float rowacc[NW][Q];
-  __shared__ float colacc[Q];
-  __shared__ float qv[Q];
-  __shared__ float ddtd[Q];
   __shared__ float red[2 * NW];
 
-  const int bkh = blockIdx.x;
+  // (b, k, h) item and column split of this workgroup
+  const int xcd = blockIdx.x % 8, grp = blockIdx.x / 8;
+  const int bkh = (grp / NSPLIT) * 8 + xcd, split = grp % NSPLIT;
+  if (bkh >= nitems) return;  // whole workgroup, before any barrier
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
-  const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * H * P
+  const int64_t rs = (int64_t)H * P;      // row stride of x / dy / dx
+  const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * rs
   const T* xh = x + (row0 * H + h) * P;
-  const int64_t rs = (int64_t)H * P;
+  const T* ch = C + (row0 * G + g) * N;    // row i: ch + i * G * N
+  const T* wbb = wb + (int64_t)((b * K + k) * G + g) * TILES * 256;
+  const T* hinh = hin + (int64_t)bkh * P * N;
+  const T* gsth = gst + (int64_t)bkh * P * N;
+  float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;  // rows: splits' row sums, column sums, q, <dxt, x>
 
-  if (P < 32) {
-    T* z = &DYs[0][0][0];
-    for (int e = threadIdx.x; e < 2 * SR * (PP + PADQ); e += NTH) z[e] = from_f<T>(0.0f);
-    __syncthreads();
-  }
-  stage_rows<T, T, N, NTH>(&Hs[0][0], N + PADN, hin + (int64_t)bkh * P * N, N, P, nullptr);
-  stage_rows<T, T, N, NTH>(&Gs[0][0], N + PADN, gst + (int64_t)bkh * P * N, N, P, nullptr);
-  const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-  for (int i = threadIdx.x; i < Q; i += NTH) {
-    cs[i] = csc[i];
-    dts[i] = to_f(dt[(row0 + i) * H + h]);
+  // column tile of wave w, slot sl, in this split
+  auto tile_of = [&](int w, int sl) {
+    const int o = split * NW + w;
+    return (sl & 1) ? 2 * NO - 1 - o : o;
+  };
+  int Js[NSLOT];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) rowacc[w][i] = 0.0f;
-  }
-  // slab registers and their LDS placement
-  V sv[SPT];
-  auto slab_load = [&](int sl) {
+  for (int sl = 0; sl < NSLOT; ++sl) Js[sl] = tile_of(wave, sl);
+
+  // ---- slab staging: registers <- global (next slab), LDS <- registers
+  V cv[CPT], wv[WPT];
+  auto slab_load = [&](int s) {
 #pragma unroll
-    for (int n = 0; n < SPT; ++n) {
+    for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (u < SPIECES) sv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * sl + u / CUQ) * rs + (u % CUQ) * VN);
+      if (u < CPIECES) cv[n] = *reinterpret_cast<const V*>(ch + (int64_t)(SR * s + u / CUN) * G * N + (u % CUN) * VN);
+    }
+#pragma unroll
+    for (int n = 0; n < WPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      const int t = u / (256 / VN), piece = u % (256 / VN);
+      const int half = t / (NW * NSLOT), w = (t / NSLOT) % NW, sl = t % NSLOT;
+      const int I = 2 * s + half, J = tile_of(w, sl);
+      if (u < WPIECES && J <= I) wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J) * 256 + piece * VN);
     }
   };
   auto slab_store = [&](int bf) {
 #pragma unroll
-    for (int n = 0; n < SPT; ++n) {
+    for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (u < SPIECES) {
-        const int r = u / CUQ, p0 = (u % CUQ) * VN;
-        *reinterpret_cast<V*>(&DYs[bf][r][p0]) = sv[n];
+      if (u < CPIECES) *reinterpret_cast<V*>(&Cs[bf][u / CUN][(u % CUN) * VN]) = cv[n];
+    }
 #pragma unroll
-        for (int e = 0; e < VN; ++e) DYts[bf][p0 + e][r] = sv[n][e];
-      }
+    for (int n = 0; n < WPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (u < WPIECES) *reinterpret_cast<V*>(&Ws[bf][u * VN]) = wv[n];
     }
   };
-  slab_load(0);
+
+  // ---- prologue: per-token scalars, dy, the last slab, x and the state operands
+  const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+  for (int i = threadIdx.x; i < Q; i += NTH) {
+    cs[i] = csc[i];
+    dts[i] = to_f(dt[(row0 + i) * H + h]);
+  }
+  {
+    V yv[YPT];
+#pragma unroll
+    for (int n = 0; n < YPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (u < YPIECES) yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(u / CUP) * rs + (u % CUP) * VN);
+    }
+#pragma unroll
+    for (int n = 0; n < YPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (u < YPIECES) *reinterpret_cast<V*>(&DY[u / CUP][(u % CUP) * VN]) = yv[n];
+    }
+  }
+  slab_load(NS - 1);
+  Frag<T> xf[NSLOT][NKP];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl)
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(xf[sl][kp], xh + (int64_t)(16 * Js[sl] + c) * rs, kp * 32, q);
+  // Hin rows 16 tw .. 16 tw + 15 (this wave's share of the C.Hin^T products)
+  const int tw = wave % TP;
+  Frag<T> hf[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(hf[ks], hinh + (16 * tw + c) * N, ks * 32 + 8 * q);
+
+  // state part of dxt^T: e_j (Gk B_j^T) with K = dstate; <Gk, Hin> (split 0)
+  f4 adx[NSLOT][TP];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl)
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) adx[sl][tp] = f4{0.f, 0.f, 0.f, 0.f};
+  float gh = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    Frag<T> gf[TP], bfr[NSLOT];
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) frag_load_k<N>(gf[tp], gsth + (16 * tp + c) * N, ks * 32 + 8 * q);
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl)
+      frag_load_k<N>(bfr[sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl)
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], gf[tp], bfr[sl]);
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) {
+      if (split != 0 || tp != wave) continue;  // waves 0 .. TP-1 of split 0 cover Hin rows 16 tp ..
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) gh += frag_get(gf[tp], s8) * frag_get(hf[ks], s8);
+    }
+  }
   slab_store(0);
   __syncthreads();
 
   const float cs_last = cs[Q - 1];
   const float Dh = Dp[h];
-  const int64_t tbase = (int64_t)((b * K + k) * G + g) * TILES * 256;
-  const T* wfb = wf + tbase;
-  const T* wbb = wb + tbase;
-
-  // column tiles of this wave: J = 8 (s / 2) + (s even ? wave : 7 - wave)
-  int Js[NSLOT];
-#pragma unroll
-  for (int sl = 0; sl < NSLOT; ++sl) Js[sl] = 8 * (sl / 2) + ((sl & 1) ? 7 - wave : wave);
-
-  f4 adx[NSLOT][TP];
-  Frag<T> xf[NSLOT][NKP];
-  float colsum[NSLOT];
+  // e_j scaling and q_j = dt_j <x_j, e_j B_j^T Gk>  (j = 16 J + c in this lane)
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) {
-    const int J = Js[sl];
-    colsum[sl] = 0.0f;
-#pragma unroll
-    for (int tp = 0; tp < TP; ++tp) adx[sl][tp] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_k<P>(xf[sl][kp], xh + (int64_t)(16 * J + c) * rs, kp * 32 + 8 * q);
-    // state part: e_j B_j^T Gk (K = dstate)
-    const T* brow = B + ((row0 + 16 * J + c) * G + g) * N;
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      Frag<T> fa;
-      frag_load_k<N>(fa, brow, ks * 32 + 8 * q);
-#pragma unroll
-      for (int tp = 0; tp < TP; ++tp) {
-        Frag<T> fb;
-        frag_load_k<N>(fb, &Gs[tp * 16 + c][0], ks * 32 + 8 * q);
-        mma(adx[sl][tp], fa, fb);
-      }
-    }
-    // q_j = dt_j <x_j, e_j B_j^T Gk>
-    const f4 csr = *reinterpret_cast<const f4*>(&cs[16 * J + 4 * q]);
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+    const int j = 16 * Js[sl] + c;
+    const float e = __expf(cs_last - cs[j]);
+    float qs = 0.0f;
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        adx[sl][tp][r] *= __expf(cs_last - csr[r]);
-        part[r] += adx[sl][tp][r] * to_f(xh[(int64_t)(16 * J + 4 * q + r) * rs + 16 * tp + c]);
+        adx[sl][tp][r] *= e;
+        qs += adx[sl][tp][r] * frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 16 * J + 4 * q + r;
-      const float sq = sum16(part[r]) * dts[j];
-      if (c == 0) qv[j] = sq;
-    }
+    qs = sum_q(qs) * dts[j];
+    if (q == 0) part[(NSPLIT + 1) * Q + j] = qs;
   }
 
-  for (int s = 0; s < NS; ++s) {
-    const int bf = s & 1;
-    if (s + 1 < NS) slab_load(s + 1);
-    // state -> output part of dcs for the slab's two row tiles: exp(cs_i) <dy_i, Hin^T C_i>
-    if (wave == ((2 * s) & 3) || wave == ((2 * s + 1) & 3)) {
-      const int half = (wave == ((2 * s) & 3)) ? 0 : 1;
-      const int I = 2 * s + half;
-      f4 acc[TP];
+  float colsum[NSLOT];
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
-      const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+  for (int sl = 0; sl < NSLOT; ++sl) colsum[sl] = 0.0f;
+  float dd = 0.0f;
+
+  for (int it = 0; it < NS; ++it) {
+    const int s = NS - 1 - it, bf = it & 1;
+    if (it + 1 < NS) slab_load(s - 1);
+    const int rb = 32 * s;  // first row of the slab
+
+    // row sums of this slab's two row tiles (per lane: rows rb + 16 half + 4q + r)
+    float rowtot[2][4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rowtot[half][r] = 0.0f;
+
+    // state -> output part: exp(cs_i) <dy_i, Hin^T C_i> over this wave's 16
+    // columns p.  Split sp takes the slab's row tile sp (all of them when
+    // there is one split); its TP output tiles are dealt over the waves.
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (NSPLIT == 2 && half != split) continue;
+      if (((NSPLIT == 2 ? 0 : half * TP) + tw) % NW != wave) continue;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
         Frag<T> fa;
-        frag_load_k<N>(fa, crow, ks * 32 + 8 * q);
-#pragma unroll
-        for (int tp = 0; tp < TP; ++tp) {
-          Frag<T> fb;
-          frag_load_k<N>(fb, &Hs[tp * 16 + c][0], ks * 32 + 8 * q);
-          mma(acc[tp], fa, fb);
-        }
+        frag_load_k<N>(fa, &Cs[bf][16 * half + c][0], ks * 32 + 8 * q);
+        mma(acc, fa, hf[ks]);
       }
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      const int i0 = rb + 16 * half + 4 * q;
+      const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) {
-        const V4 dv = *reinterpret_cast<const V4*>(&DYts[bf][tp * 16 + c][16 * half + 4 * q]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[r] += acc[tp][r] * to_f(dv[r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * q + r;
-        const float sq = sum16(part[r]) * __expf(cs[i]);
-        if (c == 0) rowacc[wave][i] += sq;
-      }
+      for (int r = 0; r < 4; ++r) rowtot[half][r] += __expf(csi[r]) * (acc[r] * to_f(DY[i0 + r][16 * tw + c]));
     }
-    // intra pairs (I in this slab, J owned), I >= J
-    float rowpart[2] = {0.f, 0.f};
+
+    // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
+    Frag<T> fdt[TP];
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) {
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+        fdt[tp].v[s8] = DY[rb + (s8 < 4 ? 4 * q + s8 : 16 + 4 * q + s8 - 4)][16 * tp + c];
+    }
+
+    // intra-chunk pairs (I in this slab, J owned), I >= J
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       const int J = Js[sl];
       if (J > 2 * s + 1) continue;
-      const int cj = 16 * J + c;             // lane's column j in R
+      const int cj = 16 * J + c;             // lane's column j
       const float cs_cj = cs[cj];
-      const int rj0 = 16 * J + 4 * q;        // lane's rows j in R^T
-      const f4 cs_rj = *reinterpret_cast<const f4*>(&cs[rj0]);
-      const f4 dt_rj = *reinterpret_cast<const f4*>(&dts[rj0]);
-      // C.B^T tiles of the pair (both lane orders)
-      V4 wv[2], wtv[2];
+      const float dt_cj = dts[cj];
+      Frag<T> fa;                            // P[i][j] as the B operand (col j, K = i)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int I = 2 * s + half;
         if (I >= J) {
-          wv[half] = *reinterpret_cast<const V4*>(wbb + (int64_t)tri_index(I, J) * 256 + l * 4);
-          wtv[half] = *reinterpret_cast<const V4*>(wfb + (int64_t)tri_index(I, J) * 256 + l * 4);
-        }
-      }
-      Frag<T> fa;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int I = 2 * s + half;
-        if (I >= J) {
-          Frag<T> fd[NKP];
-#pragma unroll
-          for (int kp = 0; kp < NKP; ++kp) frag_load(fd[kp], &DYs[bf][16 * half + c][kp * 32 + 8 * q]);
-          f4 dp = {0.f, 0.f, 0.f, 0.f}, dpt = {0.f, 0.f, 0.f, 0.f};
+          f4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kp = 0; kp < NKP; ++kp) {
-            mma(dp, fd[kp], xf[sl][kp]);   // lane: column j = cj, rows i = 16I + 4q + r
-            mma(dpt, xf[sl][kp], fd[kp]);  // lane: column i = 16I + c, rows j = rj0 + r
+            Frag<T> fd;
+            frag_load_chained<P>(fd, &DY[16 * I + c][0], kp * 32, q);
+            mma(dp, fd, xf[sl][kp]);         // lane: column j = cj, rows i = 16I + 4q + r
           }
           const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
-          const int ci = 16 * I + c;
-          const float cs_ci = cs[ci];
-          float rsum = 0.0f;
+          const V4 wt = *reinterpret_cast<const V4*>(&Ws[bf][((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
-            const float pv = to_f(wv[half][r]) * lam;
-            // the diagonal R_jj enters a row sum and a column sum with opposite
-            // signs and cancels exactly, so it is left out of both
-            if (i0 + r > cj) colsum[sl] += dp[r] * pv;
+            const float pv = to_f(wt[r]) * lam;
             frag_set<T>(fa, half * 4 + r, pv);
-            const float lamt = (ci > rj0 + r) ? __expf(cs_ci - cs_rj[r]) : 0.0f;
-            rsum += dpt[r] * dt_rj[r] * (to_f(wtv[half][r]) * lamt);
+            const float rv = (i0 + r > cj) ? dp[r] * pv * dt_cj : 0.0f;
+            colsum[sl] += rv;
+            rowtot[half][r] += rv;
           }
-          rowpart[half] += rsum;
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, 0.0f);
         }
       }
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) {
-        Frag<T> fb;
-        frag_load2(fb, &DYts[bf][tp * 16 + c][4 * q], &DYts[bf][tp * 16 + c][16 + 4 * q]);
-        mma(adx[sl][tp], fa, fb);
-      }
+      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], fdt[tp], fa);
     }
+
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const float sq = sum_q(rowpart[half]);
-      if (q == 0) rowacc[wave][16 * (2 * s + half) + c] += sq;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = sum16(rowtot[half][r]);
+        if (c == r) rowacc[wave][rb + 16 * half + 4 * q + r] = v;
+      }
     }
-    if (s + 1 < NS) slab_store(bf ^ 1);
+    // next slab into the other buffer (its last readers passed the previous barrier)
+    if (it + 1 < NS) slab_store(bf ^ 1);
+
+    // column tiles whose rows are in this slab are complete: dx, <dxt_j, x_j>, column sums
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const int J = Js[sl];
+      if ((J >> 1) != s) continue;
+      const int j = 16 * J + c;
+      const float csum = sum_q(colsum[sl]);
+      const float dtj = dts[j];
+      T* dxr = dx + ((row0 + j) * H + h) * P;
+      float xd = 0.0f;
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        const V4 dv = *reinterpret_cast<const V4*>(&DY[j][16 * tp + 4 * q]);
+        V4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xv = frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
+          const float dyv = to_f(dv[r]);
+          xd += adx[sl][tp][r] * xv;
+          dd += dyv * xv;
+          o[r] = from_f<T>(dtj * adx[sl][tp][r] + Dh * dyv);
+        }
+        *reinterpret_cast<V4*>(dxr + 16 * tp + 4 * q) = o;
+      }
+      xd = sum_q(xd);
+      if (q == 0) {
+        part[NSPLIT * Q + j] = csum;
+        part[(NSPLIT + 2) * Q + j] = xd;
+      }
+    }
     __syncthreads();
   }
 
-  // per owned column tile: column sums, ddt (direct part), dx, and this wave's share of sum <dy, x>
-  float dd = 0.0f;
+  // this split's row sums (fixed wave order) and scalars
+  for (int i = threadIdx.x; i < Q; i += NTH) {
+    float v = 0.0f;
 #pragma unroll
-  for (int sl = 0; sl < NSLOT; ++sl) {
-    const int J = Js[sl];
-    const int cj = 16 * J + c;
-    const float cs_sum = sum_q(colsum[sl]) * dts[cj];
-    if (q == 0) colacc[cj] = cs_sum;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
-      const int p = tp * 16 + c;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * J + 4 * q + r;
-        const float xv = to_f(xh[(int64_t)j * rs + p]);
-        const float dv = to_f(dyh[(int64_t)j * rs + p]);
-        part[r] += adx[sl][tp][r] * xv;
-        dd += dv * xv;
-        dx[((row0 + j) * H + h) * P + p] = from_f<T>(dts[j] * adx[sl][tp][r] + Dh * dv);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sq = sum16(part[r]);
-      if (c == 0) ddtd[16 * J + 4 * q + r] = sq;
-    }
+    for (int w = 0; w < NW; ++w) v += rowacc[w][i];
+    part[split * Q + i] = v;
   }
-
-  // <Gk, Hin_k>
-  float gh = 0.0f;
-  for (int e = threadIdx.x; e < P * N; e += NTH) gh += to_f(Gs[e / N][e % N]) * to_f(Hs[e / N][e % N]);
   gh = wave_sum(gh);
   dd = wave_sum(dd);
   if (l == 0) { red[wave] = gh; red[NW + wave] = dd; }
   __syncthreads();
-
-  // assemble dcs, reverse cumsum, ddt, partial dA / dD (wave 0)
-  if (wave == 0) {
+  if (threadIdx.x == 0) {
     float ghs = 0.0f, dds = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) { ghs += red[w]; dds += red[NW + w]; }
-    // dl_j = sum_{i >= j} (row sum_i - column sum_i)  [suffix sum]
-    //      + sum_{j' < j} q_j'                          [exclusive prefix sum]
-    //      + exp(cs_{Q-1}) <Gk, Hin_k>
-    // (the q terms, added at the chunk end and subtracted at each token, are
-    // summed directly as a prefix so no large terms cancel)
-    float v[TPL], qp[TPL];
+    float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
+    if (split == 0) sc[0] = ghs;
+    sc[1 + split] = dds;
+  }
+}
+
+// dl, ddt and the chunk's dA / dD partials from the per-token partial sums of
+// k_chunk_scan_bwd; one wave per (b, k, h), Q / 64 consecutive tokens per lane:
+//   dl_j = sum_{i >= j} (row sum_i - column sum_i)  [suffix sum]
+//        + sum_{j' < j} q_j'                          [exclusive prefix sum]
+//        + exp(cs_{Q-1}) <Gk, Hin_k>
+// (the q terms, added at the chunk end and subtracted at each token, are
+// summed directly as a prefix so no large terms cancel), then
+//   ddt_j = A dl_j + <dxt_j, x_j>,  dA partial = sum_j dt_j dl_j.
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
+                                                     const float* __restrict__ cs_g, const T* __restrict__ dt,
+                                                     const float* __restrict__ Ap, T* __restrict__ ddt,
+                                                     float* __restrict__ dapart, float* __restrict__ ddpart,
+                                                     int nitems, int L, int H, int K) {
+  constexpr int NSPLIT = scan_bwd_splits(Q);
+  constexpr int TPL = Q / kWave;
+  const int bkh = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (bkh >= nitems) return;  // whole wave; no workgroup barrier below
+  const int l = lane_id();
+  const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
+  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;
+  const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
+  float v[TPL], qp[TPL];
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      const int i = l * TPL + t;
-      float rsum = 0.0f;
+  for (int t = 0; t < TPL; ++t) {
+    const int i = l * TPL + t;
+    float rsum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) rsum += rowacc[w][i];
-      v[t] = rsum - colacc[i];
-      qp[t] = qv[i];
-    }
+    for (int sp = 0; sp < NSPLIT; ++sp) rsum += part[sp * Q + i];
+    v[t] = rsum - part[NSPLIT * Q + i];
+    qp[t] = part[(NSPLIT + 1) * Q + i];
+  }
 #pragma unroll
-    for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
-    float qrun = 0.0f;  // exclusive prefix of q inside this lane's tokens
+  for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
+  float qrun = 0.0f;  // exclusive prefix of q inside this lane's tokens
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      const float qt = qp[t];
-      qp[t] = qrun;
-      qrun += qt;
-    }
-    const float incl = wave_inclusive_suffix(v[0]);
-    float excl = __shfl_down(incl, 1, kWave);
-    if (l == kWave - 1) excl = 0.0f;
-    const float qincl = wave_inclusive_scan(qrun);
-    const float qexcl = qincl - qrun;
-    const float tail = __expf(cs_last) * ghs;
-    const float Ah = Ap[h];
-    float da = 0.0f;
+  for (int t = 0; t < TPL; ++t) {
+    const float qt = qp[t];
+    qp[t] = qrun;
+    qrun += qt;
+  }
+  const float incl = wave_inclusive_suffix(v[0]);
+  float excl = __shfl_down(incl, 1, kWave);
+  if (l == kWave - 1) excl = 0.0f;
+  const float qincl = wave_inclusive_scan(qrun);
+  const float qexcl = qincl - qrun;
+  const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+  const float tail = __expf(csc[Q - 1]) * sc[0];
+  const float Ah = Ap[h];
+  float da = 0.0f;
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      const int j = l * TPL + t;
-      const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
-      da += dts[j] * dl;
-      ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + ddtd[j]);
-    }
-    da = wave_sum(da);
-    if (l == 0) {
-      dapart[bkh] = da;
-      ddpart[bkh] = dds;
-    }
+  for (int t = 0; t < TPL; ++t) {
+    const int j = l * TPL + t;
+    const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
+    da += to_f(dt[(row0 + j) * H + h]) * dl;
+    ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + part[(NSPLIT + 2) * Q + j]);
+  }
+  da = wave_sum(da);
+  if (l == 0) {
+    float dds = 0.0f;
+#pragma unroll
+    for (int sp = 0; sp < NSPLIT; ++sp) dds += sc[1 + sp];
+    dapart[bkh] = da;
+    ddpart[bkh] = dds;
   }
 }
 
@@ -837,10 +910,12 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
-    k_chunk_scan_bwd<T, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.A, a.D, B, C, hin, gst, static_cast<const T*>(a.wf), w, dy, static_cast<T*>(a.dx),
-        static_cast<T*>(a.ddt),
-        a.dapart, a.ddpart, L, H, G, K);
+    const int nitems = b * K * H;
+    const int groups = (nitems + 7) / 8;
+    k_chunk_scan_bwd<T, Q, P, N><<<dim3(groups * 8 * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
+        x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, L, H, G, K);
+    k_dl_assemble<T, Q><<<dim3((nitems + 3) / 4), dim3(256), 0, st>>>(
+        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, nitems, L, H, K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int64_t nbc = (int64_t)b * L * G * N;  // elements of dB / dC

@@ -171,10 +171,19 @@ __device__ __forceinline__ float wave_inclusive_suffix(float v) {
   }
   return v;
 }
-// Sum over the 16 lanes sharing lane / 16 (result valid in every lane).
+// Register-only lane move inside each row of 16 lanes (a DPP operand).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// Sum over the 16 lanes sharing lane / 16 (result valid in every lane):
+// neighbours inside quads, the two pairs of each quad (quad_perm), the two
+// quads of each half-row (row_half_mirror), the two half-rows (row_mirror).
 __device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, kWave);
+  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
   return v;
 }
 // Sum over the 4 lanes sharing lane % 16 (lanes l, l^16, l^32, l^48).

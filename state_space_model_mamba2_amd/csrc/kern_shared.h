@@ -25,6 +25,23 @@ __device__ __forceinline__ void frag_load_k(Frag<T>& f, const T* row, int k0) {
   else frag_zero(f);
 }
 
+// Chained-mapping fragment of a row (K-values k0 + 4q + s for s < 4 and
+// k0 + 16 + 4q + s - 4 for s >= 4); with KD = 16 the second run is zero.
+template <int KD, typename T>
+__device__ __forceinline__ void frag_load_chained(Frag<T>& f, const T* row, int k0, int q) {
+  if constexpr (KD % 32 == 0) {
+    frag_load2(f, row + k0 + 4 * q, row + k0 + 16 + 4 * q);
+  } else {
+    static_assert(KD == 16, "K extent must be 16 or a multiple of 32");
+    const typename Vec4<T>::type a = *reinterpret_cast<const typename Vec4<T>::type*>(row + k0 + 4 * q);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      frag_set<T>(f, s, to_f(a[s]));
+      frag_set<T>(f, s + 4, 0.0f);
+    }
+  }
+}
+
 // Index of the lower-triangle 16x16 tile (I, J), J <= I.
 __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 

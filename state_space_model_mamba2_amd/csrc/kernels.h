@@ -20,7 +20,8 @@ struct Layout {
   // forward scratch
   size_t s_off, fwd_bytes;
   // backward scratch
-  size_t w_off, dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, bwd_bytes;
+  size_t w_off, dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, dlpart_off, dlscal_off,
+      bwd_bytes;
   int64_t nslice;  // head slices of the group-level backward kernels
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
 };
@@ -52,7 +53,13 @@ struct BwdArgs {
   float* dbpart;   // [nslice][b][L][G][N] fp32 partials of dB
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
+  float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
+  float* dlscal;   // [b][K][H][scan_bwd_splits(Q) + 1]: <Gk, Hin_k> and per-split sum <dy, x>
 };
+
+// Workgroups that share one (batch, chunk, head) in the backward chunk kernel
+// (each owns an interleaved half of the chunk's 16-token column tiles).
+constexpr int scan_bwd_splits(int Q) { return Q >= 256 ? Q / 128 : 1; }
 
 // Kernel timing hook (see ssd_probe in the public header).
 struct ProbeScope {
