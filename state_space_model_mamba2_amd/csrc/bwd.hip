@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
     for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (u < CPIECES) cv[n] = *reinterpret_cast<const V*>(ch + (int64_t)(SR * s + u / CUN) * G * N + (u % CUN) * VN);
+      if (CPIECES % NTH == 0 || u < CPIECES)
+        cv[n] = *reinterpret_cast<const V*>(ch + (int64_t)(SR * s + u / CUN) * G * N + (u % CUN) * VN);
     }
 #pragma unroll
     for (int n = 0; n < WPT; ++n) {
@@ -117,40 +118,44 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       const int t = u / (256 / VN), piece = u % (256 / VN);
       const int half = t / (NW * NSLOT), w = (t / NSLOT) % NW, sl = t % NSLOT;
       const int I = 2 * s + half, J = tile_of(w, sl);
-      if (u < WPIECES && J <= I) wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J) * 256 + piece * VN);
+      // tiles with J > I are never read: load the in-range tile (I, I) instead, so
+      // the loads carry no branch
+      if (WPIECES % NTH == 0 || u < WPIECES)
+        wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + piece * VN);
     }
   };
   auto slab_store = [&](int bf) {
 #pragma unroll
     for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (u < CPIECES) *reinterpret_cast<V*>(&Cs[bf][u / CUN][(u % CUN) * VN]) = cv[n];
+      if (CPIECES % NTH == 0 || u < CPIECES) *reinterpret_cast<V*>(&Cs[bf][u / CUN][(u % CUN) * VN]) = cv[n];
     }
 #pragma unroll
     for (int n = 0; n < WPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (u < WPIECES) *reinterpret_cast<V*>(&Ws[bf][u * VN]) = wv[n];
+      if (WPIECES % NTH == 0 || u < WPIECES) *reinterpret_cast<V*>(&Ws[bf][u * VN]) = wv[n];
     }
   };
 
-  // ---- prologue: per-token scalars, dy, the last slab, x and the state operands
+  // ---- prologue.  Every global load of the prologue is issued first, in one
+  // straight-line block, so they are all in flight together; LDS stores and
+  // products follow.
+  constexpr int QPT = (Q + NTH - 1) / NTH;
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-  for (int i = threadIdx.x; i < Q; i += NTH) {
-    cs[i] = csc[i];
-    dts[i] = to_f(dt[(row0 + i) * H + h]);
+  float csv[QPT], dtv[QPT];
+#pragma unroll
+  for (int n = 0; n < QPT; ++n) {
+    const int i = threadIdx.x + NTH * n;
+    if (Q % NTH == 0 || i < Q) {
+      csv[n] = csc[i];
+      dtv[n] = to_f(dt[(row0 + i) * H + h]);
+    }
   }
-  {
-    V yv[YPT];
+  V yv[YPT];
 #pragma unroll
-    for (int n = 0; n < YPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (u < YPIECES) yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(u / CUP) * rs + (u % CUP) * VN);
-    }
-#pragma unroll
-    for (int n = 0; n < YPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (u < YPIECES) *reinterpret_cast<V*>(&DY[u / CUP][(u % CUP) * VN]) = yv[n];
-    }
+  for (int n = 0; n < YPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (YPIECES % NTH == 0 || u < YPIECES) yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(u / CUP) * rs + (u % CUP) * VN);
   }
   slab_load(NS - 1);
   Frag<T> xf[NSLOT][NKP];
@@ -163,32 +168,52 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   Frag<T> hf[NK];
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(hf[ks], hinh + (16 * tw + c) * N, ks * 32 + 8 * q);
+  Frag<T> gf[NK][TP], bfr[NK][NSLOT];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) frag_load_k<N>(gf[ks][tp], gsth + (16 * tp + c) * N, ks * 32 + 8 * q);
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl)
+      frag_load_k<N>(bfr[ks][sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
+  }
 
-  // state part of dxt^T: e_j (Gk B_j^T) with K = dstate; <Gk, Hin> (split 0)
+  // LDS stores of the per-token scalars and dy (their loads were issued first)
+#pragma unroll
+  for (int n = 0; n < QPT; ++n) {
+    const int i = threadIdx.x + NTH * n;
+    if (Q % NTH == 0 || i < Q) {
+      cs[i] = csv[n];
+      dts[i] = dtv[n];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < YPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[u / CUP][(u % CUP) * VN]) = yv[n];
+  }
+
+  // state part of dxt^T: e_j (Gk B_j^T) with K = dstate
   f4 adx[NSLOT][TP];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl)
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) adx[sl][tp] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl)
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], gf[ks][tp], bfr[ks][sl]);
+  // <Gk, Hin>: waves 0 .. TP-1 of split 0 each cover Hin rows 16 tp .. 16 tp + 15
   float gh = 0.0f;
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    Frag<T> gf[TP], bfr[NSLOT];
+  for (int tp = 0; tp < TP; ++tp) {
+    if (split != 0 || tp != wave) continue;
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) frag_load_k<N>(gf[tp], gsth + (16 * tp + c) * N, ks * 32 + 8 * q);
+    for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl)
-      frag_load_k<N>(bfr[sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
-#pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl)
-#pragma unroll
-      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], gf[tp], bfr[sl]);
-#pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
-      if (split != 0 || tp != wave) continue;  // waves 0 .. TP-1 of split 0 cover Hin rows 16 tp ..
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) gh += frag_get(gf[tp], s8) * frag_get(hf[ks], s8);
-    }
+      for (int s8 = 0; s8 < 8; ++s8) gh += frag_get(gf[ks][tp], s8) * frag_get(hf[ks], s8);
   }
   slab_store(0);
   __syncthreads();
@@ -259,15 +284,57 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         fdt[tp].v[s8] = DY[rb + (s8 < 4 ? 4 * q + s8 : 16 + 4 * q + s8 - 4)][16 * tp + c];
     }
 
-    // intra-chunk pairs (I in this slab, J owned), I >= J
+    // intra-chunk pairs (I in this slab, J owned), I >= J.
+    // Column tiles wholly before the slab ("full" pairs, the common case):
+    // both row tiles lie after every column, so no mask is needed and the
+    // decay factors at the slab's first row rb:
+    //   Lam_ij = exp(cs_i - cs_rb) exp(cs_rb - cs_j),  both factors <= 1
+    // (cs does not increase along the chunk).  Tiles J = 2s, 2s + 1 hold the
+    // diagonal and take the masked direct form.
+    float arow[2][4];                        // exp(cs_i - cs_rb), rows of this lane
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl) {
+    for (int half = 0; half < 2; ++half) {
+      const f4 csi = *reinterpret_cast<const f4*>(&cs[rb + 16 * half + 4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) arow[half][r] = __expf(csi[r] - cs[rb]);
+    }
+    auto full_pair = [&](int sl) {
+      const int cj = 16 * Js[sl] + c;
+      const float bj = __expf(cs[rb] - cs[cj]);
+      const float bdt = bj * dts[cj];
+      f4 dp[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        dp[half] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) {
+          Frag<T> fd;
+          frag_load_chained<P>(fd, &DY[rb + 16 * half + c][0], kp * 32, q);
+          mma(dp[half], fd, xf[sl][kp]);     // lane: column j = cj, rows i = rb + 16 half + 4q + r
+        }
+      }
+      Frag<T> fa;                            // P[i][j] as the B operand (col j, K = i)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const V4 wt = *reinterpret_cast<const V4*>(&Ws[bf][((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = to_f(wt[r]) * arow[half][r];
+          frag_set<T>(fa, half * 4 + r, t * bj);
+          const float rv = dp[half][r] * t * bdt;   // the same value enters both sums
+          colsum[sl] += rv;
+          rowtot[half][r] += rv;
+        }
+      }
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], fdt[tp], fa);
+    };
+    auto diag_pair = [&](int sl) {
       const int J = Js[sl];
-      if (J > 2 * s + 1) continue;
       const int cj = 16 * J + c;             // lane's column j
       const float cs_cj = cs[cj];
       const float dt_cj = dts[cj];
-      Frag<T> fa;                            // P[i][j] as the B operand (col j, K = i)
+      Frag<T> fa;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int I = 2 * s + half;
@@ -277,7 +344,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
           for (int kp = 0; kp < NKP; ++kp) {
             Frag<T> fd;
             frag_load_chained<P>(fd, &DY[16 * I + c][0], kp * 32, q);
-            mma(dp, fd, xf[sl][kp]);         // lane: column j = cj, rows i = 16I + 4q + r
+            mma(dp, fd, xf[sl][kp]);
           }
           const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
@@ -287,6 +354,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
             const float pv = to_f(wt[r]) * lam;
             frag_set<T>(fa, half * 4 + r, pv);
+            // the diagonal R_jj enters a row sum and a column sum with opposite
+            // signs and cancels exactly, so it is left out of both
             const float rv = (i0 + r > cj) ? dp[r] * pv * dt_cj : 0.0f;
             colsum[sl] += rv;
             rowtot[half][r] += rv;
@@ -298,7 +367,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       }
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], fdt[tp], fa);
+    };
+    if constexpr (NSLOT == 2) {
+      const bool f0 = Js[0] < 2 * s, f1 = Js[1] < 2 * s;
+      if (f0 && f1) {                        // one straight-line block for both slots
+        full_pair(0);
+        full_pair(1);
+      } else if (f0) {
+        full_pair(0);
+      } else if (f1) {
+        full_pair(1);
+      }
+    } else {
+      if (Js[0] < 2 * s) full_pair(0);
     }
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl)
+      if ((Js[sl] >> 1) == s) diag_pair(sl);
 
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
