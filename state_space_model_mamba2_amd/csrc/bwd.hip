@@ -722,119 +722,65 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
 }
 
 // ---------------------------------------------------------------------------
-// dC / dB for one (b, k, g) and one 64-row block RB of the chunk:
-//   dC_i = sum_{h in g} exp(cs_i) Hin_k^T dy_i + sum_{j <= i} dW_ij B_j
-//   dB_j = sum_{h in g} e_j dt_j Gk^T x_j      + sum_{i >= j} dW_ij C_i
-// The head sums are one product with K = (head, headdim): the rows (dy or x,
-// pre-scaled) and the transposed state of HS heads are staged per step
-// through two LDS buffers (each thread loads the next step into registers
-// while the current step's products run).  blockIdx.z selects a slice of hps
-// heads; every slice writes an fp32 partial, and slice 0 also adds the dW
-// part: the dW rows (or columns), summed over the dW slices in a fixed
-// order, and B (or C) are staged and multiplied with K = tokens.
+// Head sums of dC / dB for one (b, k, g), one 64-row block RB of the chunk
+// and one slice of hps heads (blockIdx.z):
+//   dC: part[i][n] = sum_{h in slice} exp(cs_i) sum_p dy_i[p] Hin_k[p][n]
+//   dB: part[j][n] = sum_{h in slice} e_j dt_j  sum_p x_j[p]  Gk[p][n]
+// One product per head with K = headdim on the matrix cores.  Each wave
+// owns 16 rows: their dy (or x) fragments come straight from global memory
+// (K = headdim is contiguous there) and take the row's scale in registers;
+// the head's state is staged row-major in LDS (double-buffered, the next
+// head is loaded into registers while the current one is used) and read
+// K-major with the transposing LDS read.  Every slice writes an fp32
+// partial; k_bc_final adds the slices and the dW part.
 template <typename T, int Q, int P, int N, bool DB>
-__global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* __restrict__ dt,
-                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                             const T* __restrict__ state, const float* __restrict__ dw,
-                                             const T* __restrict__ M, float* __restrict__ out,
-                                             int L, int H, int G, int K, int hps, int nslice_dw) {
-  constexpr int HS = sizeof(T) == 2 ? 2 : 1;  // heads per step (fp32 staging would not fit two)
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int PP = P < 32 ? 32 : P;  // K extent per head, padded to a 32-step
-  constexpr int RP = PP + PAD;
-  constexpr int TN = N / 16;
+__global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const T* __restrict__ dt,
+                                                  const float* __restrict__ cs_g, const T* __restrict__ dy,
+                                                  const T* __restrict__ state, float* __restrict__ out,
+                                                  int L, int H, int G, int K, int hps) {
+  constexpr int NTH = 256;
+  constexpr int TN = N / 16, NKP = (P + 31) / 32;
   constexpr int VN = Vec16<T>::n;
+  constexpr int SP = N + 16;                 // state row pitch (8 mod 16 dwords for N = 64, 128)
+  constexpr int SPIECES = P * N / VN;
+  constexpr int SPT = (SPIECES + NTH - 1) / NTH;
+  static_assert(P == 16 || P % 32 == 0, "headdim");
   typedef typename Vec16<T>::type V;
-  typedef typename Vec4<T>::type V4;
-  // phase 1 buffers: As[2][HS][64][RP], Ss[2][HS][N][RP]; phase 2: Ws[64][Q+PAD], Mt[N][Q+PAD]
-  constexpr size_t PH1 = sizeof(T) * 2 * HS * (64 + N) * RP;
-  constexpr size_t PH2 = sizeof(T) * (64 * (Q + PAD) + N * (Q + PAD));
-  constexpr size_t LDSB = PH1 > PH2 ? PH1 : PH2;
-  static_assert(LDSB <= 160 * 1024, "LDS exceeds 160 KiB");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDSB];
-  T* As = reinterpret_cast<T*>(lds);
-  T* Ss = As + 2 * HS * 64 * RP;
-  auto A_at = [&](int bf, int hs, int r) { return As + ((bf * HS + hs) * 64 + r) * RP; };
-  auto S_at = [&](int bf, int hs, int n) { return Ss + ((bf * HS + hs) * N + n) * RP; };
+  __shared__ __attribute__((aligned(16))) T Ss[2][P][SP];
 
   const int bkg = blockIdx.x, RB = blockIdx.y;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
-  const int r0 = 64 * RB;
   const int hpg = H / G;
   const int h0 = g * hpg + blockIdx.z * hps;
   const int nh = min(hps, hpg - (int)blockIdx.z * hps);
-  const int nstage = (nh + HS - 1) / HS;
+  const int i = 64 * RB + 16 * wave + c;     // this lane's row (A operand)
+  const T* U = DB ? x : dy;
 
-  if (P < 32) {
-    for (int e = threadIdx.x; e < (int)(PH1 / sizeof(T)); e += 256) As[e] = from_f<T>(0.0f);
-  }
-
-  // per step: rows (64 x P, 16-byte pieces) and state units (4 state rows p x 16 bytes of n)
-  constexpr int RU = 64 * (P / VN);            // row pieces per head
-  constexpr int SU = (P / 4) * (N / VN);       // state units per head
-  constexpr int RPT = (HS * RU + 255) / 256;
-  constexpr int SPT = (HS * SU + 255) / 256;
-  V rv[RPT];
-  float rsc[RPT];
-  V sv[SPT][4];
-
-  auto load = [&](int st) {
-#pragma unroll
-    for (int n = 0; n < RPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      rsc[n] = 0.0f;
-      if (u >= HS * RU) continue;
-      const int hs = u / RU, rem = u % RU, r = rem / (P / VN), cu = rem % (P / VN);
-      const int hh = st * HS + hs;
-      if (hh >= nh) continue;
-      const int h = h0 + hh;
-      const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-      const int i = r0 + r;
-      rv[n] = *reinterpret_cast<const V*>((DB ? x : dy) + ((row0 + i) * H + h) * P + cu * VN);
-      rsc[n] = DB ? __expf(csb[Q - 1] - csb[i]) * to_f(dt[(row0 + i) * H + h]) : __expf(csb[i]);
-    }
+  // registers of the head in flight
+  V sv[SPT];
+  Frag<T> av[NKP];
+  float ascale = 0.0f;
+  auto load = [&](int hh) {
+    const int h = h0 + hh;
+    const T* st = state + (((int64_t)b * K + k) * H + h) * P * N;
 #pragma unroll
     for (int n = 0; n < SPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      if (u >= HS * SU) continue;
-      const int hs = u / SU, rem = u % SU, p4 = rem / (N / VN), cu = rem % (N / VN);
-      const int hh = st * HS + hs;
-      if (hh >= nh) continue;
-      const int h = h0 + hh;
-      const T* sp = state + (((int64_t)b * K + k) * H + h) * P * N + (int64_t)(4 * p4) * N + cu * VN;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sv[n][rr] = *reinterpret_cast<const V*>(sp + rr * N);
+      const int u = threadIdx.x + NTH * n;
+      if (SPIECES % NTH == 0 || u < SPIECES) sv[n] = *reinterpret_cast<const V*>(st + u * VN);
     }
+    const T* urow = U + ((row0 + i) * H + h) * P;
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], urow, kp * 32, q);
+    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+    ascale = DB ? __expf(csb[Q - 1] - csb[i]) * to_f(dt[(row0 + i) * H + h]) : __expf(csb[i]);
   };
   auto store = [&](int bf) {
 #pragma unroll
-    for (int n = 0; n < RPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      if (u >= HS * RU) continue;
-      const int hs = u / RU, rem = u % RU, r = rem / (P / VN), cu = rem % (P / VN);
-      T* d = A_at(bf, hs, r) + cu * VN;
-#pragma unroll
-      for (int e0 = 0; e0 < VN; e0 += 4) {
-        V4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = from_f<T>(to_f(rv[n][e0 + e]) * rsc[n]);
-        *reinterpret_cast<V4*>(d + e0) = w;
-      }
-    }
-#pragma unroll
     for (int n = 0; n < SPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      if (u >= HS * SU) continue;
-      const int hs = u / SU, rem = u % SU, p4 = rem / (N / VN), cu = rem % (N / VN);
-#pragma unroll
-      for (int e = 0; e < VN; ++e) {
-        V4 w;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) w[rr] = sv[n][rr][e];
-        *reinterpret_cast<V4*>(S_at(bf, hs, cu * VN + e) + 4 * p4) = w;
-      }
+      const int u = threadIdx.x + NTH * n;
+      if (SPIECES % NTH == 0 || u < SPIECES) *reinterpret_cast<V*>(&Ss[bf][u / (N / VN)][(u % (N / VN)) * VN]) = sv[n];
     }
   };
 
@@ -842,108 +788,124 @@ __global__ __launch_bounds__(256) void k_dbc(const T* __restrict__ x, const T* _
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) acc[tn] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // phase 1: head sums (K = head x headdim)
-  if (P < 32) __syncthreads();
   load(0);
   store(0);
-  for (int st = 0; st < nstage; ++st) {
-    const int bf = st & 1;
-    __syncthreads();
-    if (st + 1 < nstage) load(st + 1);
-    for (int hs = 0; hs < HS; ++hs) {
-      if (st * HS + hs >= nh) break;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int bf = hh & 1;
+    // the current head's row fragments, scaled
+    Frag<T> fa[NKP];
 #pragma unroll
-      for (int kp = 0; kp < PP / 32; ++kp) {
-        Frag<T> fa;
-        frag_load(fa, A_at(bf, hs, 16 * wave + c) + kp * 32 + 8 * q);
+    for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          Frag<T> fb;
-          frag_load(fb, S_at(bf, hs, 16 * tn + c) + kp * 32 + 8 * q);
-          mma(acc[tn], fa, fb);
-        }
-      }
-    }
-    if (st + 1 < nstage) store(bf ^ 1);
-  }
-  __syncthreads();
-
-  // phase 2 (slice 0 only): dW part (K = tokens)
-  if (blockIdx.z == 0) {
-    T* Ws = reinterpret_cast<T*>(lds);   // [64][Q + PAD]
-    T* Mt = Ws + 64 * (Q + PAD);         // [N][Q + PAD]
-    const float* dwb = dw + (int64_t)bkg * Q * Q;
-    const int64_t dws = (int64_t)gridDim.x * Q * Q;  // stride between dW slices
-    const int kb0 = DB ? r0 : 0;             // first token of the K range
-    const int kr = DB ? Q - r0 : r0 + 64;    // K range length (multiple of 64)
-    if (!DB) {
-      // Ws[r][j] = sum_s dW_s[r0 + r][j], j < kr
-      for (int u = threadIdx.x; u < 64 * (kr / 4); u += 256) {
-        const int r = u / (kr / 4), j4 = (u % (kr / 4)) * 4;
-        f4 v = *reinterpret_cast<const f4*>(dwb + (int64_t)(r0 + r) * Q + j4);
-        for (int sl = 1; sl < nslice_dw; ++sl) v += *reinterpret_cast<const f4*>(dwb + sl * dws + (int64_t)(r0 + r) * Q + j4);
-        V4 w;
+      for (int s8 = 0; s8 < 8; ++s8) frag_set<T>(fa[kp], s8, frag_get(av[kp], s8) * ascale);
+    __syncthreads();  // head hh is in buffer bf; buffer bf ^ 1 is no longer read
+    if (hh + 1 < nh) load(hh + 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = from_f<T>(v[e]);
-        *reinterpret_cast<V4*>(Ws + r * (Q + PAD) + j4) = w;
-      }
-    } else {
-      // Ws[j][i - r0] = sum_s dW_s[i][r0 + j], i in [r0, Q)
-      for (int u = threadIdx.x; u < (kr / 4) * 16; u += 256) {
-        const int i4 = (u / 16) * 4, j4 = (u % 16) * 4;
-        f4 v[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) v[rr] = *reinterpret_cast<const f4*>(dwb + (int64_t)(r0 + i4 + rr) * Q + r0 + j4);
-        for (int sl = 1; sl < nslice_dw; ++sl) {
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            v[rr] += *reinterpret_cast<const f4*>(dwb + sl * dws + (int64_t)(r0 + i4 + rr) * Q + r0 + j4);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          V4 w;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) w[rr] = from_f<T>(v[rr][e]);
-          *reinterpret_cast<V4*>(Ws + (j4 + e) * (Q + PAD) + i4) = w;
-        }
-      }
-    }
-    stage_transposed<T, T, N, 256>(Mt, Q + PAD, M + ((row0 + kb0) * G + g) * N, (int64_t)G * N, kr, nullptr);
-    __syncthreads();
-    for (int ks = 0; ks < kr / 32; ++ks) {
-      Frag<T> fa;
-      frag_load(fa, Ws + (16 * wave + c) * (Q + PAD) + ks * 32 + 8 * q);
+    for (int kp = 0; kp < NKP; ++kp) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
         Frag<T> fb;
-        frag_load(fb, Mt + (16 * tn + c) * (Q + PAD) + ks * 32 + 8 * q);
-        mma(acc[tn], fa, fb);
+        frag_load_kmajor<P>(fb, &Ss[bf][0][0], SP, kp * 32, 16 * tn, q, c);
+        mma(acc[tn], fa[kp], fb);
       }
     }
+    if (hh + 1 < nh) store(bf ^ 1);
   }
   float* o = out + (int64_t)blockIdx.z * gridDim.x * Q * N;  // slice stride b*K*G*Q*N = b*L*G*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 16 * wave + 4 * q + r;
+      const int row = 64 * RB + 16 * wave + 4 * q + r;
       o[((row0 + row) * G + g) * N + 16 * tn + c] = acc[tn][r];
     }
   }
 }
 
-// out[e] = sum_s part[s][e] in slice order, converted to the storage dtype.
-template <typename T>
-__global__ __launch_bounds__(256) void k_sum_slices(const float* __restrict__ part, T* __restrict__ out,
-                                                    int64_t n, int nslice) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= n) return;
-  f4 v = *reinterpret_cast<const f4*>(part + e);
-  for (int sl = 1; sl < nslice; ++sl) v += *reinterpret_cast<const f4*>(part + sl * n + e);
-  typename Vec4<T>::type w;
+// ---------------------------------------------------------------------------
+// dC / dB for one (b, k, g) and one 64-row block RB: the head-slice partials
+// summed in slice order, plus the dW part
+//   dC_i = ... + sum_{j <= i} dW_ij B_j        dB_j = ... + sum_{i >= j} dW_ij C_i
+// with dW the fixed-order sum of its head-slice partials.  K = tokens, in
+// 64-token blocks: the dW block (converted to the storage type) and the B
+// (or C) rows are staged row-major in LDS; dC reads dW rows directly, dB reads
+// them K-major, and B / C are read K-major (transposing LDS read).
+template <typename T, int Q, int N, bool DB>
+__global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part, const float* __restrict__ dw,
+                                                  const T* __restrict__ M, T* __restrict__ out, int L, int G,
+                                                  int K, int nslice, int nslice_dw) {
+  constexpr int NTH = 256;
+  constexpr int TN = N / 16, NB = Q / 64;
+  constexpr int VN = Vec16<T>::n;
+  constexpr int WP = 64 + 16, MP = N + 16;   // row pitches (8 mod 16 dwords)
+  constexpr int MPIECES = 64 * N / VN;
+  constexpr int MPT = (MPIECES + NTH - 1) / NTH;
+  typedef typename Vec16<T>::type V;
+  __shared__ __attribute__((aligned(16))) T Wb[64][WP];
+  __shared__ __attribute__((aligned(16))) T Ms[64][MP];
+
+  const int bkg = blockIdx.x, RB = blockIdx.y;
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int r0 = 64 * RB;
+  const int64_t dws = (int64_t)gridDim.x * Q * Q;  // dW slice stride
+  const float* dwb = dw + (int64_t)bkg * Q * Q;
+
+  f4 acc[TN];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
-  *reinterpret_cast<typename Vec4<T>::type*>(out + e) = w;
+  for (int tn = 0; tn < TN; ++tn) acc[tn] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int kb0 = DB ? RB : 0, kb1 = DB ? NB - 1 : RB;
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    // dW block: rows i, columns j (dC: i in RB, j in kb; dB: i in kb, j in RB)
+    const int ib = DB ? kb : RB, jb = DB ? RB : kb;
+    for (int e = threadIdx.x * 4; e < 64 * 64; e += NTH * 4) {
+      const int il = e / 64, jl = e % 64;
+      const float* src = dwb + (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
+      f4 v = *reinterpret_cast<const f4*>(src);
+      for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(src + z * dws);
+      typename Vec4<T>::type w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
+      *reinterpret_cast<typename Vec4<T>::type*>(&Wb[il][jl]) = w;
+    }
+    // B rows j (dC) or C rows i (dB) of block kb
+#pragma unroll
+    for (int n = 0; n < MPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (MPIECES % NTH == 0 || u < MPIECES) {
+        const int rr = u / (N / VN), cu = u % (N / VN);
+        *reinterpret_cast<V*>(&Ms[rr][cu * VN]) =
+            *reinterpret_cast<const V*>(M + ((row0 + 64 * kb + rr) * G + g) * N + cu * VN);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      Frag<T> fa;
+      if (DB) frag_load_kmajor<64>(fa, &Wb[0][0], WP, kp * 32, 16 * wave, q, c);   // row j, K = i
+      else frag_load2(fa, &Wb[16 * wave + c][kp * 32 + 4 * q], &Wb[16 * wave + c][kp * 32 + 16 + 4 * q]);
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        Frag<T> fb;
+        frag_load_kmajor<64>(fb, &Ms[0][0], MP, kp * 32, 16 * tn, q, c);
+        mma(acc[tn], fa, fb);
+      }
+    }
+    __syncthreads();
+  }
+  const int64_t ps = (int64_t)gridDim.x * Q * N;  // head-slice partial stride
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t e = ((row0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + 16 * tn + c;
+      float v = part[e];
+      for (int z = 1; z < nslice; ++z) v += part[z * ps + e];
+      out[e] = from_f<T>(v + acc[tn][r]);
+    }
+  }
 }
 
 // Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
@@ -1003,7 +965,6 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, nitems, L, H, K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
-  const int64_t nbc = (int64_t)b * L * G * N;  // elements of dB / dC
   {
     ProbeScope ps(probe, SSD_K_DW, st);
     const int nb = Q / 64;
@@ -1014,15 +975,17 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);
-    k_dbc<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, a.dw, B, a.dcpart, L, H, G, K, hps, S);
-    k_sum_slices<T><<<dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0, st>>>(a.dcpart, static_cast<T*>(a.dC), nbc, S);
+    k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, hin, a.dcpart, L, H, G, K, hps);
+    k_bc_final<T, Q, N, false><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
+        a.dcpart, a.dw, B, static_cast<T*>(a.dC), L, G, K, S, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DB, st);
-    k_dbc<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, gst, a.dw, C, a.dbpart, L, H, G, K, hps, S);
-    k_sum_slices<T><<<dim3((unsigned)((nbc / 4 + 255) / 256)), dim3(256), 0, st>>>(a.dbpart, static_cast<T*>(a.dB), nbc, S);
+    k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, gst, a.dbpart, L, H, G, K, hps);
+    k_bc_final<T, Q, N, true><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
+        a.dbpart, a.dw, C, static_cast<T*>(a.dB), L, G, K, S, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);

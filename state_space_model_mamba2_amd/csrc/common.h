@@ -82,6 +82,37 @@ __device__ __forceinline__ void frag_load2(Frag<float>& f, const float* p0, cons
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
+// Fragment whose K runs down the rows of a row-major LDS tile ("K-major"):
+// lane (q, c) receives tile[k0 + kc(q, s)][col0 + c] for the chained K
+// mapping kc(q, s) = 4q + s (s < 4), 16 + 4q + s - 4 (s >= 4).  With
+// KD = 16 the second run (rows k0 + 16 ..) is zero and never read.
+// bf16 uses the gfx950 transposing LDS read ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane l supplies the address of 4 consecutive values
+// (row k0 + 4q + l/4, columns col0 + 4(l%4) ..) and receives column col0 + l
+// of the group's 4 rows.  Rows must be 8-byte aligned; a row pitch of 8
+// (mod 16) dwords keeps the 16 rows of one read on distinct banks.
+// fp32 has no transposing read and takes eight scalar reads.
+template <int KD>
+__device__ __forceinline__ void frag_load_kmajor(Frag<bf16>& f, const bf16* tile, int pitch, int k0, int col0, int q,
+                                                 int c) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const bf16* a0 = tile + (k0 + 4 * q + (c >> 2)) * pitch + col0 + 4 * (c & 3);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(a0));
+  v4s hi = {0, 0, 0, 0};
+  if constexpr (KD % 32 == 0) hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(a0 + 16 * pitch));
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <int KD>
+__device__ __forceinline__ void frag_load_kmajor(Frag<float>& f, const float* tile, int pitch, int k0, int col0,
+                                                 int q, int c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int k = s < 4 ? 4 * q + s : 16 + 4 * q + s - 4;
+    f.v[s] = (KD % 32 == 0 || s < 4) ? tile[(k0 + k) * pitch + col0 + c] : 0.0f;
+  }
+}
+
 // ---- LDS staging --------------------------------------------------------------
 // 4 consecutive storage elements (one lane's share of an accumulator tile).
 template <typename T> struct Vec4;
