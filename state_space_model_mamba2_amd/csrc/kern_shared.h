@@ -119,18 +119,27 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
 // Chunk state: out[b][k][h][p][n] = sum_i w_i U[kQ+i][h][p] V[kQ+i][g][n]
 //   forward  (BWD = false): U = x,  V = B, w_i = dt_i exp(cs_{Q-1} - cs_i)
 //   backward (BWD = true) : U = dy, V = C, w_i = exp(cs_i)
-// An (P x Q)(Q x N) product on the matrix cores, K = tokens, staged through
-// LDS 64 tokens at a time with both operands transposed so K is contiguous.
+// A (P x Q)(Q x N) product on the matrix cores with K = tokens.  Both
+// operands have K as their outer index in memory, so KB-token blocks of U
+// (rows scaled by w_i on the way) and V are staged row-major in LDS and both
+// fragments are read K-major with the transposing LDS read.  Blocks are
+// double-buffered: the next block is loaded into registers while the
+// current one is used.  One workgroup (4 waves) per (b, k, h).
 template <typename T, int Q, int P, int N, bool BWD>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, const T* __restrict__ V,
                                                      const T* __restrict__ dt, const float* __restrict__ cs,
                                                      float* __restrict__ out, int L, int H, int G, int K) {
-  constexpr int KB = 64;
-  constexpr int PAD = 16 / sizeof(T);
+  constexpr int NTH = 256;
+  constexpr int KB = 32;                           // tokens per block
+  constexpr int NB = Q / KB;
+  constexpr int UP = P + 16, VP = N + 16;          // row pitches (8 mod 16 dwords for 64 / 128 wide rows)
   constexpr int TM = P / 16, TN = N / 16, NT = TM * TN, TPW = (NT + 3) / 4;
-  __shared__ __attribute__((aligned(16))) T Ut[P][KB + PAD];
-  __shared__ __attribute__((aligned(16))) T Vt[N][KB + PAD];
-  __shared__ float w[Q];
+  constexpr int VN = Vec16<T>::n;
+  constexpr int UPIECES = KB * P / VN, VPIECES = KB * N / VN;
+  constexpr int UPT = (UPIECES + NTH - 1) / NTH, VPT = (VPIECES + NTH - 1) / NTH;
+  typedef typename Vec16<T>::type V16;
+  __shared__ __attribute__((aligned(16))) T Us[2][KB][UP];
+  __shared__ __attribute__((aligned(16))) T Vs[2][KB][VP];
 
   const int bkh = blockIdx.x;
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
@@ -139,44 +148,79 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const float* csc = cs + (((int64_t)b * H + h) * K + k) * Q;
   const float cs_last = csc[Q - 1];
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
-    if (BWD) w[i] = __expf(csc[i]);
-    else w[i] = to_f(dt[(row0 + i) * H + h]) * __expf(cs_last - csc[i]);
-  }
-  __syncthreads();
+
+  V16 uv[UPT], vv[VPT];
+  float uw[UPT];
+  auto load = [&](int blk) {
+#pragma unroll
+    for (int n = 0; n < UPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (UPIECES % NTH == 0 || u < UPIECES) {
+        const int i = KB * blk + u / (P / VN);
+        uv[n] = *reinterpret_cast<const V16*>(U + ((row0 + i) * H + h) * P + (u % (P / VN)) * VN);
+        uw[n] = BWD ? __expf(csc[i]) : to_f(dt[(row0 + i) * H + h]) * __expf(cs_last - csc[i]);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < VPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (VPIECES % NTH == 0 || u < VPIECES)
+        vv[n] = *reinterpret_cast<const V16*>(V + ((row0 + KB * blk + u / (N / VN)) * G + g) * N + (u % (N / VN)) * VN);
+    }
+  };
+  auto store = [&](int bf) {
+#pragma unroll
+    for (int n = 0; n < UPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (UPIECES % NTH == 0 || u < UPIECES) {
+        V16 w;
+#pragma unroll
+        for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(uv[n][e]) * uw[n]);
+        *reinterpret_cast<V16*>(&Us[bf][u / (P / VN)][(u % (P / VN)) * VN]) = w;
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < VPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (VPIECES % NTH == 0 || u < VPIECES)
+        *reinterpret_cast<V16*>(&Vs[bf][u / (N / VN)][(u % (N / VN)) * VN]) = vv[n];
+    }
+  };
 
   f4 acc[TPW];
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < Q / KB; ++kb) {
-    stage_transposed<T, T, P, 256>(&Ut[0][0], KB + PAD, U + ((row0 + kb * KB) * H + h) * P, (int64_t)H * P, KB, w + kb * KB);
-    stage_transposed<T, T, N, 256>(&Vt[0][0], KB + PAD, V + ((row0 + kb * KB) * G + g) * N, (int64_t)G * N, KB, nullptr);
-    __syncthreads();
+  load(0);
+  store(0);
+  for (int blk = 0; blk < NB; ++blk) {
+    const int bf = blk & 1;
+    __syncthreads();  // block blk is in buffer bf; buffer bf ^ 1 is no longer read
+    if (blk + 1 < NB) load(blk + 1);
 #pragma unroll
     for (int ks = 0; ks < KB / 32; ++ks) {
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const int j = wave + 4 * u;
+      for (int t = 0; t < TPW; ++t) {
+        const int j = wave + 4 * t;
         if (j < NT) {
           const int tm = j / TN, tn = j % TN;
           Frag<T> fa, fb;
-          frag_load(fa, &Ut[tm * 16 + c][ks * 32 + 8 * q]);
-          frag_load(fb, &Vt[tn * 16 + c][ks * 32 + 8 * q]);
-          mma(acc[u], fa, fb);
+          frag_load_kmajor<32>(fa, &Us[bf][0][0], UP, ks * 32, tm * 16, q, c);
+          frag_load_kmajor<32>(fb, &Vs[bf][0][0], VP, ks * 32, tn * 16, q, c);
+          mma(acc[t], fa, fb);
         }
       }
     }
-    __syncthreads();
+    if (blk + 1 < NB) store(bf ^ 1);
   }
   float* o = out + (int64_t)bkh * P * N;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int j = wave + 4 * u;
+  for (int t = 0; t < TPW; ++t) {
+    const int j = wave + 4 * t;
     if (j < NT) {
       const int tm = j / TN, tn = j % TN;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[u][r];
+      for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[t][r];
     }
   }
 }
