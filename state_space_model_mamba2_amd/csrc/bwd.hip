@@ -549,33 +549,32 @@ __global__ __launch_bounds__(256) void k_tiles_to_bwd(const T* __restrict__ wf, 
 //   dW_ij = sum_{h in g} <dy_i, xt_j> exp(cs_i - cs_j)   (j <= i, else 0)
 // Off-diagonal blocks (IB > JB): every i lies after every j, so with the
 // reference token r = 64 JB + 63 (last of block JB) the decay splits as
-// exp(cs_i - cs_r) exp(cs_r - cs_j), both factors <= 1.  The factors are
-// folded into the operands while they are staged in LDS, so dW_IJ is one
-// product with K = (head, headdim) accumulated on the matrix cores across
-// heads.  Diagonal blocks stage unscaled operands and apply the masked decay
-// per head.  Heads are staged HS at a time through two LDS buffers: each
-// thread loads its share of the next stage into registers, the products of
-// the current stage run, then the registers are written to the other buffer.
-// Wave w owns the block's 16-row tile w and all four 16-column tiles.
+// exp(cs_i - cs_r) exp(cs_r - cs_j), both factors <= 1; the row factor goes
+// onto the dy fragments in registers and the column factor (with dt_j) onto
+// the x rows as they are staged, so dW_IJ is one product with K = (head,
+// headdim) accumulated on the matrix cores across heads.  Diagonal blocks
+// multiply each head's product by the masked decay element-wise.
+// Wave w owns the block's rows 16w .. 16w + 15: their dy fragments come
+// straight from global memory (K = headdim is contiguous there); the head's
+// 64 x rows are staged row-major in LDS once per workgroup (double-buffered,
+// the next head is loaded into registers while the current one is used).
 // blockIdx.z selects a slice of hps heads of the group; each slice writes its
 // own partial dW (summed later in a fixed order).
 template <typename T, int Q, int P, bool DIAG>
 __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __restrict__ dt,
                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
                                             float* __restrict__ dw, int L, int H, int G, int K, int hps) {
-  constexpr int HS = 2;                     // heads per stage
-  constexpr int PP = P < 32 ? 32 : P;       // K extent per head, padded to a 32-step
-  constexpr int PAD = 16 / sizeof(T);
-  constexpr int RP = PP + PAD;              // LDS row pitch
-  constexpr int VN = Vec16<T>::n, CU = P / VN;
-  constexpr int UNITS = HS * 2 * 64 * CU;   // 16-byte row pieces per stage
-  constexpr int UPT = (UNITS + 255) / 256;  // per thread
+  constexpr int NTH = 256;
+  constexpr int NKP = (P + 31) / 32;
+  constexpr int XP = P + 16 / sizeof(T);    // row pitch of the staged x rows
+  constexpr int VN = Vec16<T>::n;
+  constexpr int XPIECES = 64 * P / VN;
+  constexpr int XPT = (XPIECES + NTH - 1) / NTH;
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T As[2][HS][64][RP];
-  __shared__ __attribute__((aligned(16))) T Bs[2][HS][64][RP];
-  __shared__ __attribute__((aligned(16))) float csI[2][HS][64];
-  __shared__ __attribute__((aligned(16))) float csJ[2][HS][64];
-  __shared__ __attribute__((aligned(16))) float dtJ[2][HS][64];
+  __shared__ __attribute__((aligned(16))) T Xs[2][64][XP];
+  __shared__ __attribute__((aligned(16))) float csJ[2][64];   // DIAG: cs_j, dt_j of the staged head
+  __shared__ __attribute__((aligned(16))) float dtJ[2][64];
+
   const int bkg = blockIdx.x;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   int IB, JB;
@@ -591,126 +590,100 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
   const int hpg = H / G;
   const int h0 = g * hpg + blockIdx.z * hps;                  // first head of this slice
   const int nh = min(hps, hpg - (int)blockIdx.z * hps);       // heads in this slice
-  const int nstage = (nh + HS - 1) / HS;
   const int i0 = 64 * IB, j0 = 64 * JB, ref = j0 + 63;
+  const int ia = i0 + 16 * wave + c;                          // this lane's row (A operand)
 
-  if (P < 32) {  // zero the padded K columns once; staging never writes them
-    T* a = &As[0][0][0][0];
-    for (int e = threadIdx.x; e < 2 * HS * 64 * RP; e += 256) a[e] = from_f<T>(0.0f);
-    T* bb = &Bs[0][0][0][0];
-    for (int e = threadIdx.x; e < 2 * HS * 64 * RP; e += 256) bb[e] = from_f<T>(0.0f);
-  }
-
-  // registers of the stage in flight
-  V rv[UPT];
-  float rs[UPT];
-  float fcs_i = 0.f, fcs_j = 0.f, fdt_j = 0.f;  // DIAG factors: thread t < 64*HS holds row t%64 of head t/64
-
-  auto load = [&](int st) {
+  // registers of the head in flight
+  V xv[XPT];
+  float xs[XPT];
+  Frag<T> av[NKP];
+  float ascale = 1.0f, jcs = 0.0f, jdt = 0.0f;
+  auto load = [&](int hh) {
+    const int h = h0 + hh;
+    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
 #pragma unroll
-    for (int n = 0; n < UPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      rs[n] = 0.0f;
-      if (u >= UNITS) continue;
-      const int hs = u / (2 * 64 * CU), rem = u % (2 * 64 * CU);
-      const int which = rem / (64 * CU), r = (rem % (64 * CU)) / CU, cu = rem % CU;
-      const int hh = st * HS + hs;
-      if (hh >= nh) continue;
-      const int h = h0 + hh;
-      const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-      if (which == 0) {
-        rv[n] = *reinterpret_cast<const V*>(dy + ((row0 + i0 + r) * H + h) * P + cu * VN);
-        rs[n] = DIAG ? 1.0f : __expf(csb[i0 + r] - csb[ref]);
-      } else {
-        rv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + cu * VN);
-        rs[n] = DIAG ? 1.0f : to_f(dt[(row0 + j0 + r) * H + h]) * __expf(csb[ref] - csb[j0 + r]);
+    for (int n = 0; n < XPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (XPIECES % NTH == 0 || u < XPIECES) {
+        const int r = u / (P / VN);
+        xv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
+        xs[n] = DIAG ? 1.0f : to_f(dt[(row0 + j0 + r) * H + h]) * __expf(csb[ref] - csb[j0 + r]);
       }
     }
-    if (DIAG && threadIdx.x < 64 * HS) {
-      const int hs = threadIdx.x / 64, t = threadIdx.x % 64, hh = st * HS + hs;
-      if (hh < nh) {
-        const int h = h0 + hh;
-        const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-        fcs_i = csb[i0 + t];
-        fcs_j = csb[j0 + t];
-        fdt_j = to_f(dt[(row0 + j0 + t) * H + h]);
-      }
+    const T* arow = dy + ((row0 + ia) * H + h) * P;
+#pragma unroll
+    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], arow, kp * 32, q);
+    if (!DIAG) ascale = __expf(csb[ia] - csb[ref]);
+    if (DIAG && threadIdx.x < 64) {
+      jcs = csb[j0 + threadIdx.x];
+      jdt = to_f(dt[(row0 + j0 + threadIdx.x) * H + h]);
     }
   };
   auto store = [&](int bf) {
 #pragma unroll
-    for (int n = 0; n < UPT; ++n) {
-      const int u = threadIdx.x + 256 * n;
-      if (u >= UNITS) continue;
-      const int hs = u / (2 * 64 * CU), rem = u % (2 * 64 * CU);
-      const int which = rem / (64 * CU), r = (rem % (64 * CU)) / CU, cu = rem % CU;
-      T* d = (which == 0 ? &As[bf][hs][r][0] : &Bs[bf][hs][r][0]) + cu * VN;
-      if (DIAG) {
-        *reinterpret_cast<V*>(d) = rv[n];
-      } else {
+    for (int n = 0; n < XPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (XPIECES % NTH == 0 || u < XPIECES) {
+        T* d = &Xs[bf][u / (P / VN)][(u % (P / VN)) * VN];
+        if (DIAG) {
+          *reinterpret_cast<V*>(d) = xv[n];
+        } else {
+          V w;
 #pragma unroll
-        for (int e0 = 0; e0 < VN; e0 += 4) {
-          typename Vec4<T>::type w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = from_f<T>(to_f(rv[n][e0 + e]) * rs[n]);
-          *reinterpret_cast<typename Vec4<T>::type*>(d + e0) = w;
+          for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(xv[n][e]) * xs[n]);
+          *reinterpret_cast<V*>(d) = w;
         }
       }
     }
-    if (DIAG && threadIdx.x < 64 * HS) {
-      const int hs = threadIdx.x / 64, t = threadIdx.x % 64;
-      csI[bf][hs][t] = fcs_i;
-      csJ[bf][hs][t] = fcs_j;
-      dtJ[bf][hs][t] = fdt_j;
+    if (DIAG && threadIdx.x < 64) {
+      csJ[bf][threadIdx.x] = jcs;
+      dtJ[bf][threadIdx.x] = jdt;
     }
   };
 
   f4 acc[4];
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) acc[tj] = f4{0.f, 0.f, 0.f, 0.f};
-
   load(0);
   store(0);
-  for (int st = 0; st < nstage; ++st) {
-    const int bf = st & 1;
-    __syncthreads();  // stage st is in buffer bf; buffer bf ^ 1 is no longer read
-    if (st + 1 < nstage) load(st + 1);
-    for (int hs = 0; hs < HS; ++hs) {
-      if (st * HS + hs >= nh) break;
-      Frag<T> fa[PP / 32];
+  for (int hh = 0; hh < nh; ++hh) {
+    const int bf = hh & 1;
+    Frag<T> fa[NKP];
 #pragma unroll
-      for (int kp = 0; kp < PP / 32; ++kp) frag_load(fa[kp], &As[bf][hs][16 * wave + c][kp * 32 + 8 * q]);
+    for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        if (DIAG) {
-          if (tj > wave) continue;  // strictly above the diagonal: zero
-          f4 dp = {0.f, 0.f, 0.f, 0.f};
+      for (int s8 = 0; s8 < 8; ++s8) frag_set<T>(fa[kp], s8, DIAG ? frag_get(av[kp], s8) : frag_get(av[kp], s8) * ascale);
+    float csi[4];
+    if (DIAG) {
+      const float* csb = cs_g + (((int64_t)b * H + h0 + hh) * K + k) * Q;
 #pragma unroll
-          for (int kp = 0; kp < PP / 32; ++kp) {
-            Frag<T> fb;
-            frag_load(fb, &Bs[bf][hs][16 * tj + c][kp * 32 + 8 * q]);
-            mma(dp, fa[kp], fb);
-          }
-          const f4 csi = *reinterpret_cast<const f4*>(&csI[bf][hs][16 * wave + 4 * q]);
-          const int jl = 16 * tj + c;
-          const float csj = csJ[bf][hs][jl], dtj = dtJ[bf][hs][jl];
+      for (int r = 0; r < 4; ++r) csi[r] = csb[i0 + 16 * wave + 4 * q + r];
+    }
+    __syncthreads();  // head hh is in buffer bf; buffer bf ^ 1 is no longer read
+    if (hh + 1 < nh) load(hh + 1);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int il = 16 * wave + 4 * q + r;
-            const float lam = (il >= jl) ? __expf(csi[r] - csj) : 0.0f;
-            acc[tj][r] += dp[r] * dtj * lam;
-          }
-        } else {
+    for (int tj = 0; tj < 4; ++tj) {
+      if (DIAG && tj > wave) continue;  // strictly above the diagonal: zero
+      f4 dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kp = 0; kp < PP / 32; ++kp) {
-            Frag<T> fb;
-            frag_load(fb, &Bs[bf][hs][16 * tj + c][kp * 32 + 8 * q]);
-            mma(acc[tj], fa[kp], fb);
-          }
+      for (int kp = 0; kp < NKP; ++kp) {
+        Frag<T> fb;
+        frag_load_chained<P>(fb, &Xs[bf][16 * tj + c][0], kp * 32, q);
+        if (DIAG) mma(dp, fa[kp], fb);
+        else mma(acc[tj], fa[kp], fb);
+      }
+      if (DIAG) {
+        const int jl = 16 * tj + c;
+        const float csj = csJ[bf][jl], dtj = dtJ[bf][jl];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int il = 16 * wave + 4 * q + r;
+          const float lam = (il >= jl) ? __expf(csi[r] - csj) : 0.0f;
+          acc[tj][r] += dp[r] * dtj * lam;
         }
       }
     }
-    if (st + 1 < nstage) store(bf ^ 1);
+    if (hh + 1 < nh) store(bf ^ 1);
   }
   float* o = dw + ((int64_t)blockIdx.z * gridDim.x + bkg) * Q * Q;
 #pragma unroll

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
                                                      const T* __restrict__ dt, const float* __restrict__ cs,
                                                      float* __restrict__ out, int L, int H, int G, int K) {
   constexpr int NTH = 256;
-  constexpr int KB = 32;                           // tokens per block
+  constexpr int KB = 64;                           // tokens per block
   constexpr int NB = Q / KB;
   constexpr int UP = P + 16, VP = N + 16;          // row pitches (8 mod 16 dwords for 64 / 128 wide rows)
   constexpr int TM = P / 16, TN = N / 16, NT = TM * TN, TPW = (NT + 3) / 4;
