@@ -6,28 +6,39 @@ namespace ssd {
 // ---------------------------------------------------------------------------
 // Chunk scan: for chunk k of head h, rows i in [0, Q):
 //   y_i = exp(cs_i) C_i^T Hin_k  +  sum_{j <= i} (C_i . B_j) exp(cs_i - cs_j) dt_j x_j  +  D_h x_i
-// One workgroup (4 waves) per (b, k, h).  Output rows are dealt to waves in
-// 16-row tiles (zig-zag, so the causal triangle splits evenly).  For each row
-// tile a wave
-//   1. accumulates C_i . Hin over dstate on the matrix cores and scales rows by exp(cs_i),
-//   2. walks source tokens j in steps of 32: reads the precomputed C.B^T
-//      accumulator tiles, applies the decay mask exp(cs_i - cs_j) dt_j (zero
-//      for j > i) in fp32, and feeds the result straight back as the A
-//      fragment of the product with x (chained K mapping), accumulating y,
+// One workgroup (4 waves) per (b, k, h).  Output row tiles of 16 tokens are
+// dealt to waves in a zig-zag, so the causal triangle splits evenly.  The
+// products are formed transposed, y^T = Hin C^T + x^T P^T, so that a lane
+// holds 4 consecutive headdim entries of one token (lane (q, c): y[16I + c]
+// [16tp + 4q + r]): the row scale exp(cs_i) is one value per lane and the
+// stores are 8-byte vectors.  For each row tile a wave
+//   1. accumulates Hin . C_i over dstate on the matrix cores and scales by exp(cs_i),
+//   2. walks source tokens j in steps of 32: the precomputed C.B^T tiles
+//      (forward lane order) times the decay mask exp(cs_i - cs_j) dt_j (zero
+//      for j > i) form the B fragment; x^T comes K-major from the staged x
+//      rows through the transposing LDS read,
 //   3. adds D x and stores.
-// x is staged once per workgroup, transposed (tokens contiguous); the entering
-// state Hin_k is staged as [p][n].
+// x rows of the chunk and the entering state Hin_k are staged once per
+// workgroup.  Each wave loads the C rows and all C.B^T tiles of its next row
+// tile while it computes the current one.
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256) void k_chunk_scan_fwd(const T* __restrict__ x, const T* __restrict__ dt,
-                                                        const float* __restrict__ cs_g, const float* __restrict__ Dp,
-                                                        const T* __restrict__ C, const T* __restrict__ hin,
-                                                        const T* __restrict__ wt, T* __restrict__ y,
-                                                        int L, int H, int G, int K) {
-  constexpr int PADQ = 16 / sizeof(T), PADN = 16 / sizeof(T);
+__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__ x, const T* __restrict__ dt,
+                                                           const float* __restrict__ cs_g, const float* __restrict__ Dp,
+                                                           const T* __restrict__ C, const T* __restrict__ hin,
+                                                           const T* __restrict__ wt, T* __restrict__ y,
+                                                           int L, int H, int G, int K) {
+  constexpr int NTH = 256, NW = 4;
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
-  constexpr int NK = (N + 31) / 32;
-  __shared__ __attribute__((aligned(16))) T Xt[P][Q + PADQ];
-  __shared__ __attribute__((aligned(16))) T Hs[P][N + PADN];
+  constexpr int NK = (N + 31) / 32, NJ2 = NT / 2;
+  constexpr int NSLOT = (NT + NW - 1) / NW;     // row tiles per wave
+  constexpr int XPITCH = P + 16, HPITCH = N + 16 / sizeof(T);
+  constexpr int VN = Vec16<T>::n;
+  constexpr int XPIECES = Q * P / VN, HPIECES = P * N / VN;
+  constexpr int XPT = (XPIECES + NTH - 1) / NTH, HPT = (HPIECES + NTH - 1) / NTH;
+  typedef typename Vec4<T>::type V4;
+  typedef typename Vec16<T>::type V;
+  __shared__ __attribute__((aligned(16))) T Xs[Q][XPITCH];
+  __shared__ __attribute__((aligned(16))) T Hs[P][HPITCH];
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
 
@@ -36,90 +47,133 @@ __global__ __launch_bounds__(256) void k_chunk_scan_fwd(const T* __restrict__ x,
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const T* wtb = wt + (int64_t)((b * K + k) * G + g) * TILES * 256;
 
-  stage_transposed<T, T, P, 256>(&Xt[0][0], Q + PADQ, x + (row0 * H + h) * P, (int64_t)H * P, Q, nullptr);
-  stage_rows<T, T, N, 256>(&Hs[0][0], N + PADN, hin + (int64_t)bkh * P * N, N, P, nullptr);
+  // row tiles of this wave (zig-zag); NT may be smaller than the wave count
+  int Is[NSLOT];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) Is[sl] = 2 * NW * (sl / 2) + ((sl & 1) ? 2 * NW - 1 - wave : wave);
+
+  // per-row-tile operands: C rows (B operand, K = dstate) and the C.B^T tiles (I, J <= I)
+  Frag<T> cf[2][NK];
+  V4 wv[2][NT];
+  auto tile_load = [&](int set, int I) {
+    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(cf[set][ks], crow, ks * 32 + 8 * q);
+#pragma unroll
+    for (int J = 0; J < NT; ++J)  // tiles past the diagonal are never used: load (I, I) instead
+      wv[set][J] = *reinterpret_cast<const V4*>(wtb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + l * 4);
+  };
+
+  // ---- prologue: all loads first, then LDS stores
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
-    cs[i] = csc[i];
-    dts[i] = to_f(dt[(row0 + i) * H + h]);
+  constexpr int QPT = (Q + NTH - 1) / NTH;
+  float csv[QPT], dtv[QPT];
+#pragma unroll
+  for (int n = 0; n < QPT; ++n) {
+    const int i = threadIdx.x + NTH * n;
+    if (Q % NTH == 0 || i < Q) {
+      csv[n] = csc[i];
+      dtv[n] = to_f(dt[(row0 + i) * H + h]);
+    }
+  }
+  V xr[XPT], hr[HPT];
+#pragma unroll
+  for (int n = 0; n < XPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (XPIECES % NTH == 0 || u < XPIECES)
+      xr[n] = *reinterpret_cast<const V*>(x + ((row0 + u / (P / VN)) * H + h) * P + (u % (P / VN)) * VN);
+  }
+#pragma unroll
+  for (int n = 0; n < HPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (HPIECES % NTH == 0 || u < HPIECES) hr[n] = *reinterpret_cast<const V*>(hin + (int64_t)bkh * P * N + u * VN);
+  }
+  if (Is[0] < NT) tile_load(0, Is[0]);
+#pragma unroll
+  for (int n = 0; n < QPT; ++n) {
+    const int i = threadIdx.x + NTH * n;
+    if (Q % NTH == 0 || i < Q) {
+      cs[i] = csv[n];
+      dts[i] = dtv[n];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < XPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (XPIECES % NTH == 0 || u < XPIECES) *reinterpret_cast<V*>(&Xs[u / (P / VN)][(u % (P / VN)) * VN]) = xr[n];
+  }
+#pragma unroll
+  for (int n = 0; n < HPT; ++n) {
+    const int u = threadIdx.x + NTH * n;
+    if (HPIECES % NTH == 0 || u < HPIECES) *reinterpret_cast<V*>(&Hs[u / (N / VN)][(u % (N / VN)) * VN]) = hr[n];
   }
   __syncthreads();
 
   const float Dh = Dp[h];
-  const T* wtb = wt + (int64_t)((b * K + k) * G + g) * TILES * 256;
-
-  for (int I = 0; I < NT; ++I) {
-    if (zigzag_owner<4>(I) != wave) continue;
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int I = Is[sl];
+    if (I >= NT) break;
+    const int set = sl & 1;
+    if (sl + 1 < NSLOT && Is[sl + 1] < NT) tile_load(set ^ 1, Is[sl + 1]);
     f4 acc[TP];
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
 
-    // 1. state -> output: C_i . Hin (K = dstate)
-    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+    // 1. state -> output: Hin . C_i (K = dstate); lane column i = 16I + c
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      Frag<T> fa;
-      frag_load_k<N>(fa, crow, ks * 32 + 8 * q);
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        Frag<T> fb;
-        frag_load_k<N>(fb, &Hs[tp * 16 + c][0], ks * 32 + 8 * q);
-        mma(acc[tp], fa, fb);
+        Frag<T> fh;
+        frag_load_k<N>(fh, &Hs[16 * tp + c][0], ks * 32 + 8 * q);
+        mma(acc[tp], fh, cf[set][ks]);
       }
     }
+    const int ci = 16 * I + c;
+    const float cs_i = cs[ci];
     {
-      const f4 csr = *reinterpret_cast<const f4*>(&cs[16 * I + 4 * q]);
+      const float e = __expf(cs_i);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __expf(csr[r]);
-#pragma unroll
-        for (int tp = 0; tp < TP; ++tp) acc[tp][r] *= e;
-      }
+      for (int tp = 0; tp < TP; ++tp) acc[tp] *= e;
     }
 
     // 2. intra-chunk: sum_{j <= i} W_ij exp(cs_i - cs_j) dt_j x_j
-    const int ci = 16 * I + c;  // this lane's row i in the W tiles
-    const float cs_i = cs[ci];
-    for (int J2 = 0; 2 * J2 <= I; ++J2) {
-      Frag<T> fa;
+#pragma unroll
+    for (int J2 = 0; J2 < NJ2; ++J2) {
+      if (2 * J2 > I) break;
+      Frag<T> fa;                              // P^T as the B operand: col i, K = j (chained)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int J = 2 * J2 + half;
         const int j0 = 16 * J + 4 * q;
-        if (J <= I) {
-          const typename Vec4<T>::type wv =
-              *reinterpret_cast<const typename Vec4<T>::type*>(wtb + (int64_t)tri_index(I, J) * 256 + l * 4);
-          const f4 csj = *reinterpret_cast<const f4*>(&cs[j0]);
-          const f4 dtj = *reinterpret_cast<const f4*>(&dts[j0]);
+        const f4 csj = *reinterpret_cast<const f4*>(&cs[j0]);
+        const f4 dtj = *reinterpret_cast<const f4*>(&dts[j0]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float m = (j0 + r <= ci) ? __expf(cs_i - csj[r]) * dtj[r] : 0.0f;
-            frag_set<T>(fa, half * 4 + r, to_f(wv[r]) * m);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, 0.0f);
+        for (int r = 0; r < 4; ++r) {
+          const float m = (J <= I && j0 + r <= ci) ? __expf(cs_i - csj[r]) * dtj[r] : 0.0f;
+          frag_set<T>(fa, half * 4 + r, to_f(wv[set][J][r]) * m);
         }
       }
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        Frag<T> fb;
-        frag_load2(fb, &Xt[tp * 16 + c][32 * J2 + 4 * q], &Xt[tp * 16 + c][32 * J2 + 16 + 4 * q]);
-        mma(acc[tp], fa, fb);
+        Frag<T> fx;                            // x^T: row p = 16tp + c, K = j (chained)
+        frag_load_kmajor<32>(fx, &Xs[0][0], XPITCH, 32 * J2, 16 * tp, q, c);
+        mma(acc[tp], fx, fa);
       }
     }
 
-    // 3. + D x, store rows i = 16I + 4q + r, column p = 16tp + c
+    // 3. + D x, store y[i][16tp + 4q + r]
+    T* yr = y + ((row0 + ci) * H + h) * P;
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
-      const int p = tp * 16 + c;
-      const typename Vec4<T>::type xv = *reinterpret_cast<const typename Vec4<T>::type*>(&Xt[p][16 * I + 4 * q]);
+      const V4 xv = *reinterpret_cast<const V4*>(&Xs[ci][16 * tp + 4 * q]);
+      V4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * q + r;
-        y[((row0 + i) * H + h) * P + p] = from_f<T>(acc[tp][r] + Dh * to_f(xv[r]));
-      }
+      for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[tp][r] + Dh * to_f(xv[r]));
+      *reinterpret_cast<V4*>(yr + 16 * tp + 4 * q) = o;
     }
   }
 }
