@@ -57,19 +57,24 @@ Layout make_layout(const ssd_shape* s) {
   y.w_off = o;      o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.dhloc_off = o;  o += align_up(states * 4);
   y.g_off = o;      o += align_up(states * y.esz);
-  // Head slices for the group-level backward kernels: enough workgroups to
-  // fill the chip (about 1024 per launch) without slicing finer than a head.
-  {
+  // Head slices for the group-level backward kernels (each slice writes an
+  // fp32 partial that is summed in a fixed order): about `target` workgroups
+  // per launch, never finer than one head.  Measured at the 2.7B shape
+  // (b*K*G*Q/64 = 256): two slices for both is fastest; more slices cost more
+  // in partial sums than the extra parallelism gains, one slice starves dW.
+  auto slices = [&](int64_t target) {
     const int64_t base = y.b * y.K * y.G * (y.Q / 64);
     const int64_t hpg = y.H / y.G;
-    int64_t sl = (1024 + base - 1) / base;
+    int64_t sl = (target + base - 1) / base;
     if (sl > hpg) sl = hpg;
     if (sl < 1) sl = 1;
-    y.nslice = sl;
-  }
+    return sl;
+  };
+  y.nslice = slices(512);
+  y.nslice_bc = slices(512);
   y.dw_off = o;     o += align_up((size_t)(y.nslice * y.b * y.K * y.G * y.Q * y.Q) * 4);
-  y.dcpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.L * y.G * y.N) * 4);
-  y.dbpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.L * y.G * y.N) * 4);
+  y.dcpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.L * y.G * y.N) * 4);
+  y.dbpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.L * y.G * y.N) * 4);
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   const int64_t nsp = scan_bwd_splits((int)y.Q);

@@ -938,6 +938,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, nitems, L, H, K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
+  const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;
   {
     ProbeScope ps(probe, SSD_K_DW, st);
     const int nb = Q / 64;
@@ -948,17 +949,17 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);
-    k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, a.dcpart, L, H, G, K, hps);
+    k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, hin, a.dcpart, L, H, G, K, hpsb);
     k_bc_final<T, Q, N, false><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        a.dcpart, a.dw, B, static_cast<T*>(a.dC), L, G, K, S, S);
+        a.dcpart, a.dw, B, static_cast<T*>(a.dC), L, G, K, Sb, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DB, st);
-    k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, S), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, gst, a.dbpart, L, H, G, K, hps);
+    k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, gst, a.dbpart, L, H, G, K, hpsb);
     k_bc_final<T, Q, N, true><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        a.dbpart, a.dw, C, static_cast<T*>(a.dB), L, G, K, S, S);
+        a.dbpart, a.dw, C, static_cast<T*>(a.dB), L, G, K, Sb, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);

@@ -22,7 +22,8 @@ struct Layout {
   // backward scratch
   size_t w_off, dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, dlpart_off, dlscal_off,
       bwd_bytes;
-  int64_t nslice;  // head slices of the group-level backward kernels
+  int64_t nslice;     // head slices of the dW kernel
+  int64_t nslice_bc;  // head slices of the dB / dC head sums
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
 };
 
@@ -49,8 +50,8 @@ struct BwdArgs {
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
-  float* dcpart;   // [nslice][b][L][G][N] fp32 partials of dC
-  float* dbpart;   // [nslice][b][L][G][N] fp32 partials of dB
+  float* dcpart;   // [nslice_bc][b][L][G][N] fp32 partials of dC
+  float* dbpart;   // [nslice_bc][b][L][G][N] fp32 partials of dB
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
   float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
