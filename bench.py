@@ -189,6 +189,100 @@ def cpu_baseline(shape, inp_full, batch_rows: int, heads: int):
                       f"tokens/s scaled linearly by x{scale:g} (batch x heads) to the full workload"}
 
 
+# HIP kernels that make up each timed kernel of the step (a probe brackets
+# all of them); names may come mangled or demangled from rocprofv3.
+def kernel_matches(bench_kernel: str, name: str) -> bool:
+    fwd_flag = "Lb0E" in name or "false>" in name
+    bwd_flag = "Lb1E" in name or "true>" in name
+    rules = {
+        "chunk_cumsum": "k_chunk_cumsum" in name,
+        "bmm_fwd": "k_bmm_tiles" in name,
+        "chunk_state": "k_chunk_state" in name and fwd_flag,
+        "state_passing": "k_state_passing_fwd" in name,
+        "chunk_scan": "k_chunk_scan_fwd" in name,
+        "bmm_bwd": "k_tiles_to_bwd" in name,
+        "chunk_state_bwd": "k_chunk_state" in name and bwd_flag,
+        "state_passing_bwd": "k_state_passing_bwd" in name,
+        "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,
+        "dw": "k_dw" in name,
+        "dc": ("k_bc_heads" in name or "k_bc_final" in name) and fwd_flag,
+        "db": ("k_bc_heads" in name or "k_bc_final" in name) and bwd_flag,
+        "da_dd": "k_da_dd" in name,
+    }
+    return rules.get(bench_kernel, False)
+
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the blit kernel behind a device-to-device copy
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no rocprofv3 counter_collection.csv under {d}")
+    return rows
+
+
+def _per_dispatch_kib(rows, counter: str, match) -> float:
+    """Sum over the matching HIP kernels of their mean per-dispatch counter value (KiB)."""
+    by_kernel = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or not match(r["Kernel_Name"]):
+            continue
+        d = by_kernel.setdefault(r["Kernel_Name"], {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not by_kernel:
+        raise SystemExit(f"no dispatch with counter {counter} matched")
+    return sum(sum(v.values()) / len(v) for v in by_kernel.values())
+
+
+def write_traffic(pmc_dir: str, kernel: str, workload: str, copy_bytes: int, commands: list) -> None:
+    """HBM traffic per launch of `kernel` from two rocprofv3 --pmc passes
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for a device-to-device copy of `copy_bytes` bytes (which
+    reads and writes exactly that many bytes)."""
+    fetch = _per_dispatch_kib(_counter_rows(os.path.join(pmc_dir, "fetch")), "FETCH_SIZE",
+                              lambda n: kernel_matches(kernel, n))
+    write = _per_dispatch_kib(_counter_rows(os.path.join(pmc_dir, "write")), "WRITE_SIZE",
+                              lambda n: kernel_matches(kernel, n))
+    cf = _per_dispatch_kib(_counter_rows(os.path.join(pmc_dir, "copy_fetch")), "FETCH_SIZE", lambda n: COPY_KERNEL in n)
+    cw = _per_dispatch_kib(_counter_rows(os.path.join(pmc_dir, "copy_write")), "WRITE_SIZE", lambda n: COPY_KERNEL in n)
+    f_fetch = copy_bytes / (cf * 1024.0)
+    f_write = copy_bytes / (cw * 1024.0)
+    traffic = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
+    out = {"kernel": kernel, "workload": workload, "source_hash": source_hash(),
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_factor": f_fetch, "write_factor": f_write,
+           "read_bytes": fetch * 1024.0 * f_fetch, "written_bytes": write * 1024.0 * f_write,
+           "traffic_bytes": traffic, "commands": commands}
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def summarize_stats(csv_path: str, command: str, title: str) -> str:
+    """Markdown table from a rocprofv3 --kernel-trace --stats *_kernel_stats.csv."""
+    import csv
+    with open(csv_path) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+             "rocprofv3 kernel statistics (durations in microseconds):", "",
+             "| kernel | calls | total us | average us | % of GPU time |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        n = r["Name"]
+        for a, b in [("_ZN3ssd", ""), ("IDF16bLi256ELi64ELi128E", "<bf16,256,64,128>")]:
+            n = n.replace(a, b)
+        lines.append(f"| `{n[:90]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def load_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
     was taken on the current kernel sources; else None."""
@@ -215,7 +309,25 @@ def main():
                     help="only run warmup + steps (for rocprofv3); no breakdown, no CPU baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration mode: time a plain device copy of this many bytes and exit")
+    ap.add_argument("--write-traffic", metavar="PMC_DIR", default=None,
+                    help="(no GPU) write profiles/traffic_<kernel>_<workload>.json from the rocprofv3 --pmc "
+                         "passes under PMC_DIR/{fetch,write,copy_fetch,copy_write}; needs --traffic-kernel "
+                         "and --copy-bytes of the calibration copy")
+    ap.add_argument("--traffic-kernel", default="chunk_scan_bwd")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="the profiling commands, recorded in the JSON")
+    ap.add_argument("--summarize-stats", metavar="CSV", default=None,
+                    help="(no GPU) print a markdown summary of a rocprofv3 *_kernel_stats.csv")
+    ap.add_argument("--stats-command", default="")
+    ap.add_argument("--stats-title", default="")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic, args.traffic_kernel, args.workload, args.copy_bytes, args.traffic_command)
+        return
+    if args.summarize_stats:
+        sys.stdout.write(summarize_stats(args.summarize_stats, args.stats_command, args.stats_title))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the SSD scan here is a "
