@@ -84,11 +84,13 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_
 
 // Compiled (chunk, headdim, dstate) combinations, per storage dtype.  The
 // fp32 list is shorter because the backward chunk kernel's LDS staging of
-// fp32 tiles must fit in 160 KiB per workgroup.
+// fp32 tiles must fit in 160 KiB per workgroup.  bf16 at chunk 64 is switched
+// off: a GPU memory fault in that case under an earlier backward kernel was
+// never traced to a cause, so the case stays unavailable until one is shown.
 #define SSD_BF16_CONFIGS(X) \
-  X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
-  X(64, 64, 64) X(128, 64, 64) X(256, 64, 64) \
-  X(64, 64, 128) X(128, 64, 128) X(256, 64, 128)
+  X(128, 16, 16) X(256, 16, 16) \
+  X(128, 64, 64) X(256, 64, 64) \
+  X(128, 64, 128) X(256, 64, 128)
 #define SSD_F32_CONFIGS(X) \
   X(64, 16, 16) X(128, 16, 16) X(256, 16, 16) \
   X(64, 64, 64) X(128, 64, 64) \

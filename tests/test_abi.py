@@ -48,6 +48,7 @@ def check(lib, s):
 def test_shape_checks(lib):
     assert check(lib, shape()) == OK
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=64)) == OK
+    assert check(lib, shape(chunk=64)) == UNSUPPORTED                        # bf16 chunk 64 switched off
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128, dstate=64)) == OK
     assert check(lib, shape(seqlen=500)) == INVALID          # seqlen % chunk
     assert check(lib, shape(nheads=5)) == INVALID            # nheads % ngroups
