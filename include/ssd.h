@@ -61,7 +61,11 @@ typedef enum {
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 /* Problem size.  chunk is the chunk length Q of the chunked scan; seqlen must
- * be a multiple of it.  dtype is an ssd_dtype. */
+ * be a multiple of it.  dtype is an ssd_dtype.  Compiled (chunk, headdim,
+ * dstate) combinations (others give SSD_ERR_UNSUPPORTED):
+ *   SSD_BF16: chunk 128 or 256 with (headdim, dstate) (16, 16), (64, 64), (64, 128)
+ *   SSD_F32 : chunk 64, 128 or 256 with (16, 16); chunk 64 or 128 with (64, 64);
+ *             chunk 64 with (64, 128)                                          */
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t dtype;
@@ -87,13 +91,13 @@ typedef enum {
     SSD_K_CHUNK_STATE = 2,       /* decay-weighted B^T x per chunk and head */
     SSD_K_STATE_PASSING = 3,     /* sequential inter-chunk state scan */
     SSD_K_CHUNK_SCAN = 4,        /* intra-chunk masked product + state-to-output + D x */
-    SSD_K_BMM_BWD = 5,           /* C.B^T per chunk and group (backward tile order) */
+    SSD_K_BMM_BWD = 5,           /* C.B^T tiles in backward lane order (from the saved forward tiles) */
     SSD_K_CHUNK_STATE_BWD = 6,   /* exp(cs) C^T dy per chunk and head */
     SSD_K_STATE_PASSING_BWD = 7, /* reverse inter-chunk state scan */
-    SSD_K_CHUNK_SCAN_BWD = 8,    /* dx, ddt and per-chunk dA/dD partials */
+    SSD_K_CHUNK_SCAN_BWD = 8,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
     SSD_K_DW = 9,                /* head-summed masked dY.X^T per chunk and group */
-    SSD_K_DC = 10,               /* dC */
-    SSD_K_DB = 11,               /* dB */
+    SSD_K_DC = 10,               /* dC: head sums per slice, then slice sum + dW.B */
+    SSD_K_DB = 11,               /* dB: head sums per slice, then slice sum + dW^T.C */
     SSD_K_DA_DD = 12,            /* fixed-order dA / dD reduction */
     SSD_NUM_KERNELS = 13
 } ssd_kernel_id;
