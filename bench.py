@@ -58,11 +58,10 @@ def kernel_model(s, esz):
     bkh, bkg = b * K * H, b * K * G
     m = {
         "chunk_cumsum": (DT + CS, 0),
-        "bmm_fwd": (2 * BC + WT, 2 * bkg * tri * N),
+        "bmm_fwd": (2 * BC + 2 * WT, 4 * bkg * tri * N),  # both lane orders
         "chunk_state": (X + BC + DT + CS + ST4, 2 * bkh * Q * P * N),
         "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
         "chunk_scan": (2 * X + DT + CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
-        "bmm_bwd": (2 * BC + WT, 2 * bkg * tri * N),
         "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
         "state_passing_bwd": (ST4 + STe, 0),
         "chunk_scan_bwd": (3 * X + 2 * DT + CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
@@ -200,7 +199,6 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
         "chunk_state": "k_chunk_state" in name and fwd_flag,
         "state_passing": "k_state_passing_fwd" in name,
         "chunk_scan": "k_chunk_scan_fwd" in name,
-        "bmm_bwd": "k_tiles_to_bwd" in name,
         "chunk_state_bwd": "k_chunk_state" in name and bwd_flag,
         "state_passing_bwd": "k_state_passing_bwd" in name,
         "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,

@@ -87,19 +87,18 @@ typedef struct {
 /* Kernel identifiers, for timing one kernel with an ssd_probe. */
 typedef enum {
     SSD_K_CHUNK_CUMSUM = 0,      /* per-chunk inclusive cumsum of dt*A */
-    SSD_K_BMM_FWD = 1,           /* C.B^T per chunk and group (forward tile order) */
+    SSD_K_BMM_FWD = 1,           /* C.B^T per chunk and group, in the forward and the backward lane order */
     SSD_K_CHUNK_STATE = 2,       /* decay-weighted B^T x per chunk and head */
     SSD_K_STATE_PASSING = 3,     /* sequential inter-chunk state scan */
     SSD_K_CHUNK_SCAN = 4,        /* intra-chunk masked product + state-to-output + D x */
-    SSD_K_BMM_BWD = 5,           /* C.B^T tiles in backward lane order (from the saved forward tiles) */
-    SSD_K_CHUNK_STATE_BWD = 6,   /* exp(cs) C^T dy per chunk and head */
-    SSD_K_STATE_PASSING_BWD = 7, /* reverse inter-chunk state scan */
-    SSD_K_CHUNK_SCAN_BWD = 8,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
-    SSD_K_DW = 9,                /* head-summed masked dY.X^T per chunk and group */
-    SSD_K_DC = 10,               /* dC: head sums per slice, then slice sum + dW.B */
-    SSD_K_DB = 11,               /* dB: head sums per slice, then slice sum + dW^T.C */
-    SSD_K_DA_DD = 12,            /* fixed-order dA / dD reduction */
-    SSD_NUM_KERNELS = 13
+    SSD_K_CHUNK_STATE_BWD = 5,   /* exp(cs) C^T dy per chunk and head */
+    SSD_K_STATE_PASSING_BWD = 6, /* reverse inter-chunk state scan */
+    SSD_K_CHUNK_SCAN_BWD = 7,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
+    SSD_K_DW = 8,                /* head-summed masked dY.X^T per chunk and group */
+    SSD_K_DC = 9,                /* dC: head sums per slice, then slice sum + dW.B */
+    SSD_K_DB = 10,               /* dB: head sums per slice, then slice sum + dW^T.C */
+    SSD_K_DA_DD = 11,            /* fixed-order dA / dD reduction */
+    SSD_NUM_KERNELS = 12
 } ssd_kernel_id;
 
 /* Optional timing hook: when passed to ssd_fwd/ssd_bwd and `kernel` names a

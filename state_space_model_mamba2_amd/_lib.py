@@ -11,7 +11,7 @@ SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ER
 SSD_F32, SSD_BF16 = 0, 1
 
 KERNELS = ["chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
-           "bmm_bwd", "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"]
+           "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"]
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
 

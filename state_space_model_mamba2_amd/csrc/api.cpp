@@ -49,12 +49,12 @@ Layout make_layout(const ssd_shape* s) {
   y.cs_off = o;   o += align_up((size_t)(y.b * y.H * y.K * y.Q) * 4);
   y.hin_off = o;  o += align_up(states * y.esz);
   y.wt_off = o;   o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
+  y.wtb_off = o;  o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.saved_bytes = o;
   o = 0;
   y.s_off = o;    o += align_up(states * 4);
   y.fwd_bytes = o;
   o = 0;
-  y.w_off = o;      o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.dhloc_off = o;  o += align_up(states * 4);
   y.g_off = o;      o += align_up(states * y.esz);
   // Head slices for the group-level backward kernels (each slice writes an
@@ -114,7 +114,7 @@ const char* ssd_status_string(ssd_status st) {
 const char* ssd_kernel_name(int32_t k) {
   static const char* names[SSD_NUM_KERNELS] = {
       "chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
-      "bmm_bwd", "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"};
+      "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"};
   if (k < 0 || k >= SSD_NUM_KERNELS) return nullptr;
   return names[k];
 }
@@ -146,6 +146,7 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   a.hin = at<char>(saved_ws, lay.hin_off);
   a.S = at<float>(scratch, lay.s_off);
   a.wt = at<char>(saved_ws, lay.wt_off);
+  a.wtb = at<char>(saved_ws, lay.wtb_off);
 
   bool dispatched = false;
 #define SSD_DISPATCH(TT, Q_, P_, N_)                                  \
@@ -189,9 +190,8 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, flo
   a.x = sv->x; a.dt = sv->dt; a.B = sv->B; a.C = sv->C; a.dy = dy; a.A = sv->A; a.D = sv->D;
   a.cs = at<float>(sv->saved_ws, lay.cs_off);
   a.hin = at<char>(sv->saved_ws, lay.hin_off);
-  a.wf = at<char>(sv->saved_ws, lay.wt_off);
+  a.w = at<char>(sv->saved_ws, lay.wtb_off);
   a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
-  a.w = at<char>(scratch, lay.w_off);
   a.dhloc = at<float>(scratch, lay.dhloc_off);
   a.gst = at<char>(scratch, lay.g_off);
   a.dw = at<float>(scratch, lay.dw_off);

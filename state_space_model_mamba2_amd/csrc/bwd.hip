@@ -451,37 +451,48 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 }
 
 // dl, ddt and the chunk's dA / dD partials from the per-token partial sums of
-// k_chunk_scan_bwd; one wave per (b, k, h), Q / 64 consecutive tokens per lane:
+// k_chunk_scan_bwd:
 //   dl_j = sum_{i >= j} (row sum_i - column sum_i)  [suffix sum]
 //        + sum_{j' < j} q_j'                          [exclusive prefix sum]
 //        + exp(cs_{Q-1}) <Gk, Hin_k>
 // (the q terms, added at the chunk end and subtracted at each token, are
 // summed directly as a prefix so no large terms cancel), then
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dA partial = sum_j dt_j dl_j.
+// One workgroup per (b, k) and 16 heads: 16 lanes per head, Q / 16
+// consecutive tokens per lane, so a token's dt and ddt entries of the 16
+// heads are one contiguous run.
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
                                                      const float* __restrict__ cs_g, const T* __restrict__ dt,
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
-                                                     int nitems, int L, int H, int K) {
+                                                     int L, int H, int K) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
-  constexpr int TPL = Q / kWave;
-  const int bkh = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (bkh >= nitems) return;  // whole wave; no workgroup barrier below
-  const int l = lane_id();
-  const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
+  constexpr int TPL = Q / 16;
+  const int nhb = (H + 15) / 16;
+  const int hb = blockIdx.x % nhb, bk = blockIdx.x / nhb;
+  const int k = bk % K, b = bk / K;
+  const int hl = threadIdx.x / 16, jl = threadIdx.x % 16;
+  const int h = 16 * hb + hl;
+  if (h >= H) return;  // whole 16-lane group; only width-16 shuffles below
+  const int bkh = bk * H + h;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
   const float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;
   const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
+  const int j0 = jl * TPL;
   float v[TPL], qp[TPL];
 #pragma unroll
-  for (int t = 0; t < TPL; ++t) {
-    const int i = l * TPL + t;
-    float rsum = 0.0f;
+  for (int t = 0; t < TPL; t += 4) {
+    f4 rs = *reinterpret_cast<const f4*>(part + j0 + t);
 #pragma unroll
-    for (int sp = 0; sp < NSPLIT; ++sp) rsum += part[sp * Q + i];
-    v[t] = rsum - part[NSPLIT * Q + i];
-    qp[t] = part[(NSPLIT + 1) * Q + i];
+    for (int sp = 1; sp < NSPLIT; ++sp) rs += *reinterpret_cast<const f4*>(part + sp * Q + j0 + t);
+    const f4 cl = *reinterpret_cast<const f4*>(part + NSPLIT * Q + j0 + t);
+    const f4 qq = *reinterpret_cast<const f4*>(part + (NSPLIT + 1) * Q + j0 + t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[t + e] = rs[e] - cl[e];
+      qp[t + e] = qq[e];
+    }
   }
 #pragma unroll
   for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
@@ -492,54 +503,38 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
     qp[t] = qrun;
     qrun += qt;
   }
-  const float incl = wave_inclusive_suffix(v[0]);
-  float excl = __shfl_down(incl, 1, kWave);
-  if (l == kWave - 1) excl = 0.0f;
-  const float qincl = wave_inclusive_scan(qrun);
+  // across the 16 lanes of the head: suffix of the block sums v[0], prefix of qrun
+  float incl = v[0], qincl = qrun;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const float o = __shfl_down(incl, off, 16);
+    if (jl + off < 16) incl += o;
+    const float p = __shfl_up(qincl, off, 16);
+    if (jl >= off) qincl += p;
+  }
+  float excl = __shfl_down(incl, 1, 16);
+  if (jl == 15) excl = 0.0f;
   const float qexcl = qincl - qrun;
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
   const float tail = __expf(csc[Q - 1]) * sc[0];
   const float Ah = Ap[h];
+  const float* xd = part + (NSPLIT + 2) * Q + j0;
   float da = 0.0f;
 #pragma unroll
   for (int t = 0; t < TPL; ++t) {
-    const int j = l * TPL + t;
+    const int j = j0 + t;
     const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
     da += to_f(dt[(row0 + j) * H + h]) * dl;
-    ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + part[(NSPLIT + 2) * Q + j]);
+    ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + xd[t]);
   }
-  da = wave_sum(da);
-  if (l == 0) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) da += __shfl_xor(da, off, 16);
+  if (jl == 0) {
     float dds = 0.0f;
 #pragma unroll
     for (int sp = 0; sp < NSPLIT; ++sp) dds += sc[1 + sp];
     dapart[bkh] = da;
     ddpart[bkh] = dds;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Backward-order C.B^T tiles from the forward-order tiles the forward pass
-// saved: a per-tile lane transpose through LDS, so both orders hold the same
-// rounded values (tile (I, J): forward lane (q, c) holds W[16I + c][16J + 4q + r],
-// backward lane (q, c) holds W[16I + 4q + r][16J + c]).
-template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_tiles_to_bwd(const T* __restrict__ wf, T* __restrict__ wb, int nsplit) {
-  constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
-  __shared__ float tb[4][16][17];
-  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t base = (int64_t)blockIdx.x * TILES * 256;
-  typedef typename Vec4<T>::type V4;
-  for (int idx = blockIdx.y * 4 + wave; idx < TILES; idx += nsplit * 4) {
-    const V4 v = *reinterpret_cast<const V4*>(wf + base + (int64_t)idx * 256 + l * 4);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tb[wave][c][4 * q + r] = to_f(v[r]);  // tb[i_local][j_local]
-    __builtin_amdgcn_wave_barrier();
-    V4 o;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[r] = from_f<T>(tb[wave][4 * q + r][c]);
-    *reinterpret_cast<V4*>(wb + base + (int64_t)idx * 256 + l * 4) = o;
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -912,13 +907,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   const T* C = static_cast<const T*>(a.C);
   const T* dy = static_cast<const T*>(a.dy);
   const T* hin = static_cast<const T*>(a.hin);
-  T* w = static_cast<T*>(a.w);
+  const T* w = static_cast<const T*>(a.w);
   T* gst = static_cast<T*>(a.gst);
-  {
-    ProbeScope ps(probe, SSD_K_BMM_BWD, st);
-    const int nsplit = 4;
-    k_tiles_to_bwd<T, Q><<<dim3(b * K * G, nsplit), dim3(256), 0, st>>>(static_cast<const T*>(a.wf), w, nsplit);
-  }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
     k_chunk_state<T, Q, P, N, true><<<dim3(b * K * H), dim3(256), 0, st>>>(dy, C, dt, a.cs, a.dhloc, L, H, G, K);
@@ -934,8 +924,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     const int groups = (nitems + 7) / 8;
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(groups * 8 * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, L, H, G, K);
-    k_dl_assemble<T, Q><<<dim3((nitems + 3) / 4), dim3(256), 0, st>>>(
-        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, nitems, L, H, K);
+    k_dl_assemble<T, Q><<<dim3(b * K * ((H + 15) / 16)), dim3(256), 0, st>>>(
+        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, L, H, K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;

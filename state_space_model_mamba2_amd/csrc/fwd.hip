@@ -193,8 +193,9 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_BMM_FWD, st);
-    const int nsplit = 8;
-    k_bmm_tiles<T, Q, N, true><<<dim3(b * K * G, nsplit), dim3(256), 0, st>>>(B, C, wt, L, G, K, nsplit);
+    constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
+    k_bmm_tiles<T, Q, N><<<dim3(b * K * G, (TILES + 3) / 4), dim3(256), 0, st>>>(
+        B, C, wt, static_cast<T*>(a.wtb), L, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);

@@ -75,44 +75,50 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, c
 
 // ---------------------------------------------------------------------------
 // W = C.B^T per (b, k, g), stored as lower-triangle 16x16 accumulator tiles in
-// the lane order the consumer reads them (4 elements per lane, 256 per tile):
-//   FWD_ORDER : tile (I, J) lane l holds W[16I + l%16][16J + 4q + r]
-//               (the consumer walks source tokens j inside a lane)
-//   BWD_ORDER : tile (I, J) lane l holds W[16I + 4q + r][16J + l%16]
-// K-dimension of every product is dstate.
-template <typename T, int Q, int N, bool FWD_ORDER>
+// the two lane orders the consumers read (4 elements per lane, 256 per tile):
+//   forward order  : tile (I, J) lane l holds W[16I + l%16][16J + 4q + r]
+//   backward order : tile (I, J) lane l holds W[16I + 4q + r][16J + l%16]
+// (q = l / 16, r = 0..3).  Both come from the same fragments of B rows J and
+// C rows I with the operands swapped; K of every product is dstate.  One
+// tile per wave: every load is issued before the first product.
+template <typename T, int Q, int N>
 __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, const T* __restrict__ C,
-                                                   T* __restrict__ Wt, int L, int G, int K, int nsplit) {
+                                                   T* __restrict__ wf, T* __restrict__ wb, int L, int G, int K) {
   constexpr int NT = Q / 16;
   constexpr int TILES = NT * (NT + 1) / 2;
+  constexpr int NK = (N + 31) / 32;
   const int bkg = blockIdx.x;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int idx = blockIdx.y * 4 + wave;
+  if (idx >= TILES) return;  // whole wave; no barrier in this kernel
+  int I = 0;
+  while ((I + 1) * (I + 2) / 2 <= idx) ++I;
+  const int J = idx - I * (I + 1) / 2;
   const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
-  T* out = Wt + (int64_t)bkg * TILES * 256;
-  const int slot = blockIdx.y * 4 + wave, nslots = nsplit * 4;
-  int idx = 0;
-  for (int I = 0; I < NT; ++I) {
-    for (int J = 0; J <= I; ++J, ++idx) {
-      if (idx % nslots != slot) continue;
-      // FWD_ORDER: D[row j][col i] = B_j . C_i  (A operand = B rows, B operand = C rows)
-      // BWD_ORDER: D[row i][col j] = C_i . B_j
-      const T* arow = FWD_ORDER ? B + ((row0 + 16 * J + c) * G + g) * N : C + ((row0 + 16 * I + c) * G + g) * N;
-      const T* brow = FWD_ORDER ? C + ((row0 + 16 * I + c) * G + g) * N : B + ((row0 + 16 * J + c) * G + g) * N;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const T* brow = B + ((row0 + 16 * J + c) * G + g) * N;
+  const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+  Frag<T> fb[NK], fc[NK];
 #pragma unroll
-      for (int ks = 0; ks < (N + 31) / 32; ++ks) {
-        Frag<T> fa, fb;
-        frag_load_k<N>(fa, arow, ks * 32 + 8 * q);
-        frag_load_k<N>(fb, brow, ks * 32 + 8 * q);
-        mma(acc, fa, fb);
-      }
-      typename Vec4<T>::type v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = from_f<T>(acc[r]);
-      *reinterpret_cast<typename Vec4<T>::type*>(out + (int64_t)idx * 256 + l * 4) = v;
-    }
+  for (int ks = 0; ks < NK; ++ks) {
+    frag_load_k<N>(fb[ks], brow, ks * 32 + 8 * q);
+    frag_load_k<N>(fc[ks], crow, ks * 32 + 8 * q);
   }
+  f4 af = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) {
+    mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
+    mma(ab, fc[ks], fb[ks]);  // [row i][col j] = C_i . B_j
+  }
+  typename Vec4<T>::type vf, vb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    vf[r] = from_f<T>(af[r]);
+    vb[r] = from_f<T>(ab[r]);
+  }
+  const int64_t o = ((int64_t)bkg * TILES + idx) * 256 + l * 4;
+  *reinterpret_cast<typename Vec4<T>::type*>(wf + o) = vf;
+  *reinterpret_cast<typename Vec4<T>::type*>(wb + o) = vb;
 }
 
 // ---------------------------------------------------------------------------

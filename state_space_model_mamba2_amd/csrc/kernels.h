@@ -16,11 +16,11 @@ struct Layout {
   int64_t b, L, H, P, N, G, Q, K;
   size_t esz;  // bytes per storage element (2 for bf16, 4 for fp32)
   // saved workspace
-  size_t cs_off, hin_off, wt_off, saved_bytes;
+  size_t cs_off, hin_off, wt_off, wtb_off, saved_bytes;
   // forward scratch
   size_t s_off, fwd_bytes;
   // backward scratch
-  size_t w_off, dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, dlpart_off, dlscal_off,
+  size_t dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, dlpart_off, dlscal_off,
       bwd_bytes;
   int64_t nslice;     // head slices of the dW kernel
   int64_t nslice_bc;  // head slices of the dB / dC head sums
@@ -35,7 +35,8 @@ struct FwdArgs {
   float* cs;    // [b][H][K][Q]
   void* hin;    // [b][K][H][P][N]  storage dtype
   float* S;     // [b][K][H][P][N]
-  void* wt;     // C.B^T tiles, forward order (kept in the saved workspace)
+  void* wt;     // C.B^T tiles, forward lane order (kept in the saved workspace)
+  void* wtb;    // C.B^T tiles, backward lane order (kept in the saved workspace)
 };
 
 struct BwdArgs {
@@ -43,10 +44,9 @@ struct BwdArgs {
   const float *A, *D;
   const float* cs;
   const void* hin;
-  const void* wf;  // C.B^T tiles, forward order (saved by the forward pass)
   void *dx, *ddt, *dB, *dC;
   float *dA, *dD;
-  void* w;         // C.B^T tiles, backward order
+  const void* w;   // C.B^T tiles, backward lane order (saved by the forward pass)
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
