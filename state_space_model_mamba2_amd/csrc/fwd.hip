@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   __shared__ __attribute__((aligned(16))) T Hs[P][HPITCH];
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
+  __shared__ __attribute__((aligned(16))) float bfac[Q];  // dt_j exp(cs_r - cs_j), r = last token of j's 32-token step
 
   const int bkh = blockIdx.x;
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
@@ -94,9 +95,12 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
 #pragma unroll
   for (int n = 0; n < QPT; ++n) {
     const int i = threadIdx.x + NTH * n;
+    // token r = i | 31 sits in the same wave (32-token steps align with waves)
+    const float csr = __shfl(csv[n], (threadIdx.x | 31) & (kWave - 1), kWave);
     if (Q % NTH == 0 || i < Q) {
       cs[i] = csv[n];
       dts[i] = dtv[n];
+      bfac[i] = __expf(csr - csv[n]) * dtv[n];
     }
   }
 #pragma unroll
@@ -140,21 +144,35 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
       for (int tp = 0; tp < TP; ++tp) acc[tp] *= e;
     }
 
-    // 2. intra-chunk: sum_{j <= i} W_ij exp(cs_i - cs_j) dt_j x_j
+    // 2. intra-chunk: sum_{j <= i} W_ij exp(cs_i - cs_j) dt_j x_j.  Steps of 32
+    // source tokens wholly before row tile I factor the decay at the step's
+    // last token r: exp(cs_i - cs_r) (one per lane) times bfac_j (both <= 1);
+    // the step holding the diagonal takes the masked direct form.
 #pragma unroll
     for (int J2 = 0; J2 < NJ2; ++J2) {
       if (2 * J2 > I) break;
       Frag<T> fa;                              // P^T as the B operand: col i, K = j (chained)
+      if (2 * J2 + 1 < I) {
+        const float ai = __expf(cs_i - cs[32 * J2 + 31]);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int J = 2 * J2 + half;
-        const int j0 = 16 * J + 4 * q;
-        const f4 csj = *reinterpret_cast<const f4*>(&cs[j0]);
-        const f4 dtj = *reinterpret_cast<const f4*>(&dts[j0]);
+        for (int half = 0; half < 2; ++half) {
+          const int J = 2 * J2 + half;
+          const f4 bj = *reinterpret_cast<const f4*>(&bfac[16 * J + 4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float m = (J <= I && j0 + r <= ci) ? __expf(cs_i - csj[r]) * dtj[r] : 0.0f;
-          frag_set<T>(fa, half * 4 + r, to_f(wv[set][J][r]) * m);
+          for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, to_f(wv[set][J][r]) * (ai * bj[r]));
+        }
+      } else {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int J = 2 * J2 + half;
+          const int j0 = 16 * J + 4 * q;
+          const f4 csj = *reinterpret_cast<const f4*>(&cs[j0]);
+          const f4 dtj = *reinterpret_cast<const f4*>(&dts[j0]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float m = (J <= I && j0 + r <= ci) ? __expf(cs_i - csj[r]) * dtj[r] : 0.0f;
+            frag_set<T>(fa, half * 4 + r, to_f(wv[set][J][r]) * m);
+          }
         }
       }
 #pragma unroll
