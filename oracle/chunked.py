@@ -18,7 +18,8 @@ ports, written out from its definition in the recurrence:
 and the backward, the reverse-mode gradient of <dy, y> through those steps:
 
     dHloc_k  = sum_i exp(cs_i) dy_i C_i^T
-    Gk       = dH_{k+1},  dH_K = 0,  dH_k = dHloc_k + exp(cs_{Q-1}) dH_{k+1}
+    Gk       = dH_{k+1},  dH_K = dS_fin (final-state cotangent, default 0),
+    dH_k     = dHloc_k + exp(cs_{Q-1}) dH_{k+1},   dS0 = dH_0
     dxt_j    = sum_{i>=j} Lam_ij W_ij dy_i + exp(cs_{Q-1} - cs_j) Gk B_j    (xt = dt x)
     dP_ij    = <dy_i, xt_j>,  R = dP o Lam o W
     dcs_i    = sum_j R_ij - sum_i' R_i'i + <dy_i, yoff_i> - q_i
@@ -33,6 +34,12 @@ and the backward, the reverse-mode gradient of <dy, y> through those steps:
 
 States are kept as [P][N] (headdim x dstate).  numpy einsum serves as the
 matrix product; nothing is blocked or fused beyond the chunking itself.
+
+When Q does not divide the sequence length, the last chunk is shorter: it
+holds the remaining L mod Q tokens, and the same steps apply with its own
+length.  It is evaluated as a chunk of that length that starts from the state
+the full chunks leave, and its initial-state gradient is the cotangent of the
+state leaving the full chunks.
 """
 from __future__ import annotations
 
@@ -42,8 +49,7 @@ import numpy as np
 def _split(x, dt, B, C, Q):
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if L % Q:
-        raise ValueError("seqlen must be a multiple of the chunk length")
+    assert L % Q == 0
     K = L // Q
     return (b, L, H, P, N, G, K,
             x.reshape(b, K, Q, H, P), dt.reshape(b, K, Q, H),
@@ -66,13 +72,46 @@ def _group_sum(a, G):
     return a.reshape(sh[:-2] + (G, H // G, sh[-1])).sum(-2)
 
 
-def ssd_chunked(x, dt, A, B, C, D, chunk, dy=None):
-    """Forward (and, with dy, backward) of the chunked algorithm.
+def ssd_chunked(x, dt, A, B, C, D, chunk, dy=None, initial_state=None, dfinal_state=None):
+    """Forward (and, with dy, backward) of the chunked algorithm, started from
+    initial_state (zero if None) with final-state cotangent dfinal_state
+    (zero if None).
 
-    Returns a dict holding the outputs, the gradients and every intermediate
-    (cs, S, Hin, W, dHloc, Gk, dcs, dl, dxt, dW, dC_off, dB_state)."""
+    Returns a dict holding the outputs and the gradients (dinitial_state
+    among them).  When the chunk length divides the sequence length it also
+    holds every intermediate (cs, S, Hin, W, dHloc, Gk, dcs, dl, dxt, dW,
+    dC_off, dB_state); with a shorter last chunk it holds the dicts of the two
+    parts under "full" and "tail" instead."""
     x, dt, A, B, C, D = (np.asarray(a, dtype=np.float64) for a in (x, dt, A, B, C, D))
     Q = int(chunk)
+    L = x.shape[1]
+    Lf = (L // Q) * Q
+    if Lf in (0, L):
+        return _chunked_aligned(x, dt, A, B, C, D, Q if Lf else L, dy, initial_state, dfinal_state)
+    # Shorter last chunk of L - Lf tokens.  Its entry state is what the full
+    # chunks leave; the full chunks' backward needs the tail's dS0 as their
+    # final-state cotangent, so the full part runs forward first.
+    dyf = None if dy is None else np.asarray(dy, dtype=np.float64)
+    full_fwd = _chunked_aligned(x[:, :Lf], dt[:, :Lf], A, B[:, :Lf], C[:, :Lf], D, Q, None, initial_state, None)
+    tail = _chunked_aligned(x[:, Lf:], dt[:, Lf:], A, B[:, Lf:], C[:, Lf:], D, L - Lf,
+                            None if dyf is None else dyf[:, Lf:], full_fwd["final_state"], dfinal_state)
+    out = dict(y=np.concatenate([full_fwd["y"], tail["y"]], axis=1), final_state=tail["final_state"],
+               tail=tail)
+    if dyf is None:
+        out["full"] = full_fwd
+        return out
+    full = _chunked_aligned(x[:, :Lf], dt[:, :Lf], A, B[:, :Lf], C[:, :Lf], D, Q, dyf[:, :Lf], initial_state,
+                            tail["dinitial_state"])
+    out["full"] = full
+    for k in ("dx", "ddt", "dB", "dC"):
+        out[k] = np.concatenate([full[k], tail[k]], axis=1)
+    out["dA"] = full["dA"] + tail["dA"]
+    out["dD"] = full["dD"] + tail["dD"]
+    out["dinitial_state"] = full["dinitial_state"]
+    return out
+
+
+def _chunked_aligned(x, dt, A, B, C, D, Q, dy, initial_state, dfinal_state):
     b, L, H, P, N, G, K, xc, dtc, Bc, Cc = _split(x, dt, B, C, Q)
     hg = np.arange(H) // (H // G)
     Bh, Ch = Bc[:, :, :, hg, :], Cc[:, :, :, hg, :]           # [b,K,Q,H,N]
@@ -82,6 +121,8 @@ def ssd_chunked(x, dt, A, B, C, D, chunk, dy=None):
     w = np.exp(cs_last[:, :, None, :] - cs) * dtc
     S = np.einsum("bkqh,bkqhp,bkqhn->bkhpn", w, xc, Bh)
     Hin = np.zeros((b, K + 1, H, P, N))
+    if initial_state is not None:
+        Hin[:, 0] = initial_state
     for k in range(K):
         Hin[:, k + 1] = np.exp(cs_last[:, k])[..., None, None] * Hin[:, k] + S[:, k]
 
@@ -103,6 +144,8 @@ def ssd_chunked(x, dt, A, B, C, D, chunk, dy=None):
     dyc = np.asarray(dy, dtype=np.float64).reshape(b, K, Q, H, P)
     dHloc = np.einsum("bkih,bkihp,bkihn->bkhpn", ecs, dyc, Ch)
     dH = np.zeros((b, K + 1, H, P, N))
+    if dfinal_state is not None:
+        dH[:, K] = dfinal_state
     for k in reversed(range(K)):
         dH[:, k] = dHloc[:, k] + np.exp(cs_last[:, k])[..., None, None] * dH[:, k + 1]
     Gk = dH[:, 1:]                                            # Gk[:, k] = dH_{k+1}
@@ -132,6 +175,6 @@ def ssd_chunked(x, dt, A, B, C, D, chunk, dy=None):
 
     out.update(dx=dx.reshape(b, L, H, P), ddt=ddt.reshape(b, L, H), dA=dA,
                dB=dB.reshape(b, L, G, N), dC=dC.reshape(b, L, G, N), dD=dD,
-               dHloc=dHloc, Gk=Gk, dcs=dcs, dl=dl, dxt=dxt.reshape(b, L, H, P), dW=dW,
+               dinitial_state=dH[:, 0].copy(), dHloc=dHloc, Gk=Gk, dcs=dcs, dl=dl, dxt=dxt.reshape(b, L, H, P), dW=dW,
                dC_off=dC_off.reshape(b, L, G, N), dB_state=dB_state.reshape(b, L, G, N))
     return out

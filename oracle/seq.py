@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE (see the package docstring).  Arrays are float64 numpy
 arrays in the layouts x/dy [b][L][H][P], dt [b][L][H], B/C [b][L][G][N],
-A/D [H]; final_state is [b][H][P][N].
+A/D [H]; final_state, initial_state, dinitial_state and dfinal_state are
+[b][H][P][N] (element [p][n] is the state's entry [n][p]).
 """
 from __future__ import annotations
 
@@ -34,9 +35,9 @@ def _load():
         build()
         lib = ctypes.CDLL(LIB_PATH)
         i64, dp, ci = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_int
-        lib.oracle_ssd_fwd.argtypes = [i64] * 6 + [dp] * 8 + [ci]
+        lib.oracle_ssd_fwd.argtypes = [i64] * 6 + [dp] * 9 + [ci]
         lib.oracle_ssd_fwd.restype = ci
-        lib.oracle_ssd_bwd.argtypes = [i64] * 6 + [dp] * 13 + [ci]
+        lib.oracle_ssd_bwd.argtypes = [i64] * 6 + [dp] * 16 + [ci]
         lib.oracle_ssd_bwd.restype = ci
         lib.oracle_max_threads.restype = ci
         _lib = lib
@@ -61,23 +62,43 @@ def _dims(x, B):
     return b, L, H, P, N, G
 
 
-def ssd_fwd(x, dt, A, B, C, D, nthreads: int = 0):
-    """y [b,L,H,P] and final_state [b,H,P,N] of the sequential recurrence."""
+def _state(a, b, H, P, N):
+    if a is None:
+        return None
+    a = _f64(a)
+    if a.shape != (b, H, P, N):
+        raise ValueError(f"state must have shape {(b, H, P, N)}, got {a.shape}")
+    return a
+
+
+def _pn(a):
+    return _p(a) if a is not None else None
+
+
+def ssd_fwd(x, dt, A, B, C, D, initial_state=None, nthreads: int = 0):
+    """y [b,L,H,P] and final_state [b,H,P,N] of the sequential recurrence
+    started from initial_state (zero if None)."""
     x, dt, A, B, C, D = map(_f64, (x, dt, A, B, C, D))
     b, L, H, P, N, G = _dims(x, B)
+    s0 = _state(initial_state, b, H, P, N)
     y = np.empty_like(x)
     fs = np.empty((b, H, P, N), dtype=np.float64)
     rc = _load().oracle_ssd_fwd(b, L, H, P, N, G, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D),
-                                _p(y), _p(fs), nthreads)
+                                _pn(s0), _p(y), _p(fs), nthreads)
     if rc:
         raise RuntimeError(f"oracle_ssd_fwd failed ({rc})")
     return y, fs
 
 
-def ssd_bwd(x, dt, A, B, C, D, dy, nthreads: int = 0):
-    """Gradients (dx, ddt, dA, dB, dC, dD) of <dy, y> w.r.t. the inputs."""
+def ssd_bwd(x, dt, A, B, C, D, dy, initial_state=None, dfinal_state=None, nthreads: int = 0):
+    """Gradients (dx, ddt, dA, dB, dC, dD, dinitial_state) of
+    <dy, y> + <dfinal_state, final_state> w.r.t. the inputs, for the
+    recurrence started from initial_state (None means zero for both)."""
     x, dt, A, B, C, D, dy = map(_f64, (x, dt, A, B, C, D, dy))
     b, L, H, P, N, G = _dims(x, B)
+    s0 = _state(initial_state, b, H, P, N)
+    dfs = _state(dfinal_state, b, H, P, N)
+    ds0 = np.empty((b, H, P, N), dtype=np.float64)
     dx = np.empty_like(x)
     ddt = np.empty_like(dt)
     dA = np.empty_like(A)
@@ -85,7 +106,8 @@ def ssd_bwd(x, dt, A, B, C, D, dy, nthreads: int = 0):
     dC = np.empty_like(C)
     dD = np.empty_like(D)
     rc = _load().oracle_ssd_bwd(b, L, H, P, N, G, _p(x), _p(dt), _p(A), _p(B), _p(C), _p(D), _p(dy),
-                                _p(dx), _p(ddt), _p(dA), _p(dB), _p(dC), _p(dD), nthreads)
+                                _pn(s0), _pn(dfs), _p(dx), _p(ddt), _p(dA), _p(dB), _p(dC), _p(dD),
+                                _p(ds0), nthreads)
     if rc:
         raise RuntimeError(f"oracle_ssd_bwd failed ({rc})")
-    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD)
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dinitial_state=ds0)

@@ -12,16 +12,19 @@
  * recurrence, evaluated token by token with no chunking:
  *
  *   for every batch b and head h, with group g = h / (nheads / ngroups):
- *     state S_{-1} = 0                                   (dstate x headdim)
+ *     state S_{-1} = S0 (the initial state, zero when none is given;
+ *                        dstate x headdim)
  *     a_t   = exp(dt_t * A_h)
  *     S_t   = a_t * S_{t-1} + dt_t * B_t x_t^T          (B_t: dstate, x_t: headdim)
  *     y_t   = S_t^T C_t + D_h * x_t
  *   final_state[b][h][p][n] = S_{L-1}[n][p]
  *
- * Backward: the exact reverse-mode gradient of the scalar  sum_t <dy_t, y_t>
- * (zero cotangent on final_state), derived by hand from the recurrence:
+ * Backward: the exact reverse-mode gradient of the scalar
+ *   sum_t <dy_t, y_t> + <dS_fin, final_state>
+ * (dS_fin, the final-state cotangent, zero when none is given), derived by
+ * hand from the recurrence:
  *
- *   Gt = dL/dS_t satisfies  G_{L-1} = C_{L-1} dy_{L-1}^T,
+ *   Gt = dL/dS_t satisfies  G_{L-1} = C_{L-1} dy_{L-1}^T + dS_fin,
  *                           G_t     = C_t dy_t^T + a_{t+1} G_{t+1}
  *   dC_t  += S_t dy_t                      (summed over the heads of the group)
  *   dx_t   = dt_t G_t^T B_t + D_h dy_t
@@ -30,13 +33,17 @@
  *   ddt_t  = B_t^T G_t x_t + A_h r_t
  *   dA_h  += dt_t r_t
  *   dD_h  += <dy_t, x_t>
+ *   dS0    = a_0 G_0                       (gradient of the initial state)
  *
  * S_{t-1} is re-derived during the reverse sweep from float64 checkpoints
  * taken every ORACLE_SEG steps; re-running the same float64 operations in the
  * same order reproduces the forward states bit for bit.
  *
  * Layouts (row-major, float64): x, y, dx, dy [b][L][H][P]; dt, ddt [b][L][H];
- * B, C, dB, dC [b][L][G][N]; A, D, dA, dD [H]; final_state [b][H][P][N].
+ * B, C, dB, dC [b][L][G][N]; A, D, dA, dD [H]; final_state, initial state,
+ * its gradient and the final-state cotangent [b][H][P][N] (element [p][n]
+ * is S[n][p]).  Every state pointer may be NULL: a missing initial state or
+ * cotangent is zero, a missing gradient output is not written.
  */
 #include <math.h>
 #include <stdint.h>
@@ -74,10 +81,21 @@ static void step_state(double *S, int64_t N, int64_t P, double a, double dt,
     }
 }
 
+/* S[n][p] = src[p][n] (src in the [P][N] interface layout), or zero. */
+static void load_state(double *S, const double *src, int64_t N, int64_t P) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t p = 0; p < P; ++p) S[n * P + p] = src ? src[p * N + n] : 0.0;
+}
+
+static void store_state(double *dst, const double *S, int64_t N, int64_t P) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t p = 0; p < P; ++p) dst[p * N + n] = S[n * P + p];
+}
+
 int oracle_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                    const double *x, const double *dt, const double *A,
                    const double *B, const double *C, const double *D,
-                   double *y, double *final_state, int nthreads) {
+                   const double *init_state, double *y, double *final_state, int nthreads) {
     if (batch <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G) return 1;
     set_threads(nthreads);
     const int64_t hpg = H / G;
@@ -91,6 +109,7 @@ int oracle_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
             err = 2;
             continue;
         }
+        load_state(S, init_state ? init_state + (b * H + h) * P * N : NULL, N, P);
         for (int64_t t = 0; t < L; ++t) {
             const double dtt = dt[(b * L + t) * H + h];
             const double a = exp(dtt * A[h]);
@@ -106,11 +125,7 @@ int oracle_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
                 for (int64_t p = 0; p < P; ++p) yt[p] += cn * row[p];
             }
         }
-        if (final_state) {
-            double *fs = final_state + (b * H + h) * P * N;
-            for (int64_t n = 0; n < N; ++n)
-                for (int64_t p = 0; p < P; ++p) fs[p * N + n] = S[n * P + p];
-        }
+        if (final_state) store_state(final_state + (b * H + h) * P * N, S, N, P);
         free(S);
     }
     return err;
@@ -119,8 +134,9 @@ int oracle_ssd_fwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
 int oracle_ssd_bwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                    const double *x, const double *dt, const double *A,
                    const double *B, const double *C, const double *D, const double *dy,
+                   const double *init_state, const double *dfinal_state,
                    double *dx, double *ddt, double *dA, double *dB, double *dC, double *dD,
-                   int nthreads) {
+                   double *dinit_state, int nthreads) {
     if (batch <= 0 || L <= 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G) return 1;
     set_threads(nthreads);
     const int64_t hpg = H / G;
@@ -140,7 +156,7 @@ int oracle_ssd_bwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t bh = 0; bh < batch * H; ++bh) {
         const int64_t b = bh / H, h = bh % H, g = h / hpg;
-        /* ckpt[s] = state before segment s, i.e. S_{s*SEG - 1} (zero for s = 0). */
+        /* ckpt[s] = state before segment s, i.e. S_{s*SEG - 1} (S0 for s = 0). */
         double *ckpt = (double *)calloc((size_t)(nseg * NP), sizeof(double));
         double *seg = (double *)malloc((size_t)(ORACLE_SEG * NP) * sizeof(double));
         double *Gs = (double *)calloc((size_t)NP, sizeof(double));
@@ -154,7 +170,7 @@ int oracle_ssd_bwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
         /* Forward sweep: record checkpoints. */
         {
             double *S = seg; /* scratch state */
-            memset(S, 0, (size_t)NP * sizeof(double));
+            load_state(S, init_state ? init_state + (b * H + h) * P * N : NULL, N, P);
             for (int64_t t = 0; t < L; ++t) {
                 if (t % ORACLE_SEG == 0) memcpy(ckpt + (t / ORACLE_SEG) * NP, S, (size_t)NP * sizeof(double));
                 const double dtt = dt[(b * L + t) * H + h];
@@ -163,7 +179,9 @@ int oracle_ssd_bwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
             }
         }
         double dA_acc = 0.0, dD_acc = 0.0;
-        /* Reverse sweep.  Gs holds a_{t+1} G_{t+1} on entry to step t. */
+        /* Reverse sweep.  Gs holds a_{t+1} G_{t+1} on entry to step t; on
+         * entry to the last step that is the final-state cotangent. */
+        load_state(Gs, dfinal_state ? dfinal_state + (b * H + h) * P * N : NULL, N, P);
         for (int64_t s = nseg - 1; s >= 0; --s) {
             const int64_t t0 = s * ORACLE_SEG;
             const int64_t t1 = (t0 + ORACLE_SEG < L) ? t0 + ORACLE_SEG : L;
@@ -226,6 +244,8 @@ int oracle_ssd_bwd(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N, in
                 for (int64_t i = 0; i < NP; ++i) Gs[i] *= a;
             }
         }
+        /* Gs now holds a_0 G_0 = dL/dS_{-1}. */
+        if (dinit_state) store_state(dinit_state + (b * H + h) * P * N, Gs, N, P);
         dAh[b * H + h] = dA_acc;
         dDh[b * H + h] = dD_acc;
         free(ckpt); free(seg); free(Gs); free(tmp);
