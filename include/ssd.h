@@ -8,13 +8,18 @@
  * kernels for.  The post gives no formula; the layer it names computes, for
  * every batch b and head h (group g = h / (nheads / ngroups)):
  *
- *     S_{-1} = 0                                        state, dstate x headdim
+ *     S_{-1} = S0 (initial state, zero unless given)    state, dstate x headdim
  *     S_t    = exp(dt_t A_h) S_{t-1} + dt_t B_t x_t^T
  *     y_t    = S_t^T C_t + D_h x_t
+ *     final_state = S_{L-1}
  *
  * with a scalar A_h and D_h per head.  ssd_bwd returns the exact reverse-mode
- * gradients of the scalar sum_t <dy_t, y_t> (the cotangent of final_state is
- * zero): dx, ddt, dA, dB, dC, dD.
+ * gradients of the scalar sum_t <dy_t, y_t> + <dS_fin, final_state> (dS_fin,
+ * the final-state cotangent, zero unless given): dx, ddt, dA, dB, dC, dD and,
+ * on request, dS0.  A nonzero initial state and cotangent are what carry a
+ * sequence across calls: a sequence cut in two runs as two calls, the second
+ * started from the first's final_state, and the second's dS0 is the first's
+ * dS_fin in the backward.
  *
  * Preconditions (not checked on the device): A_h <= 0 and dt >= 0, so every
  * per-step decay lies in [0, 1]; dt is the step after any softplus.
@@ -24,8 +29,9 @@
  *     dt, ddt          [batch][seqlen][nheads]             dtype
  *     B, C, dB, dC     [batch][seqlen][ngroups][dstate]    dtype
  *     A, D, dA, dD     [nheads]                            float32
- *     final_state      [batch][nheads][headdim][dstate]    float32
- *                      (element [p][n] is S_{L-1}[n][p])
+ *     final_state, initial_state, dfinal_state, dinitial_state
+ *                      [batch][nheads][headdim][dstate]    float32
+ *                      (element [p][n] is the state's entry [n][p])
  * "dtype" is float32 (SSD_F32) or bfloat16 (SSD_BF16); accumulation is
  * always float32.  Every pointer is a device pointer aligned to 16 bytes.
  *
@@ -73,7 +79,7 @@ typedef struct {
 } ssd_shape;
 
 /* Forward-to-backward context, filled by ssd_fwd.  It borrows the input
- * pointers and the saved workspace: x, dt, A, B, C, D and saved_ws must stay
+ * pointers (not initial_state) and the saved workspace: x, dt, A, B, C, D and saved_ws must stay
  * alive and unmodified until the ssd_bwd that consumes this context has
  * finished on its stream. */
 typedef struct {
@@ -123,7 +129,9 @@ size_t ssd_bwd_scratch_bytes(const ssd_shape *shape);
  * compiled in; otherwise the error ssd_fwd would return for it. */
 ssd_status ssd_check_shape(const ssd_shape *shape);
 
-/* Forward pass: y and final_state from x, dt, A, B, C, D.
+/* Forward pass: y and final_state from x, dt, A, B, C, D, starting from
+ * initial_state (NULL means zero; it is read during the call only, the
+ * backward keeps its own copy in saved_ws).
  * y is written; final_state is written if non-NULL.  saved_ws (>=
  * ssd_saved_bytes) receives what ssd_bwd needs; saved_out, if non-NULL, is
  * filled with the context ssd_bwd consumes.  scratch (>= ssd_fwd_scratch_bytes)
@@ -132,16 +140,21 @@ ssd_status ssd_check_shape(const ssd_shape *shape);
 ssd_status ssd_fwd(const ssd_shape *shape,
                    const void *x, const void *dt, const float *A,
                    const void *B, const void *C, const float *D,
+                   const float *initial_state,
                    void *y, float *final_state,
                    void *saved_ws, size_t saved_ws_bytes, ssd_saved *saved_out,
                    void *scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe *probe);
 
-/* Backward pass: gradients of sum <dy, y> for the forward that filled
- * `saved`.  dx, ddt, dA, dB, dC, dD are overwritten (not accumulated).
+/* Backward pass: gradients of sum <dy, y> + <dfinal_state, final_state>
+ * for the forward that filled `saved` (dfinal_state NULL means zero).
+ * dx, ddt, dA, dB, dC, dD are overwritten (not accumulated); dinitial_state,
+ * the gradient of the forward's initial state, is written if non-NULL (also
+ * when the forward started from zero).
  * scratch must hold ssd_bwd_scratch_bytes(&saved->shape). probe may be NULL. */
-ssd_status ssd_bwd(const ssd_saved *saved, const void *dy,
+ssd_status ssd_bwd(const ssd_saved *saved, const void *dy, const float *dfinal_state,
                    void *dx, void *ddt, float *dA, void *dB, void *dC, float *dD,
+                   float *dinitial_state,
                    void *scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe *probe);
 

@@ -53,9 +53,9 @@ def load():
         f = getattr(lib, name)
         f.argtypes, f.restype = [PShape], sz
     lib.ssd_check_shape.argtypes, lib.ssd_check_shape.restype = [PShape], st
-    lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
+    lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
     lib.ssd_fwd.restype = st
-    lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
+    lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
     lib.ssd_bwd.restype = st
     lib.ssd_status_string.argtypes, lib.ssd_status_string.restype = [st], ctypes.c_char_p
     lib.ssd_kernel_name.argtypes, lib.ssd_kernel_name.restype = [ctypes.c_int32], ctypes.c_char_p

@@ -126,9 +126,9 @@ size_t ssd_fwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_
 size_t ssd_bwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_layout(s).bwd_bytes : 0; }
 
 ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
-                   const float* D, void* y, float* final_state, void* saved_ws, size_t saved_ws_bytes,
-                   ssd_saved* saved_out, void* scratch, size_t scratch_bytes, hipStream_t stream,
-                   const ssd_probe* probe) {
+                   const float* D, const float* initial_state, void* y, float* final_state, void* saved_ws,
+                   size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch, size_t scratch_bytes,
+                   hipStream_t stream, const ssd_probe* probe) {
   const ssd_status st = check_shape(s);
   if (st != SSD_OK) return st;
   if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_INVALID_ARGUMENT;
@@ -136,12 +136,14 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
   if (final_state && !aligned16(final_state)) return SSD_ERR_INVALID_ARGUMENT;
+  if (initial_state && !aligned16(initial_state)) return SSD_ERR_INVALID_ARGUMENT;
   const Layout lay = make_layout(s);
   if (!saved_ws || saved_ws_bytes < lay.saved_bytes) return SSD_ERR_WORKSPACE;
   if (!scratch || scratch_bytes < lay.fwd_bytes) return SSD_ERR_WORKSPACE;
 
   FwdArgs a{};
   a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y; a.final_state = final_state;
+  a.init = initial_state;
   a.cs = at<float>(saved_ws, lay.cs_off);
   a.hin = at<char>(saved_ws, lay.hin_off);
   a.S = at<float>(scratch, lay.s_off);
@@ -171,15 +173,17 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   return SSD_OK;
 }
 
-ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, float* dA, void* dB, void* dC, float* dD,
-                   void* scratch, size_t scratch_bytes, hipStream_t stream, const ssd_probe* probe) {
+ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_state, void* dx, void* ddt, float* dA,
+                   void* dB, void* dC, float* dD, float* dinitial_state, void* scratch, size_t scratch_bytes,
+                   hipStream_t stream, const ssd_probe* probe) {
   if (!sv) return SSD_ERR_INVALID_ARGUMENT;
   const ssd_shape* s = &sv->shape;
   const ssd_status st = check_shape(s);
   if (st != SSD_OK) return st;
   if (!sv->x || !sv->dt || !sv->A || !sv->B || !sv->C || !sv->D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {sv->x, sv->dt, sv->A, sv->B, sv->C, sv->D, dy, dx, ddt, dA, dB, dC, dD, sv->saved_ws, scratch};
+  const void* ptrs[] = {sv->x, sv->dt, sv->A, sv->B, sv->C, sv->D, dy, dx, ddt, dA, dB, dC, dD, sv->saved_ws, scratch,
+                        dfinal_state, dinitial_state};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
   const Layout lay = make_layout(s);
@@ -192,6 +196,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, void* dx, void* ddt, flo
   a.hin = at<char>(sv->saved_ws, lay.hin_off);
   a.w = at<char>(sv->saved_ws, lay.wtb_off);
   a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
+  a.dfinal = dfinal_state; a.dinit = dinitial_state;
   a.dhloc = at<float>(scratch, lay.dhloc_off);
   a.gst = at<char>(scratch, lay.g_off);
   a.dw = at<float>(scratch, lay.dw_off);

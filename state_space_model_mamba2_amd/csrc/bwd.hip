@@ -916,7 +916,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
     const int PN = P * N;
-    k_state_passing_bwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(a.dhloc, a.cs, gst, H, K, PN);
+    k_state_passing_bwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(a.dhloc, a.cs, a.dfinal, gst, a.dinit, H, K, PN);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);

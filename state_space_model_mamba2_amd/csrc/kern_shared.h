@@ -234,17 +234,18 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
 // ---------------------------------------------------------------------------
 // Forward state passing, elementwise over the P*N state entries of each
 // (b, h) and sequential over chunks:
-//   hin[k] = h;  h = exp(cs_{Q-1}(k)) h + S[k];   final = h.
+//   h = init (zero if null);  hin[k] = h;  h = exp(cs_{Q-1}(k)) h + S[k];   final = h.
 // Each thread owns 4 consecutive entries (16-byte loads of S).
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restrict__ S, const float* __restrict__ cs,
-                                                           T* __restrict__ hin, float* __restrict__ final_state,
-                                                           int H, int K, int PN) {
+                                                           const float* __restrict__ init, T* __restrict__ hin,
+                                                           float* __restrict__ final_state, int H, int K, int PN) {
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= PN) return;
   const int bh = blockIdx.y, h = bh % H, b = bh / H;
   const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
   f4 st = {0.f, 0.f, 0.f, 0.f};
+  if (init) st = *reinterpret_cast<const f4*>(init + (int64_t)bh * PN + e);
   for (int k = 0; k < K; ++k) {
     const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
     const f4 s = *reinterpret_cast<const f4*>(S + off);
@@ -258,16 +259,20 @@ __global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restri
   if (final_state) *reinterpret_cast<f4*>(final_state + (int64_t)bh * PN + e) = st;
 }
 
-// Reverse state passing: g = 0; for k = K-1..0: gout[k] = g; g = dhloc[k] + exp(cs_{Q-1}(k)) g.
-// gout[k] is the gradient w.r.t. the state leaving chunk k.
+// Reverse state passing: g = dfinal (zero if null); for k = K-1..0:
+// gout[k] = g; g = dhloc[k] + exp(cs_{Q-1}(k)) g.  gout[k] is the gradient
+// w.r.t. the state leaving chunk k; the g left at the end is the gradient
+// w.r.t. the initial state, written to dinit if non-null.
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_state_passing_bwd(const float* __restrict__ dhloc, const float* __restrict__ cs,
-                                                           T* __restrict__ gout, int H, int K, int PN) {
+                                                           const float* __restrict__ dfinal, T* __restrict__ gout,
+                                                           float* __restrict__ dinit, int H, int K, int PN) {
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= PN) return;
   const int bh = blockIdx.y, h = bh % H, b = bh / H;
   const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
   f4 gs = {0.f, 0.f, 0.f, 0.f};
+  if (dfinal) gs = *reinterpret_cast<const f4*>(dfinal + (int64_t)bh * PN + e);
   for (int k = K - 1; k >= 0; --k) {
     const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
     typename Vec4<T>::type v;
@@ -278,6 +283,7 @@ __global__ __launch_bounds__(256) void k_state_passing_bwd(const float* __restri
     const float alpha = __expf(csb[(int64_t)k * Q]);
     gs = d + alpha * gs;
   }
+  if (dinit) *reinterpret_cast<f4*>(dinit + (int64_t)bh * PN + e) = gs;
 }
 
 }  // namespace ssd

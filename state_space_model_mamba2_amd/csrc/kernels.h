@@ -30,6 +30,7 @@ struct Layout {
 struct FwdArgs {
   const void *x, *dt, *B, *C;
   const float *A, *D;
+  const float* init;  // [b][H][P][N] initial state, or null for zero
   void* y;
   float* final_state;
   float* cs;    // [b][H][K][Q]
@@ -46,6 +47,8 @@ struct BwdArgs {
   const void* hin;
   void *dx, *ddt, *dB, *dC;
   float *dA, *dD;
+  const float* dfinal;  // [b][H][P][N] final-state cotangent, or null for zero
+  float* dinit;         // [b][H][P][N] initial-state gradient, or null
   const void* w;   // C.B^T tiles, backward lane order (saved by the forward pass)
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)

@@ -18,6 +18,15 @@ Recipe (one draw per tensor, in this order, from numpy's PCG64 generator
 
     dt = softplus(dt_raw + dt_bias)             (the post-softplus step size)
 
+States for the runs that start from a given state or carry a final-state
+cotangent come from their own generator, ``default_rng([seed, 1])``, so the
+draws above do not move:
+
+    initial_state ~ N(0, 1)                     [batch, nheads, headdim, dstate]
+    dfinal_state  ~ N(0, 1)                     [batch, nheads, headdim, dstate]
+
+both float32 in every mode.
+
 The dt parameterisation (softplus of a per-head bias drawn log-uniformly so
 that softplus(bias) lies in [lo, hi]) and A = -exp(U[ln 1, ln 16]) follow the
 usual Mamba-2 initialisation; they only shape the synthetic workload.
@@ -140,3 +149,13 @@ def generate(shape: Shape, seed: int = 0, dt_sigma2: float = 0.5) -> Inputs:
     elif s.dtype != "f32":
         raise ValueError(f"unknown dtype {s.dtype!r}")
     return Inputs(s, x, dt, A, B, C, D, dy)
+
+
+def generate_states(shape: Shape, seed: int = 0):
+    """(initial_state, dfinal_state), float32 [batch, nheads, headdim, dstate]."""
+    s = shape
+    rng = np.random.default_rng([seed, 1])
+    dims = (s.batch, s.nheads, s.headdim, s.dstate)
+    s0 = rng.standard_normal(dims, dtype=np.float32)
+    dfs = rng.standard_normal(dims, dtype=np.float32)
+    return s0, dfs

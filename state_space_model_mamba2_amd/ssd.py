@@ -1,7 +1,8 @@
 """Python face of libssd: the Mamba-2 SSD chunked scan, forward and backward.
 
-    y, final_state, ctx = fwd(x, dt, A, B, C, D, chunk)
-    grads = bwd(dy, ctx)          # dict: dx, ddt, dA, dB, dC, dD
+    y, final_state, ctx = fwd(x, dt, A, B, C, D, chunk, initial_state=None)
+    grads = bwd(dy, ctx, dfinal_state=None)   # dict: dx, ddt, dA, dB, dC, dD
+                                              # (+ dinitial_state on request)
 
 Tensors are torch tensors on the GPU (torch supplies device memory and the
 stream).  Every step of the computation runs in libssd's HIP kernels; this
@@ -9,8 +10,9 @@ module only checks dtypes/contiguity, allocates outputs and workspaces and
 passes pointers.  It raises if libssd.so has not been built.
 
 Layouts: x, y, dx, dy [b, L, H, P]; dt, ddt [b, L, H]; B, C, dB, dC [b, L, G, N];
-A, D, dA, dD [H] float32; final_state [b, H, P, N] float32.  x, dt, B, C, dy
-share one dtype (torch.bfloat16 or torch.float32).
+A, D, dA, dD [H] float32; final_state, initial_state, dfinal_state and
+dinitial_state [b, H, P, N] float32.  x, dt, B, C, dy share one dtype
+(torch.bfloat16 or torch.float32).
 """
 from __future__ import annotations
 
@@ -91,12 +93,22 @@ def _validate(x, dt, A, B, C, D):
         raise ValueError("shape mismatch among x, B, C")
 
 
-def fwd(x, dt, A, B, C, D, chunk: int, *, stream=None, probe: _lib.Probe | None = None,
-        out: torch.Tensor | None = None, scratch: torch.Tensor | None = None, want_final_state: bool = True):
-    """Forward pass.  Returns (y, final_state or None, Context)."""
+def _check_state(t, shape, name):
+    if t is None:
+        return
+    want = (shape.batch, shape.nheads, shape.headdim, shape.dstate)
+    if t.dtype != torch.float32 or tuple(t.shape) != want or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {want}")
+
+
+def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = None, stream=None,
+        probe: _lib.Probe | None = None, out: torch.Tensor | None = None, scratch: torch.Tensor | None = None,
+        want_final_state: bool = True):
+    """Forward pass from initial_state (zero if None).  Returns (y, final_state or None, Context)."""
     lib = _lib.load()
     _validate(x, dt, A, B, C, D)
     shape = shape_of(x, B, chunk, _DTYPES[x.dtype])
+    _check_state(initial_state, shape, "initial_state")
     _check(lib.ssd_check_shape(ctypes.byref(shape)), "ssd_fwd")
     dev = x.device
     saved_bytes = lib.ssd_saved_bytes(ctypes.byref(shape))
@@ -109,7 +121,7 @@ def fwd(x, dt, A, B, C, D, chunk: int, *, stream=None, probe: _lib.Probe | None 
         scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=dev)
     saved = _lib.Saved()
     code = lib.ssd_fwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                       _ptr(y), _ptr(fs) if fs is not None else None, _ptr(saved_ws), saved_bytes,
+                       _ptr(initial_state) if initial_state is not None else None, _ptr(y), _ptr(fs) if fs is not None else None, _ptr(saved_ws), saved_bytes,
                        ctypes.byref(saved), _ptr(scratch), scratch.numel(), _stream_handle(stream),
                        ctypes.byref(probe) if probe is not None else None)
     _check(code, "ssd_fwd")
@@ -117,12 +129,16 @@ def fwd(x, dt, A, B, C, D, chunk: int, *, stream=None, probe: _lib.Probe | None 
     return y, fs, ctx
 
 
-def bwd(dy, ctx: Context, *, stream=None, probe: _lib.Probe | None = None, scratch: torch.Tensor | None = None):
-    """Backward pass: gradients of sum(dy * y).  Returns a dict of tensors."""
+def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dinitial_state: bool = False,
+        stream=None, probe: _lib.Probe | None = None, scratch: torch.Tensor | None = None):
+    """Backward pass: gradients of sum(dy * y) + sum(dfinal_state * final_state)
+    (dfinal_state None means zero).  Returns a dict of tensors, with
+    dinitial_state when want_dinitial_state is set."""
     lib = _lib.load()
     x, dt, A, B, C, D = ctx.tensors
     if dy.dtype != x.dtype or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
         raise ValueError("dy must be a contiguous GPU tensor with x's shape and dtype")
+    _check_state(dfinal_state, ctx.shape, "dfinal_state")
     scratch_bytes = lib.ssd_bwd_scratch_bytes(ctypes.byref(ctx.shape))
     if scratch is None or scratch.numel() < scratch_bytes:
         scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=x.device)
@@ -132,11 +148,18 @@ def bwd(dy, ctx: Context, *, stream=None, probe: _lib.Probe | None = None, scrat
     dC = torch.empty_like(C)
     dA = torch.empty_like(A)
     dD = torch.empty_like(D)
-    code = lib.ssd_bwd(ctypes.byref(ctx.saved), _ptr(dy), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC),
-                       _ptr(dD), _ptr(scratch), scratch.numel(), _stream_handle(stream),
-                       ctypes.byref(probe) if probe is not None else None)
+    s = ctx.shape
+    ds0 = torch.empty((s.batch, s.nheads, s.headdim, s.dstate), dtype=torch.float32,
+                      device=x.device) if want_dinitial_state else None
+    code = lib.ssd_bwd(ctypes.byref(ctx.saved), _ptr(dy), _ptr(dfinal_state) if dfinal_state is not None else None,
+                       _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+                       _ptr(ds0) if ds0 is not None else None, _ptr(scratch), scratch.numel(),
+                       _stream_handle(stream), ctypes.byref(probe) if probe is not None else None)
     _check(code, "ssd_bwd")
-    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD)
+    g = dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD)
+    if ds0 is not None:
+        g["dinitial_state"] = ds0
+    return g
 
 
 def to_device(inp, device="cuda"):

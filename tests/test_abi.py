@@ -83,11 +83,11 @@ FAKE = 0x100000  # aligned, never dereferenced: every call below fails validatio
 
 
 def fwd(lib, s, **over):
-    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, y=FAKE, fs=FAKE, ws=FAKE, ws_bytes=0,
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, s0=None, y=FAKE, fs=FAKE, ws=FAKE, ws_bytes=0,
                 scratch=FAKE, scratch_bytes=0)
     args.update(over)
     return lib.ssd_fwd(ctypes.byref(s), args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"],
-                       args["y"], args["fs"], args["ws"], args["ws_bytes"], None, args["scratch"],
+                       args["s0"], args["y"], args["fs"], args["ws"], args["ws_bytes"], None, args["scratch"],
                        args["scratch_bytes"], None, None)
 
 
@@ -100,11 +100,13 @@ def test_fwd_rejects_before_launch(lib):
     for k in ["x", "dt", "A", "B", "C", "D", "y"]:
         assert fwd(lib, s, **{k: None}, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID, k
     assert fwd(lib, s, x=FAKE + 8, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID  # misaligned
+    assert fwd(lib, s, s0=FAKE + 4, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID
     assert fwd(lib, s, ws_bytes=need_ws - 1, scratch_bytes=need_scr) == WORKSPACE
     assert fwd(lib, s, ws=None, ws_bytes=need_ws, scratch_bytes=need_scr) == WORKSPACE
     assert fwd(lib, s, ws_bytes=need_ws, scratch_bytes=need_scr - 1) == WORKSPACE
     assert fwd(lib, s, ws_bytes=need_ws, scratch=None, scratch_bytes=need_scr) == WORKSPACE
-    assert lib.ssd_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, FAKE, 0, None, None) == INVALID
+    assert lib.ssd_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, None, FAKE, 0, None,
+                       None) == INVALID
 
 
 def test_bwd_rejects_before_launch(lib):
@@ -112,13 +114,15 @@ def test_bwd_rejects_before_launch(lib):
     sv = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lib.ssd_saved_bytes(ctypes.byref(s)))
     need = lib.ssd_bwd_scratch_bytes(ctypes.byref(s))
 
-    def bwd(saved, dy=FAKE, scratch=FAKE, nbytes=need, dx=FAKE):
-        return lib.ssd_bwd(ctypes.byref(saved) if saved is not None else None, dy, dx, FAKE, FAKE, FAKE, FAKE,
-                           FAKE, scratch, nbytes, None, None)
+    def bwd(saved, dy=FAKE, scratch=FAKE, nbytes=need, dx=FAKE, dfs=None, ds0=None):
+        return lib.ssd_bwd(ctypes.byref(saved) if saved is not None else None, dy, dfs, dx, FAKE, FAKE, FAKE, FAKE,
+                           FAKE, ds0, scratch, nbytes, None, None)
 
     assert bwd(None) == INVALID
     assert bwd(sv, dy=None) == INVALID
     assert bwd(sv, dx=None) == INVALID
+    assert bwd(sv, dfs=FAKE + 4) == INVALID  # misaligned optional state pointers
+    assert bwd(sv, ds0=FAKE + 8) == INVALID
     assert bwd(sv, nbytes=need - 1) == WORKSPACE
     assert bwd(sv, scratch=None) == WORKSPACE
     small = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16)

@@ -22,24 +22,33 @@ def to_np(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, chunk, device="cuda"):
-    """Forward + backward through libssd; returns (outputs dict of numpy float64, ctx)."""
+def run_gpu(inp, chunk, device="cuda", states=None):
+    """Forward + backward through libssd; returns (outputs dict of numpy float64, ctx).
+    states: optional (initial_state, dfinal_state) float32 numpy arrays; with
+    them the outputs include dinitial_state."""
     import torch
     from state_space_model_mamba2_amd import ssd
 
     dev = ssd.to_device(inp, device)
-    y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk)
-    g = ssd.bwd(dev["dy"], ctx)
+    s0 = dfs = None
+    if states is not None:
+        s0, dfs = (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device) for a in states)
+    y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk, initial_state=s0)
+    g = ssd.bwd(dev["dy"], ctx, dfinal_state=dfs, want_dinitial_state=states is not None)
     torch.cuda.synchronize()
     out = dict(y=to_np(y), final_state=to_np(fs))
     out.update({k: to_np(v) for k, v in g.items()})
     return out, ctx
 
 
-def run_oracle(inp, nthreads=0):
+def run_oracle(inp, nthreads=0, states=None):
+    """Oracle outputs; without states the dinitial_state entry is dropped."""
     from oracle import seq
 
     f = {k: inp.as_f64(k) for k in NAMES_IN + ["dy"]}
-    y, fs = seq.ssd_fwd(*(f[k] for k in NAMES_IN), nthreads=nthreads)
-    g = seq.ssd_bwd(*(f[k] for k in NAMES_IN), f["dy"], nthreads=nthreads)
+    s0, dfs = (None, None) if states is None else (np.asarray(a, np.float64) for a in states)
+    y, fs = seq.ssd_fwd(*(f[k] for k in NAMES_IN), initial_state=s0, nthreads=nthreads)
+    g = seq.ssd_bwd(*(f[k] for k in NAMES_IN), f["dy"], initial_state=s0, dfinal_state=dfs, nthreads=nthreads)
+    if states is None:
+        g.pop("dinitial_state")
     return dict(y=y, final_state=fs, **g)
