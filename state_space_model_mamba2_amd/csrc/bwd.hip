@@ -779,7 +779,8 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
     }
     if (hh + 1 < nh) store(bf ^ 1);
   }
-  float* o = out + (int64_t)blockIdx.z * gridDim.x * Q * N;  // slice stride b*K*G*Q*N = b*L*G*N
+  // slice stride b*G*L*N (gridDim.x = b*K*G; L >= K*Q is the row stride)
+  float* o = out + (int64_t)blockIdx.z * (gridDim.x / K) * L * N;
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -863,7 +864,7 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
     }
     __syncthreads();
   }
-  const int64_t ps = (int64_t)gridDim.x * Q * N;  // head-slice partial stride
+  const int64_t ps = (int64_t)(gridDim.x / K) * L * N;  // head-slice partial stride b*G*L*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -877,8 +878,10 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
 }
 
 // Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
-// thread sums a strided slice, then a fixed tree combines the slices.
+// thread sums a strided slice, then a fixed tree combines the slices; an
+// optional per-head addend (the shorter last chunk's sums) comes last.
 __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart, const float* __restrict__ ddpart,
+                                               const float* __restrict__ add_a, const float* __restrict__ add_d,
                                                float* __restrict__ dA, float* __restrict__ dD, int BK, int H) {
   __shared__ float ra[4], rd[4];
   const int h = blockIdx.x;
@@ -893,8 +896,8 @@ __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart,
   if (lane_id() == 0) { ra[wave] = sa; rd[wave] = sd; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]);
-    dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]);
+    dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]) + (add_a ? add_a[h] : 0.0f);
+    dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]) + (add_d ? add_d[h] : 0.0f);
   }
 }
 
@@ -953,7 +956,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
-    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA, a.dD, b * K, H);
+    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA_add, a.dD_add, a.dA, a.dD, b * K, H);
   }
 }
 

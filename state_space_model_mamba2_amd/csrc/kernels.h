@@ -59,6 +59,7 @@ struct BwdArgs {
   float* ddpart;   // [b][K][H]
   float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
   float* dlscal;   // [b][K][H][scan_bwd_splits(Q) + 1]: <Gk, Hin_k> and per-split sum <dy, x>
+  const float *dA_add, *dD_add;  // [H] added to dA / dD after the chunk sums, or null
 };
 
 // Workgroups that share one (batch, chunk, head) in the backward chunk kernel
@@ -77,6 +78,15 @@ struct ProbeScope {
     if (p && p->kernel == id) (void)hipEventRecord(p->stop, s);
   }
 };
+
+// Copies between the rows [row0, row0 + nvalid) of each of the b sequences
+// of a tensor with row stride L and a zero-padded [b][Q] row buffer
+// (pad_rows fills the rows past nvalid with zero bytes; unpad_rows copies the
+// nvalid rows back).  rowbytes is even; both pointers are 16-byte aligned.
+void pad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
+              int64_t b, hipStream_t st);
+void unpad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
+                int64_t b, hipStream_t st);
 
 template <typename T, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);

@@ -50,7 +50,8 @@ def test_shape_checks(lib):
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=64)) == OK
     assert check(lib, shape(chunk=64)) == UNSUPPORTED                        # bf16 chunk 64 switched off
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128, dstate=64)) == OK
-    assert check(lib, shape(seqlen=500)) == INVALID          # seqlen % chunk
+    assert check(lib, shape(seqlen=500)) == OK               # shorter last chunk
+    assert check(lib, shape(seqlen=7)) == OK                 # a single, shorter chunk
     assert check(lib, shape(nheads=5)) == INVALID            # nheads % ngroups
     for k in ["batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"]:
         assert check(lib, shape(**{k: 0})) == INVALID, k
@@ -74,7 +75,13 @@ def test_workspace_sizes(lib):
     assert saved >= b * H * K * Q * 4 + b * K * H * P * N * 2
     assert lib.ssd_fwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * 4
     assert lib.ssd_bwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * (4 + 2) + b * K * G * Q * Q * 4
-    assert lib.ssd_saved_bytes(ctypes.byref(shape(seqlen=500))) == 0
+    assert lib.ssd_saved_bytes(ctypes.byref(shape(nheads=5))) == 0
+    # a shorter last chunk runs as one more zero-padded chunk: its padded
+    # copies of x, dt, B, C are kept from the forward to the backward
+    ragged = lib.ssd_saved_bytes(ctypes.byref(shape(seqlen=500)))
+    assert ragged >= saved - b * H * Q * 4 + b * Q * (H * P + H + 2 * G * N) * 2
+    for f in (lib.ssd_saved_bytes, lib.ssd_fwd_scratch_bytes, lib.ssd_bwd_scratch_bytes):
+        assert f(ctypes.byref(shape(seqlen=7))) > 0
     # sizes grow linearly with batch
     assert lib.ssd_saved_bytes(ctypes.byref(shape(batch=4))) > saved
 
@@ -95,7 +102,7 @@ def test_fwd_rejects_before_launch(lib):
     s = shape()
     need_ws = lib.ssd_saved_bytes(ctypes.byref(s))
     need_scr = lib.ssd_fwd_scratch_bytes(ctypes.byref(s))
-    assert fwd(lib, shape(seqlen=500)) == INVALID
+    assert fwd(lib, shape(nheads=5)) == INVALID
     assert fwd(lib, shape(headdim=48)) == UNSUPPORTED
     for k in ["x", "dt", "A", "B", "C", "D", "y"]:
         assert fwd(lib, s, **{k: None}, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID, k
