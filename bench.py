@@ -1,9 +1,15 @@
 """Benchmark: Mamba-2 SSD chunked scan, forward + backward, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
+                    [--seqlen L] [--batch B] [--with-states]
 
 A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
-synthetic inputs (already resident in HBM).  Prints ONE JSON line on stdout;
+synthetic inputs (already resident in HBM).  --seqlen / --batch change the
+workload's sequence length / batch (a length that is not a multiple of the
+chunk adds a shorter last chunk); --with-states starts the forward from a
+seeded initial state and gives the backward a seeded final-state cotangent,
+returning the initial-state gradient as well (one GPU's share of a sequence
+split across GPUs).  Prints ONE JSON line on stdout;
 diagnostics (per-kernel times) go to stderr.
 
 The roofline object describes the kernel with the largest share of the step:
@@ -40,9 +46,11 @@ def log(*a):
 # ---------------------------------------------------------------------------
 # Algorithmic traffic and work per launch of each kernel.
 def kernel_model(s, esz):
+    """Bytes and flops per launch over the whole chunks (a shorter last chunk
+    runs as a separate launch of each kernel, which the probes do not time)."""
     b, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
     K = L // Q
-    T = b * L
+    T = b * K * Q
     nt = Q // 16
     tiles = nt * (nt + 1) // 2
     X = T * H * P * esz              # one x-sized tensor
@@ -117,9 +125,10 @@ def make_probe(kernel_id, start, stop):
 
 
 def run_step(ssd, dev, chunk, fscr, bscr, fprobe=None, bprobe=None):
+    s0, dfs = dev.get("initial_state"), dev.get("dfinal_state")
     y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk,
-                         scratch=fscr, probe=fprobe)
-    g = ssd.bwd(dev["dy"], ctx, scratch=bscr, probe=bprobe)
+                         initial_state=s0, scratch=fscr, probe=fprobe)
+    g = ssd.bwd(dev["dy"], ctx, dfinal_state=dfs, want_dinitial_state=s0 is not None, scratch=bscr, probe=bprobe)
     return y, fs, g
 
 
@@ -300,6 +309,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--seqlen", type=int, default=None, help="override the workload's sequence length")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
+    ap.add_argument("--with-states", action="store_true",
+                    help="seeded initial state and final-state cotangent; dinitial_state returned")
     ap.add_argument("--cpu-heads", type=int, default=80, help="heads in the oracle CPU-baseline slice")
     ap.add_argument("--cpu-batch", type=int, default=4, help="batch rows in the oracle CPU-baseline slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,12 +364,17 @@ def main():
         return
 
     _lib.load()  # fail loudly if the HIP library is missing
-    shape = inputs.workload(args.workload)
+    over = {k: v for k, v in (("seqlen", args.seqlen), ("batch", args.batch)) if v is not None}
+    shape = inputs.workload(args.workload, **over)
     esz = 2 if shape.dtype == "bf16" else 4
     log(f"[bench] workload {args.workload}: {shape}")
     t0 = time.perf_counter()
     inp = inputs.generate(shape, seed=0)
     dev = ssd.to_device(inp, "cuda")
+    if args.with_states:
+        s0, dfs = inputs.generate_states(shape, seed=0)
+        dev["initial_state"] = torch.from_numpy(s0).cuda()
+        dev["dfinal_state"] = torch.from_numpy(dfs).cuda()
     torch.cuda.synchronize()
     log(f"[bench] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
 
@@ -406,7 +424,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": nbytes / t_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": hbm_frac}
-    roof["traffic"] = load_traffic(dom, args.workload)
+    roof["traffic"] = load_traffic(dom, args.workload) if not over and not args.with_states else None
     roof["kernel"] = dom
     roof["kernel_ms"] = dom_ms
     roof["algorithmic_bytes"] = nbytes
@@ -444,7 +462,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": shape.batch, "seqlen": shape.seqlen,
                    "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
-                   "ngroups": shape.ngroups, "chunk": shape.chunk, "parallelism": "single-gpu"},
+                   "ngroups": shape.ngroups, "chunk": shape.chunk, "parallelism": "single-gpu",
+                   "initial_state": bool(args.with_states)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_ms": breakdown or None,

@@ -61,13 +61,18 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   y.g_off = o;      o += align_up(states * y.esz);
   // Head slices for the group-level backward kernels (each slice writes an
   // fp32 partial that is summed in a fixed order): about `target` workgroups
-  // per launch, never finer than one head.  Measured at the 2.7B shape
-  // (b*K*G*Q/64 = 256): two slices for both is fastest; more slices cost more
-  // in partial sums than the extra parallelism gains, one slice starves dW.
+  // per launch, never finer than one head and never more than kMaxSlices.
+  // Measured at the 2.7B shape (b*K*G*Q/64 = 256): two slices for both is
+  // fastest; more slices cost more in partial sums than the extra parallelism
+  // gains, one slice starves dW.  Small problems (a one-chunk tail) would ask
+  // for dozens of slices, whose serial partial sums on few workgroups cost far
+  // more than the heads they spread.
+  constexpr int64_t kMaxSlices = 4;
   auto slices = [&](int64_t target) {
     const int64_t base = y.b * y.K * y.G * (y.Q / 64);
     const int64_t hpg = y.H / y.G;
     int64_t sl = (target + base - 1) / base;
+    if (sl > kMaxSlices) sl = kMaxSlices;
     if (sl > hpg) sl = hpg;
     if (sl < 1) sl = 1;
     return sl;
@@ -75,8 +80,8 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   y.nslice = slices(512);
   y.nslice_bc = slices(512);
   y.dw_off = o;     o += align_up((size_t)(y.nslice * y.b * y.K * y.G * y.Q * y.Q) * 4);
-  y.dcpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.L * y.G * y.N) * 4);
-  y.dbpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.L * y.G * y.N) * 4);
+  y.dcpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.K * y.Q * y.G * y.N) * 4);
+  y.dbpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.K * y.Q * y.G * y.N) * 4);
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   const int64_t nsp = scan_bwd_splits((int)y.Q);
@@ -86,63 +91,46 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   return y;
 }
 
-// A sequence of L tokens runs as Kf = L / Q whole chunks in place (the
-// "main" problem, row stride L) and, when Lr = L % Q > 0, its last Lr tokens
-// as a one-chunk "tail" problem on zero-padded copies ([b][Q] rows, kept in
-// the saved workspace for the inputs and in scratch for dy and the tail's
-// outputs).  The tail starts from the state the main part leaves and returns
-// the cotangent of that state, which seeds the main part's backward; the
-// tail's dA / dD are added after the main part's chunk sums.
+// A sequence of L tokens runs as K = ceil(L / Q) chunks.  The whole ones
+// are read and written in place; when L % Q = Lr > 0, the last one (chunk kf
+// = L / Q) holds Lr tokens and runs on zero-padded copies of Q rows per
+// sequence: the inputs' copies are made by the forward and kept in the saved
+// workspace, dy's copy and the last chunk's outputs live in the backward
+// scratch, and the valid rows are copied back to the caller's tensors.
 struct Plan {
-  Layout main, tail;
-  bool has_main, has_tail;
-  int64_t Kf, Lr;
-  // saved workspace
-  size_t sv_main, sv_tail, sv_tx, sv_tdt, sv_tB, sv_tC, saved_bytes;
-  // forward scratch
-  size_t fw_main, fw_tail, fw_fsmid, fw_ty, fwd_bytes;
-  // backward scratch
-  size_t bw_main, bw_tail, bw_tdy, bw_tdx, bw_tddt, bw_tdB, bw_tdC, bw_tdA, bw_tdD, bw_tds0, bwd_bytes;
+  Layout lay;
+  int64_t kf, Lr;
+  size_t sv_tx, sv_tdt, sv_tB, sv_tC, saved_bytes;
+  size_t fw_ty, fwd_bytes;
+  size_t bw_tdy, bw_tdx, bw_tddt, bw_tdB, bw_tdC, bwd_bytes;
 };
 
 Plan make_plan(const ssd_shape* s) {
   Plan p{};
   const int64_t Q = s->chunk, L = s->seqlen;
-  p.Kf = L / Q;
+  p.kf = L / Q;
   p.Lr = L % Q;
-  p.has_main = p.Kf > 0;
-  p.has_tail = p.Lr > 0;
-  if (p.has_main) p.main = make_layout(s, L, p.Kf);
-  if (p.has_tail) p.tail = make_layout(s, Q, 1);
+  p.lay = make_layout(s, L, (L + Q - 1) / Q);
+  const bool tail = p.Lr > 0;
   const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
   const size_t b = s->batch, H = s->nheads, P = s->headdim, N = s->dstate, G = s->ngroups, q = Q;
-  const size_t xrows = align_up(b * q * H * P * esz), trows = align_up(b * q * H * esz);
-  const size_t brows = align_up(b * q * G * N * esz), state = align_up(b * H * P * N * 4);
-  size_t o = 0;
-  p.sv_main = o;  if (p.has_main) o += p.main.saved_bytes;
-  p.sv_tail = o;  if (p.has_tail) o += p.tail.saved_bytes;
-  p.sv_tx = o;    if (p.has_tail) o += xrows;
-  p.sv_tdt = o;   if (p.has_tail) o += trows;
-  p.sv_tB = o;    if (p.has_tail) o += brows;
-  p.sv_tC = o;    if (p.has_tail) o += brows;
+  const size_t xrows = tail ? align_up(b * q * H * P * esz) : 0, trows = tail ? align_up(b * q * H * esz) : 0;
+  const size_t brows = tail ? align_up(b * q * G * N * esz) : 0;
+  size_t o = p.lay.saved_bytes;
+  p.sv_tx = o;  o += xrows;
+  p.sv_tdt = o; o += trows;
+  p.sv_tB = o;  o += brows;
+  p.sv_tC = o;  o += brows;
   p.saved_bytes = o;
-  o = 0;
-  p.fw_main = o;  if (p.has_main) o += p.main.fwd_bytes;
-  p.fw_tail = o;  if (p.has_tail) o += p.tail.fwd_bytes;
-  p.fw_fsmid = o; if (p.has_tail) o += state;
-  p.fw_ty = o;    if (p.has_tail) o += xrows;
+  o = p.lay.fwd_bytes;
+  p.fw_ty = o;  o += xrows;
   p.fwd_bytes = o;
-  o = 0;
-  p.bw_main = o;  if (p.has_main) o += p.main.bwd_bytes;
-  p.bw_tail = o;  if (p.has_tail) o += p.tail.bwd_bytes;
-  p.bw_tdy = o;   if (p.has_tail) o += xrows;
-  p.bw_tdx = o;   if (p.has_tail) o += xrows;
-  p.bw_tddt = o;  if (p.has_tail) o += trows;
-  p.bw_tdB = o;   if (p.has_tail) o += brows;
-  p.bw_tdC = o;   if (p.has_tail) o += brows;
-  p.bw_tdA = o;   if (p.has_tail) o += align_up(H * 4);
-  p.bw_tdD = o;   if (p.has_tail) o += align_up(H * 4);
-  p.bw_tds0 = o;  if (p.has_tail) o += state;
+  o = p.lay.bwd_bytes;
+  p.bw_tdy = o;  o += xrows;
+  p.bw_tdx = o;  o += xrows;
+  p.bw_tddt = o; o += trows;
+  p.bw_tdB = o;  o += brows;
+  p.bw_tdC = o;  o += brows;
   p.bwd_bytes = o;
   return p;
 }
@@ -264,33 +252,29 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
   const int64_t b = s->batch, L = s->seqlen, Q = s->chunk, H = s->nheads, G = s->ngroups;
   const int64_t P = s->headdim, N = s->dstate;
-  float* fs_mid = pl.has_tail ? at<float>(scratch, pl.fw_fsmid) : nullptr;
-  if (pl.has_main) {
-    FwdArgs a{};
-    a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
-    a.init = initial_state;
-    a.final_state = pl.has_tail ? fs_mid : final_state;
-    set_fwd_ws(a, pl.main, at<char>(saved_ws, pl.sv_main), at<char>(scratch, pl.fw_main));
-    dispatch_fwd(s->dtype, pl.main, a, stream, probe);
+  FwdArgs a{};
+  a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
+  a.init = initial_state;
+  a.final_state = final_state;
+  a.rows.L = L;
+  a.rows.kf = (int)pl.kf;
+  set_fwd_ws(a, pl.lay, saved_ws, scratch);
+  if (pl.Lr > 0) {
+    a.rows.x = at<char>(saved_ws, pl.sv_tx);
+    a.rows.dt = at<char>(saved_ws, pl.sv_tdt);
+    a.rows.B = at<char>(saved_ws, pl.sv_tB);
+    a.rows.C = at<char>(saved_ws, pl.sv_tC);
+    a.rows.y = at<char>(scratch, pl.fw_ty);
+    const RowCopy in{{x, dt, B, C},
+                     {const_cast<void*>(a.rows.x), const_cast<void*>(a.rows.dt), const_cast<void*>(a.rows.B),
+                      const_cast<void*>(a.rows.C)},
+                     {H * P * (int64_t)esz, H * (int64_t)esz, G * N * (int64_t)esz, G * N * (int64_t)esz}, 4};
+    pad_rows(in, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
-  if (pl.has_tail) {
-    const int64_t row0 = pl.Kf * Q;
-    void* tx = at<char>(saved_ws, pl.sv_tx);
-    void* tdt = at<char>(saved_ws, pl.sv_tdt);
-    void* tB = at<char>(saved_ws, pl.sv_tB);
-    void* tC = at<char>(saved_ws, pl.sv_tC);
-    void* ty = at<char>(scratch, pl.fw_ty);
-    pad_rows(x, tx, H * P * esz, L, row0, pl.Lr, Q, b, stream);
-    pad_rows(dt, tdt, H * esz, L, row0, pl.Lr, Q, b, stream);
-    pad_rows(B, tB, G * N * esz, L, row0, pl.Lr, Q, b, stream);
-    pad_rows(C, tC, G * N * esz, L, row0, pl.Lr, Q, b, stream);
-    FwdArgs a{};
-    a.x = tx; a.dt = tdt; a.B = tB; a.C = tC; a.A = A; a.D = D; a.y = ty;
-    a.init = pl.has_main ? fs_mid : initial_state;
-    a.final_state = final_state;
-    set_fwd_ws(a, pl.tail, at<char>(saved_ws, pl.sv_tail), at<char>(scratch, pl.fw_tail));
-    dispatch_fwd(s->dtype, pl.tail, a, stream, pl.has_main ? nullptr : probe);
-    unpad_rows(ty, y, H * P * esz, L, row0, pl.Lr, Q, b, stream);
+  dispatch_fwd(s->dtype, pl.lay, a, stream, probe);
+  if (pl.Lr > 0) {
+    const RowCopy out{{a.rows.y}, {y}, {H * P * (int64_t)esz}, 1};
+    unpad_rows(out, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
   if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
 
@@ -324,43 +308,32 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
   const int64_t b = s->batch, L = s->seqlen, Q = s->chunk, H = s->nheads, G = s->ngroups;
   const int64_t P = s->headdim, N = s->dstate;
-  float* tds0 = pl.has_tail ? at<float>(scratch, pl.bw_tds0) : nullptr;
-  float* tdA = pl.has_tail ? at<float>(scratch, pl.bw_tdA) : nullptr;
-  float* tdD = pl.has_tail ? at<float>(scratch, pl.bw_tdD) : nullptr;
-  // The tail goes first: its initial-state gradient is the main part's
-  // final-state cotangent.
-  if (pl.has_tail) {
-    const int64_t row0 = pl.Kf * Q;
-    void* tdy = at<char>(scratch, pl.bw_tdy);
-    void* tdx = at<char>(scratch, pl.bw_tdx);
-    void* tddt = at<char>(scratch, pl.bw_tddt);
-    void* tdB = at<char>(scratch, pl.bw_tdB);
-    void* tdC = at<char>(scratch, pl.bw_tdC);
-    pad_rows(dy, tdy, H * P * esz, L, row0, pl.Lr, Q, b, stream);
-    BwdArgs a{};
-    a.x = at<char>(sv->saved_ws, pl.sv_tx); a.dt = at<char>(sv->saved_ws, pl.sv_tdt);
-    a.B = at<char>(sv->saved_ws, pl.sv_tB); a.C = at<char>(sv->saved_ws, pl.sv_tC);
-    a.dy = tdy; a.A = sv->A; a.D = sv->D;
-    a.dx = tdx; a.ddt = tddt; a.dB = tdB; a.dC = tdC;
-    a.dA = pl.has_main ? tdA : dA; a.dD = pl.has_main ? tdD : dD;
-    a.dfinal = dfinal_state;
-    a.dinit = pl.has_main ? tds0 : dinitial_state;
-    set_bwd_ws(a, pl.tail, at<char>(sv->saved_ws, pl.sv_tail), at<char>(scratch, pl.bw_tail));
-    dispatch_bwd(s->dtype, pl.tail, a, stream, pl.has_main ? nullptr : probe);
-    unpad_rows(tdx, dx, H * P * esz, L, row0, pl.Lr, Q, b, stream);
-    unpad_rows(tddt, ddt, H * esz, L, row0, pl.Lr, Q, b, stream);
-    unpad_rows(tdB, dB, G * N * esz, L, row0, pl.Lr, Q, b, stream);
-    unpad_rows(tdC, dC, G * N * esz, L, row0, pl.Lr, Q, b, stream);
+  BwdArgs a{};
+  a.x = sv->x; a.dt = sv->dt; a.B = sv->B; a.C = sv->C; a.dy = dy; a.A = sv->A; a.D = sv->D;
+  a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
+  a.dfinal = dfinal_state; a.dinit = dinitial_state;
+  a.rows.L = L;
+  a.rows.kf = (int)pl.kf;
+  set_bwd_ws(a, pl.lay, sv->saved_ws, scratch);
+  if (pl.Lr > 0) {
+    a.rows.x = at<char>(sv->saved_ws, pl.sv_tx);
+    a.rows.dt = at<char>(sv->saved_ws, pl.sv_tdt);
+    a.rows.B = at<char>(sv->saved_ws, pl.sv_tB);
+    a.rows.C = at<char>(sv->saved_ws, pl.sv_tC);
+    a.rows.dy = at<char>(scratch, pl.bw_tdy);
+    a.rows.dx = at<char>(scratch, pl.bw_tdx);
+    a.rows.ddt = at<char>(scratch, pl.bw_tddt);
+    a.rows.dB = at<char>(scratch, pl.bw_tdB);
+    a.rows.dC = at<char>(scratch, pl.bw_tdC);
+    const RowCopy in{{dy}, {const_cast<void*>(a.rows.dy)}, {H * P * (int64_t)esz}, 1};
+    pad_rows(in, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
-  if (pl.has_main) {
-    BwdArgs a{};
-    a.x = sv->x; a.dt = sv->dt; a.B = sv->B; a.C = sv->C; a.dy = dy; a.A = sv->A; a.D = sv->D;
-    a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
-    a.dfinal = pl.has_tail ? tds0 : dfinal_state;
-    a.dinit = dinitial_state;
-    a.dA_add = tdA; a.dD_add = tdD;
-    set_bwd_ws(a, pl.main, at<char>(sv->saved_ws, pl.sv_main), at<char>(scratch, pl.bw_main));
-    dispatch_bwd(s->dtype, pl.main, a, stream, probe);
+  dispatch_bwd(s->dtype, pl.lay, a, stream, probe);
+  if (pl.Lr > 0) {
+    const RowCopy out{{a.rows.dx, a.rows.ddt, a.rows.dB, a.rows.dC},
+                      {dx, ddt, dB, dC},
+                      {H * P * (int64_t)esz, H * (int64_t)esz, G * N * (int64_t)esz, G * N * (int64_t)esz}, 4};
+    unpad_rows(out, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
   if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
     const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin, const T* __restrict__ gst,
     const T* __restrict__ wb, const T* __restrict__ dy, T* __restrict__ dx, float* __restrict__ dlpart,
-    float* __restrict__ dlscal, int nitems, int L, int H, int G, int K) {
+    float* __restrict__ dlscal, int nitems, const RowMap rm, int H, int G, int K) {
   constexpr int NW = 4, NTH = NW * kWave;
   constexpr int NSPLIT = scan_bwd_splits(Q);
   constexpr int PADR = 16 / sizeof(T);    // row padding: 16-byte aligned rows, spread banks
@@ -84,7 +84,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dt = rows_in(rm, k, dt, rm.dt);
+  B = rows_in(rm, k, B, rm.B);
+  C = rows_in(rm, k, C, rm.C);
+  dy = rows_in(rm, k, dy, rm.dy);
+  dx = rows_out(rm, k, dx, rm.dx);
   const int64_t rs = (int64_t)H * P;      // row stride of x / dy / dx
   const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * rs
   const T* xh = x + (row0 * H + h) * P;
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
                                                      const float* __restrict__ cs_g, const T* __restrict__ dt,
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
-                                                     int L, int H, int K) {
+                                                     const RowMap rm, int H, int K) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
   constexpr int TPL = Q / 16;
   const int nhb = (H + 15) / 16;
@@ -476,7 +482,9 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   const int h = 16 * hb + hl;
   if (h >= H) return;  // whole 16-lane group; only width-16 shuffles below
   const int bkh = bk * H + h;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  dt = rows_in(rm, k, dt, rm.dt);
+  ddt = rows_out(rm, k, ddt, rm.ddt);
   const float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;
   const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
   const int j0 = jl * TPL;
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
 template <typename T, int Q, int P, bool DIAG>
 __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __restrict__ dt,
                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                            float* __restrict__ dw, int L, int H, int G, int K, int hps) {
+                                            float* __restrict__ dw, const RowMap rm, int H, int G, int K, int hps) {
   constexpr int NTH = 256;
   constexpr int NKP = (P + 31) / 32;
   constexpr int XP = P + 16 / sizeof(T);    // row pitch of the staged x rows
@@ -581,7 +589,10 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
     JB = blockIdx.y - IB * (IB - 1) / 2;
   }
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dt = rows_in(rm, k, dt, rm.dt);
+  dy = rows_in(rm, k, dy, rm.dy);
   const int hpg = H / G;
   const int h0 = g * hpg + blockIdx.z * hps;                  // first head of this slice
   const int nh = min(hps, hpg - (int)blockIdx.z * hps);       // heads in this slice
@@ -705,7 +716,7 @@ template <typename T, int Q, int P, int N, bool DB>
 __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const T* __restrict__ dt,
                                                   const float* __restrict__ cs_g, const T* __restrict__ dy,
                                                   const T* __restrict__ state, float* __restrict__ out,
-                                                  int L, int H, int G, int K, int hps) {
+                                                  const RowMap rm, int H, int G, int K, int hps) {
   constexpr int NTH = 256;
   constexpr int TN = N / 16, NKP = (P + 31) / 32;
   constexpr int VN = Vec16<T>::n;
@@ -719,7 +730,11 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
   const int bkg = blockIdx.x, RB = blockIdx.y;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dt = rows_in(rm, k, dt, rm.dt);
+  dy = rows_in(rm, k, dy, rm.dy);
+  const int64_t prow0 = ((int64_t)b * K + k) * Q;  // row of the fp32 partials (chunk rows)
   const int hpg = H / G;
   const int h0 = g * hpg + blockIdx.z * hps;
   const int nh = min(hps, hpg - (int)blockIdx.z * hps);
@@ -779,14 +794,13 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
     }
     if (hh + 1 < nh) store(bf ^ 1);
   }
-  // slice stride b*G*L*N (gridDim.x = b*K*G; L >= K*Q is the row stride)
-  float* o = out + (int64_t)blockIdx.z * (gridDim.x / K) * L * N;
+  float* o = out + (int64_t)blockIdx.z * gridDim.x * Q * N;  // slice stride b*K*G*Q*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 64 * RB + 16 * wave + 4 * q + r;
-      o[((row0 + row) * G + g) * N + 16 * tn + c] = acc[tn][r];
+      o[((prow0 + row) * G + g) * N + 16 * tn + c] = acc[tn][r];
     }
   }
 }
@@ -801,8 +815,8 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
 // them K-major, and B / C are read K-major (transposing LDS read).
 template <typename T, int Q, int N, bool DB>
 __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part, const float* __restrict__ dw,
-                                                  const T* __restrict__ M, T* __restrict__ out, int L, int G,
-                                                  int K, int nslice, int nslice_dw) {
+                                                  const T* __restrict__ M, T* __restrict__ out, const RowMap rm,
+                                                  int G, int K, int nslice, int nslice_dw) {
   constexpr int NTH = 256;
   constexpr int TN = N / 16, NB = Q / 64;
   constexpr int VN = Vec16<T>::n;
@@ -816,7 +830,10 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
   const int bkg = blockIdx.x, RB = blockIdx.y;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  M = rows_in(rm, k, M, DB ? rm.C : rm.B);
+  out = rows_out(rm, k, out, DB ? rm.dB : rm.dC);
+  const int64_t prow0 = ((int64_t)b * K + k) * Q;  // row of the fp32 partials (chunk rows)
   const int r0 = 64 * RB;
   const int64_t dws = (int64_t)gridDim.x * Q * Q;  // dW slice stride
   const float* dwb = dw + (int64_t)bkg * Q * Q;
@@ -864,24 +881,23 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
     }
     __syncthreads();
   }
-  const int64_t ps = (int64_t)(gridDim.x / K) * L * N;  // head-slice partial stride b*G*L*N
+  const int64_t ps = (int64_t)gridDim.x * Q * N;  // head-slice partial stride b*K*G*Q*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t e = ((row0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + 16 * tn + c;
+      const int rr = r0 + 16 * wave + 4 * q + r;
+      const int64_t e = ((prow0 + rr) * G + g) * N + 16 * tn + c;
       float v = part[e];
       for (int z = 1; z < nslice; ++z) v += part[z * ps + e];
-      out[e] = from_f<T>(v + acc[tn][r]);
+      out[((row0 + rr) * G + g) * N + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
     }
   }
 }
 
 // Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
-// thread sums a strided slice, then a fixed tree combines the slices; an
-// optional per-head addend (the shorter last chunk's sums) comes last.
+// thread sums a strided slice, then a fixed tree combines the slices.
 __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart, const float* __restrict__ ddpart,
-                                               const float* __restrict__ add_a, const float* __restrict__ add_d,
                                                float* __restrict__ dA, float* __restrict__ dD, int BK, int H) {
   __shared__ float ra[4], rd[4];
   const int h = blockIdx.x;
@@ -896,14 +912,14 @@ __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart,
   if (lane_id() == 0) { ra[wave] = sa; rd[wave] = sd; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]) + (add_a ? add_a[h] : 0.0f);
-    dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]) + (add_d ? add_d[h] : 0.0f);
+    dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]);
+    dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]);
   }
 }
 
 template <typename T, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_probe* probe) {
-  const int b = (int)lay.b, L = (int)lay.L, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
+  const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
   const T* x = static_cast<const T*>(a.x);
   const T* dt = static_cast<const T*>(a.dt);
   const T* B = static_cast<const T*>(a.B);
@@ -914,7 +930,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
-    k_chunk_state<T, Q, P, N, true><<<dim3(b * K * H), dim3(256), 0, st>>>(dy, C, dt, a.cs, a.dhloc, L, H, G, K);
+    k_chunk_state<T, Q, P, N, true><<<dim3(b * K * H), dim3(256), 0, st>>>(dy, C, dt, a.cs, a.dhloc, a.rows, H, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
@@ -926,37 +942,37 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     const int nitems = b * K * H;
     const int groups = (nitems + 7) / 8;
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(groups * 8 * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, L, H, G, K);
+        x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     k_dl_assemble<T, Q><<<dim3(b * K * ((H + 15) / 16)), dim3(256), 0, st>>>(
-        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, L, H, K);
+        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.rows, H, K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;
   {
     ProbeScope ps(probe, SSD_K_DW, st);
     const int nb = Q / 64;
-    k_dw<T, Q, P, true><<<dim3(b * K * G, nb, S), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, L, H, G, K, hps);
+    k_dw<T, Q, P, true><<<dim3(b * K * G, nb, S), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps);
     if (nb > 1)
       k_dw<T, Q, P, false><<<dim3(b * K * G, nb * (nb - 1) / 2, S), dim3(256), 0, st>>>(
-          x, dt, a.cs, dy, a.dw, L, H, G, K, hps);
+          x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps);
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);
     k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, a.dcpart, L, H, G, K, hpsb);
+        x, dt, a.cs, dy, hin, a.dcpart, a.rows, H, G, K, hpsb);
     k_bc_final<T, Q, N, false><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        a.dcpart, a.dw, B, static_cast<T*>(a.dC), L, G, K, Sb, S);
+        a.dcpart, a.dw, B, static_cast<T*>(a.dC), a.rows, G, K, Sb, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DB, st);
     k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, gst, a.dbpart, L, H, G, K, hpsb);
+        x, dt, a.cs, dy, gst, a.dbpart, a.rows, H, G, K, hpsb);
     k_bc_final<T, Q, N, true><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
-        a.dbpart, a.dw, C, static_cast<T*>(a.dB), L, G, K, Sb, S);
+        a.dbpart, a.dw, C, static_cast<T*>(a.dB), a.rows, G, K, Sb, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
-    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA_add, a.dD_add, a.dA, a.dD, b * K, H);
+    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA, a.dD, b * K, H);
   }
 }
 

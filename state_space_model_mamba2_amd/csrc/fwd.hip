@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
                                                            const float* __restrict__ cs_g, const float* __restrict__ Dp,
                                                            const T* __restrict__ C, const T* __restrict__ hin,
                                                            const T* __restrict__ wt, T* __restrict__ y,
-                                                           int L, int H, int G, int K) {
+                                                           const RowMap rm, int H, int G, int K) {
   constexpr int NTH = 256, NW = 4;
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NJ2 = NT / 2;
@@ -47,7 +47,11 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dt = rows_in(rm, k, dt, rm.dt);
+  C = rows_in(rm, k, C, rm.C);
+  y = rows_out(rm, k, y, rm.y);
   const T* wtb = wt + (int64_t)((b * K + k) * G + g) * TILES * 256;
 
   // row tiles of this wave (zig-zag); NT may be smaller than the wave count
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
 
 template <typename T, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_probe* probe) {
-  const int b = (int)lay.b, L = (int)lay.L, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
+  const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
   const T* x = static_cast<const T*>(a.x);
   const T* dt = static_cast<const T*>(a.dt);
   const T* B = static_cast<const T*>(a.B);
@@ -207,17 +211,17 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   T* wt = static_cast<T*>(a.wt);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_CUMSUM, st);
-    k_chunk_cumsum<T, Q><<<dim3(b * H * K), dim3(64), 0, st>>>(dt, a.A, a.cs, L, H, K);
+    k_chunk_cumsum<T, Q><<<dim3(b * H * K), dim3(64), 0, st>>>(dt, a.A, a.cs, a.rows, H, K);
   }
   {
     ProbeScope ps(probe, SSD_K_BMM_FWD, st);
     constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
     k_bmm_tiles<T, Q, N><<<dim3(b * K * G, (TILES + 3) / 4), dim3(256), 0, st>>>(
-        B, C, wt, static_cast<T*>(a.wtb), L, G, K);
+        B, C, wt, static_cast<T*>(a.wtb), a.rows, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    k_chunk_state<T, Q, P, N, false><<<dim3(b * K * H), dim3(256), 0, st>>>(x, B, dt, a.cs, a.S, L, H, G, K);
+    k_chunk_state<T, Q, P, N, false><<<dim3(b * K * H), dim3(256), 0, st>>>(x, B, dt, a.cs, a.S, a.rows, H, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);
@@ -227,7 +231,7 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
     k_chunk_scan_fwd<T, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), L, H, G, K);
+        x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K);
   }
 }
 

@@ -42,6 +42,20 @@ __device__ __forceinline__ void frag_load_chained(Frag<T>& f, const T* row, int 
   }
 }
 
+// First row of chunk k of sequence b, and the tensor that holds it: the
+// caller's for whole chunks, the zero-padded copy for a shorter last chunk.
+__device__ __forceinline__ int64_t chunk_row0(const RowMap& rm, int b, int k, int Q) {
+  return k == rm.kf ? (int64_t)b * Q : (int64_t)b * rm.L + (int64_t)k * Q;
+}
+template <typename T>
+__device__ __forceinline__ const T* rows_in(const RowMap& rm, int k, const T* p, const void* tail) {
+  return k == rm.kf ? static_cast<const T*>(tail) : p;
+}
+template <typename T>
+__device__ __forceinline__ T* rows_out(const RowMap& rm, int k, T* p, void* tail) {
+  return k == rm.kf ? static_cast<T*>(tail) : p;
+}
+
 // Index of the lower-triangle 16x16 tile (I, J), J <= I.
 __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
@@ -51,17 +65,19 @@ __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 
 // chunk-wide prefix comes from a wave64 shuffle scan.
 template <typename T, int Q>
 __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, const float* __restrict__ A,
-                                                     float* __restrict__ cs, int L, int H, int K) {
+                                                     float* __restrict__ cs, const RowMap rm, int H, int K) {
   constexpr int TPL = Q / kWave;
   const int bhk = blockIdx.x;
   const int k = bhk % K, bh = bhk / K, h = bh % H, b = bh / H;
   const int l = threadIdx.x;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  dt = rows_in(rm, k, dt, rm.dt);
   const float a = A[h];
   float v[TPL];
 #pragma unroll
   for (int j = 0; j < TPL; ++j) {
-    const int64_t t = (int64_t)k * Q + l * TPL + j;
-    v[j] = to_f(dt[((int64_t)b * L + t) * H + h]) * a;
+    const int64_t t = row0 + l * TPL + j;
+    v[j] = to_f(dt[t * H + h]) * a;
   }
 #pragma unroll
   for (int j = 1; j < TPL; ++j) v[j] += v[j - 1];
@@ -83,7 +99,8 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, c
 // tile per wave: every load is issued before the first product.
 template <typename T, int Q, int N>
 __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, const T* __restrict__ C,
-                                                   T* __restrict__ wf, T* __restrict__ wb, int L, int G, int K) {
+                                                   T* __restrict__ wf, T* __restrict__ wb, const RowMap rm, int G,
+                                                   int K) {
   constexpr int NT = Q / 16;
   constexpr int TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32;
@@ -95,7 +112,9 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
   int I = 0;
   while ((I + 1) * (I + 2) / 2 <= idx) ++I;
   const int J = idx - I * (I + 1) / 2;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  B = rows_in(rm, k, B, rm.B);
+  C = rows_in(rm, k, C, rm.C);
   const T* brow = B + ((row0 + 16 * J + c) * G + g) * N;
   const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
   Frag<T> fb[NK], fc[NK];
@@ -134,7 +153,7 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
 template <typename T, int Q, int P, int N, bool BWD>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, const T* __restrict__ V,
                                                      const T* __restrict__ dt, const float* __restrict__ cs,
-                                                     float* __restrict__ out, int L, int H, int G, int K) {
+                                                     float* __restrict__ out, const RowMap rm, int H, int G, int K) {
   constexpr int NTH = 256;
   constexpr int KB = 64;                           // tokens per block
   constexpr int NB = Q / KB;
@@ -151,7 +170,10 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int64_t row0 = (int64_t)b * L + (int64_t)k * Q;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  U = rows_in(rm, k, U, BWD ? rm.dy : rm.x);
+  V = rows_in(rm, k, V, BWD ? rm.C : rm.B);
+  dt = rows_in(rm, k, dt, rm.dt);
   const float* csc = cs + (((int64_t)b * H + h) * K + k) * Q;
   const float cs_last = csc[Q - 1];
 

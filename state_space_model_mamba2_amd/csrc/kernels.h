@@ -27,12 +27,25 @@ struct Layout {
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
 };
 
+// Token rows of the chunks.  Chunk k of sequence b starts at row b * L + k * Q
+// of the caller's tensors.  When the sequence length is not a multiple of Q,
+// the last chunk (k == kf) reads and writes zero-padded one-chunk copies
+// instead ([b][Q] rows, sequence b's starting at row b * Q), so that every
+// chunk has Q rows; kf = K when every chunk is whole.
+struct RowMap {
+  int64_t L;
+  int kf;
+  const void *x, *dt, *B, *C, *dy;  // zero-padded inputs of chunk kf
+  void *y, *dx, *ddt, *dB, *dC;     // its outputs, copied back afterwards
+};
+
 struct FwdArgs {
   const void *x, *dt, *B, *C;
   const float *A, *D;
   const float* init;  // [b][H][P][N] initial state, or null for zero
   void* y;
   float* final_state;
+  RowMap rows;
   float* cs;    // [b][H][K][Q]
   void* hin;    // [b][K][H][P][N]  storage dtype
   float* S;     // [b][K][H][P][N]
@@ -53,13 +66,13 @@ struct BwdArgs {
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
-  float* dcpart;   // [nslice_bc][b][L][G][N] fp32 partials of dC
-  float* dbpart;   // [nslice_bc][b][L][G][N] fp32 partials of dB
+  float* dcpart;   // [nslice_bc][b][K][Q][G][N] fp32 partials of dC (chunk rows)
+  float* dbpart;   // [nslice_bc][b][K][Q][G][N] fp32 partials of dB (chunk rows)
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
   float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
   float* dlscal;   // [b][K][H][scan_bwd_splits(Q) + 1]: <Gk, Hin_k> and per-split sum <dy, x>
-  const float *dA_add, *dD_add;  // [H] added to dA / dD after the chunk sums, or null
+  RowMap rows;
 };
 
 // Workgroups that share one (batch, chunk, head) in the backward chunk kernel
@@ -80,13 +93,18 @@ struct ProbeScope {
 };
 
 // Copies between the rows [row0, row0 + nvalid) of each of the b sequences
-// of a tensor with row stride L and a zero-padded [b][Q] row buffer
-// (pad_rows fills the rows past nvalid with zero bytes; unpad_rows copies the
-// nvalid rows back).  rowbytes is even; both pointers are 16-byte aligned.
-void pad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-              int64_t b, hipStream_t st);
-void unpad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-                int64_t b, hipStream_t st);
+// of up to four tensors with row stride L and zero-padded [b][Q] row buffers
+// (pad: the buffers' rows past nvalid get zero bytes; unpad: the nvalid rows
+// are copied back), in one launch.  Row sizes are even; every pointer is
+// 16-byte aligned.
+struct RowCopy {
+  const void* src[4];
+  void* dst[4];
+  int64_t rowbytes[4];
+  int n;
+};
+void pad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st);
+void unpad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st);
 
 template <typename T, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);

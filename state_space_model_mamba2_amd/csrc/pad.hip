@@ -1,14 +1,14 @@
 // Row copies between a sequence's last, shorter chunk and a zero-padded
 // one-chunk buffer.  A sequence whose length is not a multiple of the chunk
-// length Q runs its whole chunks in place and its remaining tokens as one
-// chunk of Q rows, the rows past the sequence's end set to zero: a zero step
-// size leaves the state and the chunk's cumulative decay unchanged, and zero
-// x, B, C and dy rows contribute nothing to any output or gradient.
+// length Q has its last chunk read from and written to such buffers of Q
+// rows, the rows past the sequence's end set to zero: a zero step size
+// leaves the state and the chunk's cumulative decay unchanged, and zero x, B,
+// C and dy rows contribute nothing to any output or gradient.
 //
-// Rows are `rowbytes` bytes; sequence b's rows start at row b * L of the
-// strided tensor and at row b * Q of the padded buffer.  The copies work in
-// the widest unit (16, 8, 4 or 2 bytes) that divides the row size; both base
-// pointers are 16-byte aligned.
+// Sequence b's rows start at row b * L of the strided tensor and at row b * Q
+// of the padded buffer.  One launch copies up to four tensors (blockIdx.y
+// picks the tensor), each in the widest unit (16, 8, 4 or 2 bytes) that
+// divides its row size; every pointer is 16-byte aligned.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -18,64 +18,72 @@
 namespace ssd {
 namespace {
 
-template <typename U>
-__global__ __launch_bounds__(256) void k_pad_rows(const U* __restrict__ src, U* __restrict__ dst, int64_t rowlen,
-                                                  int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-                                                  int64_t total) {
+struct CopyJob {
+  const char* src[4];
+  char* dst[4];
+  int64_t rowbytes[4];
+  int64_t L, row0, nvalid, Q;
+};
+
+template <typename U, bool PAD>
+__device__ void copy_rows(const CopyJob& j, int t, int64_t nb) {
+  const int64_t rowlen = j.rowbytes[t] / (int64_t)sizeof(U);
+  const U* src = reinterpret_cast<const U*>(j.src[t]);
+  U* dst = reinterpret_cast<U*>(j.dst[t]);
+  const int64_t rows = PAD ? j.Q : j.nvalid;  // per sequence
+  const int64_t total = nb * rows * rowlen;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = e / rowlen, col = e - r * rowlen;
-    const int64_t b = r / Q, i = r - b * Q;
-    U v{};
-    if (i < nvalid) v = src[(b * L + row0 + i) * rowlen + col];
-    dst[e] = v;
+    const int64_t b = r / rows, i = r - b * rows;
+    const int64_t strided = (b * j.L + j.row0 + i) * rowlen + col;
+    const int64_t padded = (b * j.Q + i) * rowlen + col;
+    if (PAD) {
+      U v{};
+      if (i < j.nvalid) v = src[strided];
+      dst[padded] = v;
+    } else {
+      dst[strided] = src[padded];
+    }
   }
 }
 
-template <typename U>
-__global__ __launch_bounds__(256) void k_unpad_rows(const U* __restrict__ src, U* __restrict__ dst, int64_t rowlen,
-                                                    int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-                                                    int64_t total) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = e / rowlen, col = e - r * rowlen;
-    const int64_t b = r / nvalid, i = r - b * nvalid;
-    dst[(b * L + row0 + i) * rowlen + col] = src[(b * Q + i) * rowlen + col];
+template <bool PAD>
+__global__ __launch_bounds__(256) void k_copy_rows(const CopyJob j, int64_t nb) {
+  const int t = blockIdx.y;
+  const int64_t rb = j.rowbytes[t];
+  if (rb % 16 == 0) copy_rows<uint4, PAD>(j, t, nb);
+  else if (rb % 8 == 0) copy_rows<uint2, PAD>(j, t, nb);
+  else if (rb % 4 == 0) copy_rows<uint32_t, PAD>(j, t, nb);
+  else copy_rows<uint16_t, PAD>(j, t, nb);
+}
+
+template <bool PAD>
+void launch(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st) {
+  if (c.n <= 0) return;
+  CopyJob j{};
+  int64_t most = 0;
+  for (int t = 0; t < c.n; ++t) {
+    j.src[t] = static_cast<const char*>(c.src[t]);
+    j.dst[t] = static_cast<char*>(c.dst[t]);
+    j.rowbytes[t] = c.rowbytes[t];
+    const int64_t units = b * (PAD ? Q : nvalid) * c.rowbytes[t] / 16;
+    if (units > most) most = units;
   }
-}
-
-template <typename U>
-void launch(bool pad, const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid,
-            int64_t Q, int64_t b, hipStream_t st) {
-  const int64_t rowlen = rowbytes / (int64_t)sizeof(U);
-  const int64_t total = b * (pad ? Q : nvalid) * rowlen;
-  if (total <= 0) return;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (pad)
-    k_pad_rows<U><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(static_cast<const U*>(src), static_cast<U*>(dst),
-                                                                rowlen, L, row0, nvalid, Q, total);
-  else
-    k_unpad_rows<U><<<dim3((unsigned)blocks), dim3(256), 0, st>>>(static_cast<const U*>(src), static_cast<U*>(dst),
-                                                                  rowlen, L, row0, nvalid, Q, total);
-}
-
-void dispatch(bool pad, const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid,
-              int64_t Q, int64_t b, hipStream_t st) {
-  if (rowbytes % 16 == 0) launch<uint4>(pad, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
-  else if (rowbytes % 8 == 0) launch<uint2>(pad, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
-  else if (rowbytes % 4 == 0) launch<uint32_t>(pad, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
-  else launch<uint16_t>(pad, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
+  j.L = L; j.row0 = row0; j.nvalid = nvalid; j.Q = Q;
+  int64_t blocks = (most + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 2048) blocks = 2048;
+  k_copy_rows<PAD><<<dim3((unsigned)blocks, (unsigned)c.n), dim3(256), 0, st>>>(j, b);
 }
 
 }  // namespace
 
-void pad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-              int64_t b, hipStream_t st) {
-  dispatch(true, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
+void pad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st) {
+  launch<true>(c, L, row0, nvalid, Q, b, st);
 }
 
-void unpad_rows(const void* src, void* dst, int64_t rowbytes, int64_t L, int64_t row0, int64_t nvalid, int64_t Q,
-                int64_t b, hipStream_t st) {
-  dispatch(false, src, dst, rowbytes, L, row0, nvalid, Q, b, st);
+void unpad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st) {
+  launch<false>(c, L, row0, nvalid, Q, b, st);
 }
 
 }  // namespace ssd

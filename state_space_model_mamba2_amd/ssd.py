@@ -54,9 +54,10 @@ class Context:
 
     def intermediates(self):
         """Views into the saved workspace: cs [b, H, K, Q] float32 and
-        hin [b, K, H, P, N] (entry state of each chunk, storage dtype)."""
+        hin [b, K, H, P, N] (entry state of each chunk, storage dtype), with
+        K = ceil(seqlen / chunk) (a shorter last chunk is zero-padded)."""
         s = self.shape
-        K = s.seqlen // s.chunk
+        K = -(-s.seqlen // s.chunk)
         ncs = s.batch * s.nheads * K * s.chunk
         cs = self.saved_ws[: ncs * 4].view(torch.float32).view(s.batch, s.nheads, K, s.chunk)
         off = (ncs * 4 + _ALIGN - 1) // _ALIGN * _ALIGN
