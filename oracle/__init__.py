@@ -12,4 +12,6 @@ Contents:
   chunked  -- the chunked evaluation (per-chunk quadratic block + inter-chunk
               state passing) in float64, with its intermediates
   fd       -- central finite differences of the scalar <dy, y>
+  dtproc   -- the step preprocessing dt = softplus(dt_raw + dt_bias) and
+              its chain rule
 """
