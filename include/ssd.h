@@ -58,7 +58,7 @@ extern "C" {
 
 typedef enum {
     SSD_OK = 0,
-    SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, seqlen % chunk, nheads % ngroups, misalignment */
+    SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, nheads % ngroups, unknown flag, misalignment */
     SSD_ERR_UNSUPPORTED = 2,      /* (dtype, chunk, headdim, dstate) combination not compiled in */
     SSD_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than the *_bytes query */
     SSD_ERR_HIP = 4               /* a HIP call or kernel launch failed */
@@ -66,8 +66,17 @@ typedef enum {
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
-/* Problem size.  chunk is the chunk length Q of the chunked scan; seqlen must
- * be a multiple of it.  dtype is an ssd_dtype.  Compiled (chunk, headdim,
+/* ssd_shape.flags.  SSD_DT_SOFTPLUS: the dt argument is the raw step and the
+ * scan uses dt_t = softplus(dt_raw_t + dt_bias_h), softplus(z) = log(1 + e^z)
+ * (z itself for z > 20), the Mamba-2 block's step parameterisation; in bf16
+ * mode that step is rounded to bfloat16 once.  ddt is then the gradient of
+ * the raw step, ddt_raw = ddt_step * sigmoid(dt_raw + dt_bias), and ssd_bwd
+ * can return the bias gradient, the sum of ddt_raw over batch and tokens. */
+enum { SSD_DT_SOFTPLUS = 1 };
+
+/* Problem size.  chunk is the chunk length Q of the chunked scan; when
+ * seqlen is not a multiple of it, the last chunk of every sequence holds the
+ * remaining seqlen mod Q tokens.  dtype is an ssd_dtype.  Compiled (chunk, headdim,
  * dstate) combinations (others give SSD_ERR_UNSUPPORTED):
  *   SSD_BF16: chunk 128 or 256 with (headdim, dstate) (16, 16), (64, 64), (64, 128)
  *   SSD_F32 : chunk 64, 128 or 256 with (16, 16); chunk 64 or 128 with (64, 64);
@@ -75,7 +84,7 @@ typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
     int32_t dtype;
-    int32_t reserved; /* must be 0 */
+    int32_t flags;    /* 0 or SSD_DT_SOFTPLUS */
 } ssd_shape;
 
 /* Forward-to-backward context, filled by ssd_fwd.  It borrows the input
@@ -131,7 +140,8 @@ ssd_status ssd_check_shape(const ssd_shape *shape);
 
 /* Forward pass: y and final_state from x, dt, A, B, C, D, starting from
  * initial_state (NULL means zero; it is read during the call only, the
- * backward keeps its own copy in saved_ws).
+ * backward keeps its own copy in saved_ws).  dt_bias [nheads] float32 is
+ * read only with SSD_DT_SOFTPLUS (NULL means zero).
  * y is written; final_state is written if non-NULL.  saved_ws (>=
  * ssd_saved_bytes) receives what ssd_bwd needs; saved_out, if non-NULL, is
  * filled with the context ssd_bwd consumes.  scratch (>= ssd_fwd_scratch_bytes)
@@ -140,7 +150,7 @@ ssd_status ssd_check_shape(const ssd_shape *shape);
 ssd_status ssd_fwd(const ssd_shape *shape,
                    const void *x, const void *dt, const float *A,
                    const void *B, const void *C, const float *D,
-                   const float *initial_state,
+                   const float *dt_bias, const float *initial_state,
                    void *y, float *final_state,
                    void *saved_ws, size_t saved_ws_bytes, ssd_saved *saved_out,
                    void *scratch, size_t scratch_bytes,
@@ -150,11 +160,12 @@ ssd_status ssd_fwd(const ssd_shape *shape,
  * for the forward that filled `saved` (dfinal_state NULL means zero).
  * dx, ddt, dA, dB, dC, dD are overwritten (not accumulated); dinitial_state,
  * the gradient of the forward's initial state, is written if non-NULL (also
- * when the forward started from zero).
+ * when the forward started from zero); ddt_bias [nheads] float32, the dt_bias
+ * gradient, is written if non-NULL and the shape has SSD_DT_SOFTPLUS.
  * scratch must hold ssd_bwd_scratch_bytes(&saved->shape). probe may be NULL. */
 ssd_status ssd_bwd(const ssd_saved *saved, const void *dy, const float *dfinal_state,
                    void *dx, void *ddt, float *dA, void *dB, void *dC, float *dD,
-                   float *dinitial_state,
+                   float *ddt_bias, float *dinitial_state,
                    void *scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe *probe);
 

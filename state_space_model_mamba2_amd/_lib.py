@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_F32, SSD_BF16 = 0, 1
+SSD_DT_SOFTPLUS = 1
 
 KERNELS = ["chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
            "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"]
@@ -18,7 +19,7 @@ KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
-                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class Saved(ctypes.Structure):
@@ -53,9 +54,9 @@ def load():
         f = getattr(lib, name)
         f.argtypes, f.restype = [PShape], sz
     lib.ssd_check_shape.argtypes, lib.ssd_check_shape.restype = [PShape], st
-    lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
+    lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
     lib.ssd_fwd.restype = st
-    lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
+    lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
     lib.ssd_bwd.restype = st
     lib.ssd_status_string.argtypes, lib.ssd_status_string.restype = [st], ctypes.c_char_p
     lib.ssd_kernel_name.argtypes, lib.ssd_kernel_name.restype = [ctypes.c_int32], ctypes.c_char_p
@@ -68,5 +69,5 @@ def status_string(code: int) -> str:
     return load().ssd_status_string(code).decode()
 
 
-def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype) -> Shape:
-    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, 0)
+def make_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, flags=0) -> Shape:
+    return Shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, flags)

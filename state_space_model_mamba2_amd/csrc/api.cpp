@@ -24,7 +24,7 @@ bool is_supported(int dtype, int64_t Q, int64_t P, int64_t N) {
 ssd_status check_shape(const ssd_shape* s) {
   if (!s) return SSD_ERR_INVALID_ARGUMENT;
   if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 ||
-      s->ngroups <= 0 || s->chunk <= 0 || s->reserved != 0)
+      s->ngroups <= 0 || s->chunk <= 0 || (s->flags & ~SSD_DT_SOFTPLUS) != 0)
     return SSD_ERR_INVALID_ARGUMENT;
   if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
   if (s->nheads % s->ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
@@ -94,15 +94,19 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
 // A sequence of L tokens runs as K = ceil(L / Q) chunks.  The whole ones
 // are read and written in place; when L % Q = Lr > 0, the last one (chunk kf
 // = L / Q) holds Lr tokens and runs on zero-padded copies of Q rows per
-// sequence: the inputs' copies are made by the forward and kept in the saved
-// workspace, dy's copy and the last chunk's outputs live in the backward
-// scratch, and the valid rows are copied back to the caller's tensors.
+// sequence: the x, B, C copies are made by the forward and kept in the saved
+// workspace (dt's only feeds the cumsum), dy's copy and the last chunk's
+// outputs live in the backward scratch, and the valid rows are copied back
+// to the caller's tensors.  The float32 step the cumsum writes ([b][H][K][Q],
+// like cs) is saved for the backward.
+// With SSD_DT_SOFTPLUS the backward adds per-chunk partials of the bias
+// gradient.
 struct Plan {
   Layout lay;
   int64_t kf, Lr;
-  size_t sv_tx, sv_tdt, sv_tB, sv_tC, saved_bytes;
-  size_t fw_ty, fwd_bytes;
-  size_t bw_tdy, bw_tdx, bw_tddt, bw_tdB, bw_tdC, bwd_bytes;
+  size_t sv_tx, sv_tB, sv_tC, sv_dtf, saved_bytes;
+  size_t fw_tdt, fw_ty, fwd_bytes;
+  size_t bw_tdy, bw_tdx, bw_tddt, bw_tdB, bw_tdC, bw_dbias, bwd_bytes;
 };
 
 Plan make_plan(const ssd_shape* s) {
@@ -117,12 +121,14 @@ Plan make_plan(const ssd_shape* s) {
   const size_t xrows = tail ? align_up(b * q * H * P * esz) : 0, trows = tail ? align_up(b * q * H * esz) : 0;
   const size_t brows = tail ? align_up(b * q * G * N * esz) : 0;
   size_t o = p.lay.saved_bytes;
-  p.sv_tx = o;  o += xrows;
-  p.sv_tdt = o; o += trows;
-  p.sv_tB = o;  o += brows;
-  p.sv_tC = o;  o += brows;
+  p.sv_tx = o;   o += xrows;
+  p.sv_tB = o;   o += brows;
+  p.sv_tC = o;   o += brows;
+  p.sv_dtf = o;  o += align_up(b * H * (size_t)p.lay.K * q * 4);
   p.saved_bytes = o;
+  const bool sp = (s->flags & SSD_DT_SOFTPLUS) != 0;
   o = p.lay.fwd_bytes;
+  p.fw_tdt = o; o += trows;
   p.fw_ty = o;  o += xrows;
   p.fwd_bytes = o;
   o = p.lay.bwd_bytes;
@@ -131,6 +137,7 @@ Plan make_plan(const ssd_shape* s) {
   p.bw_tddt = o; o += trows;
   p.bw_tdB = o;  o += brows;
   p.bw_tdC = o;  o += brows;
+  p.bw_dbias = o; if (sp) o += align_up(b * (size_t)p.lay.K * H * 4);
   p.bwd_bytes = o;
   return p;
 }
@@ -234,7 +241,7 @@ size_t ssd_fwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_
 size_t ssd_bwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).bwd_bytes : 0; }
 
 ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
-                   const float* D, const float* initial_state, void* y, float* final_state, void* saved_ws,
+                   const float* D, const float* dt_bias, const float* initial_state, void* y, float* final_state, void* saved_ws,
                    size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe* probe) {
   const ssd_status st = check_shape(s);
@@ -245,6 +252,7 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
     if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
   if (final_state && !aligned16(final_state)) return SSD_ERR_INVALID_ARGUMENT;
   if (initial_state && !aligned16(initial_state)) return SSD_ERR_INVALID_ARGUMENT;
+  if (dt_bias && !aligned16(dt_bias)) return SSD_ERR_INVALID_ARGUMENT;
   const Plan pl = make_plan(s);
   if (!saved_ws || saved_ws_bytes < pl.saved_bytes) return SSD_ERR_WORKSPACE;
   if (!scratch || scratch_bytes < pl.fwd_bytes) return SSD_ERR_WORKSPACE;
@@ -256,12 +264,16 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
   a.init = initial_state;
   a.final_state = final_state;
+  a.softplus = (s->flags & SSD_DT_SOFTPLUS) ? 1 : 0;
+  a.dt_bias = dt_bias;
+  a.dtf = at<float>(saved_ws, pl.sv_dtf);
   a.rows.L = L;
   a.rows.kf = (int)pl.kf;
+  a.rows.lr = (int)pl.Lr;
   set_fwd_ws(a, pl.lay, saved_ws, scratch);
   if (pl.Lr > 0) {
     a.rows.x = at<char>(saved_ws, pl.sv_tx);
-    a.rows.dt = at<char>(saved_ws, pl.sv_tdt);
+    a.rows.dt = at<char>(scratch, pl.fw_tdt);
     a.rows.B = at<char>(saved_ws, pl.sv_tB);
     a.rows.C = at<char>(saved_ws, pl.sv_tC);
     a.rows.y = at<char>(scratch, pl.fw_ty);
@@ -289,7 +301,7 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
 }
 
 ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_state, void* dx, void* ddt, float* dA,
-                   void* dB, void* dC, float* dD, float* dinitial_state, void* scratch, size_t scratch_bytes,
+                   void* dB, void* dC, float* dD, float* ddt_bias, float* dinitial_state, void* scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe* probe) {
   if (!sv) return SSD_ERR_INVALID_ARGUMENT;
   const ssd_shape* s = &sv->shape;
@@ -298,7 +310,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   if (!sv->x || !sv->dt || !sv->A || !sv->B || !sv->C || !sv->D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {sv->x, sv->dt, sv->A, sv->B, sv->C, sv->D, dy, dx, ddt, dA, dB, dC, dD, sv->saved_ws, scratch,
-                        dfinal_state, dinitial_state};
+                        dfinal_state, dinitial_state, ddt_bias};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
   const Plan pl = make_plan(s);
@@ -312,12 +324,18 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   a.x = sv->x; a.dt = sv->dt; a.B = sv->B; a.C = sv->C; a.dy = dy; a.A = sv->A; a.D = sv->D;
   a.dx = dx; a.ddt = ddt; a.dB = dB; a.dC = dC; a.dA = dA; a.dD = dD;
   a.dfinal = dfinal_state; a.dinit = dinitial_state;
+  a.dtf = at<float>(sv->saved_ws, pl.sv_dtf);
+  a.softplus = (s->flags & SSD_DT_SOFTPLUS) ? 1 : 0;
+  if (a.softplus) {
+    a.ddt_bias = ddt_bias;
+    a.dbiaspart = at<float>(scratch, pl.bw_dbias);
+  }
   a.rows.L = L;
   a.rows.kf = (int)pl.kf;
+  a.rows.lr = (int)pl.Lr;
   set_bwd_ws(a, pl.lay, sv->saved_ws, scratch);
   if (pl.Lr > 0) {
     a.rows.x = at<char>(sv->saved_ws, pl.sv_tx);
-    a.rows.dt = at<char>(sv->saved_ws, pl.sv_tdt);
     a.rows.B = at<char>(sv->saved_ws, pl.sv_tB);
     a.rows.C = at<char>(sv->saved_ws, pl.sv_tC);
     a.rows.dy = at<char>(scratch, pl.bw_tdy);

@@ -40,7 +40,7 @@ namespace ssd {
 // about the same time.
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
-    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
     const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin, const T* __restrict__ gst,
     const T* __restrict__ wb, const T* __restrict__ dy, T* __restrict__ dx, float* __restrict__ dlpart,
     float* __restrict__ dlscal, int nitems, const RowMap rm, int H, int G, int K) {
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
-  dt = rows_in(rm, k, dt, rm.dt);
+  const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   B = rows_in(rm, k, B, rm.B);
   C = rows_in(rm, k, C, rm.C);
   dy = rows_in(rm, k, dy, rm.dy);
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     const int i = threadIdx.x + NTH * n;
     if (Q % NTH == 0 || i < Q) {
       csv[n] = csc[i];
-      dtv[n] = to_f(dt[(row0 + i) * H + h]);
+      dtv[n] = dtc[i];
     }
   }
   V yv[YPT];
@@ -469,10 +469,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 // heads are one contiguous run.
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
-                                                     const float* __restrict__ cs_g, const T* __restrict__ dt,
+                                                     const float* __restrict__ cs_g, const float* __restrict__ dt,
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
-                                                     const RowMap rm, int H, int K) {
+                                                     float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
+                                                     int softplus) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
   constexpr int TPL = Q / 16;
   const int nhb = (H + 15) / 16;
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   if (h >= H) return;  // whole 16-lane group; only width-16 shuffles below
   const int bkh = bk * H + h;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
-  dt = rows_in(rm, k, dt, rm.dt);
+  const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   ddt = rows_out(rm, k, ddt, rm.ddt);
   const float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;
   const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
@@ -527,22 +528,33 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   const float tail = __expf(csc[Q - 1]) * sc[0];
   const float Ah = Ap[h];
   const float* xd = part + (NSPLIT + 2) * Q + j0;
-  float da = 0.0f;
+  float da = 0.0f, dbias = 0.0f;
 #pragma unroll
   for (int t = 0; t < TPL; ++t) {
     const int j = j0 + t;
     const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
-    da += to_f(dt[(row0 + j) * H + h]) * dl;
-    ddt[(row0 + j) * H + h] = from_f<T>(Ah * dl + xd[t]);
+    const float dtv = dtc[j];
+    da += dtv * dl;
+    float g = Ah * dl + xd[t];
+    if (softplus) {
+      // the step was softplus(z): d dt / dz = sigmoid(z) = 1 - exp(-dt)
+      g *= -expm1f(-dtv);
+      dbias += g;
+    }
+    ddt[(row0 + j) * H + h] = from_f<T>(g);
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) da += __shfl_xor(da, off, 16);
+  for (int off = 1; off < 16; off <<= 1) {
+    da += __shfl_xor(da, off, 16);
+    if (softplus) dbias += __shfl_xor(dbias, off, 16);
+  }
   if (jl == 0) {
     float dds = 0.0f;
 #pragma unroll
     for (int sp = 0; sp < NSPLIT; ++sp) dds += sc[1 + sp];
     dapart[bkh] = da;
     ddpart[bkh] = dds;
+    if (softplus) dbiaspart[bkh] = dbias;
   }
 }
 
@@ -564,7 +576,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
 // blockIdx.z selects a slice of hps heads of the group; each slice writes its
 // own partial dW (summed later in a fixed order).
 template <typename T, int Q, int P, bool DIAG>
-__global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __restrict__ dt,
+__global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float* __restrict__ dt,
                                             const float* __restrict__ cs_g, const T* __restrict__ dy,
                                             float* __restrict__ dw, const RowMap rm, int H, int G, int K, int hps) {
   constexpr int NTH = 256;
@@ -591,7 +603,6 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
-  dt = rows_in(rm, k, dt, rm.dt);
   dy = rows_in(rm, k, dy, rm.dy);
   const int hpg = H / G;
   const int h0 = g * hpg + blockIdx.z * hps;                  // first head of this slice
@@ -607,13 +618,14 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
   auto load = [&](int hh) {
     const int h = h0 + hh;
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+    const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
 #pragma unroll
     for (int n = 0; n < XPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (XPIECES % NTH == 0 || u < XPIECES) {
         const int r = u / (P / VN);
         xv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
-        xs[n] = DIAG ? 1.0f : to_f(dt[(row0 + j0 + r) * H + h]) * __expf(csb[ref] - csb[j0 + r]);
+        xs[n] = DIAG ? 1.0f : dtb[j0 + r] * __expf(csb[ref] - csb[j0 + r]);
       }
     }
     const T* arow = dy + ((row0 + ia) * H + h) * P;
@@ -622,7 +634,7 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
     if (!DIAG) ascale = __expf(csb[ia] - csb[ref]);
     if (DIAG && threadIdx.x < 64) {
       jcs = csb[j0 + threadIdx.x];
-      jdt = to_f(dt[(row0 + j0 + threadIdx.x) * H + h]);
+      jdt = dtb[j0 + threadIdx.x];
     }
   };
   auto store = [&](int bf) {
@@ -713,7 +725,7 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const T* __
 // K-major with the transposing LDS read.  Every slice writes an fp32
 // partial; k_bc_final adds the slices and the dW part.
 template <typename T, int Q, int P, int N, bool DB>
-__global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const T* __restrict__ dt,
+__global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const float* __restrict__ dt,
                                                   const float* __restrict__ cs_g, const T* __restrict__ dy,
                                                   const T* __restrict__ state, float* __restrict__ out,
                                                   const RowMap rm, int H, int G, int K, int hps) {
@@ -732,7 +744,6 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
-  dt = rows_in(rm, k, dt, rm.dt);
   dy = rows_in(rm, k, dy, rm.dy);
   const int64_t prow0 = ((int64_t)b * K + k) * Q;  // row of the fp32 partials (chunk rows)
   const int hpg = H / G;
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
 #pragma unroll
     for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], urow, kp * 32, q);
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-    ascale = DB ? __expf(csb[Q - 1] - csb[i]) * to_f(dt[(row0 + i) * H + h]) : __expf(csb[i]);
+    ascale = DB ? __expf(csb[Q - 1] - csb[i]) * dt[(((int64_t)b * H + h) * K + k) * Q + i] : __expf(csb[i]);
   };
   auto store = [&](int bf) {
 #pragma unroll
@@ -895,25 +906,30 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
   }
 }
 
-// Fixed-order sums of the per-(b, k) partials: one workgroup per head; each
-// thread sums a strided slice, then a fixed tree combines the slices.
+// Fixed-order sums of the per-(b, k) partials (dA, dD and, when requested,
+// the dt bias gradient): one workgroup per head; each thread sums a strided
+// slice, then a fixed tree combines the slices.
 __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart, const float* __restrict__ ddpart,
-                                               float* __restrict__ dA, float* __restrict__ dD, int BK, int H) {
-  __shared__ float ra[4], rd[4];
+                                               const float* __restrict__ dbiaspart, float* __restrict__ dA,
+                                               float* __restrict__ dD, float* __restrict__ dbias, int BK, int H) {
+  __shared__ float ra[4], rd[4], rb[4];
   const int h = blockIdx.x;
-  float sa = 0.0f, sd = 0.0f;
+  float sa = 0.0f, sd = 0.0f, sb = 0.0f;
   for (int i = threadIdx.x; i < BK; i += 256) {
     sa += dapart[(int64_t)i * H + h];
     sd += ddpart[(int64_t)i * H + h];
+    if (dbias) sb += dbiaspart[(int64_t)i * H + h];
   }
   sa = wave_sum(sa);
   sd = wave_sum(sd);
+  if (dbias) sb = wave_sum(sb);
   const int wave = threadIdx.x / kWave;
-  if (lane_id() == 0) { ra[wave] = sa; rd[wave] = sd; }
+  if (lane_id() == 0) { ra[wave] = sa; rd[wave] = sd; rb[wave] = sb; }
   __syncthreads();
   if (threadIdx.x == 0) {
     dA[h] = (ra[0] + ra[1]) + (ra[2] + ra[3]);
     dD[h] = (rd[0] + rd[1]) + (rd[2] + rd[3]);
+    if (dbias) dbias[h] = (rb[0] + rb[1]) + (rb[2] + rb[3]);
   }
 }
 
@@ -921,7 +937,7 @@ template <typename T, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_probe* probe) {
   const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
   const T* x = static_cast<const T*>(a.x);
-  const T* dt = static_cast<const T*>(a.dt);
+  const float* dt = a.dtf;  // the step, float32, as the forward's cumsum wrote it
   const T* B = static_cast<const T*>(a.B);
   const T* C = static_cast<const T*>(a.C);
   const T* dy = static_cast<const T*>(a.dy);
@@ -944,7 +960,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(groups * 8 * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     k_dl_assemble<T, Q><<<dim3(b * K * ((H + 15) / 16)), dim3(256), 0, st>>>(
-        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.rows, H, K);
+        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;
@@ -972,7 +988,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
-    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dA, a.dD, b * K, H);
+    k_da_dd<<<dim3(H), dim3(256), 0, st>>>(a.dapart, a.ddpart, a.dbiaspart, a.dA, a.dD,
+                                           a.softplus ? a.ddt_bias : nullptr, b * K, H);
   }
 }
 

@@ -22,7 +22,7 @@ namespace ssd {
 // workgroup.  Each wave loads the C rows and all C.B^T tiles of its next row
 // tile while it computes the current one.
 template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__ x, const T* __restrict__ dt,
+__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__ x, const float* __restrict__ dt,
                                                            const float* __restrict__ cs_g, const float* __restrict__ Dp,
                                                            const T* __restrict__ C, const T* __restrict__ hin,
                                                            const T* __restrict__ wt, T* __restrict__ y,
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
-  dt = rows_in(rm, k, dt, rm.dt);
+  const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   C = rows_in(rm, k, C, rm.C);
   y = rows_out(rm, k, y, rm.y);
   const T* wtb = wt + (int64_t)((b * K + k) * G + g) * TILES * 256;
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
     const int i = threadIdx.x + NTH * n;
     if (Q % NTH == 0 || i < Q) {
       csv[n] = csc[i];
-      dtv[n] = to_f(dt[(row0 + i) * H + h]);
+      dtv[n] = dtc[i];
     }
   }
   V xr[XPT], hr[HPT];
@@ -204,14 +204,17 @@ template <typename T, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_probe* probe) {
   const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
   const T* x = static_cast<const T*>(a.x);
-  const T* dt = static_cast<const T*>(a.dt);
+  // the cumsum writes the step in float32 (the caller's dt widened, or
+  // softplus(dt + dt_bias)); every later kernel reads that
+  const float* dt = a.dtf;
   const T* B = static_cast<const T*>(a.B);
   const T* C = static_cast<const T*>(a.C);
   T* hin = static_cast<T*>(a.hin);
   T* wt = static_cast<T*>(a.wt);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_CUMSUM, st);
-    k_chunk_cumsum<T, Q><<<dim3(b * H * K), dim3(64), 0, st>>>(dt, a.A, a.cs, a.rows, H, K);
+    k_chunk_cumsum<T, Q><<<dim3(b * H * K), dim3(64), 0, st>>>(
+        static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, a.rows, H, K, a.softplus);
   }
   {
     ProbeScope ps(probe, SSD_K_BMM_FWD, st);

@@ -63,21 +63,39 @@ __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 
 // Chunk cumsum: cs[b][h][k][i] = sum_{j <= i} dt[b][kQ + j][h] * A[h].
 // One wavefront per (b, h, k); each lane owns Q/64 consecutive tokens and the
 // chunk-wide prefix comes from a wave64 shuffle scan.
+// The step is written in float32 for every later kernel, in cs's layout
+// (dt_out[b][h][k][i], so that a chunk's steps of one head are contiguous;
+// rows past the end of a shorter last chunk get 0).  It is the caller's dt
+// widened or, with softplus set (dt then holds the raw step),
+// softplus(dt + dt_bias[h]) = log(1 + e^z) (z itself above 20).
 template <typename T, int Q>
 __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, const float* __restrict__ A,
-                                                     float* __restrict__ cs, const RowMap rm, int H, int K) {
+                                                     const float* __restrict__ dt_bias, float* __restrict__ dt_out,
+                                                     float* __restrict__ cs, const RowMap rm, int H, int K,
+                                                     int softplus) {
   constexpr int TPL = Q / kWave;
   const int bhk = blockIdx.x;
   const int k = bhk % K, bh = bhk / K, h = bh % H, b = bh / H;
   const int l = threadIdx.x;
+  const bool last = k == rm.kf;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
-  dt = rows_in(rm, k, dt, rm.dt);
+  const T* src = rows_in(rm, k, dt, rm.dt);
+  float* dst = dt_out + (int64_t)bhk * Q + l * TPL;
   const float a = A[h];
+  const float bias = (softplus && dt_bias) ? dt_bias[h] : 0.0f;
   float v[TPL];
 #pragma unroll
   for (int j = 0; j < TPL; ++j) {
-    const int64_t t = row0 + l * TPL + j;
-    v[j] = to_f(dt[t * H + h]) * a;
+    const int i = l * TPL + j;
+    const int64_t e = (row0 + i) * H + h;
+    float d = to_f(src[e]);
+    if (softplus) {
+      const float z = d + bias;
+      d = z > 20.0f ? z : log1pf(expf(z));
+    }
+    if (last && i >= rm.lr) d = 0.0f;
+    dst[j] = d;
+    v[j] = d * a;
   }
 #pragma unroll
   for (int j = 1; j < TPL; ++j) v[j] += v[j - 1];
@@ -152,7 +170,7 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
 // current one is used.  One workgroup (4 waves) per (b, k, h).
 template <typename T, int Q, int P, int N, bool BWD>
 __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, const T* __restrict__ V,
-                                                     const T* __restrict__ dt, const float* __restrict__ cs,
+                                                     const float* __restrict__ dt, const float* __restrict__ cs,
                                                      float* __restrict__ out, const RowMap rm, int H, int G, int K) {
   constexpr int NTH = 256;
   constexpr int KB = 64;                           // tokens per block
@@ -173,8 +191,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   U = rows_in(rm, k, U, BWD ? rm.dy : rm.x);
   V = rows_in(rm, k, V, BWD ? rm.C : rm.B);
-  dt = rows_in(rm, k, dt, rm.dt);
   const float* csc = cs + (((int64_t)b * H + h) * K + k) * Q;
+  const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   const float cs_last = csc[Q - 1];
 
   V16 uv[UPT], vv[VPT];
@@ -186,7 +204,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
       if (UPIECES % NTH == 0 || u < UPIECES) {
         const int i = KB * blk + u / (P / VN);
         uv[n] = *reinterpret_cast<const V16*>(U + ((row0 + i) * H + h) * P + (u % (P / VN)) * VN);
-        uw[n] = BWD ? __expf(csc[i]) : to_f(dt[(row0 + i) * H + h]) * __expf(cs_last - csc[i]);
+        uw[n] = BWD ? __expf(csc[i]) : dtc[i] * __expf(cs_last - csc[i]);
       }
     }
 #pragma unroll

@@ -35,6 +35,7 @@ struct Layout {
 struct RowMap {
   int64_t L;
   int kf;
+  int lr;  // rows of chunk kf that hold tokens (L - kf * Q)
   const void *x, *dt, *B, *C, *dy;  // zero-padded inputs of chunk kf
   void *y, *dx, *ddt, *dB, *dC;     // its outputs, copied back afterwards
 };
@@ -43,6 +44,9 @@ struct FwdArgs {
   const void *x, *dt, *B, *C;
   const float *A, *D;
   const float* init;  // [b][H][P][N] initial state, or null for zero
+  int softplus;         // dt is the raw step: the scan uses softplus(dt + dt_bias)
+  const float* dt_bias; // [H] or null (zero); read when softplus is set
+  float* dtf;           // [b][H][K][Q] float32 step the scan uses, written by the cumsum (saved)
   void* y;
   float* final_state;
   RowMap rows;
@@ -61,6 +65,10 @@ struct BwdArgs {
   void *dx, *ddt, *dB, *dC;
   float *dA, *dD;
   const float* dfinal;  // [b][H][P][N] final-state cotangent, or null for zero
+  const float* dtf;     // [b][H][K][Q] float32 step the forward used
+  int softplus;         // dt was the raw step: ddt is chained through softplus
+  float* ddt_bias;      // [H] gradient of dt_bias, or null
+  float* dbiaspart;     // [b][K][H] per-chunk partials of ddt_bias (softplus only)
   float* dinit;         // [b][H][P][N] initial-state gradient, or null
   const void* w;   // C.B^T tiles, backward lane order (saved by the forward pass)
   float* dhloc;    // [b][K][H][P][N]

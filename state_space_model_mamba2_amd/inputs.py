@@ -18,6 +18,10 @@ Recipe (one draw per tensor, in this order, from numpy's PCG64 generator
 
     dt = softplus(dt_raw + dt_bias)             (the post-softplus step size)
 
+For runs that take the raw step and apply the softplus themselves, the same
+draws also give dt_raw = N(0, dt_sigma^2) rounded like dt (storage dtype) and
+dt_bias (float32, [nheads]).
+
 States for the runs that start from a given state or carry a final-state
 cotangent come from their own generator, ``default_rng([seed, 1])``, so the
 draws above do not move:
@@ -114,6 +118,8 @@ class Inputs:
     C: np.ndarray
     D: np.ndarray
     dy: np.ndarray
+    dt_raw: np.ndarray = None   # pre-softplus step (storage dtype), same draws as dt
+    dt_bias: np.ndarray = None  # float32 [nheads]
 
     def as_f64(self, name: str) -> np.ndarray:
         """Exact float64 view of a tensor's stored values (for the oracle)."""
@@ -141,14 +147,17 @@ def generate(shape: Shape, seed: int = 0, dt_sigma2: float = 0.5) -> Inputs:
     dy = rng.standard_normal((s.batch, s.seqlen, s.nheads, s.headdim), dtype=np.float32)
 
     dt_bias = np.log(np.expm1(np.exp(u_bias)))  # inverse softplus of exp(u_bias)
-    dt = _softplus(dt_raw.astype(np.float64) * math.sqrt(dt_sigma2) + dt_bias[None, None, :]).astype(np.float32)
+    raw = dt_raw.astype(np.float64) * math.sqrt(dt_sigma2)
+    dt = _softplus(raw + dt_bias[None, None, :]).astype(np.float32)
     A = (-np.exp(u_a)).astype(np.float32)
+    raw = raw.astype(np.float32)
+    bias = dt_bias.astype(np.float32)
 
     if s.dtype == "bf16":
-        x, dt, B, C, dy = (f32_to_bf16_bits(t) for t in (x, dt, B, C, dy))
+        x, dt, B, C, dy, raw = (f32_to_bf16_bits(t) for t in (x, dt, B, C, dy, raw))
     elif s.dtype != "f32":
         raise ValueError(f"unknown dtype {s.dtype!r}")
-    return Inputs(s, x, dt, A, B, C, D, dy)
+    return Inputs(s, x, dt, A, B, C, D, dy, raw, bias)
 
 
 def generate_states(shape: Shape, seed: int = 0):

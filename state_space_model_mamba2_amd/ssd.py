@@ -1,8 +1,10 @@
 """Python face of libssd: the Mamba-2 SSD chunked scan, forward and backward.
 
-    y, final_state, ctx = fwd(x, dt, A, B, C, D, chunk, initial_state=None)
+    y, final_state, ctx = fwd(x, dt, A, B, C, D, chunk, initial_state=None,
+                              dt_softplus=False, dt_bias=None)
     grads = bwd(dy, ctx, dfinal_state=None)   # dict: dx, ddt, dA, dB, dC, dD
-                                              # (+ dinitial_state on request)
+                                              # (+ dinitial_state on request,
+                                              #  + ddt_bias with dt_softplus)
 
 Tensors are torch tensors on the GPU (torch supplies device memory and the
 stream).  Every step of the computation runs in libssd's HIP kernels; this
@@ -51,6 +53,7 @@ class Context:
     saved_ws: torch.Tensor
     shape: _lib.Shape
     dtype: torch.dtype
+    dt_bias: torch.Tensor | None = None
 
     def intermediates(self):
         """Views into the saved workspace: cs [b, H, K, Q] float32 and
@@ -67,10 +70,10 @@ class Context:
         return cs, hin
 
 
-def shape_of(x, B, chunk, dtype_code) -> _lib.Shape:
+def shape_of(x, B, chunk, dtype_code, flags=0) -> _lib.Shape:
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    return _lib.make_shape(b, L, H, P, N, G, chunk, dtype_code)
+    return _lib.make_shape(b, L, H, P, N, G, chunk, dtype_code, flags)
 
 
 def _validate(x, dt, A, B, C, D):
@@ -102,13 +105,21 @@ def _check_state(t, shape, name):
         raise ValueError(f"{name} must be a contiguous float32 GPU tensor of shape {want}")
 
 
-def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = None, stream=None,
+def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = None,
+        dt_softplus: bool = False, dt_bias: torch.Tensor | None = None, stream=None,
         probe: _lib.Probe | None = None, out: torch.Tensor | None = None, scratch: torch.Tensor | None = None,
         want_final_state: bool = True):
-    """Forward pass from initial_state (zero if None).  Returns (y, final_state or None, Context)."""
+    """Forward pass from initial_state (zero if None).  With dt_softplus, dt is
+    the raw step and the scan uses softplus(dt + dt_bias) (dt_bias [H] float32,
+    zero if None).  Returns (y, final_state or None, Context)."""
     lib = _lib.load()
     _validate(x, dt, A, B, C, D)
-    shape = shape_of(x, B, chunk, _DTYPES[x.dtype])
+    if dt_bias is not None:
+        if not dt_softplus:
+            raise ValueError("dt_bias is only used with dt_softplus=True")
+        if dt_bias.dtype != torch.float32 or tuple(dt_bias.shape) != (x.shape[2],) or not dt_bias.is_cuda:
+            raise ValueError("dt_bias must be a float32 GPU tensor of shape [nheads]")
+    shape = shape_of(x, B, chunk, _DTYPES[x.dtype], _lib.SSD_DT_SOFTPLUS if dt_softplus else 0)
     _check_state(initial_state, shape, "initial_state")
     _check(lib.ssd_check_shape(ctypes.byref(shape)), "ssd_fwd")
     dev = x.device
@@ -122,11 +133,12 @@ def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = N
         scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=dev)
     saved = _lib.Saved()
     code = lib.ssd_fwd(ctypes.byref(shape), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(dt_bias) if dt_bias is not None else None,
                        _ptr(initial_state) if initial_state is not None else None, _ptr(y), _ptr(fs) if fs is not None else None, _ptr(saved_ws), saved_bytes,
                        ctypes.byref(saved), _ptr(scratch), scratch.numel(), _stream_handle(stream),
                        ctypes.byref(probe) if probe is not None else None)
     _check(code, "ssd_fwd")
-    ctx = Context(saved, (x, dt, A, B, C, D), saved_ws, shape, x.dtype)
+    ctx = Context(saved, (x, dt, A, B, C, D), saved_ws, shape, x.dtype, dt_bias)
     return y, fs, ctx
 
 
@@ -134,7 +146,8 @@ def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dini
         stream=None, probe: _lib.Probe | None = None, scratch: torch.Tensor | None = None):
     """Backward pass: gradients of sum(dy * y) + sum(dfinal_state * final_state)
     (dfinal_state None means zero).  Returns a dict of tensors, with
-    dinitial_state when want_dinitial_state is set."""
+    dinitial_state when want_dinitial_state is set and, for a forward with
+    dt_softplus, ddt_bias (ddt is then the gradient of the raw step)."""
     lib = _lib.load()
     x, dt, A, B, C, D = ctx.tensors
     if dy.dtype != x.dtype or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
@@ -152,14 +165,19 @@ def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dini
     s = ctx.shape
     ds0 = torch.empty((s.batch, s.nheads, s.headdim, s.dstate), dtype=torch.float32,
                       device=x.device) if want_dinitial_state else None
+    softplus = bool(s.flags & _lib.SSD_DT_SOFTPLUS)
+    dbias = torch.empty_like(A) if softplus else None
     code = lib.ssd_bwd(ctypes.byref(ctx.saved), _ptr(dy), _ptr(dfinal_state) if dfinal_state is not None else None,
                        _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD),
+                       _ptr(dbias) if dbias is not None else None,
                        _ptr(ds0) if ds0 is not None else None, _ptr(scratch), scratch.numel(),
                        _stream_handle(stream), ctypes.byref(probe) if probe is not None else None)
     _check(code, "ssd_bwd")
     g = dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD)
     if ds0 is not None:
         g["dinitial_state"] = ds0
+    if dbias is not None:
+        g["ddt_bias"] = dbias
     return g
 
 
@@ -172,4 +190,5 @@ def to_device(inp, device="cuda"):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    return dict(x=t(inp.x), dt=t(inp.dt), A=t(inp.A), B=t(inp.B), C=t(inp.C), D=t(inp.D), dy=t(inp.dy))
+    return dict(x=t(inp.x), dt=t(inp.dt), A=t(inp.A), B=t(inp.B), C=t(inp.C), D=t(inp.D), dy=t(inp.dy),
+                dt_raw=t(inp.dt_raw), dt_bias=t(inp.dt_bias))

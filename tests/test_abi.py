@@ -63,8 +63,10 @@ def test_shape_checks(lib):
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=256)) == UNSUPPORTED  # fp32 LDS staging limit
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128)) == UNSUPPORTED
     s = shape()
-    s.reserved = 1
+    s.flags = 2                                              # unknown flag
     assert check(lib, s) == INVALID
+    s.flags = _lib.SSD_DT_SOFTPLUS
+    assert check(lib, s) == OK
 
 
 def test_workspace_sizes(lib):
@@ -72,16 +74,21 @@ def test_workspace_sizes(lib):
     b, L, H, P, N, G, Q = 2, 512, 4, 64, 128, 2, 256
     K = L // Q
     saved = lib.ssd_saved_bytes(ctypes.byref(s))
-    assert saved >= b * H * K * Q * 4 + b * K * H * P * N * 2
+    assert saved >= 2 * b * H * K * Q * 4 + b * K * H * P * N * 2  # cs, float32 step, Hin
     assert lib.ssd_fwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * 4
     assert lib.ssd_bwd_scratch_bytes(ctypes.byref(s)) >= b * K * H * P * N * (4 + 2) + b * K * G * Q * Q * 4
     assert lib.ssd_saved_bytes(ctypes.byref(shape(nheads=5))) == 0
-    # a shorter last chunk runs as one more zero-padded chunk: its padded
-    # copies of x, dt, B, C are kept from the forward to the backward
+    # a shorter last chunk runs on zero-padded copies: those of x, B, C are
+    # kept from the forward to the backward
     ragged = lib.ssd_saved_bytes(ctypes.byref(shape(seqlen=500)))
-    assert ragged >= saved - b * H * Q * 4 + b * Q * (H * P + H + 2 * G * N) * 2
+    assert ragged >= saved + b * Q * (H * P + 2 * G * N) * 2
     for f in (lib.ssd_saved_bytes, lib.ssd_fwd_scratch_bytes, lib.ssd_bwd_scratch_bytes):
         assert f(ctypes.byref(shape(seqlen=7))) > 0
+    # with the softplus step the backward adds per-chunk bias-gradient partials
+    sp = shape()
+    sp.flags = _lib.SSD_DT_SOFTPLUS
+    assert lib.ssd_saved_bytes(ctypes.byref(sp)) == saved
+    assert lib.ssd_bwd_scratch_bytes(ctypes.byref(sp)) >= lib.ssd_bwd_scratch_bytes(ctypes.byref(s)) + b * K * H * 4
     # sizes grow linearly with batch
     assert lib.ssd_saved_bytes(ctypes.byref(shape(batch=4))) > saved
 
@@ -90,11 +97,11 @@ FAKE = 0x100000  # aligned, never dereferenced: every call below fails validatio
 
 
 def fwd(lib, s, **over):
-    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, s0=None, y=FAKE, fs=FAKE, ws=FAKE, ws_bytes=0,
-                scratch=FAKE, scratch_bytes=0)
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, bias=None, s0=None, y=FAKE, fs=FAKE, ws=FAKE,
+                ws_bytes=0, scratch=FAKE, scratch_bytes=0)
     args.update(over)
     return lib.ssd_fwd(ctypes.byref(s), args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"],
-                       args["s0"], args["y"], args["fs"], args["ws"], args["ws_bytes"], None, args["scratch"],
+                       args["bias"], args["s0"], args["y"], args["fs"], args["ws"], args["ws_bytes"], None, args["scratch"],
                        args["scratch_bytes"], None, None)
 
 
@@ -108,12 +115,13 @@ def test_fwd_rejects_before_launch(lib):
         assert fwd(lib, s, **{k: None}, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID, k
     assert fwd(lib, s, x=FAKE + 8, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID  # misaligned
     assert fwd(lib, s, s0=FAKE + 4, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID
+    assert fwd(lib, s, bias=FAKE + 4, ws_bytes=need_ws, scratch_bytes=need_scr) == INVALID
     assert fwd(lib, s, ws_bytes=need_ws - 1, scratch_bytes=need_scr) == WORKSPACE
     assert fwd(lib, s, ws=None, ws_bytes=need_ws, scratch_bytes=need_scr) == WORKSPACE
     assert fwd(lib, s, ws_bytes=need_ws, scratch_bytes=need_scr - 1) == WORKSPACE
     assert fwd(lib, s, ws_bytes=need_ws, scratch=None, scratch_bytes=need_scr) == WORKSPACE
-    assert lib.ssd_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 0, None, FAKE, 0, None,
-                       None) == INVALID
+    assert lib.ssd_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, None, FAKE, 0,
+                       None, None) == INVALID
 
 
 def test_bwd_rejects_before_launch(lib):
@@ -121,15 +129,16 @@ def test_bwd_rejects_before_launch(lib):
     sv = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lib.ssd_saved_bytes(ctypes.byref(s)))
     need = lib.ssd_bwd_scratch_bytes(ctypes.byref(s))
 
-    def bwd(saved, dy=FAKE, scratch=FAKE, nbytes=need, dx=FAKE, dfs=None, ds0=None):
+    def bwd(saved, dy=FAKE, scratch=FAKE, nbytes=need, dx=FAKE, dfs=None, ds0=None, dbias=None):
         return lib.ssd_bwd(ctypes.byref(saved) if saved is not None else None, dy, dfs, dx, FAKE, FAKE, FAKE, FAKE,
-                           FAKE, ds0, scratch, nbytes, None, None)
+                           FAKE, dbias, ds0, scratch, nbytes, None, None)
 
     assert bwd(None) == INVALID
     assert bwd(sv, dy=None) == INVALID
     assert bwd(sv, dx=None) == INVALID
     assert bwd(sv, dfs=FAKE + 4) == INVALID  # misaligned optional state pointers
     assert bwd(sv, ds0=FAKE + 8) == INVALID
+    assert bwd(sv, dbias=FAKE + 8) == INVALID
     assert bwd(sv, nbytes=need - 1) == WORKSPACE
     assert bwd(sv, scratch=None) == WORKSPACE
     small = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16)
