@@ -1,7 +1,7 @@
 """Benchmark: Mamba-2 SSD chunked scan, forward + backward, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
-                    [--seqlen L] [--batch B] [--with-states]
+                    [--seqlen L] [--batch B] [--with-states] [--dt-softplus]
 
 A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
 synthetic inputs (already resident in HBM).  --seqlen / --batch change the
@@ -9,7 +9,8 @@ workload's sequence length / batch (a length that is not a multiple of the
 chunk adds a shorter last chunk); --with-states starts the forward from a
 seeded initial state and gives the backward a seeded final-state cotangent,
 returning the initial-state gradient as well (one GPU's share of a sequence
-split across GPUs).  Prints ONE JSON line on stdout;
+split across GPUs); --dt-softplus passes the raw step and the per-head bias
+and lets the library apply softplus(dt_raw + dt_bias) (and return ddt_bias).  Prints ONE JSON line on stdout;
 diagnostics (per-kernel times) go to stderr.
 
 The roofline object describes the kernel with the largest share of the step:
@@ -126,8 +127,10 @@ def make_probe(kernel_id, start, stop):
 
 def run_step(ssd, dev, chunk, fscr, bscr, fprobe=None, bprobe=None):
     s0, dfs = dev.get("initial_state"), dev.get("dfinal_state")
-    y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk,
-                         initial_state=s0, scratch=fscr, probe=fprobe)
+    sp = dev.get("softplus", False)
+    y, fs, ctx = ssd.fwd(dev["x"], dev["dt_raw"] if sp else dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk,
+                         initial_state=s0, dt_softplus=sp, dt_bias=dev["dt_bias"] if sp else None,
+                         scratch=fscr, probe=fprobe)
     g = ssd.bwd(dev["dy"], ctx, dfinal_state=dfs, want_dinitial_state=s0 is not None, scratch=bscr, probe=bprobe)
     return y, fs, g
 
@@ -313,6 +316,8 @@ def main():
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     ap.add_argument("--with-states", action="store_true",
                     help="seeded initial state and final-state cotangent; dinitial_state returned")
+    ap.add_argument("--dt-softplus", action="store_true",
+                    help="raw step + per-head bias; the library applies the softplus")
     ap.add_argument("--cpu-heads", type=int, default=80, help="heads in the oracle CPU-baseline slice")
     ap.add_argument("--cpu-batch", type=int, default=4, help="batch rows in the oracle CPU-baseline slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -371,6 +376,8 @@ def main():
     t0 = time.perf_counter()
     inp = inputs.generate(shape, seed=0)
     dev = ssd.to_device(inp, "cuda")
+    if args.dt_softplus:
+        dev["softplus"] = True
     if args.with_states:
         s0, dfs = inputs.generate_states(shape, seed=0)
         dev["initial_state"] = torch.from_numpy(s0).cuda()
@@ -378,7 +385,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
 
-    shp = ssd.shape_of(dev["x"], dev["B"], shape.chunk, 1 if shape.dtype == "bf16" else 0)
+    shp = ssd.shape_of(dev["x"], dev["B"], shape.chunk, 1 if shape.dtype == "bf16" else 0,
+                       _lib.SSD_DT_SOFTPLUS if args.dt_softplus else 0)
     lib = _lib.load()
     fscr = torch.empty(lib.ssd_fwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
     bscr = torch.empty(lib.ssd_bwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
@@ -424,7 +432,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": nbytes / t_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": hbm_frac}
-    roof["traffic"] = load_traffic(dom, args.workload) if not over and not args.with_states else None
+    plain = not over and not args.with_states and not args.dt_softplus
+    roof["traffic"] = load_traffic(dom, args.workload) if plain else None
     roof["kernel"] = dom
     roof["kernel_ms"] = dom_ms
     roof["algorithmic_bytes"] = nbytes
@@ -463,7 +472,7 @@ def main():
         "config": {"workload": args.workload, "batch": shape.batch, "seqlen": shape.seqlen,
                    "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
                    "ngroups": shape.ngroups, "chunk": shape.chunk, "parallelism": "single-gpu",
-                   "initial_state": bool(args.with_states)},
+                   "initial_state": bool(args.with_states), "dt_softplus": bool(args.dt_softplus)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_ms": breakdown or None,
