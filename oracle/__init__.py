@@ -14,4 +14,6 @@ Contents:
   fd       -- central finite differences of the scalar <dy, y>
   dtproc   -- the step preprocessing dt = softplus(dt_raw + dt_bias) and
               its chain rule
+  conv     -- the causal depthwise conv1d (+ bias, SiLU) before the scan, and
+              its backward
 """
