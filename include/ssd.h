@@ -169,6 +169,42 @@ ssd_status ssd_bwd(const ssd_saved *saved, const void *dy, const float *dfinal_s
                    void *scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe *probe);
 
+/* ---- Causal depthwise conv1d ------------------------------------------
+ *
+ * The convolution that feeds the scan in a Mamba block (the "causal conv"
+ * kernel the LightOn page "Training Mamba on AMD GPUs", section "Individual
+ * Kernels", times): per channel c, a width-W filter w[c][0..W-1], a bias and
+ * an optional SiLU,
+ *     z[b][t][c] = bias[c] + sum_k w[c][k] x[b][t - (W-1) + k][c],
+ *     y = silu(z) = z / (1 + e^-z)   (or y = z)
+ * Rows before the sequence are x_prev's [b][W-1][C] (times -(W-1)..-1) or
+ * zero: with x_prev a sequence cut into pieces runs as separate calls.
+ * ssd_conv1d_bwd returns the gradients of <dy, y>: dx, dw, dbias and the
+ * halo's gradient dx_prev (the last W-1 rows of the previous piece add it).
+ *
+ * Layouts: x, y, dy, dx [batch][seqlen][channels] and x_prev, dx_prev
+ * [batch][width-1][channels] in `dtype`; w, dw [channels][width] and bias,
+ * dbias [channels] float32.  Device pointers, 16-byte aligned; bias, x_prev,
+ * dbias and dx_prev may be NULL (absent).  Supported: width 2..4, channels a
+ * multiple of 4 (else SSD_ERR_UNSUPPORTED).  Same ownership, stream and error
+ * rules as ssd_fwd / ssd_bwd; dw and dbias are overwritten, fixed-order sums
+ * (no atomics). */
+typedef struct {
+    int64_t batch, seqlen, channels;
+    int32_t width;
+    int32_t dtype;     /* ssd_dtype of x, x_prev, y, dy, dx, dx_prev */
+    int32_t silu;      /* 1: y = silu(z); 0: y = z */
+    int32_t reserved;  /* must be 0 */
+} ssd_conv_shape;
+
+ssd_status ssd_conv1d_check_shape(const ssd_conv_shape *shape);
+size_t ssd_conv1d_bwd_scratch_bytes(const ssd_conv_shape *shape);
+ssd_status ssd_conv1d_fwd(const ssd_conv_shape *shape, const void *x, const float *w, const float *bias,
+                          const void *x_prev, void *y, hipStream_t stream);
+ssd_status ssd_conv1d_bwd(const ssd_conv_shape *shape, const void *x, const float *w, const float *bias,
+                          const void *x_prev, const void *dy, void *dx, float *dw, float *dbias, void *dx_prev,
+                          void *scratch, size_t scratch_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *ssd_status_string(ssd_status status);
 

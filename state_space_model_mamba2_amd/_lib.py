@@ -28,6 +28,12 @@ class Saved(ctypes.Structure):
                 ("saved_ws", ctypes.c_void_p), ("saved_ws_bytes", ctypes.c_size_t)]
 
 
+class ConvShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
+                ("width", ctypes.c_int32), ("dtype", ctypes.c_int32), ("silu", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 class Probe(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("start", ctypes.c_void_p), ("stop", ctypes.c_void_p)]
@@ -58,6 +64,13 @@ def load():
     lib.ssd_fwd.restype = st
     lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
     lib.ssd_bwd.restype = st
+    PConv = ctypes.POINTER(ConvShape)
+    lib.ssd_conv1d_check_shape.argtypes, lib.ssd_conv1d_check_shape.restype = [PConv], st
+    lib.ssd_conv1d_bwd_scratch_bytes.argtypes, lib.ssd_conv1d_bwd_scratch_bytes.restype = [PConv], sz
+    lib.ssd_conv1d_fwd.argtypes = [PConv, vp, vp, vp, vp, vp, vp]
+    lib.ssd_conv1d_fwd.restype = st
+    lib.ssd_conv1d_bwd.argtypes = [PConv, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_conv1d_bwd.restype = st
     lib.ssd_status_string.argtypes, lib.ssd_status_string.restype = [st], ctypes.c_char_p
     lib.ssd_kernel_name.argtypes, lib.ssd_kernel_name.restype = [ctypes.c_int32], ctypes.c_char_p
     lib.ssd_version.argtypes, lib.ssd_version.restype = [], ctypes.c_char_p

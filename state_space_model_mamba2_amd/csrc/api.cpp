@@ -357,4 +357,68 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   return SSD_OK;
 }
 
+// ---- causal depthwise conv1d
+
+namespace {
+ssd_status conv_check(const ssd_conv_shape* s) {
+  if (!s) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->batch <= 0 || s->seqlen <= 0 || s->channels <= 0 || s->reserved != 0) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->silu != 0 && s->silu != 1) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->batch * s->seqlen > INT32_MAX || s->channels > INT32_MAX / 8 || s->batch > 65535)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (s->width < 2 || s->width > 4 || s->channels % 4 != 0) return SSD_ERR_UNSUPPORTED;
+  // one workgroup row per block of run blocks (grid y)
+  if (conv_partial_rows(s->batch, s->seqlen, s->dtype == SSD_BF16 ? 2 : 4) > 65535) return SSD_ERR_INVALID_ARGUMENT;
+  return SSD_OK;
+}
+
+ConvArgs conv_args(const ssd_conv_shape* s) {
+  ConvArgs a{};
+  a.b = s->batch; a.L = s->seqlen; a.C = s->channels;
+  a.W = s->width; a.esz = s->dtype == SSD_BF16 ? 2 : 4; a.silu = s->silu;
+  return a;
+}
+}  // namespace
+
+ssd_status ssd_conv1d_check_shape(const ssd_conv_shape* s) { return conv_check(s); }
+
+size_t ssd_conv1d_bwd_scratch_bytes(const ssd_conv_shape* s) {
+  if (conv_check(s) != SSD_OK) return 0;
+  const int esz = s->dtype == SSD_BF16 ? 2 : 4;
+  return align_up((size_t)conv_partial_rows(s->batch, s->seqlen, esz) * s->channels * (s->width + 1) * 4);
+}
+
+ssd_status ssd_conv1d_fwd(const ssd_conv_shape* s, const void* x, const float* w, const float* bias,
+                          const void* x_prev, void* y, hipStream_t stream) {
+  const ssd_status st = conv_check(s);
+  if (st != SSD_OK) return st;
+  if (!x || !w || !y) return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, w, bias, x_prev, y};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
+  ConvArgs a = conv_args(s);
+  a.x = x; a.w = w; a.bias = bias; a.x_prev = x_prev; a.y = y;
+  run_conv_fwd(a, stream);
+  return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_conv1d_bwd(const ssd_conv_shape* s, const void* x, const float* w, const float* bias,
+                          const void* x_prev, const void* dy, void* dx, float* dw, float* dbias, void* dx_prev,
+                          void* scratch, size_t scratch_bytes, hipStream_t stream) {
+  const ssd_status st = conv_check(s);
+  if (st != SSD_OK) return st;
+  if (!x || !w || !dy || !dx || !dw) return SSD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, w, bias, x_prev, dy, dx, dw, dbias, dx_prev, scratch};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!scratch || scratch_bytes < ssd_conv1d_bwd_scratch_bytes(s)) return SSD_ERR_WORKSPACE;
+  ConvArgs a = conv_args(s);
+  a.x = x; a.w = w; a.bias = bias; a.x_prev = x_prev; a.dy = dy;
+  a.dx = dx; a.dw = dw; a.dbias = dbias; a.dx_prev = dx_prev;
+  a.part = static_cast<float*>(scratch);
+  run_conv_bwd(a, stream);
+  return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // extern "C"

@@ -114,6 +114,24 @@ struct RowCopy {
 void pad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st);
 void unpad_rows(const RowCopy& c, int64_t L, int64_t row0, int64_t nvalid, int64_t Q, int64_t b, hipStream_t st);
 
+// Causal depthwise conv1d (conv.hip).
+struct ConvArgs {
+  int64_t b, L, C;
+  int W, esz, silu;
+  const void* x;        // [b][L][C]
+  const float* w;       // [C][W]
+  const float* bias;    // [C] or null
+  const void* x_prev;   // [b][W-1][C] or null (zeros)
+  void* y;              // forward output
+  const void* dy;       // backward input
+  void *dx, *dx_prev;   // backward outputs (dx_prev may be null)
+  float *dw, *dbias;    // backward outputs (dbias may be null)
+  float* part;          // [conv_partial_rows][C][W + 1] scratch
+};
+int64_t conv_partial_rows(int64_t b, int64_t L, int esz);
+void run_conv_fwd(const ConvArgs& a, hipStream_t st);
+void run_conv_bwd(const ConvArgs& a, hipStream_t st);
+
 template <typename T, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);
 template <typename T, int Q, int P, int N>

@@ -168,3 +168,46 @@ def generate_states(shape: Shape, seed: int = 0):
     s0 = rng.standard_normal(dims, dtype=np.float32)
     dfs = rng.standard_normal(dims, dtype=np.float32)
     return s0, dfs
+
+
+# ---------------------------------------------------------------------------
+# Causal depthwise conv1d before the scan.  Its channels are the Mamba-2
+# block's conv width nheads*headdim + 2*ngroups*dstate (x, B and C together)
+# of each workload; width 4.
+CONV_WORKLOADS = {
+    name: dict(batch=w["batch"], seqlen=w["seqlen"],
+               channels=w["nheads"] * w["headdim"] + 2 * w["ngroups"] * w["dstate"], width=4, dtype=w["dtype"])
+    for name, w in WORKLOADS.items()
+}
+
+
+@dataclasses.dataclass
+class ConvInputs:
+    """x, x_prev, dy in the storage form (uint16 bf16 bits or float32); w, bias float32."""
+    x: np.ndarray
+    w: np.ndarray
+    bias: np.ndarray
+    x_prev: np.ndarray
+    dy: np.ndarray
+    dtype: str
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return (bf16_bits_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+def generate_conv(batch: int, seqlen: int, channels: int, width: int, dtype: str, seed: int = 0) -> ConvInputs:
+    """Draw order x ~ N(0,1), w ~ U(-1/sqrt(W), 1/sqrt(W)) (the usual conv
+    initialisation for fan-in W), bias likewise, x_prev ~ N(0,1), dy ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, channels), dtype=np.float32)
+    lim = 1.0 / math.sqrt(width)
+    w = rng.uniform(-lim, lim, (channels, width)).astype(np.float32)
+    bias = rng.uniform(-lim, lim, channels).astype(np.float32)
+    x_prev = rng.standard_normal((batch, width - 1, channels), dtype=np.float32)
+    dy = rng.standard_normal((batch, seqlen, channels), dtype=np.float32)
+    if dtype == "bf16":
+        x, x_prev, dy = (f32_to_bf16_bits(t) for t in (x, x_prev, dy))
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return ConvInputs(x, w, bias, x_prev, dy, dtype)

@@ -181,6 +181,68 @@ def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dini
     return g
 
 
+def _conv_shape(x, w, silu):
+    b, L, C = x.shape
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    if w.dtype != torch.float32 or w.dim() != 2 or w.shape[0] != C:
+        raise ValueError("w must be float32 [channels, width]")
+    return _lib.ConvShape(b, L, C, w.shape[1], _DTYPES[x.dtype], 1 if silu else 0, 0)
+
+
+def _check_conv_tensors(shape, x, w, bias, x_prev):
+    for name, t in (("x", x), ("w", w), ("bias", bias), ("x_prev", x_prev)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if bias is not None and (bias.dtype != torch.float32 or tuple(bias.shape) != (shape.channels,)):
+        raise ValueError("bias must be float32 [channels]")
+    if x_prev is not None and (x_prev.dtype != x.dtype
+                               or tuple(x_prev.shape) != (shape.batch, shape.width - 1, shape.channels)):
+        raise ValueError("x_prev must have x's dtype and shape [batch, width - 1, channels]")
+
+
+def conv1d_fwd(x, w, bias=None, x_prev=None, silu=True, *, stream=None):
+    """Causal depthwise conv1d: y[b,t,c] = act(bias[c] + sum_k w[c,k] x[b,t-(W-1)+k,c]).
+    x [b, L, C] (bf16 or fp32), w [C, W] fp32, bias [C] fp32, x_prev [b, W-1, C] (rows before t = 0)."""
+    lib = _lib.load()
+    shape = _conv_shape(x, w, silu)
+    _check_conv_tensors(shape, x, w, bias, x_prev)
+    _check(lib.ssd_conv1d_check_shape(ctypes.byref(shape)), "ssd_conv1d_fwd")
+    y = torch.empty_like(x)
+    code = lib.ssd_conv1d_fwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(bias) if bias is not None else None,
+                              _ptr(x_prev) if x_prev is not None else None, _ptr(y), _stream_handle(stream))
+    _check(code, "ssd_conv1d_fwd")
+    return y
+
+
+def conv1d_bwd(x, w, dy, bias=None, x_prev=None, silu=True, *, want_dx_prev=False, stream=None):
+    """Gradients of <dy, conv1d_fwd(...)>: dict dx, dw, dbias (if bias given), dx_prev (on request)."""
+    lib = _lib.load()
+    shape = _conv_shape(x, w, silu)
+    _check_conv_tensors(shape, x, w, bias, x_prev)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous() or not dy.is_cuda:
+        raise ValueError("dy must be a contiguous GPU tensor with x's shape and dtype")
+    _check(lib.ssd_conv1d_check_shape(ctypes.byref(shape)), "ssd_conv1d_bwd")
+    nbytes = lib.ssd_conv1d_bwd_scratch_bytes(ctypes.byref(shape))
+    scratch = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    dx = torch.empty_like(x)
+    dw = torch.empty_like(w)
+    dbias = torch.empty_like(bias) if bias is not None else None
+    dprev = torch.empty((shape.batch, shape.width - 1, shape.channels), dtype=x.dtype,
+                        device=x.device) if want_dx_prev else None
+    code = lib.ssd_conv1d_bwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(bias) if bias is not None else None,
+                              _ptr(x_prev) if x_prev is not None else None, _ptr(dy), _ptr(dx), _ptr(dw),
+                              _ptr(dbias) if dbias is not None else None, _ptr(dprev) if dprev is not None else None,
+                              _ptr(scratch), nbytes, _stream_handle(stream))
+    _check(code, "ssd_conv1d_bwd")
+    g = dict(dx=dx, dw=dw)
+    if dbias is not None:
+        g["dbias"] = dbias
+    if dprev is not None:
+        g["dx_prev"] = dprev
+    return g
+
+
 def to_device(inp, device="cuda"):
     """Upload a seeded numpy draw (inputs.Inputs) as torch tensors of its storage dtype."""
     import numpy as np

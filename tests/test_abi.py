@@ -155,3 +155,30 @@ def test_strings(lib):
         assert lib.ssd_kernel_name(i).decode() == n
     assert lib.ssd_kernel_name(len(_lib.KERNELS)) is None
     assert lib.ssd_kernel_name(-1) is None
+
+
+def conv_shape(**kw):
+    d = dict(batch=2, seqlen=100, channels=64, width=4, dtype=_lib.SSD_BF16, silu=1, reserved=0)
+    d.update(kw)
+    return _lib.ConvShape(**d)
+
+
+def test_conv_shape_checks_and_rejections(lib):
+    chk = lambda s: lib.ssd_conv1d_check_shape(ctypes.byref(s))
+    assert chk(conv_shape()) == OK
+    assert chk(conv_shape(dtype=_lib.SSD_F32, width=2, silu=0)) == OK
+    assert chk(conv_shape(width=5)) == UNSUPPORTED and chk(conv_shape(width=1)) == UNSUPPORTED
+    assert chk(conv_shape(channels=66)) == UNSUPPORTED
+    for k in ["batch", "seqlen", "channels"]:
+        assert chk(conv_shape(**{k: 0})) == INVALID, k
+    assert chk(conv_shape(silu=2)) == INVALID and chk(conv_shape(reserved=1)) == INVALID
+    assert chk(conv_shape(dtype=9)) == INVALID
+    s = conv_shape()
+    need = lib.ssd_conv1d_bwd_scratch_bytes(ctypes.byref(s))
+    assert need >= 2 * 64 * 5 * 4
+    assert lib.ssd_conv1d_fwd(ctypes.byref(s), None, FAKE, None, None, FAKE, None) == INVALID
+    assert lib.ssd_conv1d_fwd(ctypes.byref(s), FAKE + 4, FAKE, None, None, FAKE, None) == INVALID
+    bwd = lambda scratch, nbytes, dx=FAKE: lib.ssd_conv1d_bwd(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, dx, FAKE,
+                                                               None, None, scratch, nbytes, None)
+    assert bwd(FAKE, need, dx=None) == INVALID
+    assert bwd(FAKE, need - 1) == WORKSPACE and bwd(None, need) == WORKSPACE
