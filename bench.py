@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
                     [--seqlen L] [--batch B] [--with-states] [--dt-softplus]
+    python bench.py --op conv1d [--workload mamba2_2p7b] [--batch B] [--seqlen L]
 
 A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
 synthetic inputs (already resident in HBM).  --seqlen / --batch change the
@@ -17,6 +18,10 @@ The roofline object describes the kernel with the largest share of the step:
 its algorithmic bytes and flops per launch (formulas in kernel_model below)
 over its average launch duration, measured with HIP events that libssd records
 around that kernel on the launch stream during the timed steps.
+
+--op conv1d times the causal depthwise conv1d before the scan instead (one
+ssd_conv1d_fwd + ssd_conv1d_bwd per step, with bias, SiLU and a halo) on the
+workload's conv shape (channels = nheads*headdim + 2*ngroups*dstate).
 
 cpu_baseline: the float64 oracle on a bounded slice of the same workload
 (one batch row, a subset of heads), timed on this host's cores and scaled
@@ -306,8 +311,77 @@ def load_traffic(kernel: str, workload: str):
     return d.get("traffic_bytes")
 
 
+def conv_bench(args):
+    """Causal depthwise conv1d: fwd + bwd per step.  Each direction is also
+    timed alone over `steps` back-to-back calls with events on the launch
+    stream (one call is short next to the Python launch overhead, so events
+    around single calls would count the host's gaps); roofline against HBM."""
+    import numpy as np
+    import torch
+    from state_space_model_mamba2_amd import _lib, inputs, ssd
+
+    _lib.load()
+    cw = dict(inputs.CONV_WORKLOADS[args.workload])
+    cw.update({k: v for k, v in (("seqlen", args.seqlen), ("batch", args.batch)) if v is not None})
+    b, L, C, W, dtype = cw["batch"], cw["seqlen"], cw["channels"], cw["width"], cw["dtype"]
+    esz = 2 if dtype == "bf16" else 4
+    log(f"[bench] conv1d {args.workload}: {cw}")
+    ci = inputs.generate_conv(b, L, C, W, dtype, seed=0)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    x, w, bias, prev, dy = dev(ci.x), dev(ci.w), dev(ci.bias), dev(ci.x_prev), dev(ci.dy)
+
+    fwd = lambda: ssd.conv1d_fwd(x, w, bias, prev)
+    bwd = lambda: ssd.conv1d_bwd(x, w, dy, bias, prev, want_dx_prev=True)
+
+    def timed(fn, n):
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    fwd_ms = timed(fwd, args.steps)
+    bwd_ms = timed(bwd, args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    X = b * L * C * esz
+    fwd_bytes = 2 * X + C * (W + 1) * 4                     # x in, y out, w, bias
+    bwd_bytes = 3 * X + 2 * C * (W + 1) * 4                 # x, dy in, dx out, w, bias in, dw, dbias out
+    dom, dom_ms, nbytes = ("conv1d_bwd", bwd_ms, bwd_bytes) if bwd_ms >= fwd_ms else ("conv1d_fwd", fwd_ms, fwd_bytes)
+    achieved = nbytes / (dom_ms / 1e3) / 1e9
+    log(f"[bench] conv1d fwd {fwd_ms:.4f} ms ({fwd_bytes / fwd_ms / 1e6:.0f} GB/s), "
+        f"bwd {bwd_ms:.4f} ms ({bwd_bytes / bwd_ms / 1e6:.0f} GB/s), step {ms:.4f} ms")
+    out = {"metric": "causal conv1d fwd+bwd tokens/s per GPU", "value": b * L / (ms / 1e3), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+           "config": {"workload": f"conv1d_{args.workload}", "batch": b, "seqlen": L, "channels": C, "width": W,
+                      "silu": True, "parallelism": "single-gpu"},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom, "kernel_ms": dom_ms,
+                        "algorithmic_bytes": nbytes},
+           "kernel_ms": {"conv1d_fwd": fwd_ms, "conv1d_bwd": bwd_ms}, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
+    ap.add_argument("--op", choices=["ssd", "conv1d"], default="ssd")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
@@ -349,6 +423,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the SSD scan here is a "
               f"single-GPU build and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "conv1d":
+        conv_bench(args)
+        return
 
     import torch
     from state_space_model_mamba2_amd import _lib, inputs, ssd
