@@ -61,8 +61,8 @@ def kernel_model(s, esz):
     tiles = nt * (nt + 1) // 2
     X = T * H * P * esz              # one x-sized tensor
     BC = T * G * N * esz             # one of B / C
-    DT = T * H * esz
-    CS = b * H * K * Q * 4
+    DT = T * H * esz                 # dt / ddt in the caller's layout
+    CS = b * H * K * Q * 4           # cs, or the float32 step the cumsum writes in cs's layout
     ST4 = b * K * H * P * N * 4      # chunk states, fp32
     STe = b * K * H * P * N * esz    # chunk states, storage dtype
     WT = b * K * G * tiles * 256 * esz
@@ -71,17 +71,17 @@ def kernel_model(s, esz):
     tri = Q * (Q + 1) // 2
     bkh, bkg = b * K * H, b * K * G
     m = {
-        "chunk_cumsum": (DT + CS, 0),
+        "chunk_cumsum": (DT + 2 * CS, 0),                 # dt in; cs and the float32 step out
         "bmm_fwd": (2 * BC + 2 * WT, 4 * bkg * tri * N),  # both lane orders
-        "chunk_state": (X + BC + DT + CS + ST4, 2 * bkh * Q * P * N),
+        "chunk_state": (X + BC + 2 * CS + ST4, 2 * bkh * Q * P * N),
         "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
-        "chunk_scan": (2 * X + DT + CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
+        "chunk_scan": (2 * X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
         "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
         "state_passing_bwd": (ST4 + STe, 0),
-        "chunk_scan_bwd": (3 * X + 2 * DT + CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
-        "dw": (2 * X + DT + CS + DW, 2 * bkh * tri * P),
+        "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
+        "dw": (2 * X + 2 * CS + DW, 2 * bkh * tri * P),
         "dc": (X + CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
-        "db": (X + DT + CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
+        "db": (X + 2 * CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
         "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
     }
     return m
