@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
                     [--seqlen L] [--batch B] [--with-states] [--dt-softplus]
+                    [--dtype fp8 --fwd-only]
     python bench.py --op conv1d [--workload mamba2_2p7b] [--batch B] [--seqlen L]
 
 A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
@@ -11,7 +12,9 @@ chunk adds a shorter last chunk); --with-states starts the forward from a
 seeded initial state and gives the backward a seeded final-state cotangent,
 returning the initial-state gradient as well (one GPU's share of a sequence
 split across GPUs); --dt-softplus passes the raw step and the per-head bias
-and lets the library apply softplus(dt_raw + dt_bias) (and return ddt_bias).  Prints ONE JSON line on stdout;
+and lets the library apply softplus(dt_raw + dt_bias) (and return ddt_bias);
+--dtype changes the storage mode (fp8: x, B, C as E4M3 codes, forward only, so
+it needs --fwd-only); --fwd-only times the forward pass alone.  Prints ONE JSON line on stdout;
 diagnostics (per-kernel times) go to stderr.
 
 The roofline object describes the kernel with the largest share of the step:
@@ -42,7 +45,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "SSD fwd+bwd tokens/s per GPU + % of bf16 MFMA peak / % HBM peak"
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks
+# dense matrix-core peaks; in fp8 mode only C.B^T runs on the FP8 matrix
+# cores, every other product (and the dominant kernels) on the bf16 ones
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 2500.0}
 
 
 def log(*a):
@@ -57,10 +62,12 @@ def kernel_model(s, esz):
     b, L, H, P, N, G, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk
     K = L // Q
     T = b * K * Q
+    eszx = 1 if s.dtype == "fp8" else esz   # x, B, C storage
     nt = Q // 16
     tiles = nt * (nt + 1) // 2
-    X = T * H * P * esz              # one x-sized tensor
-    BC = T * G * N * esz             # one of B / C
+    X = T * H * P * esz              # one x-sized tensor in the step dtype (y, dy, dx)
+    XI = T * H * P * eszx            # x as stored
+    BC = T * G * N * eszx            # one of B / C
     DT = T * H * esz                 # dt / ddt in the caller's layout
     CS = b * H * K * Q * 4           # cs, or the float32 step the cumsum writes in cs's layout
     ST4 = b * K * H * P * N * 4      # chunk states, fp32
@@ -73,9 +80,9 @@ def kernel_model(s, esz):
     m = {
         "chunk_cumsum": (DT + 2 * CS, 0),                 # dt in; cs and the float32 step out
         "bmm_fwd": (2 * BC + 2 * WT, 4 * bkg * tri * N),  # both lane orders
-        "chunk_state": (X + BC + 2 * CS + ST4, 2 * bkh * Q * P * N),
+        "chunk_state": (XI + BC + 2 * CS + ST4, 2 * bkh * Q * P * N),
         "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
-        "chunk_scan": (2 * X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
+        "chunk_scan": (XI + X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
         "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
         "state_passing_bwd": (ST4 + STe, 0),
         "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
@@ -136,6 +143,8 @@ def run_step(ssd, dev, chunk, fscr, bscr, fprobe=None, bprobe=None):
     y, fs, ctx = ssd.fwd(dev["x"], dev["dt_raw"] if sp else dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk,
                          initial_state=s0, dt_softplus=sp, dt_bias=dev["dt_bias"] if sp else None,
                          scratch=fscr, probe=fprobe)
+    if dev.get("fwd_only", False):
+        return y, fs, None
     g = ssd.bwd(dev["dy"], ctx, dfinal_state=dfs, want_dinitial_state=s0 is not None, scratch=bscr, probe=bprobe)
     return y, fs, g
 
@@ -147,6 +156,8 @@ def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
     out = {}
     fwd_ids = range(0, 5)
     for kid, name in enumerate(_lib.KERNELS):
+        if dev.get("fwd_only", False) and kid not in fwd_ids:
+            continue
         evs = [(hip.event(), hip.event()) for _ in range(reps)]
         for a, b in evs:
             p = make_probe(kid, a, b)
@@ -392,6 +403,8 @@ def main():
                     help="seeded initial state and final-state cotangent; dinitial_state returned")
     ap.add_argument("--dt-softplus", action="store_true",
                     help="raw step + per-head bias; the library applies the softplus")
+    ap.add_argument("--dtype", choices=["f32", "bf16", "fp8"], default=None, help="override the storage mode")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward pass alone")
     ap.add_argument("--cpu-heads", type=int, default=80, help="heads in the oracle CPU-baseline slice")
     ap.add_argument("--cpu-batch", type=int, default=4, help="batch rows in the oracle CPU-baseline slice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -447,15 +460,21 @@ def main():
         return
 
     _lib.load()  # fail loudly if the HIP library is missing
-    over = {k: v for k, v in (("seqlen", args.seqlen), ("batch", args.batch)) if v is not None}
+    over = {k: v for k, v in (("seqlen", args.seqlen), ("batch", args.batch), ("dtype", args.dtype))
+            if v is not None}
     shape = inputs.workload(args.workload, **over)
-    esz = 2 if shape.dtype == "bf16" else 4
+    if shape.dtype == "fp8" and not args.fwd_only:
+        print("fp8 storage is forward only: add --fwd-only", file=sys.stderr)
+        sys.exit(2)
+    esz = 4 if shape.dtype == "f32" else 2
     log(f"[bench] workload {args.workload}: {shape}")
     t0 = time.perf_counter()
     inp = inputs.generate(shape, seed=0)
     dev = ssd.to_device(inp, "cuda")
     if args.dt_softplus:
         dev["softplus"] = True
+    if args.fwd_only:
+        dev["fwd_only"] = True
     if args.with_states:
         s0, dfs = inputs.generate_states(shape, seed=0)
         dev["initial_state"] = torch.from_numpy(s0).cuda()
@@ -463,8 +482,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
 
-    shp = ssd.shape_of(dev["x"], dev["B"], shape.chunk, 1 if shape.dtype == "bf16" else 0,
-                       _lib.SSD_DT_SOFTPLUS if args.dt_softplus else 0)
+    code = {"f32": _lib.SSD_F32, "bf16": _lib.SSD_BF16, "fp8": _lib.SSD_FP8}[shape.dtype]
+    shp = ssd.shape_of(dev["x"], dev["B"], shape.chunk, code, _lib.SSD_DT_SOFTPLUS if args.dt_softplus else 0)
     lib = _lib.load()
     fscr = torch.empty(lib.ssd_fwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
     bscr = torch.empty(lib.ssd_bwd_scratch_bytes(ctypes.byref(shp)), dtype=torch.uint8, device="cuda")
@@ -529,13 +548,13 @@ def main():
         log(f"  sum of kernels {tot:.4f} ms vs step {ms_per_step:.4f} ms")
 
     cpu = None
-    if not args.no_cpu_baseline and args.profile_kernel is None:
+    if not args.no_cpu_baseline and args.profile_kernel is None and not args.fwd_only:
         log("[bench] timing the float64 oracle on a bounded sample ...")
         cpu = cpu_baseline(shape, inp, args.cpu_batch, args.cpu_heads)
         log(f"[bench] {cpu['sample']}")
 
     out = {
-        "metric": METRIC,
+        "metric": "SSD fwd tokens/s per GPU" if args.fwd_only else METRIC,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -33,7 +33,12 @@
  *                      [batch][nheads][headdim][dstate]    float32
  *                      (element [p][n] is the state's entry [n][p])
  * "dtype" is float32 (SSD_F32) or bfloat16 (SSD_BF16); accumulation is
- * always float32.  Every pointer is a device pointer aligned to 16 bytes.
+ * always float32.  SSD_FP8 (forward only; ssd_bwd returns
+ * SSD_ERR_UNSUPPORTED): x, B and C are OCP FP8 E4M3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; one byte each, no scale),
+ * every other dtype tensor bfloat16; C.B^T runs on the FP8 matrix cores and
+ * the other products widen the codes to bfloat16 (exactly).  Every pointer is
+ * a device pointer aligned to 16 bytes.
  *
  * Ownership: the caller allocates every buffer (inputs, outputs, the saved
  * workspace and the scratch workspaces); the library never allocates or frees
@@ -64,7 +69,7 @@ typedef enum {
     SSD_ERR_HIP = 4               /* a HIP call or kernel launch failed */
 } ssd_status;
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_FP8 = 2 } ssd_dtype;
 
 /* ssd_shape.flags.  SSD_DT_SOFTPLUS: the dt argument is the raw step and the
  * scan uses dt_t = softplus(dt_raw_t + dt_bias_h), softplus(z) = log(1 + e^z)
@@ -78,7 +83,7 @@ enum { SSD_DT_SOFTPLUS = 1 };
  * seqlen is not a multiple of it, the last chunk of every sequence holds the
  * remaining seqlen mod Q tokens.  dtype is an ssd_dtype.  Compiled (chunk, headdim,
  * dstate) combinations (others give SSD_ERR_UNSUPPORTED):
- *   SSD_BF16: chunk 128 or 256 with (headdim, dstate) (16, 16), (64, 64), (64, 128)
+ *   SSD_BF16, SSD_FP8: chunk 128 or 256 with (headdim, dstate) (16, 16), (64, 64), (64, 128)
  *   SSD_F32 : chunk 64, 128 or 256 with (16, 16); chunk 64 or 128 with (64, 64);
  *             chunk 64 with (64, 128)                                          */
 typedef struct {

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
 SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
-SSD_F32, SSD_BF16 = 0, 1
+SSD_F32, SSD_BF16, SSD_FP8 = 0, 1, 2
 SSD_DT_SOFTPLUS = 1
 
 KERNELS = ["chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",

@@ -15,7 +15,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool is_supported(int dtype, int64_t Q, int64_t P, int64_t N) {
 #define SSD_MATCH(Q_, P_, N_) if (Q == Q_ && P == P_ && N == N_) return true;
-  if (dtype == SSD_BF16) { SSD_BF16_CONFIGS(SSD_MATCH) }
+  if (dtype == SSD_BF16 || dtype == SSD_FP8) { SSD_BF16_CONFIGS(SSD_MATCH) }
   if (dtype == SSD_F32) { SSD_F32_CONFIGS(SSD_MATCH) }
 #undef SSD_MATCH
   return false;
@@ -26,7 +26,7 @@ ssd_status check_shape(const ssd_shape* s) {
   if (s->batch <= 0 || s->seqlen <= 0 || s->nheads <= 0 || s->headdim <= 0 || s->dstate <= 0 ||
       s->ngroups <= 0 || s->chunk <= 0 || (s->flags & ~SSD_DT_SOFTPLUS) != 0)
     return SSD_ERR_INVALID_ARGUMENT;
-  if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SSD_F32 && s->dtype != SSD_BF16 && s->dtype != SSD_FP8) return SSD_ERR_INVALID_ARGUMENT;
   if (s->nheads % s->ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
   // Grid dimensions and 32-bit index products used inside the kernels.
   const int64_t K = (s->seqlen + s->chunk - 1) / s->chunk;
@@ -43,7 +43,7 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   Layout y{};
   y.b = s->batch; y.L = L; y.H = s->nheads; y.P = s->headdim; y.N = s->dstate;
   y.G = s->ngroups; y.Q = s->chunk; y.K = K;
-  y.esz = s->dtype == SSD_BF16 ? 2 : 4;
+  y.esz = s->dtype == SSD_F32 ? 4 : 2;  // states, tiles, y, dt: bf16 unless fp32
   const int64_t nt = y.Q / 16;
   y.wtiles = nt * (nt + 1) / 2;
   const size_t states = (size_t)(y.b * y.K * y.H * y.P * y.N);
@@ -116,10 +116,12 @@ Plan make_plan(const ssd_shape* s) {
   p.Lr = L % Q;
   p.lay = make_layout(s, L, (L + Q - 1) / Q);
   const bool tail = p.Lr > 0;
-  const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
+  const size_t esz = s->dtype == SSD_F32 ? 4 : 2;                          // dt, y, dy, dx, ddt
+  const size_t eszx = s->dtype == SSD_F32 ? 4 : (s->dtype == SSD_FP8 ? 1 : 2);  // x, B, C
   const size_t b = s->batch, H = s->nheads, P = s->headdim, N = s->dstate, G = s->ngroups, q = Q;
-  const size_t xrows = tail ? align_up(b * q * H * P * esz) : 0, trows = tail ? align_up(b * q * H * esz) : 0;
-  const size_t brows = tail ? align_up(b * q * G * N * esz) : 0;
+  const size_t xrows = tail ? align_up(b * q * H * P * eszx) : 0, trows = tail ? align_up(b * q * H * esz) : 0;
+  const size_t yrows = tail ? align_up(b * q * H * P * esz) : 0;
+  const size_t brows = tail ? align_up(b * q * G * N * eszx) : 0;
   size_t o = p.lay.saved_bytes;
   p.sv_tx = o;   o += xrows;
   p.sv_tB = o;   o += brows;
@@ -129,11 +131,11 @@ Plan make_plan(const ssd_shape* s) {
   const bool sp = (s->flags & SSD_DT_SOFTPLUS) != 0;
   o = p.lay.fwd_bytes;
   p.fw_tdt = o; o += trows;
-  p.fw_ty = o;  o += xrows;
+  p.fw_ty = o;  o += yrows;
   p.fwd_bytes = o;
   o = p.lay.bwd_bytes;
-  p.bw_tdy = o;  o += xrows;
-  p.bw_tdx = o;  o += xrows;
+  p.bw_tdy = o;  o += yrows;
+  p.bw_tdx = o;  o += yrows;
   p.bw_tddt = o; o += trows;
   p.bw_tdB = o;  o += brows;
   p.bw_tdC = o;  o += brows;
@@ -175,17 +177,20 @@ void set_bwd_ws(BwdArgs& a, const Layout& lay, const void* saved, void* scratch)
 }
 
 bool dispatch_fwd(int dtype, const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe) {
-#define SSD_DISPATCH(TT, Q_, P_, N_)                        \
+#define SSD_DISPATCH(TT, TI, Q_, P_, N_)                    \
   if (lay.Q == Q_ && lay.P == P_ && lay.N == N_) {          \
-    run_fwd<TT, Q_, P_, N_>(lay, a, stream, probe);         \
+    run_fwd<TT, TI, Q_, P_, N_>(lay, a, stream, probe);     \
     return true;                                            \
   }
-#define SSD_DISPATCH_BF16(Q_, P_, N_) SSD_DISPATCH(bf16, Q_, P_, N_)
-#define SSD_DISPATCH_F32(Q_, P_, N_) SSD_DISPATCH(float, Q_, P_, N_)
+#define SSD_DISPATCH_BF16(Q_, P_, N_) SSD_DISPATCH(bf16, bf16, Q_, P_, N_)
+#define SSD_DISPATCH_FP8(Q_, P_, N_) SSD_DISPATCH(bf16, fp8, Q_, P_, N_)
+#define SSD_DISPATCH_F32(Q_, P_, N_) SSD_DISPATCH(float, float, Q_, P_, N_)
   if (dtype == SSD_BF16) { SSD_BF16_CONFIGS(SSD_DISPATCH_BF16) }
+  else if (dtype == SSD_FP8) { SSD_BF16_CONFIGS(SSD_DISPATCH_FP8) }
   else { SSD_F32_CONFIGS(SSD_DISPATCH_F32) }
 #undef SSD_DISPATCH
 #undef SSD_DISPATCH_BF16
+#undef SSD_DISPATCH_FP8
 #undef SSD_DISPATCH_F32
   return false;
 }
@@ -257,7 +262,8 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
   if (!saved_ws || saved_ws_bytes < pl.saved_bytes) return SSD_ERR_WORKSPACE;
   if (!scratch || scratch_bytes < pl.fwd_bytes) return SSD_ERR_WORKSPACE;
 
-  const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
+  const int64_t esz = s->dtype == SSD_F32 ? 4 : 2;                          // dt, y
+  const int64_t eszx = s->dtype == SSD_F32 ? 4 : (s->dtype == SSD_FP8 ? 1 : 2);  // x, B, C
   const int64_t b = s->batch, L = s->seqlen, Q = s->chunk, H = s->nheads, G = s->ngroups;
   const int64_t P = s->headdim, N = s->dstate;
   FwdArgs a{};
@@ -280,12 +286,12 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
     const RowCopy in{{x, dt, B, C},
                      {const_cast<void*>(a.rows.x), const_cast<void*>(a.rows.dt), const_cast<void*>(a.rows.B),
                       const_cast<void*>(a.rows.C)},
-                     {H * P * (int64_t)esz, H * (int64_t)esz, G * N * (int64_t)esz, G * N * (int64_t)esz}, 4};
+                     {H * P * eszx, H * esz, G * N * eszx, G * N * eszx}, 4};
     pad_rows(in, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
   dispatch_fwd(s->dtype, pl.lay, a, stream, probe);
   if (pl.Lr > 0) {
-    const RowCopy out{{a.rows.y}, {y}, {H * P * (int64_t)esz}, 1};
+    const RowCopy out{{a.rows.y}, {y}, {H * P * esz}, 1};
     unpad_rows(out, L, pl.kf * Q, pl.Lr, Q, b, stream);
   }
   if (hipGetLastError() != hipSuccess) return SSD_ERR_HIP;
@@ -307,6 +313,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   const ssd_shape* s = &sv->shape;
   const ssd_status st = check_shape(s);
   if (st != SSD_OK) return st;
+  if (s->dtype == SSD_FP8) return SSD_ERR_UNSUPPORTED;  // FP8 operands: forward only
   if (!sv->x || !sv->dt || !sv->A || !sv->B || !sv->C || !sv->D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {sv->x, sv->dt, sv->A, sv->B, sv->C, sv->D, dy, dx, ddt, dA, dB, dC, dD, sv->saved_ws, scratch,
@@ -317,7 +324,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   if (!sv->saved_ws || sv->saved_ws_bytes < pl.saved_bytes) return SSD_ERR_WORKSPACE;
   if (!scratch || scratch_bytes < pl.bwd_bytes) return SSD_ERR_WORKSPACE;
 
-  const size_t esz = s->dtype == SSD_BF16 ? 2 : 4;
+  const size_t esz = s->dtype == SSD_F32 ? 4 : 2;
   const int64_t b = s->batch, L = s->seqlen, Q = s->chunk, H = s->nheads, G = s->ngroups;
   const int64_t P = s->headdim, N = s->dstate;
   BwdArgs a{};

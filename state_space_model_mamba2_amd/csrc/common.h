@@ -41,6 +41,41 @@ template <typename T> struct Vec16;
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
 template <> struct Vec16<float> { typedef f4 type; static constexpr int n = 4; };
 
+// ---- FP8 (OCP E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// no infinities, S.1111.111 is NaN) ----------------------------------------
+typedef unsigned char fp8;
+
+// Eight codes (little-endian bytes of w) widened to bf16, exactly: every E4M3
+// value is a bf16 value.  gfx950's packed conversion with scale 1 widens two
+// codes (bytes 0-1, or 2-3 with the high selector) in element order; checked
+// on the GPU against the exact value of all 256 codes (NaN stays NaN, -0 is
+// kept).  A bit-manipulation widening cost ten ALU operations per code and
+// made the FP8 forward slower than bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  typedef __bf16 bf16x4l __attribute__((ext_vector_type(4)));
+  const bf16x4l lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const bf16x4l hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One 16-byte vector of compute type T from 8 (bf16) or 4 (fp32) elements of
+// storage type TI at p: a plain load, or eight FP8 codes widened to bf16.
+template <typename T, typename TI>
+__device__ __forceinline__ typename Vec16<T>::type load_vec16(const TI* p);
+template <>
+__device__ __forceinline__ bf16x8 load_vec16<bf16, bf16>(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+template <>
+__device__ __forceinline__ f4 load_vec16<float, float>(const float* p) { return *reinterpret_cast<const f4*>(p); }
+template <>
+__device__ __forceinline__ bf16x8 load_vec16<bf16, fp8>(const fp8* p) {
+  return e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(p));
+}
+
 // ---- fragments --------------------------------------------------------------
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
@@ -59,9 +94,13 @@ template <> __device__ __forceinline__ void frag_set<bf16>(Frag<bf16>& f, int s,
 template <> __device__ __forceinline__ void frag_set<float>(Frag<float>& f, int s, float v) { f.v[s] = v; }
 template <typename T> __device__ __forceinline__ float frag_get(const Frag<T>& f, int s) { return (float)f.v[s]; }
 
-// 8 contiguous elements (16-byte aligned for bf16, 32-byte pair for fp32).
+// 8 contiguous elements (16-byte aligned for bf16, 32-byte pair for fp32;
+// eight FP8 codes, 8-byte aligned, are widened to a bf16 fragment).
 __device__ __forceinline__ void frag_load(Frag<bf16>& f, const bf16* p) {
   f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void frag_load(Frag<bf16>& f, const fp8* p) {
+  f.v = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(p));
 }
 __device__ __forceinline__ void frag_load(Frag<float>& f, const float* p) {
   f4 a = *reinterpret_cast<const f4*>(p);

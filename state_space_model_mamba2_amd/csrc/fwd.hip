@@ -21,10 +21,10 @@ namespace ssd {
 // x rows of the chunk and the entering state Hin_k are staged once per
 // workgroup.  Each wave loads the C rows and all C.B^T tiles of its next row
 // tile while it computes the current one.
-template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__ x, const float* __restrict__ dt,
+template <typename T, typename TI, int Q, int P, int N>
+__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict__ x, const float* __restrict__ dt,
                                                            const float* __restrict__ cs_g, const float* __restrict__ Dp,
-                                                           const T* __restrict__ C, const T* __restrict__ hin,
+                                                           const TI* __restrict__ C, const T* __restrict__ hin,
                                                            const T* __restrict__ wt, T* __restrict__ y,
                                                            const RowMap rm, int H, int G, int K) {
   constexpr int NTH = 256, NW = 4;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   Frag<T> cf[2][NK];
   V4 wv[2][NT];
   auto tile_load = [&](int set, int I) {
-    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+    const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(cf[set][ks], crow, ks * 32 + 8 * q);
 #pragma unroll
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   for (int n = 0; n < XPT; ++n) {
     const int u = threadIdx.x + NTH * n;
     if (XPIECES % NTH == 0 || u < XPIECES)
-      xr[n] = *reinterpret_cast<const V*>(x + ((row0 + u / (P / VN)) * H + h) * P + (u % (P / VN)) * VN);
+      xr[n] = load_vec16<T, TI>(x + ((row0 + u / (P / VN)) * H + h) * P + (u % (P / VN)) * VN);
   }
 #pragma unroll
   for (int n = 0; n < HPT; ++n) {
@@ -200,15 +200,15 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const T* __restrict__
   }
 }
 
-template <typename T, int Q, int P, int N>
+template <typename T, typename TI, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_probe* probe) {
   const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
-  const T* x = static_cast<const T*>(a.x);
+  const TI* x = static_cast<const TI*>(a.x);
   // the cumsum writes the step in float32 (the caller's dt widened, or
   // softplus(dt + dt_bias)); every later kernel reads that
   const float* dt = a.dtf;
-  const T* B = static_cast<const T*>(a.B);
-  const T* C = static_cast<const T*>(a.C);
+  const TI* B = static_cast<const TI*>(a.B);
+  const TI* C = static_cast<const TI*>(a.C);
   T* hin = static_cast<T*>(a.hin);
   T* wt = static_cast<T*>(a.wt);
   {
@@ -219,12 +219,12 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_BMM_FWD, st);
     constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
-    k_bmm_tiles<T, Q, N><<<dim3(b * K * G, (TILES + 3) / 4), dim3(256), 0, st>>>(
+    k_bmm_tiles<T, TI, Q, N><<<dim3(b * K * G, (TILES + 3) / 4), dim3(256), 0, st>>>(
         B, C, wt, static_cast<T*>(a.wtb), a.rows, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    k_chunk_state<T, Q, P, N, false><<<dim3(b * K * H), dim3(256), 0, st>>>(x, B, dt, a.cs, a.S, a.rows, H, G, K);
+    k_chunk_state<T, TI, Q, P, N, false><<<dim3(b * K * H), dim3(256), 0, st>>>(x, B, dt, a.cs, a.S, a.rows, H, G, K);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);
@@ -233,14 +233,16 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
-    k_chunk_scan_fwd<T, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
+    k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K);
   }
 }
 
-#define SSD_INST_FWD_BF16(Q_, P_, N_) template void run_fwd<bf16, Q_, P_, N_>(const Layout&, const FwdArgs&, hipStream_t, const ssd_probe*);
-#define SSD_INST_FWD_F32(Q_, P_, N_) template void run_fwd<float, Q_, P_, N_>(const Layout&, const FwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_FWD_BF16(Q_, P_, N_) template void run_fwd<bf16, bf16, Q_, P_, N_>(const Layout&, const FwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_FWD_FP8(Q_, P_, N_) template void run_fwd<bf16, fp8, Q_, P_, N_>(const Layout&, const FwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_FWD_F32(Q_, P_, N_) template void run_fwd<float, float, Q_, P_, N_>(const Layout&, const FwdArgs&, hipStream_t, const ssd_probe*);
 SSD_BF16_CONFIGS(SSD_INST_FWD_BF16)
+SSD_BF16_CONFIGS(SSD_INST_FWD_FP8)
 SSD_F32_CONFIGS(SSD_INST_FWD_F32)
 
 }  // namespace ssd

@@ -2,6 +2,8 @@
 //   chunk cumsum, C.B^T tiles, chunk state (decay-weighted U^T V per chunk)
 //   and the forward / reverse inter-chunk state scans.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -19,8 +21,8 @@ template <> __device__ __forceinline__ void frag_zero<float>(Frag<float>& f) {
 
 // 8 contiguous K-values starting at k0 of a row whose K-extent is KD; zero
 // beyond KD (KD = 16 leaves the upper half of a 32-wide step empty).
-template <int KD, typename T>
-__device__ __forceinline__ void frag_load_k(Frag<T>& f, const T* row, int k0) {
+template <int KD, typename T, typename TI>
+__device__ __forceinline__ void frag_load_k(Frag<T>& f, const TI* row, int k0) {
   if (KD % 32 == 0 || k0 < KD) frag_load(f, row + k0);
   else frag_zero(f);
 }
@@ -114,9 +116,12 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, c
 //   backward order : tile (I, J) lane l holds W[16I + 4q + r][16J + l%16]
 // (q = l / 16, r = 0..3).  Both come from the same fragments of B rows J and
 // C rows I with the operands swapped; K of every product is dstate.  One
-// tile per wave: every load is issued before the first product.
-template <typename T, int Q, int N>
-__global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, const T* __restrict__ C,
+// tile per wave: every load is issued before the first product.  With FP8
+// (E4M3) B and C the products run on the FP8 matrix cores, whose fragment is
+// the bf16 one with one byte per K-value (checked on gfx950: OCP E4M3
+// operands, lane (q, c) supplies row c, K-values 8q .. 8q + 7).
+template <typename T, typename TI, int Q, int N>
+__global__ __launch_bounds__(256) void k_bmm_tiles(const TI* __restrict__ B, const TI* __restrict__ C,
                                                    T* __restrict__ wf, T* __restrict__ wb, const RowMap rm, int G,
                                                    int K) {
   constexpr int NT = Q / 16;
@@ -133,19 +138,34 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   B = rows_in(rm, k, B, rm.B);
   C = rows_in(rm, k, C, rm.C);
-  const T* brow = B + ((row0 + 16 * J + c) * G + g) * N;
-  const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
-  Frag<T> fb[NK], fc[NK];
-#pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    frag_load_k<N>(fb[ks], brow, ks * 32 + 8 * q);
-    frag_load_k<N>(fc[ks], crow, ks * 32 + 8 * q);
-  }
+  const TI* brow = B + ((row0 + 16 * J + c) * G + g) * N;
+  const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
   f4 af = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (std::is_same<TI, fp8>::value) {
+    long fb[NK], fc[NK];
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) {
-    mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
-    mma(ab, fc[ks], fb[ks]);  // [row i][col j] = C_i . B_j
+    for (int ks = 0; ks < NK; ++ks) {
+      const int kk = ks * 32 + 8 * q;
+      fb[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(brow + kk) : 0;
+      fc[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(crow + kk) : 0;
+    }
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      af = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fb[ks], fc[ks], af, 0, 0, 0);
+      ab = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fc[ks], fb[ks], ab, 0, 0, 0);
+    }
+  } else {
+    Frag<T> fb[NK], fc[NK];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      frag_load_k<N>(fb[ks], brow, ks * 32 + 8 * q);
+      frag_load_k<N>(fc[ks], crow, ks * 32 + 8 * q);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
+      mma(ab, fc[ks], fb[ks]);  // [row i][col j] = C_i . B_j
+    }
   }
   typename Vec4<T>::type vf, vb;
 #pragma unroll
@@ -168,8 +188,8 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const T* __restrict__ B, cons
 // fragments are read K-major with the transposing LDS read.  Blocks are
 // double-buffered: the next block is loaded into registers while the
 // current one is used.  One workgroup (4 waves) per (b, k, h).
-template <typename T, int Q, int P, int N, bool BWD>
-__global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, const T* __restrict__ V,
+template <typename T, typename TI, int Q, int P, int N, bool BWD>
+__global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
                                                      float* __restrict__ out, const RowMap rm, int H, int G, int K) {
   constexpr int NTH = 256;
@@ -203,7 +223,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
       const int u = threadIdx.x + NTH * n;
       if (UPIECES % NTH == 0 || u < UPIECES) {
         const int i = KB * blk + u / (P / VN);
-        uv[n] = *reinterpret_cast<const V16*>(U + ((row0 + i) * H + h) * P + (u % (P / VN)) * VN);
+        uv[n] = load_vec16<T, TI>(U + ((row0 + i) * H + h) * P + (u % (P / VN)) * VN);
         uw[n] = BWD ? __expf(csc[i]) : dtc[i] * __expf(cs_last - csc[i]);
       }
     }
@@ -211,7 +231,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const T* __restrict__ U, co
     for (int n = 0; n < VPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (VPIECES % NTH == 0 || u < VPIECES)
-        vv[n] = *reinterpret_cast<const V16*>(V + ((row0 + KB * blk + u / (N / VN)) * G + g) * N + (u % (N / VN)) * VN);
+        vv[n] = load_vec16<T, TI>(V + ((row0 + KB * blk + u / (N / VN)) * G + g) * N + (u % (N / VN)) * VN);
     }
   };
   auto store = [&](int bf) {

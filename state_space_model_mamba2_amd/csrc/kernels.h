@@ -10,6 +10,7 @@
 namespace ssd {
 
 typedef __bf16 bf16;
+typedef unsigned char fp8;  // OCP FP8 E4M3 code
 
 // Workspace regions, all offsets in bytes from the workspace base and 256-byte aligned.
 struct Layout {
@@ -132,7 +133,9 @@ int64_t conv_partial_rows(int64_t b, int64_t L, int esz);
 void run_conv_fwd(const ConvArgs& a, hipStream_t st);
 void run_conv_bwd(const ConvArgs& a, hipStream_t st);
 
-template <typename T, int Q, int P, int N>
+// T: compute and storage type of dt, y, states and tiles; TI: storage type of
+// x, B and C (T, or fp8 with T = bf16).
+template <typename T, typename TI, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);
 template <typename T, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_probe* probe);

@@ -39,6 +39,8 @@ Normal tensors are drawn in float32 (numpy's float32 ziggurat) for speed at
 the long-context size; the small per-head tensors are drawn in float64.  Every
 tensor is rounded to float32 (round-to-nearest-even); in bf16 mode x, dt, B,
 C and dy are then rounded again to bfloat16 (RNE).  A and D always stay float32.
+In fp8 mode x, B and C are rounded from float32 to OCP FP8 E4M3 codes (nearest,
+ties to even, saturating at +-448) and dt, dy to bfloat16.
 """
 from __future__ import annotations
 
@@ -105,11 +107,48 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+def _e4m3_table() -> np.ndarray:
+    """Value of every OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent field 0 is subnormal, S.1111.111 is NaN)."""
+    c = np.arange(256)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    v = s * v
+    v[(c & 0x7F) == 0x7F] = np.nan
+    return v
+
+
+E4M3_VALUES = _e4m3_table()
+
+
+def e4m3_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact value of each E4M3 code."""
+    return E4M3_VALUES[np.asarray(b, dtype=np.uint8)].astype(np.float32)
+
+
+def f32_to_e4m3_bits(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to the even code, saturating at
+    +-448 (the largest finite value); returns uint8 codes."""
+    a = np.asarray(a, dtype=np.float64)
+    pos = E4M3_VALUES[:0x7F]                      # codes 0x00 .. 0x7E, increasing
+    mag = np.minimum(np.abs(a), pos[-1])
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, len(pos) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = mag - pos[lo], pos[hi] - mag
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(mag == pos[hi], hi, code).astype(np.uint8)
+    return np.where(np.signbit(a), code | 0x80, code).astype(np.uint8)  # the sign survives rounding to zero
+
+
 @dataclasses.dataclass
 class Inputs:
     """One seeded draw.  Tensors are numpy arrays in their storage form:
     float32 arrays in f32 mode; uint16 bfloat16 bit patterns in bf16 mode
-    (x, dt, B, C, dy).  A and D are always float32."""
+    (x, dt, B, C, dy); in fp8 mode uint8 E4M3 codes for x, B, C and bfloat16
+    bits for dt, dy.  A and D are always float32."""
     shape: Shape
     x: np.ndarray
     dt: np.ndarray
@@ -126,6 +165,8 @@ class Inputs:
         a = getattr(self, name)
         if a.dtype == np.uint16:
             return bf16_bits_to_f32(a).astype(np.float64)
+        if a.dtype == np.uint8:
+            return E4M3_VALUES[a]
         return a.astype(np.float64)
 
 
@@ -155,6 +196,9 @@ def generate(shape: Shape, seed: int = 0, dt_sigma2: float = 0.5) -> Inputs:
 
     if s.dtype == "bf16":
         x, dt, B, C, dy, raw = (f32_to_bf16_bits(t) for t in (x, dt, B, C, dy, raw))
+    elif s.dtype == "fp8":
+        x, B, C = (f32_to_e4m3_bits(t) for t in (x, B, C))
+        dt, dy, raw = (f32_to_bf16_bits(t) for t in (dt, dy, raw))
     elif s.dtype != "f32":
         raise ValueError(f"unknown dtype {s.dtype!r}")
     return Inputs(s, x, dt, A, B, C, D, dy, raw, bias)

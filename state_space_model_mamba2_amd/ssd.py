@@ -25,7 +25,7 @@ import torch
 
 from . import _lib
 
-_DTYPES = {torch.float32: _lib.SSD_F32, torch.bfloat16: _lib.SSD_BF16}
+_DTYPES = {torch.float32: _lib.SSD_F32, torch.bfloat16: _lib.SSD_BF16, torch.float8_e4m3fn: _lib.SSD_FP8}
 _ALIGN = 256
 
 
@@ -76,12 +76,17 @@ def shape_of(x, B, chunk, dtype_code, flags=0) -> _lib.Shape:
     return _lib.make_shape(b, L, H, P, N, G, chunk, dtype_code, flags)
 
 
+def _step_dtype(x_dtype):
+    """dtype of dt, y and the gradients: x's, or bfloat16 when x, B, C are FP8."""
+    return torch.bfloat16 if x_dtype == torch.float8_e4m3fn else x_dtype
+
+
 def _validate(x, dt, A, B, C, D):
     if x.dtype not in _DTYPES:
-        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
-    for name, t in (("dt", dt), ("B", B), ("C", C)):
-        if t.dtype != x.dtype:
-            raise TypeError(f"{name} must have dtype {x.dtype}, got {t.dtype}")
+        raise TypeError(f"x must be bfloat16, float32 or float8_e4m3fn, got {x.dtype}")
+    for name, t, want in (("dt", dt, _step_dtype(x.dtype)), ("B", B, x.dtype), ("C", C, x.dtype)):
+        if t.dtype != want:
+            raise TypeError(f"{name} must have dtype {want}, got {t.dtype}")
     for name, t in (("A", A), ("D", D)):
         if t.dtype != torch.float32:
             raise TypeError(f"{name} must be float32")
@@ -125,7 +130,7 @@ def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = N
     dev = x.device
     saved_bytes = lib.ssd_saved_bytes(ctypes.byref(shape))
     scratch_bytes = lib.ssd_fwd_scratch_bytes(ctypes.byref(shape))
-    y = out if out is not None else torch.empty_like(x)
+    y = out if out is not None else torch.empty(x.shape, dtype=_step_dtype(x.dtype), device=x.device)
     fs = torch.empty((shape.batch, shape.nheads, shape.headdim, shape.dstate), dtype=torch.float32,
                      device=dev) if want_final_state else None
     saved_ws = torch.empty(saved_bytes, dtype=torch.uint8, device=dev)
@@ -138,7 +143,7 @@ def fwd(x, dt, A, B, C, D, chunk: int, *, initial_state: torch.Tensor | None = N
                        ctypes.byref(saved), _ptr(scratch), scratch.numel(), _stream_handle(stream),
                        ctypes.byref(probe) if probe is not None else None)
     _check(code, "ssd_fwd")
-    ctx = Context(saved, (x, dt, A, B, C, D), saved_ws, shape, x.dtype, dt_bias)
+    ctx = Context(saved, (x, dt, A, B, C, D), saved_ws, shape, _step_dtype(x.dtype), dt_bias)
     return y, fs, ctx
 
 
@@ -150,6 +155,8 @@ def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dini
     dt_softplus, ddt_bias (ddt is then the gradient of the raw step)."""
     lib = _lib.load()
     x, dt, A, B, C, D = ctx.tensors
+    if x.dtype == torch.float8_e4m3fn:
+        raise NotImplementedError("FP8 operands are forward only")
     if dy.dtype != x.dtype or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
         raise ValueError("dy must be a contiguous GPU tensor with x's shape and dtype")
     _check_state(dfinal_state, ctx.shape, "dfinal_state")
@@ -250,6 +257,8 @@ def to_device(inp, device="cuda"):
     def t(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        if a.dtype == np.uint8:
+            return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(device)
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     return dict(x=t(inp.x), dt=t(inp.dt), A=t(inp.A), B=t(inp.B), C=t(inp.C), D=t(inp.D), dy=t(inp.dy),

@@ -50,6 +50,7 @@ def test_shape_checks(lib):
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=64)) == OK
     assert check(lib, shape(chunk=64)) == UNSUPPORTED                        # bf16 chunk 64 switched off
     assert check(lib, shape(dtype=_lib.SSD_F32, chunk=128, dstate=64)) == OK
+    assert check(lib, shape(dtype=_lib.SSD_FP8)) == OK and check(lib, shape(dtype=_lib.SSD_FP8, chunk=64)) == UNSUPPORTED
     assert check(lib, shape(seqlen=500)) == OK               # shorter last chunk
     assert check(lib, shape(seqlen=7)) == OK                 # a single, shorter chunk
     assert check(lib, shape(nheads=5)) == INVALID            # nheads % ngroups
@@ -145,6 +146,8 @@ def test_bwd_rejects_before_launch(lib):
     assert bwd(small) == WORKSPACE
     bad = _lib.Saved(shape(nheads=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
     assert bwd(bad) == INVALID
+    fp8 = _lib.Saved(shape(dtype=_lib.SSD_FP8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
+    assert bwd(fp8) == UNSUPPORTED                           # FP8 operands: forward only
 
 
 def test_strings(lib):
