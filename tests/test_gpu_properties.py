@@ -154,3 +154,38 @@ def test_stress_zero_B(shape):
 ], ids=["bf16-one-chunk", "f32-one-chunk"])
 def test_single_chunk_shapes(shape):
     _stress(shape, lambda inp: None, STRESS_TOL[shape.dtype])
+
+
+def _stress_states(shape, mutate, tol):
+    inp = inputs.generate(shape, seed=7)
+    mutate(inp)
+    st = inputs.generate_states(shape, seed=7)
+    got, _ = run_gpu(inp, shape.chunk, states=st)
+    ref = run_oracle(inp, states=st)
+    errs = {k: max_rel(got[k], ref[k]) for k in ref}
+    print(f"[edge] {shape}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("shape", [
+    inputs.workload("mamba2_370m", batch=2, seqlen=1, nheads=4),   # one token: the whole sequence is a padded chunk
+    inputs.workload("tiny_fp32", batch=3, seqlen=1, nheads=2),
+], ids=["bf16-L1", "f32-L1"])
+def test_edge_single_token(shape):
+    _stress_states(shape, lambda inp: None, STRESS_TOL[shape.dtype])
+
+
+@pytest.mark.parametrize("shape", STRESS_SHAPES, ids=lambda s: f"{s.dtype}-q{s.chunk}")
+def test_edge_memoryless(shape):
+    # exp(dt A) underflows to exactly 0 at every step: each token sees only itself
+    def m(inp):
+        _set(inp, "A", np.full(shape.nheads, -1e4))
+        _set(inp, "dt", _f64(inp.dt) + 0.1)
+    _stress_states(shape, m, STRESS_TOL[shape.dtype])
+
+
+@pytest.mark.parametrize("shape", STRESS_SHAPES, ids=lambda s: f"{s.dtype}-q{s.chunk}")
+def test_edge_zero_step_carries_the_initial_state(shape):
+    # dt = 0: no decay and no input; the state stays S0 and y = C S0 + D x
+    _stress_states(shape, lambda inp: _set(inp, "dt", 0.0), STRESS_TOL[shape.dtype])
