@@ -946,7 +946,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
-    k_chunk_state<T, T, Q, P, N, true><<<dim3(b * K * H), dim3(256), 0, st>>>(dy, C, dt, a.cs, a.dhloc, a.rows, H, G, K);
+    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, a.dhloc, a.rows, b, H, G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);

@@ -224,7 +224,7 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    k_chunk_state<T, TI, Q, P, N, false><<<dim3(b * K * H), dim3(256), 0, st>>>(x, B, dt, a.cs, a.S, a.rows, H, G, K);
+    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, a.S, a.rows, b, H, G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);

@@ -187,8 +187,10 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const TI* __restrict__ B, con
 // (rows scaled by w_i on the way) and V are staged row-major in LDS and both
 // fragments are read K-major with the transposing LDS read.  Blocks are
 // double-buffered: the next block is loaded into registers while the
-// current one is used.  One workgroup (4 waves) per (b, k, h).
-template <typename T, typename TI, int Q, int P, int N, bool BWD>
+// current one is used.  One workgroup (4 waves) per (b, k) and HPW heads of
+// one group: V, the group's rows, is staged once for all of them, and their U
+// rows are one contiguous run per token.
+template <typename T, typename TI, int Q, int P, int N, bool BWD, int HPW>
 __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
                                                      float* __restrict__ out, const RowMap rm, int H, int G, int K) {
@@ -201,30 +203,41 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
   constexpr int UPIECES = KB * P / VN, VPIECES = KB * N / VN;
   constexpr int UPT = (UPIECES + NTH - 1) / NTH, VPT = (VPIECES + NTH - 1) / NTH;
   typedef typename Vec16<T>::type V16;
-  __shared__ __attribute__((aligned(16))) T Us[2][KB][UP];
+  __shared__ __attribute__((aligned(16))) T Us[2][HPW][KB][UP];
   __shared__ __attribute__((aligned(16))) T Vs[2][KB][VP];
 
-  const int bkh = blockIdx.x;
-  const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
-  const int g = h / (H / G);
+  const int bkhp = blockIdx.x;
+  const int HP = H / HPW;
+  const int hp = bkhp % HP, bk = bkhp / HP, k = bk % K, b = bk / K;
+  const int h0 = hp * HPW;                         // HPW consecutive heads, one group
+  const int g = h0 / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   U = rows_in(rm, k, U, BWD ? rm.dy : rm.x);
   V = rows_in(rm, k, V, BWD ? rm.C : rm.B);
-  const float* csc = cs + (((int64_t)b * H + h) * K + k) * Q;
-  const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
-  const float cs_last = csc[Q - 1];
+  const float* csc[HPW];
+  const float* dtc[HPW];
+  float cs_last[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    csc[hh] = cs + (((int64_t)b * H + h0 + hh) * K + k) * Q;
+    dtc[hh] = dt + (((int64_t)b * H + h0 + hh) * K + k) * Q;
+    cs_last[hh] = csc[hh][Q - 1];
+  }
 
-  V16 uv[UPT], vv[VPT];
-  float uw[UPT];
+  V16 uv[HPW][UPT], vv[VPT];
+  float uw[HPW][UPT];
   auto load = [&](int blk) {
 #pragma unroll
-    for (int n = 0; n < UPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (UPIECES % NTH == 0 || u < UPIECES) {
-        const int i = KB * blk + u / (P / VN);
-        uv[n] = load_vec16<T, TI>(U + ((row0 + i) * H + h) * P + (u % (P / VN)) * VN);
-        uw[n] = BWD ? __expf(csc[i]) : dtc[i] * __expf(cs_last - csc[i]);
+    for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+      for (int n = 0; n < UPT; ++n) {
+        const int u = threadIdx.x + NTH * n;
+        if (UPIECES % NTH == 0 || u < UPIECES) {
+          const int i = KB * blk + u / (P / VN);
+          uv[hh][n] = load_vec16<T, TI>(U + ((row0 + i) * H + h0 + hh) * P + (u % (P / VN)) * VN);
+          uw[hh][n] = BWD ? __expf(csc[hh][i]) : dtc[hh][i] * __expf(cs_last[hh] - csc[hh][i]);
+        }
       }
     }
 #pragma unroll
@@ -236,13 +249,16 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
   };
   auto store = [&](int bf) {
 #pragma unroll
-    for (int n = 0; n < UPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (UPIECES % NTH == 0 || u < UPIECES) {
-        V16 w;
+    for (int hh = 0; hh < HPW; ++hh) {
 #pragma unroll
-        for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(uv[n][e]) * uw[n]);
-        *reinterpret_cast<V16*>(&Us[bf][u / (P / VN)][(u % (P / VN)) * VN]) = w;
+      for (int n = 0; n < UPT; ++n) {
+        const int u = threadIdx.x + NTH * n;
+        if (UPIECES % NTH == 0 || u < UPIECES) {
+          V16 w;
+#pragma unroll
+          for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(uv[hh][n][e]) * uw[hh][n]);
+          *reinterpret_cast<V16*>(&Us[bf][hh][u / (P / VN)][(u % (P / VN)) * VN]) = w;
+        }
       }
     }
 #pragma unroll
@@ -253,9 +269,11 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
     }
   };
 
-  f4 acc[TPW];
+  f4 acc[HPW][TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[hh][t] = f4{0.f, 0.f, 0.f, 0.f};
 
   load(0);
   store(0);
@@ -270,25 +288,42 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
         const int j = wave + 4 * t;
         if (j < NT) {
           const int tm = j / TN, tn = j % TN;
-          Frag<T> fa, fb;
-          frag_load_kmajor<32>(fa, &Us[bf][0][0], UP, ks * 32, tm * 16, q, c);
+          Frag<T> fb;
           frag_load_kmajor<32>(fb, &Vs[bf][0][0], VP, ks * 32, tn * 16, q, c);
-          mma(acc[t], fa, fb);
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            Frag<T> fa;
+            frag_load_kmajor<32>(fa, &Us[bf][hh][0][0], UP, ks * 32, tm * 16, q, c);
+            mma(acc[hh][t], fa, fb);
+          }
         }
       }
     }
     if (blk + 1 < NB) store(bf ^ 1);
   }
-  float* o = out + (int64_t)bkh * P * N;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int j = wave + 4 * t;
-    if (j < NT) {
-      const int tm = j / TN, tn = j % TN;
+  for (int hh = 0; hh < HPW; ++hh) {
+    float* o = out + (((int64_t)b * K + k) * H + h0 + hh) * P * N;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[t][r];
+    for (int t = 0; t < TPW; ++t) {
+      const int j = wave + 4 * t;
+      if (j < NT) {
+        const int tm = j / TN, tn = j % TN;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[hh][t][r];
+      }
     }
   }
+}
+
+// Launch of k_chunk_state: two heads per workgroup when a group's heads pair up.
+template <typename T, typename TI, int Q, int P, int N, bool BWD>
+void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, float* out, const RowMap& rm,
+                        int b, int H, int G, int K, hipStream_t st) {
+  if ((H / G) % 2 == 0)
+    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(b * K * H / 2), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K);
+  else
+    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(b * K * H), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K);
 }
 
 // ---------------------------------------------------------------------------
