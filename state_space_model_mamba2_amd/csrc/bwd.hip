@@ -24,12 +24,13 @@ namespace ssd {
 // as matrix-core accumulators (lane (q, c) holds dxt[16J + c][16tp + 4q + r]),
 // so every token's x and dxt values sit in the same lane and slot: <dxt_j, x_j>
 // and q_j need no second read of x.
-// The chunk's dy rows of this head are read once, all at the start, into LDS
-// (row-major; the dy^T operands are gathered from it).  C and the owned
-// C.B^T tiles stream through LDS in 32-row slabs from the chunk end backwards
-// (double-buffered: the next slab is loaded into registers while the current
-// one is used; these mostly hit in L2, which they share with the other heads
-// of the group).  A column tile's dxt is complete once the slab holding its
+// This head's dy rows, the group's C rows and the owned C.B^T tiles stream
+// through LDS in 32-row slabs from the chunk end backwards (double-buffered:
+// the next slab is loaded into registers while the current one is used; C
+// and the tiles mostly hit in L2, which they share with the other heads of
+// the group).  Every use of dy falls in the slab being processed, so LDS
+// holds two slabs of it, not the whole chunk; the dy^T operands come from it
+// through transposing reads.  A column tile's dxt is complete once the slab holding its
 // own rows has been used, so dx is written right there.
 // R is formed once per (I, J) tile pair on the matrix cores: lanes own a
 // column j, so column sums accumulate in-lane and row sums come from 16-lane
@@ -54,7 +55,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr int SR = 32;                  // rows per slab
   constexpr int VN = Vec16<T>::n;
   constexpr int CUP = P / VN, CUN = N / VN;
-  constexpr int YPIECES = Q * CUP, CPIECES = SR * CUN;   // 16-byte pieces: dy chunk, C slab
+  constexpr int YPIECES = SR * CUP, CPIECES = SR * CUN;  // 16-byte pieces: dy slab, C slab
+  // dy row pitch: for bf16 8 (mod 16) dwords, for the transposing reads
+  constexpr int DPITCH = sizeof(T) == 2 ? P + 2 * ((24 - (P / 2) % 16) % 16) : P + PADR;
   constexpr int YPT = (YPIECES + NTH - 1) / NTH, CPT = (CPIECES + NTH - 1) / NTH;
   // C.B^T tiles of a slab: rows I = 2s + half against every owned column tile
   // of this workgroup, slot (half, wave, sl); tiles with J > I stay unused
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   static_assert(NSPLIT == 1 || NSPLIT == 2, "a split owns one row tile of each slab");
   typedef typename Vec4<T>::type V4;
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T DY[Q][P + PADR];        // this head's dy rows of the chunk
+  __shared__ __attribute__((aligned(16))) T DY[2][SR][DPITCH];     // slab rows of this head's dy
   __shared__ __attribute__((aligned(16))) T Cs[2][SR][N + PADR];    // slab rows of C
   __shared__ __attribute__((aligned(16))) T Ws[2][WT * 256];        // slab C.B^T tiles (lane order)
   __shared__ __attribute__((aligned(16))) float cs[Q];
@@ -110,8 +113,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   for (int sl = 0; sl < NSLOT; ++sl) Js[sl] = tile_of(wave, sl);
 
   // ---- slab staging: registers <- global (next slab), LDS <- registers
-  V cv[CPT], wv[WPT];
+  V yv[YPT], cv[CPT], wv[WPT];
   auto slab_load = [&](int s) {
+#pragma unroll
+    for (int n = 0; n < YPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (YPIECES % NTH == 0 || u < YPIECES)
+        yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * s + u / CUP) * rs + (u % CUP) * VN);
+    }
 #pragma unroll
     for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
@@ -131,6 +140,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     }
   };
   auto slab_store = [&](int bf) {
+#pragma unroll
+    for (int n = 0; n < YPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[bf][u / CUP][(u % CUP) * VN]) = yv[n];
+    }
 #pragma unroll
     for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
@@ -157,12 +171,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       dtv[n] = dtc[i];
     }
   }
-  V yv[YPT];
-#pragma unroll
-  for (int n = 0; n < YPT; ++n) {
-    const int u = threadIdx.x + NTH * n;
-    if (YPIECES % NTH == 0 || u < YPIECES) yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(u / CUP) * rs + (u % CUP) * VN);
-  }
   slab_load(NS - 1);
   Frag<T> xf[NSLOT][NKP];
 #pragma unroll
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       frag_load_k<N>(bfr[ks][sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
   }
 
-  // LDS stores of the per-token scalars and dy (their loads were issued first)
+  // LDS stores of the per-token scalars (their loads were issued first)
 #pragma unroll
   for (int n = 0; n < QPT; ++n) {
     const int i = threadIdx.x + NTH * n;
@@ -192,11 +200,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       cs[i] = csv[n];
       dts[i] = dtv[n];
     }
-  }
-#pragma unroll
-  for (int n = 0; n < YPT; ++n) {
-    const int u = threadIdx.x + NTH * n;
-    if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[u / CUP][(u % CUP) * VN]) = yv[n];
   }
 
   // state part of dxt^T: e_j (Gk B_j^T) with K = dstate
@@ -278,17 +281,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       const int i0 = rb + 16 * half + 4 * q;
       const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rowtot[half][r] += __expf(csi[r]) * (acc[r] * to_f(DY[i0 + r][16 * tw + c]));
+      for (int r = 0; r < 4; ++r)
+        rowtot[half][r] += __expf(csi[r]) * (acc[r] * to_f(DY[bf][16 * half + 4 * q + r][16 * tw + c]));
     }
 
     // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
     Frag<T> fdt[TP];
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8)
-        fdt[tp].v[s8] = DY[rb + (s8 < 4 ? 4 * q + s8 : 16 + 4 * q + s8 - 4)][16 * tp + c];
-    }
+    for (int tp = 0; tp < TP; ++tp) frag_load_kmajor<SR>(fdt[tp], &DY[bf][0][0], DPITCH, 0, 16 * tp, q, c);
 
     // intra-chunk pairs (I in this slab, J owned), I >= J.
     // Column tiles wholly before the slab ("full" pairs, the common case):
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
         for (int kp = 0; kp < NKP; ++kp) {
           Frag<T> fd;
-          frag_load_chained<P>(fd, &DY[rb + 16 * half + c][0], kp * 32, q);
+          frag_load_chained<P>(fd, &DY[bf][16 * half + c][0], kp * 32, q);
           mma(dp[half], fd, xf[sl][kp]);     // lane: column j = cj, rows i = rb + 16 half + 4q + r
         }
       }
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
           for (int kp = 0; kp < NKP; ++kp) {
             Frag<T> fd;
-            frag_load_chained<P>(fd, &DY[16 * I + c][0], kp * 32, q);
+            frag_load_chained<P>(fd, &DY[bf][16 * half + c][0], kp * 32, q);
             mma(dp, fd, xf[sl][kp]);
           }
           const int i0 = 16 * I + 4 * q;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       float xd = 0.0f;
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const V4 dv = *reinterpret_cast<const V4*>(&DY[j][16 * tp + 4 * q]);
+        const V4 dv = *reinterpret_cast<const V4*>(&DY[bf][j - rb][16 * tp + 4 * q]);
         V4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
