@@ -171,6 +171,56 @@ def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
     return out
 
 
+def cold_warm(ssd, dev, chunk, fscr, bscr, reps=10):
+    """Median whole-step time (events on the stream the library launches on)
+    with the caches flushed before every step -- a 1 GiB write evicts the L2s
+    and the 256 MB Infinity Cache -- and without; plus the rate of a plain
+    1 GiB device copy, the achievable-HBM reference."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode in ("cold", "warm"):
+        ts = []
+        for i in range(reps):
+            if mode == "cold":
+                flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_step(ssd, dev, chunk, fscr, bscr)
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        out[f"{mode}_ms_per_step"] = ts[len(ts) // 2]
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    ts = []
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        flush.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    out["copy_GBps"] = 2 * src.numel() * 4 / (ts[len(ts) // 2] / 1e3) / 1e9
+    out["reps"] = reps
+    del flush, src
+    return out
+
+
+def shader_clock_mhz():
+    """Current shader clock level from the driver's sysfs table, if readable."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if line.rstrip().endswith("*"):
+                    return line.split(":", 1)[1].strip().rstrip("*").strip()
+        except OSError:
+            pass
+    return None
+
+
 def host_threads() -> int:
     n = len(os.sched_getaffinity(0))
     omp = os.environ.get("OMP_NUM_THREADS")
@@ -299,12 +349,20 @@ def summarize_stats(csv_path: str, command: str, title: str) -> str:
         rows = list(csv.DictReader(fh))
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
              "rocprofv3 kernel statistics (durations in microseconds):", "",
-             "| kernel | calls | total us | average us | % of GPU time |", "|---|---|---|---|---|"]
+             "| kernel | name as reported (truncated) | calls | total us | average us | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    import re
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         n = r["Name"]
-        for a, b in [("_ZN3ssd", ""), ("IDF16bLi256ELi64ELi128E", "<bf16,256,64,128>")]:
-            n = n.replace(a, b)
-        lines.append(f"| `{n[:90]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+        m = re.search(r"(k_[a-z_0-9]+)", n)
+        short = m.group(1) if m else n.split("(")[0].split("<")[0].replace("void ", "")[:40]
+        # the kernels' bool template flag names the variant
+        flag = re.search(r"L(b[01])E", n)
+        labels = {"k_chunk_state": ("forward", "backward"), "k_dw": ("off-diagonal blocks", "diagonal blocks"),
+                  "k_bc_heads": ("dC", "dB"), "k_bc_final": ("dC", "dB")}
+        if flag and short in labels:
+            short += f" ({labels[short][int(flag.group(1)[1])]})"
+        lines.append(f"| {short} | `{n[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     return "\n".join(lines) + "\n"
 
@@ -547,6 +605,13 @@ def main():
                 f"  {nf / v / 1e9:7.1f} TFLOP/s ({100 * nf / v / 1e9 / MFMA_PEAK_TFLOPS[shape.dtype]:5.1f}%)")
         log(f"  sum of kernels {tot:.4f} ms vs step {ms_per_step:.4f} ms")
 
+    timing = cold_warm(ssd, dev, shape.chunk, fscr, bscr) if args.profile_kernel is None else None
+    if timing:
+        timing["shader_clock"] = shader_clock_mhz()
+        roof["frac_of_copy"] = roof["achieved"] / timing["copy_GBps"] if roof["unit"] == "GB/s" else None
+        log(f"[bench] step median cold {timing['cold_ms_per_step']:.4f} ms, warm {timing['warm_ms_per_step']:.4f} ms;"
+            f" 1 GiB copy {timing['copy_GBps']:.0f} GB/s; shader clock {timing['shader_clock']}")
+
     cpu = None
     if not args.no_cpu_baseline and args.profile_kernel is None and not args.fwd_only:
         log("[bench] timing the float64 oracle on a bounded sample ...")
@@ -573,6 +638,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernel_ms": breakdown or None,
+        "timing": timing,
     }
     print(json.dumps(out), flush=True)
 
