@@ -824,21 +824,27 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
 // 64-token blocks: the dW block (converted to the storage type) and the B
 // (or C) rows are staged row-major in LDS; dC reads dW rows directly, dB reads
 // them K-major, and B / C are read K-major (transposing LDS read).
-template <typename T, int Q, int N, bool DB>
+// blockIdx.z takes one of NH parts of the dstate columns (more workgroups for
+// a launch that has only b K G (Q / 64) row blocks); each part stages its
+// own B / C columns and the whole dW block.
+template <typename T, int Q, int N, bool DB, int NH>
 __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part, const float* __restrict__ dw,
                                                   const T* __restrict__ M, T* __restrict__ out, const RowMap rm,
                                                   int G, int K, int nslice, int nslice_dw) {
   constexpr int NTH = 256;
-  constexpr int TN = N / 16, NB = Q / 64;
+  constexpr int NP = N / NH;                 // dstate columns of this part
+  constexpr int TN = NP / 16, NB = Q / 64;
   constexpr int VN = Vec16<T>::n;
-  constexpr int WP = 64 + 16, MP = N + 16;   // row pitches (8 mod 16 dwords)
-  constexpr int MPIECES = 64 * N / VN;
+  constexpr int WP = 64 + 16;                // row pitches (8 mod 16 dwords)
+  constexpr int MP = NP + ((24 - (NP * (int)sizeof(T) / 4) % 16) % 16) * 4 / (int)sizeof(T);
+  constexpr int MPIECES = 64 * NP / VN;
   constexpr int MPT = (MPIECES + NTH - 1) / NTH;
+  static_assert(N % NH == 0 && NP % 16 == 0, "dstate parts");
   typedef typename Vec16<T>::type V;
   __shared__ __attribute__((aligned(16))) T Wb[64][WP];
   __shared__ __attribute__((aligned(16))) T Ms[64][MP];
 
-  const int bkg = blockIdx.x, RB = blockIdx.y;
+  const int bkg = blockIdx.x, RB = blockIdx.y, n0 = NP * blockIdx.z;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
@@ -872,9 +878,9 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
     for (int n = 0; n < MPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (MPIECES % NTH == 0 || u < MPIECES) {
-        const int rr = u / (N / VN), cu = u % (N / VN);
+        const int rr = u / (NP / VN), cu = u % (NP / VN);
         *reinterpret_cast<V*>(&Ms[rr][cu * VN]) =
-            *reinterpret_cast<const V*>(M + ((row0 + 64 * kb + rr) * G + g) * N + cu * VN);
+            *reinterpret_cast<const V*>(M + ((row0 + 64 * kb + rr) * G + g) * N + n0 + cu * VN);
       }
     }
     __syncthreads();
@@ -898,10 +904,10 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int rr = r0 + 16 * wave + 4 * q + r;
-      const int64_t e = ((prow0 + rr) * G + g) * N + 16 * tn + c;
+      const int64_t e = ((prow0 + rr) * G + g) * N + n0 + 16 * tn + c;
       float v = part[e];
       for (int z = 1; z < nslice; ++z) v += part[z * ps + e];
-      out[((row0 + rr) * G + g) * N + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
+      out[((row0 + rr) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
     }
   }
 }
@@ -932,6 +938,9 @@ __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart,
     if (dbias) dbias[h] = (rb[0] + rb[1]) + (rb[2] + rb[3]);
   }
 }
+
+// dstate parts of k_bc_final: 32 columns each
+template <int N> constexpr int kBcParts = N >= 32 ? N / 32 : 1;
 
 template <typename T, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_probe* probe) {
@@ -976,14 +985,14 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     ProbeScope ps(probe, SSD_K_DC, st);
     k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
         x, dt, a.cs, dy, hin, a.dcpart, a.rows, H, G, K, hpsb);
-    k_bc_final<T, Q, N, false><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
+    k_bc_final<T, Q, N, false, kBcParts<N>><<<dim3(b * K * G, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
         a.dcpart, a.dw, B, static_cast<T*>(a.dC), a.rows, G, K, Sb, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DB, st);
     k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
         x, dt, a.cs, dy, gst, a.dbpart, a.rows, H, G, K, hpsb);
-    k_bc_final<T, Q, N, true><<<dim3(b * K * G, Q / 64), dim3(256), 0, st>>>(
+    k_bc_final<T, Q, N, true, kBcParts<N>><<<dim3(b * K * G, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
         a.dbpart, a.dw, C, static_cast<T*>(a.dB), a.rows, G, K, Sb, S);
   }
   {
