@@ -142,6 +142,16 @@ __device__ __forceinline__ void frag_load_kmajor(Frag<bf16>& f, const bf16* tile
   if constexpr (KD % 32 == 0) hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(a0 + 16 * pitch));
   f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
+// The same transposing read from per-lane addresses of the two 16-row runs
+// (for tiles stored in a permuted layout): lane (q, c) passes the address of
+// its 4 values in rows k0 + 4q + c/4 and k0 + 16 + 4q + c/4.
+__device__ __forceinline__ void frag_load_kmajor_at(Frag<bf16>& f, const bf16* lo_addr, const bf16* hi_addr) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(lo_addr));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(hi_addr));
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 template <int KD>
 __device__ __forceinline__ void frag_load_kmajor(Frag<float>& f, const float* tile, int pitch, int k0, int col0,
                                                  int q, int c) {

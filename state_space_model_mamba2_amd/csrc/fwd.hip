@@ -21,8 +21,16 @@ namespace ssd {
 // x rows of the chunk and the entering state Hin_k are staged once per
 // workgroup.  Each wave loads the C rows and all C.B^T tiles of its next row
 // tile while it computes the current one.
+// Column at which element (r, col) of the staged bf16 x rows is kept: the
+// 16-element groups of a row are XOR-permuted by a function of the row, so
+// the transposing reads of 4 consecutive rows (and of 8, on 64 banks) meet
+// distinct banks without row padding, and 16-byte pieces stay whole.
+__device__ __forceinline__ int xcol(int r, int col) { return col ^ (16 * ((r ^ (r >> 2)) & 3)); }
+
+// bf16 with headdim >= 64 keeps x rows unpadded (permuted), which fits three
+// workgroups on a CU at chunk 256 / headdim 64 / dstate 128.
 template <typename T, typename TI, int Q, int P, int N>
-__global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict__ x, const float* __restrict__ dt,
+__global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void k_chunk_scan_fwd(const TI* __restrict__ x, const float* __restrict__ dt,
                                                            const float* __restrict__ cs_g, const float* __restrict__ Dp,
                                                            const TI* __restrict__ C, const T* __restrict__ hin,
                                                            const T* __restrict__ wt, T* __restrict__ y,
@@ -31,7 +39,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict_
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NJ2 = NT / 2;
   constexpr int NSLOT = (NT + NW - 1) / NW;     // row tiles per wave
-  constexpr int XPITCH = P + 16, HPITCH = N + 16 / sizeof(T);
+  constexpr bool XSWZ = sizeof(T) == 2 && P % 64 == 0;
+  constexpr int XPITCH = XSWZ ? P : P + 16, HPITCH = N + 16 / sizeof(T);
   constexpr int VN = Vec16<T>::n;
   constexpr int XPIECES = Q * P / VN, HPIECES = P * N / VN;
   constexpr int XPT = (XPIECES + NTH - 1) / NTH, HPT = (HPIECES + NTH - 1) / NTH;
@@ -110,7 +119,10 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict_
 #pragma unroll
   for (int n = 0; n < XPT; ++n) {
     const int u = threadIdx.x + NTH * n;
-    if (XPIECES % NTH == 0 || u < XPIECES) *reinterpret_cast<V*>(&Xs[u / (P / VN)][(u % (P / VN)) * VN]) = xr[n];
+    if (XPIECES % NTH == 0 || u < XPIECES) {
+      const int r = u / (P / VN), col = (u % (P / VN)) * VN;
+      *reinterpret_cast<V*>(&Xs[r][XSWZ ? xcol(r, col) : col]) = xr[n];
+    }
   }
 #pragma unroll
   for (int n = 0; n < HPT; ++n) {
@@ -182,7 +194,13 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict_
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
         Frag<T> fx;                            // x^T: row p = 16tp + c, K = j (chained)
-        frag_load_kmajor<32>(fx, &Xs[0][0], XPITCH, 32 * J2, 16 * tp, q, c);
+        if constexpr (XSWZ) {
+          const int r = 32 * J2 + 4 * q + (c >> 2);  // row r + 16 has the same permutation
+          const T* a = &Xs[r][xcol(r, 16 * tp + 4 * (c & 3))];
+          frag_load_kmajor_at(fx, a, a + 16 * XPITCH);
+        } else {
+          frag_load_kmajor<32>(fx, &Xs[0][0], XPITCH, 32 * J2, 16 * tp, q, c);
+        }
         mma(acc[tp], fx, fa);
       }
     }
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_chunk_scan_fwd(const TI* __restrict_
     T* yr = y + ((row0 + ci) * H + h) * P;
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
-      const V4 xv = *reinterpret_cast<const V4*>(&Xs[ci][16 * tp + 4 * q]);
+      const V4 xv = *reinterpret_cast<const V4*>(&Xs[ci][XSWZ ? xcol(ci, 16 * tp + 4 * q) : 16 * tp + 4 * q]);
       V4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[tp][r] + Dh * to_f(xv[r]));
