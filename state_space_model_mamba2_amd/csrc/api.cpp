@@ -75,7 +75,11 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
     if (sl > kMaxSlices) sl = kMaxSlices;
     if (sl > hpg) sl = hpg;
     if (sl < 1) sl = 1;
-    return sl;
+    // the kernels give each slice ceil(hpg / sl) heads; take the slice count
+    // that this covers exactly, so no slice is empty (9 heads in 4 slices of 3
+    // would leave the last with none, and its loads would run past the group)
+    const int64_t per = (hpg + sl - 1) / sl;
+    return (hpg + per - 1) / per;
   };
   y.nslice = slices(512);
   y.nslice_bc = slices(512);

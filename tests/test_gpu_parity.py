@@ -70,3 +70,13 @@ def test_long_context_decay_small():
 def test_bf16_other_configs(chunk, headdim, dstate):
     _check(inputs.workload("mamba2_370m", batch=2, seqlen=512, nheads=4, ngroups=2, chunk=chunk,
                            headdim=headdim, dstate=dstate))
+
+
+# Head counts per group that do not split evenly into head slices (5, 6, 9
+# heads; one chunk, so the group-level backward kernels ask for the most
+# slices): every slice must hold at least one head.
+@pytest.mark.parametrize("nheads,ngroups,dtype,chunk",
+                         [(9, 1, "f32", 64), (10, 2, "f32", 64), (6, 1, "bf16", 128), (9, 1, "bf16", 256)])
+def test_uneven_head_slices(nheads, ngroups, dtype, chunk):
+    _check(inputs.workload("tiny_fp32", batch=1, seqlen=chunk, nheads=nheads, ngroups=ngroups, chunk=chunk,
+                           dtype=dtype))
