@@ -573,50 +573,59 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
 // straight from global memory (K = headdim is contiguous there); the head's
 // 64 x rows are staged row-major in LDS once per workgroup (double-buffered,
 // the next head is loaded into registers while the current one is used).
-// blockIdx.z selects a slice of hps heads of the group; each slice writes its
-// own partial dW (summed later in a fixed order).
+// A slice of hps heads of the group is summed per workgroup; each slice
+// writes its own partial dW (summed later in a fixed order).
+constexpr int DW_DEPTH = 2;  // heads in flight per dW workgroup (3 measured no faster, 4 slower)
+
+template <typename T, int P>
+struct DwLds {
+  static constexpr int XP = P + 16 / sizeof(T);  // row pitch of the staged x rows
+  __attribute__((aligned(16))) T Xs[2][64][XP];
+  __attribute__((aligned(16))) float csJ[2][64];  // diagonal blocks: cs_j, dt_j of the staged head
+  __attribute__((aligned(16))) float dtJ[2][64];
+};
+
 template <typename T, int Q, int P, bool DIAG>
-__global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float* __restrict__ dt,
-                                            const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                            float* __restrict__ dw, const RowMap rm, int H, int G, int K, int hps) {
+__device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* __restrict__ dt,
+                                         const float* __restrict__ cs_g, const T* __restrict__ dy,
+                                         float* __restrict__ dw, const RowMap& rm, int H, int G, int K, int hps,
+                                         int bkg, int nbkg, int slice, int IB, int JB, DwLds<T, P>& sm) {
   constexpr int NTH = 256;
   constexpr int NKP = (P + 31) / 32;
-  constexpr int XP = P + 16 / sizeof(T);    // row pitch of the staged x rows
+  constexpr int XP = DwLds<T, P>::XP;
   constexpr int VN = Vec16<T>::n;
   constexpr int XPIECES = 64 * P / VN;
   constexpr int XPT = (XPIECES + NTH - 1) / NTH;
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T Xs[2][64][XP];
-  __shared__ __attribute__((aligned(16))) float csJ[2][64];   // DIAG: cs_j, dt_j of the staged head
-  __shared__ __attribute__((aligned(16))) float dtJ[2][64];
+  auto& Xs = sm.Xs;
+  auto& csJ = sm.csJ;
+  auto& dtJ = sm.dtJ;
 
-  const int bkg = blockIdx.x;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
-  int IB, JB;
-  if (DIAG) {
-    IB = JB = blockIdx.y;
-  } else {
-    IB = 1;  // enumerate pairs IB > JB: y = IB (IB - 1) / 2 + JB
-    while ((IB + 1) * IB / 2 <= (int)blockIdx.y) ++IB;
-    JB = blockIdx.y - IB * (IB - 1) / 2;
-  }
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
   dy = rows_in(rm, k, dy, rm.dy);
   const int hpg = H / G;
-  const int h0 = g * hpg + blockIdx.z * hps;                  // first head of this slice
-  const int nh = min(hps, hpg - (int)blockIdx.z * hps);       // heads in this slice
+  const int h0 = g * hpg + slice * hps;                       // first head of this slice
+  const int nh = min(hps, hpg - slice * hps);                 // heads in this slice
   const int i0 = 64 * IB, j0 = 64 * JB, ref = j0 + 63;
   const int ia = i0 + 16 * wave + c;                          // this lane's row (A operand)
 
-  // registers of the head in flight
-  V xv[XPT];
-  float xs[XPT];
-  Frag<T> av[NKP];
-  float ascale = 1.0f, jcs = 0.0f, jdt = 0.0f;
-  auto load = [&](int hh) {
-    const int h = h0 + hh;
+  // DW_DEPTH heads in flight, in a ring of register sets: a set holds the raw
+  // loads of one head (x rows, and the step / cumsum values its factors come
+  // from), and the exponentials are taken only when the head is staged or
+  // used, so no load is waited for before its head's turn.  Head indices past
+  // the slice are clamped (a repeated load) so the loads carry no branch.
+  struct HeadRegs {
+    V xv[XPT];
+    float dtv[XPT], csv[XPT];          // off-diagonal: dt_j, cs_j of the staged x rows
+    Frag<T> av[NKP];                   // dy fragments of this wave's rows
+    float cref, cia, jcs, jdt, csi[4];
+  };
+  HeadRegs R[DW_DEPTH];
+  auto load = [&](HeadRegs& R, int hh) {
+    const int h = h0 + min(hh, nh - 1);
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
     const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
 #pragma unroll
@@ -624,61 +633,68 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float
       const int u = threadIdx.x + NTH * n;
       if (XPIECES % NTH == 0 || u < XPIECES) {
         const int r = u / (P / VN);
-        xv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
-        xs[n] = DIAG ? 1.0f : dtb[j0 + r] * __expf(csb[ref] - csb[j0 + r]);
+        R.xv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
+        if (!DIAG) {
+          R.dtv[n] = dtb[j0 + r];
+          R.csv[n] = csb[j0 + r];
+        }
       }
     }
     const T* arow = dy + ((row0 + ia) * H + h) * P;
 #pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], arow, kp * 32, q);
-    if (!DIAG) ascale = __expf(csb[ia] - csb[ref]);
-    if (DIAG && threadIdx.x < 64) {
-      jcs = csb[j0 + threadIdx.x];
-      jdt = dtb[j0 + threadIdx.x];
+    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(R.av[kp], arow, kp * 32, q);
+    if (!DIAG) {
+      R.cref = csb[ref];
+      R.cia = csb[ia];
+    } else {
+      const int jl = threadIdx.x & 63;   // threads 0..63 stage cs_j, dt_j
+      R.jcs = csb[j0 + jl];
+      R.jdt = dtb[j0 + jl];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R.csi[r] = csb[i0 + 16 * wave + 4 * q + r];
     }
   };
-  auto store = [&](int bf) {
+  auto store = [&](const HeadRegs& R, int bf) {
 #pragma unroll
     for (int n = 0; n < XPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (XPIECES % NTH == 0 || u < XPIECES) {
         T* d = &Xs[bf][u / (P / VN)][(u % (P / VN)) * VN];
         if (DIAG) {
-          *reinterpret_cast<V*>(d) = xv[n];
+          *reinterpret_cast<V*>(d) = R.xv[n];
         } else {
+          const float xs = R.dtv[n] * __expf(R.cref - R.csv[n]);
           V w;
 #pragma unroll
-          for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(xv[n][e]) * xs[n]);
+          for (int e = 0; e < VN; ++e) w[e] = from_f<T>(to_f(R.xv[n][e]) * xs);
           *reinterpret_cast<V*>(d) = w;
         }
       }
     }
     if (DIAG && threadIdx.x < 64) {
-      csJ[bf][threadIdx.x] = jcs;
-      dtJ[bf][threadIdx.x] = jdt;
+      csJ[bf][threadIdx.x] = R.jcs;
+      dtJ[bf][threadIdx.x] = R.jdt;
     }
   };
 
   f4 acc[4];
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) acc[tj] = f4{0.f, 0.f, 0.f, 0.f};
-  load(0);
-  store(0);
-  for (int hh = 0; hh < nh; ++hh) {
+  // head hh: its set cur was loaded DW_DEPTH heads earlier; nxt holds head hh + 1
+  auto step = [&](HeadRegs& cur, HeadRegs& nxt, int hh) {
     const int bf = hh & 1;
+    const float ascale = DIAG ? 1.0f : __expf(cur.cia - cur.cref);
     Frag<T> fa[NKP];
 #pragma unroll
     for (int kp = 0; kp < NKP; ++kp)
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) frag_set<T>(fa[kp], s8, DIAG ? frag_get(av[kp], s8) : frag_get(av[kp], s8) * ascale);
+      for (int s8 = 0; s8 < 8; ++s8)
+        frag_set<T>(fa[kp], s8, DIAG ? frag_get(cur.av[kp], s8) : frag_get(cur.av[kp], s8) * ascale);
     float csi[4];
-    if (DIAG) {
-      const float* csb = cs_g + (((int64_t)b * H + h0 + hh) * K + k) * Q;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) csi[r] = csb[i0 + 16 * wave + 4 * q + r];
-    }
+    for (int r = 0; r < 4; ++r) csi[r] = cur.csi[r];
     __syncthreads();  // head hh is in buffer bf; buffer bf ^ 1 is no longer read
-    if (hh + 1 < nh) load(hh + 1);
+    load(cur, hh + DW_DEPTH);
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       if (DIAG && tj > wave) continue;  // strictly above the diagonal: zero
@@ -701,14 +717,48 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float
         }
       }
     }
-    if (hh + 1 < nh) store(bf ^ 1);
+    store(nxt, bf ^ 1);  // head hh + 1 (a repeat past the slice, never read)
+  };
+#pragma unroll
+  for (int d = 0; d < DW_DEPTH; ++d) load(R[d], d);
+  store(R[0], 0);
+  for (int hh = 0; hh < nh; hh += DW_DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DW_DEPTH; ++d)
+      if (hh + d < nh) step(R[d], R[(d + 1) % DW_DEPTH], hh + d);
   }
-  float* o = dw + ((int64_t)blockIdx.z * gridDim.x + bkg) * Q * Q;
+  float* o = dw + ((int64_t)slice * nbkg + bkg) * Q * Q;
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
     const int j = j0 + 16 * tj + c;
 #pragma unroll
     for (int r = 0; r < 4; ++r) o[(int64_t)(i0 + 16 * wave + 4 * q + r) * Q + j] = acc[tj][r];
+  }
+}
+
+// All Q/64 (Q/64 + 1)/2 blocks of every (b, k, g) and head slice in one
+// launch.  Work item = ((b, k, g), slice); the blocks of one item are dealt
+// to workgroups 8 dispatch slots apart, which the round-robin dispatch over
+// the 8 XCDs places on one XCD at about the same time, so the x and dy rows
+// each block re-reads come from that XCD's L2.
+template <typename T, int Q, int P>
+__global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float* __restrict__ dt,
+                                            const float* __restrict__ cs_g, const T* __restrict__ dy,
+                                            float* __restrict__ dw, const RowMap rm, int H, int G, int K, int hps,
+                                            int nbkg, int nitems) {
+  constexpr int NB = Q / 64, NBLK = NB * (NB + 1) / 2;
+  __shared__ DwLds<T, P> sm;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int blk = j % NBLK, item = (j / NBLK) * 8 + xcd;
+  if (item >= nitems) return;  // whole workgroup, before any barrier
+  const int bkg = item % nbkg, slice = item / nbkg;
+  if (blk < NB) {
+    dw_block<T, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, blk, blk, sm);
+  } else {
+    const int y = blk - NB;  // pairs IB > JB: y = IB (IB - 1) / 2 + JB
+    int IB = 1;
+    while ((IB + 1) * IB / 2 <= y) ++IB;
+    dw_block<T, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2, sm);
   }
 }
 
@@ -975,11 +1025,9 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;
   {
     ProbeScope ps(probe, SSD_K_DW, st);
-    const int nb = Q / 64;
-    k_dw<T, Q, P, true><<<dim3(b * K * G, nb, S), dim3(256), 0, st>>>(x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps);
-    if (nb > 1)
-      k_dw<T, Q, P, false><<<dim3(b * K * G, nb * (nb - 1) / 2, S), dim3(256), 0, st>>>(
-          x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps);
+    const int nb = Q / 64, nbkg = b * K * G, nitems = nbkg * S;
+    k_dw<T, Q, P><<<dim3((nitems + 7) / 8 * 8 * (nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps, nbkg, nitems);
   }
   {
     ProbeScope ps(probe, SSD_K_DC, st);
