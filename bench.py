@@ -86,9 +86,10 @@ def kernel_model(s, esz):
         "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
         "state_passing_bwd": (ST4 + STe, 0),
         "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
-        "dw": (2 * X + 2 * CS + DW, 2 * bkh * tri * P),
-        "dc": (X + CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
-        "db": (X + 2 * CS + STe + DW + 2 * BC, 2 * bkh * Q * P * N + 2 * bkg * tri * N),
+        # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in, dW out
+        "dw_heads": (2 * X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
+        "dc_final": (DW + 2 * BC, 2 * bkg * tri * N),
+        "db_final": (DW + 2 * BC, 2 * bkg * tri * N),
         "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
     }
     return m
@@ -280,9 +281,9 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
         "chunk_state_bwd": "k_chunk_state" in name and bwd_flag,
         "state_passing_bwd": "k_state_passing_bwd" in name,
         "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,
-        "dw": "k_dw" in name,
-        "dc": ("k_bc_heads" in name or "k_bc_final" in name) and fwd_flag,
-        "db": ("k_bc_heads" in name or "k_bc_final" in name) and bwd_flag,
+        "dw_heads": "k_dw_heads" in name,
+        "dc_final": "k_bc_final" in name and fwd_flag,
+        "db_final": "k_bc_final" in name and bwd_flag,
         "da_dd": "k_da_dd" in name,
     }
     return rules.get(bench_kernel, False)
@@ -358,8 +359,7 @@ def summarize_stats(csv_path: str, command: str, title: str) -> str:
         short = m.group(1) if m else n.split("(")[0].split("<")[0].replace("void ", "")[:40]
         # the kernels' bool template flag names the variant
         flag = re.search(r"L(b[01])E", n)
-        labels = {"k_chunk_state": ("forward", "backward"), "k_dw": ("off-diagonal blocks", "diagonal blocks"),
-                  "k_bc_heads": ("dC", "dB"), "k_bc_final": ("dC", "dB")}
+        labels = {"k_chunk_state": ("forward", "backward"), "k_bc_final": ("dC", "dB")}
         if flag and short in labels:
             short += f" ({labels[short][int(flag.group(1)[1])]})"
         lines.append(f"| {short} | `{n[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "

@@ -114,9 +114,10 @@ typedef enum {
     SSD_K_CHUNK_STATE_BWD = 5,   /* exp(cs) C^T dy per chunk and head */
     SSD_K_STATE_PASSING_BWD = 6, /* reverse inter-chunk state scan */
     SSD_K_CHUNK_SCAN_BWD = 7,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
-    SSD_K_DW = 8,                /* head-summed masked dY.X^T per chunk and group */
-    SSD_K_DC = 9,                /* dC: head sums per slice, then slice sum + dW.B */
-    SSD_K_DB = 10,               /* dB: head sums per slice, then slice sum + dW^T.C */
+    SSD_K_DW_HEADS = 8,          /* one launch of the group-level head sums: masked dY.X^T (dW) and the
+                                    dC / dB state terms, per chunk, group and head slice */
+    SSD_K_DC_FINAL = 9,          /* dC: slice sum + dW.B */
+    SSD_K_DB_FINAL = 10,         /* dB: slice sum + dW^T.C */
     SSD_K_DA_DD = 11,            /* fixed-order dA / dD reduction */
     SSD_NUM_KERNELS = 12
 } ssd_kernel_id;

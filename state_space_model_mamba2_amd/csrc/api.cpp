@@ -59,11 +59,11 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   o = 0;
   y.dhloc_off = o;  o += align_up(states * 4);
   y.g_off = o;      o += align_up(states * y.esz);
-  // Head slices for the group-level backward kernels (each slice writes an
-  // fp32 partial that is summed in a fixed order): about `target` workgroups
-  // per launch, never finer than one head and never more than kMaxSlices.
-  // Measured at the 2.7B shape (b*K*G*Q/64 = 256): two slices for both is
-  // fastest; more slices cost more in partial sums than the extra parallelism
+  // Head slices of the group-level backward launch (dW and the dC / dB head
+  // sums; each slice writes fp32 partials that are summed in a fixed order):
+  // about `target` workgroups per kind of block, never finer than one head and
+  // never more than kMaxSlices.  Measured at the 2.7B shape
+  // (b*K*G*Q/64 = 256): two slices is fastest; more slices cost more in partial sums than the extra parallelism
   // gains, one slice starves dW.  Small problems (a one-chunk tail) would ask
   // for dozens of slices, whose serial partial sums on few workgroups cost far
   // more than the heads they spread.
@@ -82,10 +82,9 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
     return (hpg + per - 1) / per;
   };
   y.nslice = slices(512);
-  y.nslice_bc = slices(512);
   y.dw_off = o;     o += align_up((size_t)(y.nslice * y.b * y.K * y.G * y.Q * y.Q) * 4);
-  y.dcpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.K * y.Q * y.G * y.N) * 4);
-  y.dbpart_off = o; o += align_up((size_t)(y.nslice_bc * y.b * y.K * y.Q * y.G * y.N) * 4);
+  y.dcpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.K * y.Q * y.G * y.N) * 4);
+  y.dbpart_off = o; o += align_up((size_t)(y.nslice * y.b * y.K * y.Q * y.G * y.N) * 4);
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   const int64_t nsp = scan_bwd_splits((int)y.Q);
@@ -238,7 +237,7 @@ const char* ssd_status_string(ssd_status st) {
 const char* ssd_kernel_name(int32_t k) {
   static const char* names[SSD_NUM_KERNELS] = {
       "chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
-      "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw", "dc", "db", "da_dd"};
+      "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "dc_final", "db_final", "da_dd"};
   if (k < 0 || k >= SSD_NUM_KERNELS) return nullptr;
   return names[k];
 }

@@ -736,35 +736,9 @@ __device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* _
   }
 }
 
-// All Q/64 (Q/64 + 1)/2 blocks of every (b, k, g) and head slice in one
-// launch.  Work item = ((b, k, g), slice); the blocks of one item are dealt
-// to workgroups 8 dispatch slots apart, which the round-robin dispatch over
-// the 8 XCDs places on one XCD at about the same time, so the x and dy rows
-// each block re-reads come from that XCD's L2.
-template <typename T, int Q, int P>
-__global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float* __restrict__ dt,
-                                            const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                            float* __restrict__ dw, const RowMap rm, int H, int G, int K, int hps,
-                                            int nbkg, int nitems) {
-  constexpr int NB = Q / 64, NBLK = NB * (NB + 1) / 2;
-  __shared__ DwLds<T, P> sm;
-  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
-  const int blk = j % NBLK, item = (j / NBLK) * 8 + xcd;
-  if (item >= nitems) return;  // whole workgroup, before any barrier
-  const int bkg = item % nbkg, slice = item / nbkg;
-  if (blk < NB) {
-    dw_block<T, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, blk, blk, sm);
-  } else {
-    const int y = blk - NB;  // pairs IB > JB: y = IB (IB - 1) / 2 + JB
-    int IB = 1;
-    while ((IB + 1) * IB / 2 <= y) ++IB;
-    dw_block<T, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2, sm);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Head sums of dC / dB for one (b, k, g), one 64-row block RB of the chunk
-// and one slice of hps heads (blockIdx.z):
+// and one slice of hps heads:
 //   dC: part[i][n] = sum_{h in slice} exp(cs_i) sum_p dy_i[p] Hin_k[p][n]
 //   dB: part[j][n] = sum_{h in slice} e_j dt_j  sum_p x_j[p]  Gk[p][n]
 // One product per head with K = headdim on the matrix cores.  Each wave
@@ -774,22 +748,28 @@ __global__ __launch_bounds__(256) void k_dw(const T* __restrict__ x, const float
 // head is loaded into registers while the current one is used) and read
 // K-major with the transposing LDS read.  Every slice writes an fp32
 // partial; k_bc_final adds the slices and the dW part.
+template <typename T, int P, int N>
+struct BcLds {
+  static constexpr int SP = N + 16;  // state row pitch (8 mod 16 dwords for N = 64, 128)
+  __attribute__((aligned(16))) T Ss[2][P][SP];
+};
+
 template <typename T, int Q, int P, int N, bool DB>
-__global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const float* __restrict__ dt,
-                                                  const float* __restrict__ cs_g, const T* __restrict__ dy,
-                                                  const T* __restrict__ state, float* __restrict__ out,
-                                                  const RowMap rm, int H, int G, int K, int hps) {
+__device__ __forceinline__ void bc_heads_block(const T* __restrict__ x, const float* __restrict__ dt,
+                                               const float* __restrict__ cs_g, const T* __restrict__ dy,
+                                               const T* __restrict__ state, float* __restrict__ out,
+                                               const RowMap& rm, int H, int G, int K, int hps, int bkg, int nbkg,
+                                               int slice, int RB, BcLds<T, P, N>& sm) {
   constexpr int NTH = 256;
   constexpr int TN = N / 16, NKP = (P + 31) / 32;
   constexpr int VN = Vec16<T>::n;
-  constexpr int SP = N + 16;                 // state row pitch (8 mod 16 dwords for N = 64, 128)
+  constexpr int SP = BcLds<T, P, N>::SP;
   constexpr int SPIECES = P * N / VN;
   constexpr int SPT = (SPIECES + NTH - 1) / NTH;
   static_assert(P == 16 || P % 32 == 0, "headdim");
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T Ss[2][P][SP];
+  auto& Ss = sm.Ss;
 
-  const int bkg = blockIdx.x, RB = blockIdx.y;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
@@ -797,8 +777,8 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
   dy = rows_in(rm, k, dy, rm.dy);
   const int64_t prow0 = ((int64_t)b * K + k) * Q;  // row of the fp32 partials (chunk rows)
   const int hpg = H / G;
-  const int h0 = g * hpg + blockIdx.z * hps;
-  const int nh = min(hps, hpg - (int)blockIdx.z * hps);
+  const int h0 = g * hpg + slice * hps;
+  const int nh = min(hps, hpg - slice * hps);
   const int i = 64 * RB + 16 * wave + c;     // this lane's row (A operand)
   const T* U = DB ? x : dy;
 
@@ -855,7 +835,7 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
     }
     if (hh + 1 < nh) store(bf ^ 1);
   }
-  float* o = out + (int64_t)blockIdx.z * gridDim.x * Q * N;  // slice stride b*K*G*Q*N
+  float* o = out + (int64_t)slice * nbkg * Q * N;  // slice stride b*K*G*Q*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -863,6 +843,47 @@ __global__ __launch_bounds__(256) void k_bc_heads(const T* __restrict__ x, const
       const int row = 64 * RB + 16 * wave + 4 * q + r;
       o[((prow0 + row) * G + g) * N + 16 * tn + c] = acc[tn][r];
     }
+  }
+}
+
+// Every group-level head sum of the backward in one launch: per work item
+// ((b, k, g), head slice) the Q/64 row blocks of the dC and of the dB head
+// sums and the Q/64 (Q/64 + 1)/2 blocks of dW.  All of them read the same
+// dy and x rows of the item's heads (and walk the heads in the same order),
+// and the blocks of one item are dealt to workgroups 8 dispatch slots apart,
+// which the round-robin dispatch over the 8 XCDs places on one XCD at about
+// the same time: the rows come from HBM once and from that XCD's L2 for the
+// other blocks.  The heavier head-sum blocks come first in an item.
+template <typename T, int Q, int P, int N>
+__global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const float* __restrict__ dt,
+                                                  const float* __restrict__ cs_g, const T* __restrict__ dy,
+                                                  const T* __restrict__ hin, const T* __restrict__ gst,
+                                                  float* __restrict__ dw, float* __restrict__ dcpart,
+                                                  float* __restrict__ dbpart, const RowMap rm, int H, int G, int K,
+                                                  int hps, int nbkg, int nitems) {
+  constexpr int NB = Q / 64, NBLK = 2 * NB + NB * (NB + 1) / 2;
+  constexpr size_t LDS = sizeof(DwLds<T, P>) > sizeof(BcLds<T, P, N>) ? sizeof(DwLds<T, P>) : sizeof(BcLds<T, P, N>);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int blk = j % NBLK, item = (j / NBLK) * 8 + xcd;
+  if (item >= nitems) return;  // whole workgroup, before any barrier
+  const int bkg = item % nbkg, slice = item / nbkg;
+  if (blk < NB) {
+    bc_heads_block<T, Q, P, N, false>(x, dt, cs_g, dy, hin, dcpart, rm, H, G, K, hps, bkg, nbkg, slice, blk,
+                                      *reinterpret_cast<BcLds<T, P, N>*>(smem));
+  } else if (blk < 2 * NB) {
+    bc_heads_block<T, Q, P, N, true>(x, dt, cs_g, dy, gst, dbpart, rm, H, G, K, hps, bkg, nbkg, slice, blk - NB,
+                                     *reinterpret_cast<BcLds<T, P, N>*>(smem));
+  } else if (blk < 3 * NB) {
+    const int d = blk - 2 * NB;
+    dw_block<T, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, d, d,
+                            *reinterpret_cast<DwLds<T, P>*>(smem));
+  } else {
+    const int y = blk - 3 * NB;  // pairs IB > JB: y = IB (IB - 1) / 2 + JB
+    int IB = 1;
+    while ((IB + 1) * IB / 2 <= y) ++IB;
+    dw_block<T, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2,
+                             *reinterpret_cast<DwLds<T, P>*>(smem));
   }
 }
 
@@ -1022,26 +1043,22 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
-  const int Sb = (int)lay.nslice_bc, hpsb = (hpg + Sb - 1) / Sb;
+  const int nbkg = b * K * G;
   {
-    ProbeScope ps(probe, SSD_K_DW, st);
-    const int nb = Q / 64, nbkg = b * K * G, nitems = nbkg * S;
-    k_dw<T, Q, P><<<dim3((nitems + 7) / 8 * 8 * (nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, a.dw, a.rows, H, G, K, hps, nbkg, nitems);
+    ProbeScope ps(probe, SSD_K_DW_HEADS, st);
+    const int nb = Q / 64, nitems = nbkg * S;
+    k_dw_heads<T, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
+        x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems);
   }
   {
-    ProbeScope ps(probe, SSD_K_DC, st);
-    k_bc_heads<T, Q, P, N, false><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, a.dcpart, a.rows, H, G, K, hpsb);
-    k_bc_final<T, Q, N, false, kBcParts<N>><<<dim3(b * K * G, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
-        a.dcpart, a.dw, B, static_cast<T*>(a.dC), a.rows, G, K, Sb, S);
+    ProbeScope ps(probe, SSD_K_DC_FINAL, st);
+    k_bc_final<T, Q, N, false, kBcParts<N>><<<dim3(nbkg, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
+        a.dcpart, a.dw, B, static_cast<T*>(a.dC), a.rows, G, K, S, S);
   }
   {
-    ProbeScope ps(probe, SSD_K_DB, st);
-    k_bc_heads<T, Q, P, N, true><<<dim3(b * K * G, Q / 64, Sb), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, gst, a.dbpart, a.rows, H, G, K, hpsb);
-    k_bc_final<T, Q, N, true, kBcParts<N>><<<dim3(b * K * G, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
-        a.dbpart, a.dw, C, static_cast<T*>(a.dB), a.rows, G, K, Sb, S);
+    ProbeScope ps(probe, SSD_K_DB_FINAL, st);
+    k_bc_final<T, Q, N, true, kBcParts<N>><<<dim3(nbkg, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
+        a.dbpart, a.dw, C, static_cast<T*>(a.dB), a.rows, G, K, S, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);

@@ -23,8 +23,7 @@ struct Layout {
   // backward scratch
   size_t dhloc_off, g_off, dw_off, dcpart_off, dbpart_off, dapart_off, ddpart_off, dlpart_off, dlscal_off,
       bwd_bytes;
-  int64_t nslice;     // head slices of the dW kernel
-  int64_t nslice_bc;  // head slices of the dB / dC head sums
+  int64_t nslice;     // head slices of the dW / dC / dB head sums
   int64_t wtiles;  // 16x16 lower-triangle tiles per (batch, chunk, group)
 };
 
@@ -75,8 +74,8 @@ struct BwdArgs {
   float* dhloc;    // [b][K][H][P][N]
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
-  float* dcpart;   // [nslice_bc][b][K][Q][G][N] fp32 partials of dC (chunk rows)
-  float* dbpart;   // [nslice_bc][b][K][Q][G][N] fp32 partials of dB (chunk rows)
+  float* dcpart;   // [nslice][b][K][Q][G][N] fp32 partials of dC (chunk rows)
+  float* dbpart;   // [nslice][b][K][Q][G][N] fp32 partials of dB (chunk rows)
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
   float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
