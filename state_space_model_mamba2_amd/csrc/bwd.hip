@@ -38,7 +38,8 @@ namespace ssd {
 // (which cancels exactly between the two) is left out of both.
 // The workgroups of one (b, k, h) are 8 dispatch slots apart, so the
 // round-robin dispatch over the 8 XCDs runs them on one XCD (one L2) at
-// about the same time.
+// about the same time, and consecutive heads of a chunk (which share its C
+// and B rows and C.B^T tiles) run on the same XCD.
 template <typename T, int Q, int P, int N>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
@@ -80,9 +81,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   __shared__ float rowacc[NW][Q];
   __shared__ float red[2 * NW];
 
-  // (b, k, h) item and column split of this workgroup
-  const int xcd = blockIdx.x % 8, grp = blockIdx.x / 8;
-  const int bkh = (grp / NSPLIT) * 8 + xcd, split = grp % NSPLIT;
+  // (b, k, h) item and column split of this workgroup: the XCD-aware item
+  // map (consecutive heads of a chunk on one XCD) over groups of NSPLIT * 8
+  // workgroups, in which the splits of an item are 8 slots apart (one XCD)
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int split = slot % NSPLIT;
+  const int bkh = xcd_item(kXcds * (slot / NSPLIT) + xcd, nitems);
   if (bkh >= nitems) return;  // whole workgroup, before any barrier
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
@@ -1036,8 +1040,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     const int nitems = b * K * H;
-    const int groups = (nitems + 7) / 8;
-    k_chunk_scan_bwd<T, Q, P, N><<<dim3(groups * 8 * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
+    k_chunk_scan_bwd<T, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     k_dl_assemble<T, Q><<<dim3(b * K * ((H + 15) / 16)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus);

@@ -228,6 +228,18 @@ __device__ __forceinline__ void stage_rows(TD* __restrict__ dst, int dpitch, con
   }
 }
 
+// ---- XCD-aware work mapping ------------------------------------------------------
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (workgroup i
+// on XCD i % 8), and each XCD has its own L2.  Workgroup i takes item
+// (i % 8) * ceil(n / 8) + i / 8, so each XCD walks one contiguous run of
+// items in order: consecutive items (the heads of one chunk, which read that
+// chunk's B / C rows and C.B^T tiles) share one L2 instead of fetching the
+// shared rows into all eight.  The grid is xcd_grid(n) workgroups; the
+// mapped index is >= n for the padding workgroups of the last run.
+constexpr int kXcds = 8;
+__host__ __device__ constexpr int xcd_grid(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
+__device__ __forceinline__ int xcd_item(int bid, int n) { return (bid % kXcds) * ((n + kXcds - 1) / kXcds) + bid / kXcds; }
+
 // ---- wave-level scans and reductions (wave64) -------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
                                                            const float* __restrict__ cs_g, const float* __restrict__ Dp,
                                                            const TI* __restrict__ C, const T* __restrict__ hin,
                                                            const T* __restrict__ wt, T* __restrict__ y,
-                                                           const RowMap rm, int H, int G, int K) {
+                                                           const RowMap rm, int H, int G, int K, int nitems) {
   constexpr int NTH = 256, NW = 4;
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32, NJ2 = NT / 2;
@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
   __shared__ __attribute__((aligned(16))) float dts[Q];
   __shared__ __attribute__((aligned(16))) float bfac[Q];  // dt_j exp(cs_r - cs_j), r = last token of j's 32-token step
 
-  const int bkh = blockIdx.x;
+  const int bkh = xcd_item(blockIdx.x, nitems);
+  if (bkh >= nitems) return;  // whole workgroup, before any barrier
   const int h = bkh % H, bk = bkh / H, k = bk % K, b = bk / K;
   const int g = h / (H / G);
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
@@ -251,8 +252,8 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
-    k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(b * K * H), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K);
+    k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
+        x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, b * K * H);
   }
 }
 

@@ -193,7 +193,8 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const TI* __restrict__ B, con
 template <typename T, typename TI, int Q, int P, int N, bool BWD, int HPW>
 __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
-                                                     float* __restrict__ out, const RowMap rm, int H, int G, int K) {
+                                                     float* __restrict__ out, const RowMap rm, int H, int G, int K,
+                                                     int nitems) {
   constexpr int NTH = 256;
   constexpr int KB = 64;                           // tokens per block
   constexpr int NB = Q / KB;
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
   __shared__ __attribute__((aligned(16))) T Us[2][HPW][KB][UP];
   __shared__ __attribute__((aligned(16))) T Vs[2][KB][VP];
 
-  const int bkhp = blockIdx.x;
+  const int bkhp = xcd_item(blockIdx.x, nitems);
+  if (bkhp >= nitems) return;  // whole workgroup, before any barrier
   const int HP = H / HPW;
   const int hp = bkhp % HP, bk = bkhp / HP, k = bk % K, b = bk / K;
   const int h0 = hp * HPW;                         // HPW consecutive heads, one group
@@ -321,9 +323,11 @@ template <typename T, typename TI, int Q, int P, int N, bool BWD>
 void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, float* out, const RowMap& rm,
                         int b, int H, int G, int K, hipStream_t st) {
   if ((H / G) % 2 == 0)
-    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(b * K * H / 2), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K);
+    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K,
+                                                                                            b * K * H / 2);
   else
-    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(b * K * H), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K);
+    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K,
+                                                                                        b * K * H);
 }
 
 // ---------------------------------------------------------------------------
