@@ -395,13 +395,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     for (int sl = 0; sl < NSLOT; ++sl)
       if ((Js[sl] >> 1) == s) diag_pair(sl);
 
+    {
+      // the slab's 32 row totals of this wave: lane (q, c) ends with row
+      // rb + 16 half + 4q + r, half = c / 8, r = (c / 2) % 4 (lanes c, c ^ 1 alike)
+      float v8[8];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = sum16(rowtot[half][r]);
-        if (c == r) rowacc[wave][rb + 16 * half + 4 * q + r] = v;
-      }
+        for (int r = 0; r < 4; ++r) v8[4 * half + r] = rowtot[half][r];
+      rowacc[wave][rb + 16 * (c >> 3) + 4 * q + ((c >> 1) & 3)] = sum16_spread8(v8);
     }
     // next slab into the other buffer (its last readers passed the previous barrier)
     if (it + 1 < NS) slab_store(bf ^ 1);

@@ -268,15 +268,25 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-// Sum over the 16 lanes sharing lane / 16 (result valid in every lane):
-// neighbours inside quads, the two pairs of each quad (quad_perm), the two
-// quads of each half-row (row_half_mirror), the two half-rows (row_mirror).
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
+// Eight sums over each row of 16 lanes at once: every value v[0..7] is
+// summed over the 16 lanes of the row, and lane c keeps the total of value
+// 4 b3 + 2 b2 + b1 (b3, b2, b1 = bits 3, 2, 1 of c; lanes c and c ^ 1 hold the
+// same total).  A butterfly over the lane partners c ^ 15, c ^ 7, c ^ 3, c ^ 1
+// (row mirror, half-row mirror, two quad permutations) in which each exchange
+// halves the values a lane keeps: the lane whose bit is set keeps the upper
+// half and sends the lower, its partner the reverse, so 7 exchanges do the
+// work of 8 separate 4-step row sums.
+__device__ __forceinline__ float sum16_spread8(const float (&v)[8]) {
+  const int c = threadIdx.x & 15;
+  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2;
+  float w[4], z[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = (b3 ? v[k + 4] : v[k]) + dpp_mov<0x140>(b3 ? v[k] : v[k + 4]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) z[k] = (b2 ? w[k + 2] : w[k]) + dpp_mov<0x141>(b2 ? w[k] : w[k + 2]);
+  float u = (b1 ? z[1] : z[0]) + dpp_mov<0x1B>(b1 ? z[0] : z[1]);  // quad_perm [3, 2, 1, 0]
+  u += dpp_mov<0xB1>(u);                                             // quad_perm [1, 0, 3, 2]
+  return u;
 }
 // Sum over the 4 lanes sharing lane % 16 (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float sum_q(float v) {
