@@ -78,6 +78,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   __shared__ __attribute__((aligned(16))) T Ws[2][WT * 256];        // slab C.B^T tiles (lane order)
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
+  __shared__ __attribute__((aligned(16))) float ecs[Q];    // exp(cs_i)
+  __shared__ __attribute__((aligned(16))) float eslab[Q];  // exp(cs_i - cs_rb), rb = first row of i's slab
   __shared__ float rowacc[NW][Q];
   __shared__ float red[2 * NW];
 
@@ -196,13 +198,19 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       frag_load_k<N>(bfr[ks][sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
   }
 
-  // LDS stores of the per-token scalars (their loads were issued first)
+  // LDS stores of the per-token scalars (their loads were issued first) and
+  // the row factors every slab uses, formed once here instead of by every
+  // lane of a 16-lane group in every slab
+  static_assert(SR == 32 && kWave % SR == 0 && NTH % SR == 0, "a slab's first row sits in the same wave");
 #pragma unroll
   for (int n = 0; n < QPT; ++n) {
     const int i = threadIdx.x + NTH * n;
+    const float csr = __shfl(csv[n], l & ~(SR - 1), kWave);  // cs of the first row of i's slab
     if (Q % NTH == 0 || i < Q) {
       cs[i] = csv[n];
       dts[i] = dtv[n];
+      ecs[i] = __expf(csv[n]);
+      eslab[i] = __expf(csv[n] - csr);
     }
   }
 
@@ -282,11 +290,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         frag_load_k<N>(fa, &Cs[bf][16 * half + c][0], ks * 32 + 8 * q);
         mma(acc, fa, hf[ks]);
       }
-      const int i0 = rb + 16 * half + 4 * q;
-      const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
+      const f4 ei = *reinterpret_cast<const f4*>(&ecs[rb + 16 * half + 4 * q]);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        rowtot[half][r] += __expf(csi[r]) * (acc[r] * to_f(DY[bf][16 * half + 4 * q + r][16 * tw + c]));
+        rowtot[half][r] += ei[r] * (acc[r] * to_f(DY[bf][16 * half + 4 * q + r][16 * tw + c]));
     }
 
     // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
@@ -301,13 +308,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     //   Lam_ij = exp(cs_i - cs_rb) exp(cs_rb - cs_j),  both factors <= 1
     // (cs does not increase along the chunk).  Tiles J = 2s, 2s + 1 hold the
     // diagonal and take the masked direct form.
-    float arow[2][4];                        // exp(cs_i - cs_rb), rows of this lane
+    f4 arow[2];                              // exp(cs_i - cs_rb), rows of this lane
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const f4 csi = *reinterpret_cast<const f4*>(&cs[rb + 16 * half + 4 * q]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) arow[half][r] = __expf(csi[r] - cs[rb]);
-    }
+    for (int half = 0; half < 2; ++half) arow[half] = *reinterpret_cast<const f4*>(&eslab[rb + 16 * half + 4 * q]);
     auto full_pair = [&](int sl) {
       const int cj = 16 * Js[sl] + c;
       const float bj = __expf(cs[rb] - cs[cj]);
