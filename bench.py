@@ -88,8 +88,7 @@ def kernel_model(s, esz):
         "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
         # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in, dW out
         "dw_heads": (2 * X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
-        "dc_final": (DW + 2 * BC, 2 * bkg * tri * N),
-        "db_final": (DW + 2 * BC, 2 * bkg * tri * N),
+        "bc_final": (DW + 4 * BC, 4 * bkg * tri * N),  # dC and dB: dW, B, C in; dC, dB out
         "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
     }
     return m
@@ -282,8 +281,7 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
         "state_passing_bwd": "k_state_passing_bwd" in name,
         "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,
         "dw_heads": "k_dw_heads" in name,
-        "dc_final": "k_bc_final" in name and fwd_flag,
-        "db_final": "k_bc_final" in name and bwd_flag,
+        "bc_final": "k_bc_final" in name,
         "da_dd": "k_da_dd" in name,
     }
     return rules.get(bench_kernel, False)
@@ -359,7 +357,7 @@ def summarize_stats(csv_path: str, command: str, title: str) -> str:
         short = m.group(1) if m else n.split("(")[0].split("<")[0].replace("void ", "")[:40]
         # the kernels' bool template flag names the variant
         flag = re.search(r"L(b[01])E", n)
-        labels = {"k_chunk_state": ("forward", "backward"), "k_bc_final": ("dC", "dB")}
+        labels = {"k_chunk_state": ("forward", "backward")}
         if flag and short in labels:
             short += f" ({labels[short][int(flag.group(1)[1])]})"
         lines.append(f"| {short} | `{n[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "

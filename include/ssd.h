@@ -116,10 +116,9 @@ typedef enum {
     SSD_K_CHUNK_SCAN_BWD = 7,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
     SSD_K_DW_HEADS = 8,          /* one launch of the group-level head sums: masked dY.X^T (dW) and the
                                     dC / dB state terms, per chunk, group and head slice */
-    SSD_K_DC_FINAL = 9,          /* dC: slice sum + dW.B */
-    SSD_K_DB_FINAL = 10,         /* dB: slice sum + dW^T.C */
-    SSD_K_DA_DD = 11,            /* fixed-order dA / dD reduction */
-    SSD_NUM_KERNELS = 12
+    SSD_K_BC_FINAL = 9,          /* dC and dB in one launch: slice sums + dW.B and dW^T.C */
+    SSD_K_DA_DD = 10,            /* fixed-order dA / dD reduction */
+    SSD_NUM_KERNELS = 11
 } ssd_kernel_id;
 
 /* Optional timing hook: when passed to ssd_fwd/ssd_bwd and `kernel` names a

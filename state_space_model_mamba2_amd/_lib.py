@@ -12,7 +12,7 @@ SSD_F32, SSD_BF16, SSD_FP8 = 0, 1, 2
 SSD_DT_SOFTPLUS = 1
 
 KERNELS = ["chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
-           "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "dc_final", "db_final", "da_dd"]
+           "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "bc_final", "da_dd"]
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
 
 

@@ -904,27 +904,36 @@ __global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const
 // 64-token blocks: the dW block (converted to the storage type) and the B
 // (or C) rows are staged row-major in LDS; dC reads dW rows directly, dB reads
 // them K-major, and B / C are read K-major (transposing LDS read).
-// blockIdx.z takes one of NH parts of the dstate columns (more workgroups for
-// a launch that has only b K G (Q / 64) row blocks); each part stages its
-// own B / C columns and the whole dW block.
+// A block takes one of NH parts of the dstate columns (more workgroups for a
+// launch that has only b K G (Q / 64) row blocks); each part stages its own
+// B / C columns and the whole dW block.
+template <typename T, int Q, int N, int NH>
+struct BcFinalLds {
+  static constexpr int NP = N / NH;
+  static constexpr int WP = 64 + 16;         // row pitches (8 mod 16 dwords)
+  static constexpr int MP = NP + ((24 - (NP * (int)sizeof(T) / 4) % 16) % 16) * 4 / (int)sizeof(T);
+  __attribute__((aligned(16))) T Wb[64][WP];
+  __attribute__((aligned(16))) T Ms[64][MP];
+};
+
 template <typename T, int Q, int N, bool DB, int NH>
-__global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part, const float* __restrict__ dw,
-                                                  const T* __restrict__ M, T* __restrict__ out, const RowMap rm,
-                                                  int G, int K, int nslice, int nslice_dw) {
+__device__ __forceinline__ void bc_final_block(const float* __restrict__ part, const float* __restrict__ dw,
+                                               const T* __restrict__ M, T* __restrict__ out, const RowMap& rm,
+                                               int G, int K, int nslice, int nslice_dw, int bkg, int nbkg, int RB,
+                                               int zpart, BcFinalLds<T, Q, N, NH>& sm) {
   constexpr int NTH = 256;
   constexpr int NP = N / NH;                 // dstate columns of this part
   constexpr int TN = NP / 16, NB = Q / 64;
   constexpr int VN = Vec16<T>::n;
-  constexpr int WP = 64 + 16;                // row pitches (8 mod 16 dwords)
-  constexpr int MP = NP + ((24 - (NP * (int)sizeof(T) / 4) % 16) % 16) * 4 / (int)sizeof(T);
+  constexpr int WP = BcFinalLds<T, Q, N, NH>::WP, MP = BcFinalLds<T, Q, N, NH>::MP;
   constexpr int MPIECES = 64 * NP / VN;
   constexpr int MPT = (MPIECES + NTH - 1) / NTH;
   static_assert(N % NH == 0 && NP % 16 == 0, "dstate parts");
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T Wb[64][WP];
-  __shared__ __attribute__((aligned(16))) T Ms[64][MP];
+  auto& Wb = sm.Wb;
+  auto& Ms = sm.Ms;
 
-  const int bkg = blockIdx.x, RB = blockIdx.y, n0 = NP * blockIdx.z;
+  const int n0 = NP * zpart;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
   const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
@@ -932,7 +941,7 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
   out = rows_out(rm, k, out, DB ? rm.dB : rm.dC);
   const int64_t prow0 = ((int64_t)b * K + k) * Q;  // row of the fp32 partials (chunk rows)
   const int r0 = 64 * RB;
-  const int64_t dws = (int64_t)gridDim.x * Q * Q;  // dW slice stride
+  const int64_t dws = (int64_t)nbkg * Q * Q;  // dW slice stride
   const float* dwb = dw + (int64_t)bkg * Q * Q;
 
   f4 acc[TN];
@@ -978,7 +987,7 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
     }
     __syncthreads();
   }
-  const int64_t ps = (int64_t)gridDim.x * Q * N;  // head-slice partial stride b*K*G*Q*N
+  const int64_t ps = (int64_t)nbkg * Q * N;  // head-slice partial stride b*K*G*Q*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
@@ -990,6 +999,23 @@ __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ part
       out[((row0 + rr) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
     }
   }
+}
+
+// dC and dB in one launch (both read the same dW blocks): blockIdx.z < NH
+// takes dstate part z of dC, the rest the parts of dB.
+template <typename T, int Q, int N, int NH>
+__global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ dcpart, const float* __restrict__ dbpart,
+                                                  const float* __restrict__ dw, const T* __restrict__ B,
+                                                  const T* __restrict__ C, T* __restrict__ dC, T* __restrict__ dB,
+                                                  const RowMap rm, int G, int K, int nslice) {
+  __shared__ BcFinalLds<T, Q, N, NH> sm;
+  const int z = blockIdx.z;
+  if (z < NH)
+    bc_final_block<T, Q, N, false, NH>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
+                                       z, sm);
+  else
+    bc_final_block<T, Q, N, true, NH>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
+                                      z - NH, sm);
 }
 
 // Fixed-order sums of the per-(b, k) partials (dA, dD and, when requested,
@@ -1059,14 +1085,9 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
         x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems);
   }
   {
-    ProbeScope ps(probe, SSD_K_DC_FINAL, st);
-    k_bc_final<T, Q, N, false, kBcParts<N>><<<dim3(nbkg, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
-        a.dcpart, a.dw, B, static_cast<T*>(a.dC), a.rows, G, K, S, S);
-  }
-  {
-    ProbeScope ps(probe, SSD_K_DB_FINAL, st);
-    k_bc_final<T, Q, N, true, kBcParts<N>><<<dim3(nbkg, Q / 64, kBcParts<N>), dim3(256), 0, st>>>(
-        a.dbpart, a.dw, C, static_cast<T*>(a.dB), a.rows, G, K, S, S);
+    ProbeScope ps(probe, SSD_K_BC_FINAL, st);
+    k_bc_final<T, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
+        a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
