@@ -78,8 +78,8 @@ def kernel_model(s, esz):
     tri = Q * (Q + 1) // 2
     bkh, bkg = b * K * H, b * K * G
     m = {
-        "chunk_cumsum": (DT + 2 * CS, 0),                 # dt in; cs and the float32 step out
-        "bmm_fwd": (2 * BC + 2 * WT, 4 * bkg * tri * N),  # both lane orders
+        # dt in, cs and the float32 step out; B, C in, C.B^T tiles in both lane orders out
+        "cumsum_bmm": (DT + 2 * CS + 2 * BC + 2 * WT, 4 * bkg * tri * N),
         "chunk_state": (XI + BC + 2 * CS + ST4, 2 * bkh * Q * P * N),
         "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
         "chunk_scan": (XI + X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
@@ -154,7 +154,7 @@ def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
     from state_space_model_mamba2_amd import _lib
     import torch
     out = {}
-    fwd_ids = range(0, 5)
+    fwd_ids = range(0, _lib.N_FWD_KERNELS)
     for kid, name in enumerate(_lib.KERNELS):
         if dev.get("fwd_only", False) and kid not in fwd_ids:
             continue
@@ -272,8 +272,7 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
     fwd_flag = "Lb0E" in name or "false>" in name
     bwd_flag = "Lb1E" in name or "true>" in name
     rules = {
-        "chunk_cumsum": "k_chunk_cumsum" in name,
-        "bmm_fwd": "k_bmm_tiles" in name,
+        "cumsum_bmm": "k_cumsum_bmm" in name,
         "chunk_state": "k_chunk_state" in name and fwd_flag,
         "state_passing": "k_state_passing_fwd" in name,
         "chunk_scan": "k_chunk_scan_fwd" in name,
@@ -557,7 +556,7 @@ def main():
     else:
         breakdown, dom = {}, args.profile_kernel
     dom_id = _lib.KERNEL_ID[dom]
-    is_fwd = dom_id < 5
+    is_fwd = dom_id < _lib.N_FWD_KERNELS
 
     # Timed region: exactly `steps` steps; the dominant kernel is bracketed by events in each.
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]

@@ -106,19 +106,19 @@ typedef struct {
 
 /* Kernel identifiers, for timing one kernel with an ssd_probe. */
 typedef enum {
-    SSD_K_CHUNK_CUMSUM = 0,      /* per-chunk inclusive cumsum of dt*A */
-    SSD_K_BMM_FWD = 1,           /* C.B^T per chunk and group, in the forward and the backward lane order */
-    SSD_K_CHUNK_STATE = 2,       /* decay-weighted B^T x per chunk and head */
-    SSD_K_STATE_PASSING = 3,     /* sequential inter-chunk state scan */
-    SSD_K_CHUNK_SCAN = 4,        /* intra-chunk masked product + state-to-output + D x */
-    SSD_K_CHUNK_STATE_BWD = 5,   /* exp(cs) C^T dy per chunk and head */
-    SSD_K_STATE_PASSING_BWD = 6, /* reverse inter-chunk state scan */
-    SSD_K_CHUNK_SCAN_BWD = 7,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
-    SSD_K_DW_HEADS = 8,          /* one launch of the group-level head sums: masked dY.X^T (dW) and the
+    SSD_K_CUMSUM_BMM = 0,        /* one launch: per-chunk inclusive cumsum of dt*A, and C.B^T per chunk and
+                                    group in the forward and the backward lane order */
+    SSD_K_CHUNK_STATE = 1,       /* decay-weighted B^T x per chunk and head */
+    SSD_K_STATE_PASSING = 2,     /* sequential inter-chunk state scan */
+    SSD_K_CHUNK_SCAN = 3,        /* intra-chunk masked product + state-to-output + D x */
+    SSD_K_CHUNK_STATE_BWD = 4,   /* exp(cs) C^T dy per chunk and head */
+    SSD_K_STATE_PASSING_BWD = 5, /* reverse inter-chunk state scan */
+    SSD_K_CHUNK_SCAN_BWD = 6,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
+    SSD_K_DW_HEADS = 7,          /* one launch of the group-level head sums: masked dY.X^T (dW) and the
                                     dC / dB state terms, per chunk, group and head slice */
-    SSD_K_BC_FINAL = 9,          /* dC and dB in one launch: slice sums + dW.B and dW^T.C */
-    SSD_K_DA_DD = 10,            /* fixed-order dA / dD reduction */
-    SSD_NUM_KERNELS = 11
+    SSD_K_BC_FINAL = 8,          /* dC and dB in one launch: slice sums + dW.B and dW^T.C */
+    SSD_K_DA_DD = 9,             /* fixed-order dA / dD reduction */
+    SSD_NUM_KERNELS = 10
 } ssd_kernel_id;
 
 /* Optional timing hook: when passed to ssd_fwd/ssd_bwd and `kernel` names a

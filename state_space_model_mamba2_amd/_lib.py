@@ -11,9 +11,10 @@ SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ER
 SSD_F32, SSD_BF16, SSD_FP8 = 0, 1, 2
 SSD_DT_SOFTPLUS = 1
 
-KERNELS = ["chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
+KERNELS = ["cumsum_bmm", "chunk_state", "state_passing", "chunk_scan",
            "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "bc_final", "da_dd"]
 KERNEL_ID = {n: i for i, n in enumerate(KERNELS)}
+N_FWD_KERNELS = KERNELS.index("chunk_state_bwd")  # ids below this are launched by ssd_fwd, the rest by ssd_bwd
 
 
 class Shape(ctypes.Structure):

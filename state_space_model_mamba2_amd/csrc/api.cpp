@@ -236,7 +236,7 @@ const char* ssd_status_string(ssd_status st) {
 
 const char* ssd_kernel_name(int32_t k) {
   static const char* names[SSD_NUM_KERNELS] = {
-      "chunk_cumsum", "bmm_fwd", "chunk_state", "state_passing", "chunk_scan",
+      "cumsum_bmm", "chunk_state", "state_passing", "chunk_scan",
       "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "bc_final", "da_dd"};
   if (k < 0 || k >= SSD_NUM_KERNELS) return nullptr;
   return names[k];

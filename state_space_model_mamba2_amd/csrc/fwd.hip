@@ -231,15 +231,12 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   T* hin = static_cast<T*>(a.hin);
   T* wt = static_cast<T*>(a.wt);
   {
-    ProbeScope ps(probe, SSD_K_CHUNK_CUMSUM, st);
-    k_chunk_cumsum<T, Q><<<dim3(b * H * K), dim3(64), 0, st>>>(
-        static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, a.rows, H, K, a.softplus);
-  }
-  {
-    ProbeScope ps(probe, SSD_K_BMM_FWD, st);
+    ProbeScope ps(probe, SSD_K_CUMSUM_BMM, st);
     constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
-    k_bmm_tiles<T, TI, Q, N><<<dim3(b * K * G, (TILES + 3) / 4), dim3(256), 0, st>>>(
-        B, C, wt, static_cast<T*>(a.wtb), a.rows, G, K);
+    const int nbkg = b * K * G, nbhk = b * H * K;
+    k_cumsum_bmm<T, TI, Q, N><<<dim3(nbkg * ((TILES + 3) / 4) + (nbhk + 3) / 4), dim3(256), 0, st>>>(
+        static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, static_cast<T*>(a.wtb), a.rows, H, G,
+        K, a.softplus, nbkg, nbhk);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);

@@ -71,14 +71,13 @@ __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 
 // widened or, with softplus set (dt then holds the raw step),
 // softplus(dt + dt_bias[h]) = log(1 + e^z) (z itself above 20).
 template <typename T, int Q>
-__global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, const float* __restrict__ A,
-                                                     const float* __restrict__ dt_bias, float* __restrict__ dt_out,
-                                                     float* __restrict__ cs, const RowMap rm, int H, int K,
-                                                     int softplus) {
+__device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, const float* __restrict__ A,
+                                                  const float* __restrict__ dt_bias, float* __restrict__ dt_out,
+                                                  float* __restrict__ cs, const RowMap& rm, int H, int K, int softplus,
+                                                  int bhk) {
   constexpr int TPL = Q / kWave;
-  const int bhk = blockIdx.x;
   const int k = bhk % K, bh = bhk / K, h = bh % H, b = bh / H;
-  const int l = threadIdx.x;
+  const int l = lane_id();
   const bool last = k == rm.kf;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   const T* src = rows_in(rm, k, dt, rm.dt);
@@ -121,17 +120,13 @@ __global__ __launch_bounds__(64) void k_chunk_cumsum(const T* __restrict__ dt, c
 // the bf16 one with one byte per K-value (checked on gfx950: OCP E4M3
 // operands, lane (q, c) supplies row c, K-values 8q .. 8q + 7).
 template <typename T, typename TI, int Q, int N>
-__global__ __launch_bounds__(256) void k_bmm_tiles(const TI* __restrict__ B, const TI* __restrict__ C,
-                                                   T* __restrict__ wf, T* __restrict__ wb, const RowMap rm, int G,
-                                                   int K) {
+__device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI* __restrict__ C, T* __restrict__ wf,
+                                              T* __restrict__ wb, const RowMap& rm, int G, int K, int bkg, int idx) {
   constexpr int NT = Q / 16;
   constexpr int TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32;
-  const int bkg = blockIdx.x;
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
-  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
-  const int idx = blockIdx.y * 4 + wave;
-  if (idx >= TILES) return;  // whole wave; no barrier in this kernel
+  const int l = lane_id(), q = l >> 4, c = l & 15;
   int I = 0;
   while ((I + 1) * (I + 2) / 2 <= idx) ++I;
   const int J = idx - I * (I + 1) / 2;
@@ -176,6 +171,30 @@ __global__ __launch_bounds__(256) void k_bmm_tiles(const TI* __restrict__ B, con
   const int64_t o = ((int64_t)bkg * TILES + idx) * 256 + l * 4;
   *reinterpret_cast<typename Vec4<T>::type*>(wf + o) = vf;
   *reinterpret_cast<typename Vec4<T>::type*>(wb + o) = vb;
+}
+
+// The two independent first steps of the forward in one launch, one wave
+// per work item and no barrier: workgroups [0, nbmm) compute C.B^T tiles
+// (workgroup = (b, k, g) and 4 consecutive tiles), the rest the chunk cumsum
+// of 4 consecutive (b, h, k).  Both are small and latency-bound, so their
+// waves overlap instead of running as two launches one after the other.
+template <typename T, typename TI, int Q, int N>
+__global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, const float* __restrict__ A,
+                                                    const float* __restrict__ dt_bias, float* __restrict__ dt_out,
+                                                    float* __restrict__ cs, const TI* __restrict__ B,
+                                                    const TI* __restrict__ C, T* __restrict__ wf, T* __restrict__ wb,
+                                                    const RowMap rm, int H, int G, int K, int softplus, int nbkg,
+                                                    int nbhk) {
+  constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2, TB = (TILES + 3) / 4;
+  const int wave = threadIdx.x / kWave;
+  const int nbmm = nbkg * TB;
+  if ((int)blockIdx.x < nbmm) {
+    const int idx = (blockIdx.x % TB) * 4 + wave;
+    if (idx < TILES) bmm_tile_wave<T, TI, Q, N>(B, C, wf, wb, rm, G, K, blockIdx.x / TB, idx);
+  } else {
+    const int bhk = ((int)blockIdx.x - nbmm) * 4 + wave;
+    if (bhk < nbhk) chunk_cumsum_wave<T, Q>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, bhk);
+  }
 }
 
 // ---------------------------------------------------------------------------
