@@ -473,9 +473,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 // (the q terms, added at the chunk end and subtracted at each token, are
 // summed directly as a prefix so no large terms cancel), then
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dA partial = sum_j dt_j dl_j.
-// One workgroup per (b, k) and 16 heads: 16 lanes per head, Q / 16
-// consecutive tokens per lane, so a token's dt and ddt entries of the 16
-// heads are one contiguous run.
+// One wave per (b, k, h) and 4 heads per workgroup (b K H / 4 workgroups, so
+// the launch fills the chip); lane l owns the Q / 64 consecutive tokens
+// starting at l Q / 64.
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
                                                      const float* __restrict__ cs_g, const float* __restrict__ dt,
@@ -484,13 +484,15 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
                                                      float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
                                                      int softplus) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
-  constexpr int TPL = Q / 16;
-  const int nhb = (H + 15) / 16;
+  constexpr int HPB = 4;                      // heads (waves) per workgroup
+  constexpr int TPL = Q / kWave;
+  static_assert(Q % kWave == 0, "chunk");
+  const int nhb = (H + HPB - 1) / HPB;
   const int hb = blockIdx.x % nhb, bk = blockIdx.x / nhb;
   const int k = bk % K, b = bk / K;
-  const int hl = threadIdx.x / 16, jl = threadIdx.x % 16;
-  const int h = 16 * hb + hl;
-  if (h >= H) return;  // whole 16-lane group; only width-16 shuffles below
+  const int jl = lane_id();
+  const int h = HPB * hb + threadIdx.x / kWave;
+  if (h >= H) return;  // whole wave; no barrier in this kernel
   const int bkh = bk * H + h;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
@@ -500,17 +502,12 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   const int j0 = jl * TPL;
   float v[TPL], qp[TPL];
 #pragma unroll
-  for (int t = 0; t < TPL; t += 4) {
-    f4 rs = *reinterpret_cast<const f4*>(part + j0 + t);
+  for (int t = 0; t < TPL; ++t) {
+    float rs = part[j0 + t];
 #pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp) rs += *reinterpret_cast<const f4*>(part + sp * Q + j0 + t);
-    const f4 cl = *reinterpret_cast<const f4*>(part + NSPLIT * Q + j0 + t);
-    const f4 qq = *reinterpret_cast<const f4*>(part + (NSPLIT + 1) * Q + j0 + t);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[t + e] = rs[e] - cl[e];
-      qp[t + e] = qq[e];
-    }
+    for (int sp = 1; sp < NSPLIT; ++sp) rs += part[sp * Q + j0 + t];
+    v[t] = rs - part[NSPLIT * Q + j0 + t];
+    qp[t] = part[(NSPLIT + 1) * Q + j0 + t];
   }
 #pragma unroll
   for (int t = TPL - 2; t >= 0; --t) v[t] += v[t + 1];
@@ -521,17 +518,17 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
     qp[t] = qrun;
     qrun += qt;
   }
-  // across the 16 lanes of the head: suffix of the block sums v[0], prefix of qrun
+  // across the wave: suffix of the lane sums v[0], prefix of qrun
   float incl = v[0], qincl = qrun;
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    const float o = __shfl_down(incl, off, 16);
-    if (jl + off < 16) incl += o;
-    const float p = __shfl_up(qincl, off, 16);
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_down(incl, off, kWave);
+    if (jl + off < kWave) incl += o;
+    const float p = __shfl_up(qincl, off, kWave);
     if (jl >= off) qincl += p;
   }
-  float excl = __shfl_down(incl, 1, 16);
-  if (jl == 15) excl = 0.0f;
+  float excl = __shfl_down(incl, 1, kWave);
+  if (jl == kWave - 1) excl = 0.0f;
   const float qexcl = qincl - qrun;
   const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
   const float tail = __expf(csc[Q - 1]) * sc[0];
@@ -552,11 +549,8 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
     }
     ddt[(row0 + j) * H + h] = from_f<T>(g);
   }
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    da += __shfl_xor(da, off, 16);
-    if (softplus) dbias += __shfl_xor(dbias, off, 16);
-  }
+  da = wave_sum(da);
+  if (softplus) dbias = wave_sum(dbias);
   if (jl == 0) {
     float dds = 0.0f;
 #pragma unroll
@@ -1073,7 +1067,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     const int nitems = b * K * H;
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
-    k_dl_assemble<T, Q><<<dim3(b * K * ((H + 15) / 16)), dim3(256), 0, st>>>(
+    k_dl_assemble<T, Q><<<dim3(b * K * ((H + 3) / 4)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
