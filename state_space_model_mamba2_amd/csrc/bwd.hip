@@ -1080,8 +1080,15 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_BC_FINAL, st);
-    k_bc_final<T, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
-        a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
+    // Splitting the dstate columns gives a launch with few (b, k, g) items enough
+    // workgroups, but every part stages and converts the whole dW block again;
+    // once the row blocks alone make 2048 workgroups, one part takes all columns.
+    if ((int64_t)nbkg * (Q / 64) * 2 >= 2048)
+      k_bc_final<T, Q, N, 1><<<dim3(nbkg, Q / 64, 2), dim3(256), 0, st>>>(
+          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
+    else
+      k_bc_final<T, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
+          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
