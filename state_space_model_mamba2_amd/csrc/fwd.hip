@@ -133,6 +133,16 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
   __syncthreads();
 
   const float Dh = Dp[h];
+  // x^T fragment addresses of this lane at source step 0 (rows 4q + c/4 and
+  // 16 rows below).  The permutation of row r depends on r only through
+  // (r ^ r >> 2) & 3, which for r = 32 J2 + 4q + c/4 is (c/4) ^ q at every
+  // step J2, so step J2 reads 32 J2 rows further on: a constant offset.
+  int xoff[TP];
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) {
+    const int r0 = 4 * q + (c >> 2);
+    xoff[tp] = r0 * XPITCH + (XSWZ ? xcol(r0, 16 * tp + 4 * (c & 3)) : 16 * tp + 4 * (c & 3));
+  }
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) {
     const int I = Is[sl];
@@ -196,8 +206,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
       for (int tp = 0; tp < TP; ++tp) {
         Frag<T> fx;                            // x^T: row p = 16tp + c, K = j (chained)
         if constexpr (XSWZ) {
-          const int r = 32 * J2 + 4 * q + (c >> 2);  // row r + 16 has the same permutation
-          const T* a = &Xs[r][xcol(r, 16 * tp + 4 * (c & 3))];
+          const T* a = &Xs[0][0] + 32 * J2 * XPITCH + xoff[tp];  // row r + 16 has row r's permutation
           frag_load_kmajor_at(fx, a, a + 16 * XPITCH);
         } else {
           frag_load_kmajor<32>(fx, &Xs[0][0], XPITCH, 32 * J2, 16 * tp, q, c);
