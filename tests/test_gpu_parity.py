@@ -80,3 +80,18 @@ def test_bf16_other_configs(chunk, headdim, dstate):
 def test_uneven_head_slices(nheads, ngroups, dtype, chunk):
     _check(inputs.workload("tiny_fp32", batch=1, seqlen=chunk, nheads=nheads, ngroups=ngroups, chunk=chunk,
                            dtype=dtype))
+
+
+# Launch shapes whose work-item counts fit no launch granularity: 3 x 700
+# tokens (a shorter last chunk) with 10 heads in 2 groups gives 90 (b, k, h)
+# items (the XCD-aware item map pads to 96), an odd head count per group (one
+# head per chunk-state workgroup) and a last dl-assembly workgroup with 2 of
+# its 4 head waves.  8192 tokens in 8 groups give 256 (b, k, g) items, enough
+# for the dC/dB finalisation to take all dstate columns in one workgroup.
+@pytest.mark.parametrize("shape", [
+    dict(base="mamba2_370m", batch=3, seqlen=700, nheads=10, ngroups=2),
+    dict(base="long_context", batch=1, seqlen=8192, nheads=8, ngroups=8),
+], ids=["ragged_10_heads_2_groups", "8_groups_8192_tokens"])
+def test_launch_shape_edges(shape):
+    shape = dict(shape)
+    _check(inputs.workload(shape.pop("base"), **shape))
