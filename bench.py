@@ -80,11 +80,11 @@ def kernel_model(s, esz):
     m = {
         # dt in, cs and the float32 step out; B, C in, C.B^T tiles in both lane orders out
         "cumsum_bmm": (DT + 2 * CS + 2 * BC + 2 * WT, 4 * bkg * tri * N),
-        "chunk_state": (XI + BC + 2 * CS + ST4, 2 * bkh * Q * P * N),
-        "state_passing": (ST4 + STe + b * H * P * N * 4, 0),
+        "chunk_state": (XI + BC + 2 * CS + STe, 2 * bkh * Q * P * N),
+        "state_passing": (2 * STe + b * H * P * N * 4, 0),
         "chunk_scan": (XI + X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
-        "chunk_state_bwd": (X + BC + CS + ST4, 2 * bkh * Q * P * N),
-        "state_passing_bwd": (ST4 + STe, 0),
+        "chunk_state_bwd": (X + BC + CS + STe, 2 * bkh * Q * P * N),
+        "state_passing_bwd": (2 * STe, 0),
         "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
         # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in, dW out
         "dw_heads": (2 * X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),

@@ -54,10 +54,10 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   y.wtb_off = o;  o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.saved_bytes = o;
   o = 0;
-  y.s_off = o;    o += align_up(states * 4);
+  y.s_off = o;    o += align_up(states * y.esz);
   y.fwd_bytes = o;
   o = 0;
-  y.dhloc_off = o;  o += align_up(states * 4);
+  y.dhloc_off = o;  o += align_up(states * y.esz);
   y.g_off = o;      o += align_up(states * y.esz);
   // Head slices of the group-level backward launch (dW and the dC / dB head
   // sums; each slice writes fp32 partials that are summed in a fixed order):
@@ -161,14 +161,14 @@ void set_fwd_ws(FwdArgs& a, const Layout& lay, void* saved, void* scratch) {
   a.hin = at<char>(saved, lay.hin_off);
   a.wt = at<char>(saved, lay.wt_off);
   a.wtb = at<char>(saved, lay.wtb_off);
-  a.S = at<float>(scratch, lay.s_off);
+  a.S = at<char>(scratch, lay.s_off);
 }
 
 void set_bwd_ws(BwdArgs& a, const Layout& lay, const void* saved, void* scratch) {
   a.cs = at<float>(saved, lay.cs_off);
   a.hin = at<char>(saved, lay.hin_off);
   a.w = at<char>(saved, lay.wtb_off);
-  a.dhloc = at<float>(scratch, lay.dhloc_off);
+  a.dhloc = at<char>(scratch, lay.dhloc_off);
   a.gst = at<char>(scratch, lay.g_off);
   a.dw = at<float>(scratch, lay.dw_off);
   a.dcpart = at<float>(scratch, lay.dcpart_off);

@@ -1055,12 +1055,12 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
-    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, a.dhloc, a.rows, b, H, G, K, st);
+    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, static_cast<T*>(a.dhloc), a.rows, b, H, G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
     const int PN = P * N;
-    k_state_passing_bwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(a.dhloc, a.cs, a.dfinal, gst, a.dinit, H, K, PN);
+    k_state_passing_bwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.dhloc), a.cs, a.dfinal, gst, a.dinit, H, K, PN);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);

@@ -249,12 +249,12 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, a.S, a.rows, b, H, G, K, st);
+    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, static_cast<T*>(a.S), a.rows, b, H, G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);
     const int PN = P * N;
-    k_state_passing_fwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(a.S, a.cs, a.init, hin, a.final_state, H, K, PN);
+    k_state_passing_fwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.S), a.cs, a.init, hin, a.final_state, H, K, PN);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);

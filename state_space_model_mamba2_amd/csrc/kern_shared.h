@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
 template <typename T, typename TI, int Q, int P, int N, bool BWD, int HPW>
 __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
-                                                     float* __restrict__ out, const RowMap rm, int H, int G, int K,
+                                                     T* __restrict__ out, const RowMap rm, int H, int G, int K,
                                                      int nitems) {
   constexpr int NTH = 256;
   constexpr int KB = 64;                           // tokens per block
@@ -324,14 +324,14 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
   }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    float* o = out + (((int64_t)b * K + k) * H + h0 + hh) * P * N;
+    T* o = out + (((int64_t)b * K + k) * H + h0 + hh) * P * N;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int j = wave + 4 * t;
       if (j < NT) {
         const int tm = j / TN, tn = j % TN;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = acc[hh][t][r];
+        for (int r = 0; r < 4; ++r) o[(tm * 16 + 4 * q + r) * N + tn * 16 + c] = from_f<T>(acc[hh][t][r]);
       }
     }
   }
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
 
 // Launch of k_chunk_state: two heads per workgroup when a group's heads pair up.
 template <typename T, typename TI, int Q, int P, int N, bool BWD>
-void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, float* out, const RowMap& rm,
+void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, T* out, const RowMap& rm,
                         int b, int H, int G, int K, hipStream_t st) {
   if ((H / G) % 2 == 0)
     k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K,
@@ -353,9 +353,11 @@ void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* 
 // Forward state passing, elementwise over the P*N state entries of each
 // (b, h) and sequential over chunks:
 //   h = init (zero if null);  hin[k] = h;  h = exp(cs_{Q-1}(k)) h + S[k];   final = h.
-// Each thread owns 4 consecutive entries (16-byte loads of S).
+// Each thread owns 4 consecutive entries.  S comes in the storage type (the
+// chunk states are rounded to it like every stored state); the scan itself
+// runs in float32.
 template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restrict__ S, const float* __restrict__ cs,
+__global__ __launch_bounds__(256) void k_state_passing_fwd(const T* __restrict__ S, const float* __restrict__ cs,
                                                            const float* __restrict__ init, T* __restrict__ hin,
                                                            float* __restrict__ final_state, int H, int K, int PN) {
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -366,13 +368,14 @@ __global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restri
   if (init) st = *reinterpret_cast<const f4*>(init + (int64_t)bh * PN + e);
   for (int k = 0; k < K; ++k) {
     const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
-    const f4 s = *reinterpret_cast<const f4*>(S + off);
+    const typename Vec4<T>::type s = *reinterpret_cast<const typename Vec4<T>::type*>(S + off);
     const float alpha = __expf(csb[(int64_t)k * Q]);
     typename Vec4<T>::type v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = from_f<T>(st[r]);
     *reinterpret_cast<typename Vec4<T>::type*>(hin + off) = v;
-    st = alpha * st + s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[r] = alpha * st[r] + to_f(s[r]);
   }
   if (final_state) *reinterpret_cast<f4*>(final_state + (int64_t)bh * PN + e) = st;
 }
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(256) void k_state_passing_fwd(const float* __restri
 // w.r.t. the state leaving chunk k; the g left at the end is the gradient
 // w.r.t. the initial state, written to dinit if non-null.
 template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_state_passing_bwd(const float* __restrict__ dhloc, const float* __restrict__ cs,
+__global__ __launch_bounds__(256) void k_state_passing_bwd(const T* __restrict__ dhloc, const float* __restrict__ cs,
                                                            const float* __restrict__ dfinal, T* __restrict__ gout,
                                                            float* __restrict__ dinit, int H, int K, int PN) {
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
@@ -397,9 +400,10 @@ __global__ __launch_bounds__(256) void k_state_passing_bwd(const float* __restri
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = from_f<T>(gs[r]);
     *reinterpret_cast<typename Vec4<T>::type*>(gout + off) = v;
-    const f4 d = *reinterpret_cast<const f4*>(dhloc + off);
+    const typename Vec4<T>::type d = *reinterpret_cast<const typename Vec4<T>::type*>(dhloc + off);
     const float alpha = __expf(csb[(int64_t)k * Q]);
-    gs = d + alpha * gs;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gs[r] = to_f(d[r]) + alpha * gs[r];
   }
   if (dinit) *reinterpret_cast<f4*>(dinit + (int64_t)bh * PN + e) = gs;
 }

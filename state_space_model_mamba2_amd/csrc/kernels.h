@@ -52,7 +52,7 @@ struct FwdArgs {
   RowMap rows;
   float* cs;    // [b][H][K][Q]
   void* hin;    // [b][K][H][P][N]  storage dtype
-  float* S;     // [b][K][H][P][N]
+  void* S;      // [b][K][H][P][N], storage dtype
   void* wt;     // C.B^T tiles, forward lane order (kept in the saved workspace)
   void* wtb;    // C.B^T tiles, backward lane order (kept in the saved workspace)
 };
@@ -71,7 +71,7 @@ struct BwdArgs {
   float* dbiaspart;     // [b][K][H] per-chunk partials of ddt_bias (softplus only)
   float* dinit;         // [b][H][P][N] initial-state gradient, or null
   const void* w;   // C.B^T tiles, backward lane order (saved by the forward pass)
-  float* dhloc;    // [b][K][H][P][N]
+  void* dhloc;     // [b][K][H][P][N], storage dtype
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
   float* dcpart;   // [nslice][b][K][Q][G][N] fp32 partials of dC (chunk rows)
