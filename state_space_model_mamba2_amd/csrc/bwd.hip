@@ -592,7 +592,7 @@ template <typename T, int Q, int P, bool DIAG>
 __device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* __restrict__ dt,
                                          const float* __restrict__ cs_g, const T* __restrict__ dy,
                                          float* __restrict__ dw, const RowMap& rm, int H, int G, int K, int hps,
-                                         int bkg, int nbkg, int slice, int IB, int JB, DwLds<T, P>& sm) {
+                                         int bkg, int nbkg, int slice, int IB, int JB, DwLds<T, P>& sm, int dw_st) {
   constexpr int NTH = 256;
   constexpr int NKP = (P + 31) / 32;
   constexpr int XP = DwLds<T, P>::XP;
@@ -730,12 +730,24 @@ __device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* _
     for (int d = 0; d < DW_DEPTH; ++d)
       if (hh + d < nh) step(R[d], R[(d + 1) % DW_DEPTH], hh + d);
   }
-  float* o = dw + ((int64_t)slice * nbkg + bkg) * Q * Q;
+  // dw_st: a single head slice, stored in the storage dtype (the rounding the
+  // dC/dB products apply to it anyway), else float32 per-slice partials
+  if (dw_st) {
+    T* o = reinterpret_cast<T*>(dw) + (int64_t)bkg * Q * Q;
 #pragma unroll
-  for (int tj = 0; tj < 4; ++tj) {
-    const int j = j0 + 16 * tj + c;
+    for (int tj = 0; tj < 4; ++tj) {
+      const int j = j0 + 16 * tj + c;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[(int64_t)(i0 + 16 * wave + 4 * q + r) * Q + j] = acc[tj][r];
+      for (int r = 0; r < 4; ++r) o[(int64_t)(i0 + 16 * wave + 4 * q + r) * Q + j] = from_f<T>(acc[tj][r]);
+    }
+  } else {
+    float* o = dw + ((int64_t)slice * nbkg + bkg) * Q * Q;
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      const int j = j0 + 16 * tj + c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[(int64_t)(i0 + 16 * wave + 4 * q + r) * Q + j] = acc[tj][r];
+    }
   }
 }
 
@@ -863,7 +875,7 @@ __global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const
                                                   const T* __restrict__ hin, const T* __restrict__ gst,
                                                   float* __restrict__ dw, float* __restrict__ dcpart,
                                                   float* __restrict__ dbpart, const RowMap rm, int H, int G, int K,
-                                                  int hps, int nbkg, int nitems) {
+                                                  int hps, int nbkg, int nitems, int dw_st) {
   constexpr int NB = Q / 64, NBLK = 2 * NB + NB * (NB + 1) / 2;
   constexpr size_t LDS = sizeof(DwLds<T, P>) > sizeof(BcLds<T, P, N>) ? sizeof(DwLds<T, P>) : sizeof(BcLds<T, P, N>);
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS];
@@ -880,13 +892,13 @@ __global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const
   } else if (blk < 3 * NB) {
     const int d = blk - 2 * NB;
     dw_block<T, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, d, d,
-                            *reinterpret_cast<DwLds<T, P>*>(smem));
+                            *reinterpret_cast<DwLds<T, P>*>(smem), dw_st);
   } else {
     const int y = blk - 3 * NB;  // pairs IB > JB: y = IB (IB - 1) / 2 + JB
     int IB = 1;
     while ((IB + 1) * IB / 2 <= y) ++IB;
     dw_block<T, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2,
-                             *reinterpret_cast<DwLds<T, P>*>(smem));
+                             *reinterpret_cast<DwLds<T, P>*>(smem), dw_st);
   }
 }
 
@@ -914,7 +926,7 @@ template <typename T, int Q, int N, bool DB, int NH>
 __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, const float* __restrict__ dw,
                                                const T* __restrict__ M, T* __restrict__ out, const RowMap& rm,
                                                int G, int K, int nslice, int nslice_dw, int bkg, int nbkg, int RB,
-                                               int zpart, BcFinalLds<T, Q, N, NH>& sm) {
+                                               int zpart, BcFinalLds<T, Q, N, NH>& sm, int dw_st) {
   constexpr int NTH = 256;
   constexpr int NP = N / NH;                 // dstate columns of this part
   constexpr int TN = NP / 16, NB = Q / 64;
@@ -948,12 +960,17 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
     const int ib = DB ? kb : RB, jb = DB ? RB : kb;
     for (int e = threadIdx.x * 4; e < 64 * 64; e += NTH * 4) {
       const int il = e / 64, jl = e % 64;
-      const float* src = dwb + (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
-      f4 v = *reinterpret_cast<const f4*>(src);
-      for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(src + z * dws);
+      const int64_t eo = (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
       typename Vec4<T>::type w;
+      if (dw_st) {  // one slice, already in the storage dtype
+        w = *reinterpret_cast<const typename Vec4<T>::type*>(reinterpret_cast<const T*>(dw) + (int64_t)bkg * Q * Q + eo);
+      } else {
+        const float* src = dwb + eo;
+        f4 v = *reinterpret_cast<const f4*>(src);
+        for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(src + z * dws);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
+        for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
+      }
       *reinterpret_cast<typename Vec4<T>::type*>(&Wb[il][jl]) = w;
     }
     // B rows j (dC) or C rows i (dB) of block kb
@@ -1001,15 +1018,15 @@ template <typename T, int Q, int N, int NH>
 __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ dcpart, const float* __restrict__ dbpart,
                                                   const float* __restrict__ dw, const T* __restrict__ B,
                                                   const T* __restrict__ C, T* __restrict__ dC, T* __restrict__ dB,
-                                                  const RowMap rm, int G, int K, int nslice) {
+                                                  const RowMap rm, int G, int K, int nslice, int dw_st) {
   __shared__ BcFinalLds<T, Q, N, NH> sm;
   const int z = blockIdx.z;
   if (z < NH)
     bc_final_block<T, Q, N, false, NH>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
-                                       z, sm);
+                                       z, sm, dw_st);
   else
     bc_final_block<T, Q, N, true, NH>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
-                                      z - NH, sm);
+                                      z - NH, sm, dw_st);
 }
 
 // Fixed-order sums of the per-(b, k) partials (dA, dD and, when requested,
@@ -1072,11 +1089,14 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int nbkg = b * K * G;
+  // one head slice: dW goes straight to the storage dtype (bit-identical, as the
+  // dC/dB products round it to that type anyway) at half the bytes
+  const int dw_st = (S == 1 && sizeof(T) == 2) ? 1 : 0;
   {
     ProbeScope ps(probe, SSD_K_DW_HEADS, st);
     const int nb = Q / 64, nitems = nbkg * S;
     k_dw_heads<T, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems);
+        x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems, dw_st);
   }
   {
     ProbeScope ps(probe, SSD_K_BC_FINAL, st);
@@ -1085,10 +1105,10 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     // once the row blocks alone make 2048 workgroups, one part takes all columns.
     if ((int64_t)nbkg * (Q / 64) * 2 >= 2048)
       k_bc_final<T, Q, N, 1><<<dim3(nbkg, Q / 64, 2), dim3(256), 0, st>>>(
-          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
+          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
     else
       k_bc_final<T, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
-          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
+          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);
