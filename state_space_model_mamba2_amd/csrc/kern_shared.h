@@ -63,49 +63,75 @@ __device__ __forceinline__ int tri_index(int I, int J) { return I * (I + 1) / 2 
 
 // ---------------------------------------------------------------------------
 // Chunk cumsum: cs[b][h][k][i] = sum_{j <= i} dt[b][kQ + j][h] * A[h].
-// One wavefront per (b, h, k); each lane owns Q/64 consecutive tokens and the
-// chunk-wide prefix comes from a wave64 shuffle scan.
+// One wavefront per (b, HW adjacent heads, k); each lane owns Q/64
+// consecutive tokens (one HW-wide load per token: the heads' steps of a token
+// are adjacent in the caller's token-major dt) and the chunk-wide prefix of
+// each head comes from a wave64 shuffle scan.
 // The step is written in float32 for every later kernel, in cs's layout
 // (dt_out[b][h][k][i], so that a chunk's steps of one head are contiguous;
 // rows past the end of a shorter last chunk get 0).  It is the caller's dt
 // widened or, with softplus set (dt then holds the raw step),
 // softplus(dt + dt_bias[h]) = log(1 + e^z) (z itself above 20).
-template <typename T, int Q>
+template <typename T, int Q, int HW>
 __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, const float* __restrict__ A,
                                                   const float* __restrict__ dt_bias, float* __restrict__ dt_out,
                                                   float* __restrict__ cs, const RowMap& rm, int H, int K, int softplus,
-                                                  int bhk) {
+                                                  int item) {
   constexpr int TPL = Q / kWave;
-  const int k = bhk % K, bh = bhk / K, h = bh % H, b = bh / H;
+  static_assert(HW == 1 || HW == 4, "heads per wave");
+  const int HQ = H / HW;
+  const int k = item % K, bq = item / K, h0 = (bq % HQ) * HW, b = bq / HQ;
   const int l = lane_id();
   const bool last = k == rm.kf;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   const T* src = rows_in(rm, k, dt, rm.dt);
-  float* dst = dt_out + (int64_t)bhk * Q + l * TPL;
-  const float a = A[h];
-  const float bias = (softplus && dt_bias) ? dt_bias[h] : 0.0f;
-  float v[TPL];
+  float a[HW], bias[HW];
+#pragma unroll
+  for (int w = 0; w < HW; ++w) {
+    a[w] = A[h0 + w];
+    bias[w] = (softplus && dt_bias) ? dt_bias[h0 + w] : 0.0f;
+  }
+  float v[HW][TPL];
 #pragma unroll
   for (int j = 0; j < TPL; ++j) {
     const int i = l * TPL + j;
-    const int64_t e = (row0 + i) * H + h;
-    float d = to_f(src[e]);
-    if (softplus) {
-      const float z = d + bias;
-      d = z > 20.0f ? z : log1pf(expf(z));
+    const int64_t e = (row0 + i) * H + h0;
+    float d[HW];
+    if constexpr (HW == 4) {
+      const typename Vec4<T>::type d4 = *reinterpret_cast<const typename Vec4<T>::type*>(src + e);
+#pragma unroll
+      for (int w = 0; w < HW; ++w) d[w] = to_f(d4[w]);
+    } else {
+      d[0] = to_f(src[e]);
     }
-    if (last && i >= rm.lr) d = 0.0f;
-    dst[j] = d;
-    v[j] = d * a;
+#pragma unroll
+    for (int w = 0; w < HW; ++w) {
+      if (softplus) {
+        const float z = d[w] + bias[w];
+        d[w] = z > 20.0f ? z : log1pf(expf(z));
+      }
+      if (last && i >= rm.lr) d[w] = 0.0f;
+      v[w][j] = d[w];
+    }
   }
 #pragma unroll
-  for (int j = 1; j < TPL; ++j) v[j] += v[j - 1];
-  const float incl = wave_inclusive_scan(v[TPL - 1]);
-  float excl = __shfl_up(incl, 1, kWave);
-  if (l == 0) excl = 0.0f;
-  float* out = cs + (int64_t)bhk * Q + l * TPL;
+  for (int w = 0; w < HW; ++w) {
+    const int64_t bhk = ((int64_t)b * H + h0 + w) * K + k;
+    float* dst = dt_out + bhk * Q + l * TPL;
 #pragma unroll
-  for (int j = 0; j < TPL; ++j) out[j] = v[j] + excl;
+    for (int j = 0; j < TPL; ++j) {
+      dst[j] = v[w][j];
+      v[w][j] *= a[w];
+    }
+#pragma unroll
+    for (int j = 1; j < TPL; ++j) v[w][j] += v[w][j - 1];
+    const float incl = wave_inclusive_scan(v[w][TPL - 1]);
+    float excl = __shfl_up(incl, 1, kWave);
+    if (l == 0) excl = 0.0f;
+    float* out = cs + bhk * Q + l * TPL;
+#pragma unroll
+    for (int j = 0; j < TPL; ++j) out[j] = v[w][j] + excl;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -176,9 +202,9 @@ __device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI
 // The two independent first steps of the forward in one launch, one wave
 // per work item and no barrier: workgroups [0, nbmm) compute C.B^T tiles
 // (workgroup = (b, k, g) and 4 consecutive tiles), the rest the chunk cumsum
-// of 4 consecutive (b, h, k).  Both are small and latency-bound, so their
+// of 4 consecutive (b, HW heads, k).  Both are small and latency-bound, so their
 // waves overlap instead of running as two launches one after the other.
-template <typename T, typename TI, int Q, int N>
+template <typename T, typename TI, int Q, int N, int HW>
 __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, const float* __restrict__ A,
                                                     const float* __restrict__ dt_bias, float* __restrict__ dt_out,
                                                     float* __restrict__ cs, const TI* __restrict__ B,
@@ -192,8 +218,8 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
     const int idx = (blockIdx.x % TB) * 4 + wave;
     if (idx < TILES) bmm_tile_wave<T, TI, Q, N>(B, C, wf, wb, rm, G, K, blockIdx.x / TB, idx);
   } else {
-    const int bhk = ((int)blockIdx.x - nbmm) * 4 + wave;
-    if (bhk < nbhk) chunk_cumsum_wave<T, Q>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, bhk);
+    const int item = ((int)blockIdx.x - nbmm) * 4 + wave;
+    if (item < nbhk / HW) chunk_cumsum_wave<T, Q, HW>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, item);
   }
 }
 
