@@ -57,8 +57,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr int VN = Vec16<T>::n;
   constexpr int CUP = P / VN, CUN = N / VN;
   constexpr int YPIECES = SR * CUP, CPIECES = SR * CUN;  // 16-byte pieces: dy slab, C slab
-  // dy row pitch: for bf16 8 (mod 16) dwords, for the transposing reads
-  constexpr int DPITCH = sizeof(T) == 2 ? P + 2 * ((24 - (P / 2) % 16) % 16) : P + PADR;
+  // dy rows.  bf16 with headdim 64: unpadded, the 16-byte pieces of row r
+  // XOR-permuted by f(r) = 2 ((r / 2) mod 4) + (r / 8) mod 2, so that the
+  // transposing dy^T reads (per half-wave 8 rows x 32 bytes) and the row
+  // fragment reads (16 rows x 16 bytes) both meet every bank once.  Otherwise a
+  // pitch of 8 (mod 16) dwords, which serves the transposing reads.
+  constexpr bool DSWZ = sizeof(T) == 2 && P == 64;
+  constexpr int DPITCH = DSWZ ? P : sizeof(T) == 2 ? P + 2 * ((24 - (P / 2) % 16) % 16) : P + PADR;
   constexpr int YPT = (YPIECES + NTH - 1) / NTH, CPT = (CPIECES + NTH - 1) / NTH;
   // C.B^T tiles of a slab: rows I = 2s + half against every owned column tile
   // of this workgroup, slot (half, wave, sl); tiles with J > I stay unused
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   __shared__ __attribute__((aligned(16))) float eslab[Q];  // exp(cs_i - cs_rb), rb = first row of i's slab
   __shared__ float rowacc[NW][Q];
   __shared__ float red[2 * NW];
+  // storage column of dy element (r, col) of a slab
+  auto dyc = [](int r, int col) { return DSWZ ? col ^ (8 * ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) : col; };
 
   // (b, k, h) item and column split of this workgroup: the XCD-aware item
   // map (consecutive heads of a chunk on one XCD) over groups of NSPLIT * 8
@@ -149,7 +156,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
     for (int n = 0; n < YPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[bf][u / CUP][(u % CUP) * VN]) = yv[n];
+      if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[bf][u / CUP][dyc(u / CUP, (u % CUP) * VN)]) = yv[n];
     }
 #pragma unroll
     for (int n = 0; n < CPT; ++n) {
@@ -292,14 +299,31 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       }
       const f4 ei = *reinterpret_cast<const f4*>(&ecs[rb + 16 * half + 4 * q]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rowtot[half][r] += ei[r] * (acc[r] * to_f(DY[bf][16 * half + 4 * q + r][16 * tw + c]));
+      for (int r = 0; r < 4; ++r) {
+        const int yr = 16 * half + 4 * q + r;
+        rowtot[half][r] += ei[r] * (acc[r] * to_f(DY[bf][yr][dyc(yr, 16 * tw + c)]));
+      }
     }
 
     // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
     Frag<T> fdt[TP];
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) frag_load_kmajor<SR>(fdt[tp], &DY[bf][0][0], DPITCH, 0, 16 * tp, q, c);
+    for (int tp = 0; tp < TP; ++tp) {
+      if constexpr (DSWZ) {  // rows 4q + c/4 and 16 below (same permutation)
+        const int r0 = 4 * q + (c >> 2), col = 16 * tp + 4 * (c & 3);
+        frag_load_kmajor_at(fdt[tp], &DY[bf][r0][dyc(r0, col)], &DY[bf][r0 + 16][dyc(r0, col)]);
+      } else {
+        frag_load_kmajor<SR>(fdt[tp], &DY[bf][0][0], DPITCH, 0, 16 * tp, q, c);
+      }
+    }
+    // dy row 16 half + c as a chained-K A fragment (K = headdim, from kp * 32)
+    auto dy_row_frag = [&](Frag<T>& fd, int half, int kp) {
+      const int yr = 16 * half + c;
+      if constexpr (DSWZ)
+        frag_load2(fd, &DY[bf][yr][dyc(yr, kp * 32 + 4 * q)], &DY[bf][yr][dyc(yr, kp * 32 + 16 + 4 * q)]);
+      else
+        frag_load_chained<P>(fd, &DY[bf][yr][0], kp * 32, q);
+    };
 
     // intra-chunk pairs (I in this slab, J owned), I >= J.
     // Column tiles wholly before the slab ("full" pairs, the common case):
@@ -322,7 +346,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
         for (int kp = 0; kp < NKP; ++kp) {
           Frag<T> fd;
-          frag_load_chained<P>(fd, &DY[bf][16 * half + c][0], kp * 32, q);
+          dy_row_frag(fd, half, kp);
           mma(dp[half], fd, xf[sl][kp]);     // lane: column j = cj, rows i = rb + 16 half + 4q + r
         }
       }
@@ -356,7 +380,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
           for (int kp = 0; kp < NKP; ++kp) {
             Frag<T> fd;
-            frag_load_chained<P>(fd, &DY[bf][16 * half + c][0], kp * 32, q);
+            dy_row_frag(fd, half, kp);
             mma(dp, fd, xf[sl][kp]);
           }
           const int i0 = 16 * I + 4 * q;
@@ -423,7 +447,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       float xd = 0.0f;
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const V4 dv = *reinterpret_cast<const V4*>(&DY[bf][j - rb][16 * tp + 4 * q]);
+        const V4 dv = *reinterpret_cast<const V4*>(&DY[bf][j - rb][dyc(j - rb, 16 * tp + 4 * q)]);
         V4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
