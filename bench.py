@@ -17,6 +17,18 @@ and lets the library apply softplus(dt_raw + dt_bias) (and return ddt_bias);
 it needs --fwd-only); --fwd-only times the forward pass alone.  Prints ONE JSON line on stdout;
 diagnostics (per-kernel times) go to stderr.
 
+Timing: W untimed warmup steps, then exactly K timed steps.  A 1 GiB write
+before every timed step evicts the L2s and the 256 MB Infinity Cache, so each
+step starts cold; each step is bracketed by events on the launch stream, and
+the headline ms_per_step is the median of the K cold steps.  The same K steps
+run back to back on warm caches afterwards (timing.warm_ms_per_step).
+
+targets: per-kernel fractions of HBM and bf16 MFMA peak from the per-kernel
+probe times (also on flushed caches): the chunk GEMM kernels against 50 % of
+the MFMA peak beside the cap HBM alone puts on each, the two state-passing
+scans against 60 % of HBM peak, and the step against its own HBM floor
+(compulsory I/O of both passes plus five passes over the chunk states).
+
 The roofline object describes the kernel with the largest share of the step:
 its algorithmic bytes and flops per launch (formulas in kernel_model below)
 over its average launch duration, measured with HIP events that libssd records
@@ -149,8 +161,9 @@ def run_step(ssd, dev, chunk, fscr, bscr, fprobe=None, bprobe=None):
     return y, fs, g
 
 
-def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
-    """Average duration of every kernel (probed one kernel per step)."""
+def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, flush, reps=5):
+    """Average duration of every kernel (probed one kernel per step), each
+    step started on flushed caches like the timed steps."""
     from state_space_model_mamba2_amd import _lib
     import torch
     out = {}
@@ -159,7 +172,8 @@ def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
         if dev.get("fwd_only", False) and kid not in fwd_ids:
             continue
         evs = [(hip.event(), hip.event()) for _ in range(reps)]
-        for a, b in evs:
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(float(i))
             p = make_probe(kid, a, b)
             run_step(ssd, dev, chunk, fscr, bscr, fprobe=p if kid in fwd_ids else None,
                      bprobe=None if kid in fwd_ids else p)
@@ -171,28 +185,10 @@ def per_kernel_times(ssd, dev, chunk, fscr, bscr, hip, reps=5):
     return out
 
 
-def cold_warm(ssd, dev, chunk, fscr, bscr, reps=10):
-    """Median whole-step time (events on the stream the library launches on)
-    with the caches flushed before every step -- a 1 GiB write evicts the L2s
-    and the 256 MB Infinity Cache -- and without; plus the rate of a plain
-    1 GiB device copy, the achievable-HBM reference."""
+def copy_rate_gbps(flush):
+    """Rate of a plain 1 GiB device-to-device copy: the achievable-HBM reference."""
     import torch
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    out = {}
-    for mode in ("cold", "warm"):
-        ts = []
-        for i in range(reps):
-            if mode == "cold":
-                flush.fill_(float(i))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            run_step(ssd, dev, chunk, fscr, bscr)
-            b.record()
-            b.synchronize()
-            ts.append(a.elapsed_time(b))
-        ts.sort()
-        out[f"{mode}_ms_per_step"] = ts[len(ts) // 2]
-    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    src = torch.empty_like(flush).fill_(1.0)
     ts = []
     for _ in range(6):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -202,10 +198,8 @@ def cold_warm(ssd, dev, chunk, fscr, bscr, reps=10):
         b.synchronize()
         ts.append(a.elapsed_time(b))
     ts.sort()
-    out["copy_GBps"] = 2 * src.numel() * 4 / (ts[len(ts) // 2] / 1e3) / 1e9
-    out["reps"] = reps
-    del flush, src
-    return out
+    del src
+    return 2 * flush.numel() * 4 / (ts[len(ts) // 2] / 1e3) / 1e9
 
 
 def shader_clock_mhz():
@@ -218,6 +212,16 @@ def shader_clock_mhz():
                     return line.split(":", 1)[1].strip().rstrip("*").strip()
         except OSError:
             pass
+    return None
+
+
+def cpu_model() -> str | None:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
     return None
 
 
@@ -260,7 +264,7 @@ def cpu_baseline(shape, inp_full, batch_rows: int, heads: int):
     t = time.perf_counter() - t0
     scale = (shape.batch / nb) * (H / heads)
     tok_s = shape.batch * shape.seqlen / (t * scale)
-    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"float64 oracle fwd+bwd on batch rows 0..{nb - 1} of {shape.batch}, heads 0..{heads - 1} "
                       f"of {H} ({gs} group(s)), seqlen {shape.seqlen}: {t:.1f} s wall on {threads} threads; "
                       f"tokens/s scaled linearly by x{scale:g} (batch x heads) to the full workload"}
@@ -545,41 +549,70 @@ def main():
 
     hip = Hip()
     model = kernel_model(shape, esz)
+    # written before every timed step: 1 GiB evicts the L2s and the 256 MB Infinity Cache
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
 
     for _ in range(args.warmup):
         run_step(ssd, dev, shape.chunk, fscr, bscr)
     torch.cuda.synchronize()
 
     if args.profile_kernel is None:
-        breakdown = per_kernel_times(ssd, dev, shape.chunk, fscr, bscr, hip)
+        breakdown = per_kernel_times(ssd, dev, shape.chunk, fscr, bscr, hip, flush)
         dom = max(breakdown, key=breakdown.get)
     else:
         breakdown, dom = {}, args.profile_kernel
     dom_id = _lib.KERNEL_ID[dom]
     is_fwd = dom_id < _lib.N_FWD_KERNELS
 
-    # Timed region: exactly `steps` steps; the dominant kernel is bracketed by events in each.
+    # Timed region: exactly `steps` steps, each started on flushed caches (the
+    # flush is outside the step's events) and timed with events on the launch
+    # stream; the dominant kernel is bracketed by its own events in each step.
+    # The headline is the median cold step.
     evs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    step_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in evs:
+    for i, ((a, b), (sa, sb)) in enumerate(zip(evs, step_evs)):
+        flush.fill_(float(i))
         p = make_probe(dom_id, a, b)
+        sa.record()
         run_step(ssd, dev, shape.chunk, fscr, bscr, fprobe=p if is_fwd else None, bprobe=None if is_fwd else p)
+        sb.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dom_ms = sum(hip.elapsed_ms(a, b) for a, b in evs) / len(evs)
-    ms_per_step = wall * 1e3 / args.steps
+    cold = sorted(sa.elapsed_time(sb) for sa, sb in step_evs)
+    ms_per_step = cold[len(cold) // 2]
     tokens = shape.batch * shape.seqlen
     value = tokens / (ms_per_step / 1e3)
 
+    # Secondary: the same number of steps back to back on warm caches.
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(ssd, dev, shape.chunk, fscr, bscr)
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    peak_mfma = MFMA_PEAK_TFLOPS[shape.dtype]
+    ridge = peak_mfma * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+    def fracs(k, ms):
+        nb, nf = model[k]
+        t = ms / 1e3
+        return {"ms": ms, "hbm_frac": nb / t / 1e9 / HBM_PEAK_GBS, "mfma_frac": nf / t / 1e12 / peak_mfma,
+                # what HBM alone allows the matrix cores: arithmetic intensity x 8 TB/s over the peak
+                "mfma_cap_frac": min(1.0, (nf / nb) / ridge) if nb else None,
+                "algorithmic_bytes": nb, "algorithmic_flops": nf}
+
     nbytes, nflops = model[dom]
     t_s = dom_ms / 1e3
-    mfma_frac = nflops / t_s / 1e12 / MFMA_PEAK_TFLOPS[shape.dtype] if nflops else 0.0
+    mfma_frac = nflops / t_s / 1e12 / peak_mfma if nflops else 0.0
     hbm_frac = nbytes / t_s / 1e9 / HBM_PEAK_GBS
     ai = nflops / nbytes if nbytes else 0.0
-    ridge = MFMA_PEAK_TFLOPS[shape.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     if ai > ridge:
-        roof = {"bound": "mfma", "achieved": nflops / t_s / 1e12, "peak": MFMA_PEAK_TFLOPS[shape.dtype],
+        roof = {"bound": "mfma", "achieved": nflops / t_s / 1e12, "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": mfma_frac}
     else:
         roof = {"bound": "hbm", "achieved": nbytes / t_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -593,21 +626,53 @@ def main():
     roof["mfma_frac"] = mfma_frac
     roof["hbm_frac"] = hbm_frac
 
+    targets = None
     if breakdown:
-        log("[bench] per-kernel average duration (ms), algorithmic GB/s and TFLOP/s:")
+        log("[bench] per-kernel average duration (ms, flushed caches), algorithmic GB/s and TFLOP/s:")
         tot = sum(breakdown.values())
         for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1]):
             nb, nf = model[k]
             log(f"  {k:18s} {v:8.4f} ms {100 * v / tot:5.1f}%  {nb / v / 1e6:8.1f} GB/s ({100 * nb / v / 1e6 / HBM_PEAK_GBS:5.1f}%)"
-                f"  {nf / v / 1e9:7.1f} TFLOP/s ({100 * nf / v / 1e9 / MFMA_PEAK_TFLOPS[shape.dtype]:5.1f}%)")
+                f"  {nf / v / 1e9:7.1f} TFLOP/s ({100 * nf / v / 1e9 / peak_mfma:5.1f}%)")
         log(f"  sum of kernels {tot:.4f} ms vs step {ms_per_step:.4f} ms")
+        per = {k: fracs(k, v) for k, v in breakdown.items()}
+        gemm = [k for k in ("chunk_state", "chunk_scan", "chunk_state_bwd", "chunk_scan_bwd", "dw_heads") if k in per]
+        scan = [k for k in ("state_passing", "state_passing_bwd") if k in per]
+        # the step's own floor: compulsory I/O of both passes plus five passes over
+        # the chunk states (forward write and read of the entry states; backward
+        # write and read of their gradients, and a read of the entry states),
+        # at the storage element size the states are kept in
+        b_, L_, H_, P_, N_, G_ = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+        K_ = -(-L_ // shape.chunk)
+        X = b_ * L_ * H_ * P_ * esz
+        XI = b_ * L_ * H_ * P_ * (1 if shape.dtype == "fp8" else esz)
+        BCb = b_ * L_ * G_ * N_ * (1 if shape.dtype == "fp8" else esz)
+        DTb = b_ * L_ * H_ * esz
+        FS = b_ * H_ * P_ * N_ * 4
+        io = (XI + DTb + 2 * BCb + X + FS) + (0 if args.fwd_only else (X + XI + DTb + 2 * BCb + X + DTb + 2 * BCb))
+        passes = (2 if args.fwd_only else 5) * b_ * K_ * H_ * P_ * N_ * esz
+        step_floor_ms = (io + passes) / (HBM_PEAK_GBS * 1e9) * 1e3
+        targets = {
+            "chunk_gemm_mfma": {"target_frac": 0.50, "peak_tflops": peak_mfma,
+                                "kernels": {k: {"mfma_frac": per[k]["mfma_frac"], "mfma_cap_frac": per[k]["mfma_cap_frac"]}
+                                            for k in gemm}},
+            "state_passing_hbm": {"target_frac": 0.60, "peak_gbps": HBM_PEAK_GBS,
+                                  "kernels": {k: {"hbm_frac": per[k]["hbm_frac"]} for k in scan},
+                                  "met": all(per[k]["hbm_frac"] >= 0.60 for k in scan)},
+            "step_hbm_floor": {"bytes": io + passes, "ms": step_floor_ms, "frac": step_floor_ms / ms_per_step},
+            "kernels": per,
+        }
 
-    timing = cold_warm(ssd, dev, shape.chunk, fscr, bscr) if args.profile_kernel is None else None
-    if timing:
-        timing["shader_clock"] = shader_clock_mhz()
+    timing = None
+    if args.profile_kernel is None:
+        timing = {"cold_ms_per_step_median": ms_per_step, "cold_ms_per_step_max": cold[-1],
+                  "cold_ms_per_step_min": cold[0], "warm_ms_per_step": warm_ms,
+                  "wall_ms_per_step_incl_flush": wall * 1e3 / args.steps,
+                  "copy_GBps": copy_rate_gbps(flush), "shader_clock": shader_clock_mhz()}
         roof["frac_of_copy"] = roof["achieved"] / timing["copy_GBps"] if roof["unit"] == "GB/s" else None
-        log(f"[bench] step median cold {timing['cold_ms_per_step']:.4f} ms, warm {timing['warm_ms_per_step']:.4f} ms;"
+        log(f"[bench] step median cold {ms_per_step:.4f} ms, warm (back to back) {warm_ms:.4f} ms;"
             f" 1 GiB copy {timing['copy_GBps']:.0f} GB/s; shader clock {timing['shader_clock']}")
+    del flush
 
     cpu = None
     if not args.no_cpu_baseline and args.profile_kernel is None and not args.fwd_only:
@@ -631,8 +696,11 @@ def main():
         "config": {"workload": args.workload, "batch": shape.batch, "seqlen": shape.seqlen,
                    "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
                    "ngroups": shape.ngroups, "chunk": shape.chunk, "parallelism": "single-gpu",
-                   "initial_state": bool(args.with_states), "dt_softplus": bool(args.dt_softplus)},
+                   "initial_state": bool(args.with_states), "dt_softplus": bool(args.dt_softplus),
+                   "state_storage": "f32" if shape.dtype == "f32" else "bf16",
+                   "caches": "flushed before every timed step"},
         "roofline": roof,
+        "targets": targets,
         "cpu_baseline": cpu,
         "kernel_ms": breakdown or None,
         "timing": timing,

@@ -177,8 +177,8 @@ ssd_status ssd_bwd(const ssd_saved *saved, const void *dy, const float *dfinal_s
 /* ---- Causal depthwise conv1d ------------------------------------------
  *
  * The convolution that feeds the scan in a Mamba block (the "causal conv"
- * kernel the LightOn page "Training Mamba on AMD GPUs", section "Individual
- * Kernels", times): per channel c, a width-W filter w[c][0..W-1], a bias and
+ * kernel the LightOn page "Training Mamba Models on AMD MI250/MI250X GPUs
+ * with Custom Kernels", section "Individual Kernels", times): per channel c, a width-W filter w[c][0..W-1], a bias and
  * an optional SiLU,
  *     z[b][t][c] = bias[c] + sum_k w[c][k] x[b][t - (W-1) + k][c],
  *     y = silu(z) = z / (1 + e^-z)   (or y = z)

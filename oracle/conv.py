@@ -1,8 +1,9 @@
 """Causal depthwise conv1d of the Mamba block, float64 -- TEST INFRASTRUCTURE.
 
 The convolution that precedes the SSD scan in a Mamba block (the "causal
-conv" whose forward and backward the LightOn page, "Training Mamba on AMD
-GPUs", section "Individual Kernels", times on MI250).  The page gives no
+conv" whose forward and backward the LightOn page "Training Mamba Models on
+AMD MI250/MI250X GPUs with Custom Kernels", section "Individual Kernels",
+times on MI250).  The page gives no
 formula; this is the operation's definition.  Per channel c, with a width-W
 filter w[c][0..W-1], a bias and an optional activation (SiLU, z * sigmoid(z)):
 

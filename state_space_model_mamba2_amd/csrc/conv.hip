@@ -1,6 +1,7 @@
 // Causal depthwise conv1d with bias and optional SiLU, the convolution that
 // feeds the SSD scan in a Mamba block (the "causal conv" kernel of the LightOn
-// page "Training Mamba on AMD GPUs", section "Individual Kernels"):
+// page "Training Mamba Models on AMD MI250/MI250X GPUs with Custom Kernels",
+// section "Individual Kernels"):
 //   z[b][t][c] = bias[c] + sum_k w[c][k] x[b][t - (W-1) + k][c],  y = act(z)
 // token-major [b][L][C]; rows before the sequence come from x_prev
 // [b][W-1][C] or are zero.
