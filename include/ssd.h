@@ -43,7 +43,10 @@
  * Ownership: the caller allocates every buffer (inputs, outputs, the saved
  * workspace and the scratch workspaces); the library never allocates or frees
  * device memory and keeps no global mutable state, so calls are reentrant.
- * All work is enqueued on `stream`; the calls return without synchronising.
+ * The one exception is ssd_fwd_noalloc, whose scratch is a static device
+ * buffer of the library (one per GPU) and whose calls on one GPU must not
+ * overlap.  All work is enqueued on `stream`; the calls return without
+ * synchronising.
  *
  * Errors: argument checks run on the host before anything is enqueued; on
  * failure nothing is launched and an error code is returned.  A HIP launch
@@ -66,7 +69,8 @@ typedef enum {
     SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, non-positive size, nheads % ngroups, unknown flag, misalignment */
     SSD_ERR_UNSUPPORTED = 2,      /* (dtype, chunk, headdim, dstate) combination not compiled in */
     SSD_ERR_WORKSPACE = 3,        /* workspace pointer null or smaller than the *_bytes query */
-    SSD_ERR_HIP = 4               /* a HIP call or kernel launch failed */
+    SSD_ERR_HIP = 4,              /* a HIP call or kernel launch failed */
+    SSD_ERR_TOO_LARGE = 5         /* ssd_fwd_noalloc: forward scratch needed > SSD_FWD_STATIC_SCRATCH_BYTES */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_FP8 = 2 } ssd_dtype;
@@ -160,6 +164,29 @@ ssd_status ssd_fwd(const ssd_shape *shape,
                    void *saved_ws, size_t saved_ws_bytes, ssd_saved *saved_out,
                    void *scratch, size_t scratch_bytes,
                    hipStream_t stream, const ssd_probe *probe);
+
+/* Forward pass that allocates nothing and takes no scratch argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * results and saved context as ssd_fwd (the saved workspace is still the
+ * caller's); its scratch is a static device buffer of the library, 96 MiB
+ * per GPU (SSD_FWD_STATIC_SCRATCH_BYTES), held from the library's load on a
+ * GPU until the process ends.  Problems whose ssd_fwd_scratch_bytes exceeds
+ * it return SSD_ERR_TOO_LARGE before anything is launched (the Mamba2-2.7B
+ * shape, 4 x 4096 tokens with 80 heads of 64 x 128 in bf16, needs 80 MiB).
+ * `stream` must belong to the current device (SSD_ERR_INVALID_ARGUMENT
+ * otherwise; the null stream always does).  Every call on one GPU shares
+ * that GPU's buffer, so calls that overlap on one GPU (on different streams,
+ * or from different threads without ordering) race; calls ordered on one
+ * stream do not.  Nothing in the buffer needs to start at zero. */
+#define SSD_FWD_STATIC_SCRATCH_BYTES (96u * 1024u * 1024u)
+ssd_status ssd_fwd_noalloc(const ssd_shape *shape,
+                           const void *x, const void *dt, const float *A,
+                           const void *B, const void *C, const float *D,
+                           const float *dt_bias, const float *initial_state,
+                           void *y, float *final_state,
+                           void *saved_ws, size_t saved_ws_bytes, ssd_saved *saved_out,
+                           hipStream_t stream, const ssd_probe *probe);
 
 /* Backward pass: gradients of sum <dy, y> + <dfinal_state, final_state>
  * for the forward that filled `saved` (dfinal_state NULL means zero).

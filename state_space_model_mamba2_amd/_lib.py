@@ -7,7 +7,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libssd.so")
 
-SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_OK, SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP, SSD_ERR_TOO_LARGE = range(6)
+SSD_FWD_STATIC_SCRATCH_BYTES = 96 * 1024 * 1024
 SSD_F32, SSD_BF16, SSD_FP8 = 0, 1, 2
 SSD_DT_SOFTPLUS = 1
 
@@ -63,6 +64,8 @@ def load():
     lib.ssd_check_shape.argtypes, lib.ssd_check_shape.restype = [PShape], st
     lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
     lib.ssd_fwd.restype = st
+    lib.ssd_fwd_noalloc.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, PProbe]
+    lib.ssd_fwd_noalloc.restype = st
     lib.ssd_bwd.argtypes = [PSaved, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, PProbe]
     lib.ssd_bwd.restype = st
     PConv = ctypes.POINTER(ConvShape)

@@ -4,8 +4,16 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
+
+// Forward scratch of ssd_fwd_noalloc: a device global, so every GPU the
+// library runs on holds its own copy (allocated when the code object is
+// loaded on that GPU, kept until the process ends).  Host code never uses
+// this name as an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[SSD_FWD_STATIC_SCRATCH_BYTES];
 
 namespace ssd {
 namespace {
@@ -217,53 +225,29 @@ bool dispatch_bwd(int dtype, const Layout& lay, const BwdArgs& a, hipStream_t st
 }  // namespace
 }  // namespace ssd
 
-using namespace ssd;
+namespace ssd {
+namespace {
 
-extern "C" {
-
-const char* ssd_version(void) { return "0.1.0"; }
-
-const char* ssd_status_string(ssd_status st) {
-  switch (st) {
-    case SSD_OK: return "ok";
-    case SSD_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case SSD_ERR_UNSUPPORTED: return "unsupported (dtype, chunk, headdim, dstate) combination";
-    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
-    case SSD_ERR_HIP: return "HIP error";
-  }
-  return "unknown status";
-}
-
-const char* ssd_kernel_name(int32_t k) {
-  static const char* names[SSD_NUM_KERNELS] = {
-      "cumsum_bmm", "chunk_state", "state_passing", "chunk_scan",
-      "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "bc_final", "da_dd"};
-  if (k < 0 || k >= SSD_NUM_KERNELS) return nullptr;
-  return names[k];
-}
-
-ssd_status ssd_check_shape(const ssd_shape* s) { return check_shape(s); }
-
-size_t ssd_saved_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).saved_bytes : 0; }
-size_t ssd_fwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).fwd_bytes : 0; }
-size_t ssd_bwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).bwd_bytes : 0; }
-
-ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
-                   const float* D, const float* dt_bias, const float* initial_state, void* y, float* final_state, void* saved_ws,
-                   size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch, size_t scratch_bytes,
-                   hipStream_t stream, const ssd_probe* probe) {
+// Argument checks of ssd_fwd other than its scratch (nothing is launched).
+ssd_status check_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                     const float* D, const float* dt_bias, const float* initial_state, const void* y,
+                     const float* final_state, const void* saved_ws, size_t saved_ws_bytes) {
   const ssd_status st = check_shape(s);
   if (st != SSD_OK) return st;
   if (!x || !dt || !A || !B || !C || !D || !y) return SSD_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {x, dt, A, B, C, D, y, saved_ws, scratch};
+  const void* ptrs[] = {x, dt, A, B, C, D, y, saved_ws, final_state, initial_state, dt_bias};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SSD_ERR_INVALID_ARGUMENT;
-  if (final_state && !aligned16(final_state)) return SSD_ERR_INVALID_ARGUMENT;
-  if (initial_state && !aligned16(initial_state)) return SSD_ERR_INVALID_ARGUMENT;
-  if (dt_bias && !aligned16(dt_bias)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!saved_ws || saved_ws_bytes < make_plan(s).saved_bytes) return SSD_ERR_WORKSPACE;
+  return SSD_OK;
+}
+
+// The forward's launches, after every check has passed.
+ssd_status fwd_launch(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                      const float* D, const float* dt_bias, const float* initial_state, void* y, float* final_state,
+                      void* saved_ws, size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch,
+                      hipStream_t stream, const ssd_probe* probe) {
   const Plan pl = make_plan(s);
-  if (!saved_ws || saved_ws_bytes < pl.saved_bytes) return SSD_ERR_WORKSPACE;
-  if (!scratch || scratch_bytes < pl.fwd_bytes) return SSD_ERR_WORKSPACE;
 
   const int64_t esz = s->dtype == SSD_F32 ? 4 : 2;                          // dt, y
   const int64_t eszx = s->dtype == SSD_F32 ? 4 : (s->dtype == SSD_FP8 ? 1 : 2);  // x, B, C
@@ -307,6 +291,100 @@ ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const floa
     saved_out->saved_ws_bytes = saved_ws_bytes;
   }
   return SSD_OK;
+}
+
+// Device address of `scratch` on the GPU that `stream` runs on, which must be
+// the current device (hipGetSymbolAddress resolves the current device's copy).
+// Looked up once per device with that device current and kept; the lookup is
+// the only state the library keeps, written once per device under a lock.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+ssd_status static_scratch(hipStream_t stream, void** out) {
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SSD_ERR_HIP;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return SSD_ERR_HIP;
+    if (sdev != cur) return SSD_ERR_INVALID_ARGUMENT;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return SSD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[cur]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+    g_scratch_dev[cur] = p;
+  }
+  *out = g_scratch_dev[cur];
+  return SSD_OK;
+}
+
+}  // namespace
+}  // namespace ssd
+
+using namespace ssd;
+
+extern "C" {
+
+const char* ssd_version(void) { return "0.1.0"; }
+
+const char* ssd_status_string(ssd_status st) {
+  switch (st) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported (dtype, chunk, headdim, dstate) combination";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP error";
+    case SSD_ERR_TOO_LARGE:
+      return "problem too large for ssd_fwd_noalloc: its forward scratch exceeds the library's static buffer "
+             "(SSD_FWD_STATIC_SCRATCH_BYTES); use ssd_fwd with a caller-allocated scratch";
+  }
+  return "unknown status";
+}
+
+const char* ssd_kernel_name(int32_t k) {
+  static const char* names[SSD_NUM_KERNELS] = {
+      "cumsum_bmm", "chunk_state", "state_passing", "chunk_scan",
+      "chunk_state_bwd", "state_passing_bwd", "chunk_scan_bwd", "dw_heads", "bc_final", "da_dd"};
+  if (k < 0 || k >= SSD_NUM_KERNELS) return nullptr;
+  return names[k];
+}
+
+ssd_status ssd_check_shape(const ssd_shape* s) { return check_shape(s); }
+
+size_t ssd_saved_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).saved_bytes : 0; }
+size_t ssd_fwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).fwd_bytes : 0; }
+size_t ssd_bwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).bwd_bytes : 0; }
+
+ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
+                   const float* D, const float* dt_bias, const float* initial_state, void* y, float* final_state, void* saved_ws,
+                   size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch, size_t scratch_bytes,
+                   hipStream_t stream, const ssd_probe* probe) {
+  const ssd_status st = check_fwd(s, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, saved_ws,
+                                  saved_ws_bytes);
+  if (st != SSD_OK) return st;
+  if (!scratch || !aligned16(scratch)) return scratch ? SSD_ERR_INVALID_ARGUMENT : SSD_ERR_WORKSPACE;
+  if (scratch_bytes < make_plan(s).fwd_bytes) return SSD_ERR_WORKSPACE;
+  return fwd_launch(s, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, saved_ws, saved_ws_bytes,
+                    saved_out, scratch, stream, probe);
+}
+
+ssd_status ssd_fwd_noalloc(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B,
+                           const void* C, const float* D, const float* dt_bias, const float* initial_state, void* y,
+                           float* final_state, void* saved_ws, size_t saved_ws_bytes, ssd_saved* saved_out,
+                           hipStream_t stream, const ssd_probe* probe) {
+  const ssd_status st = check_fwd(s, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, saved_ws,
+                                  saved_ws_bytes);
+  if (st != SSD_OK) return st;
+  if (make_plan(s).fwd_bytes > (size_t)SSD_FWD_STATIC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+  void* scr = nullptr;
+  const ssd_status ss = static_scratch(stream, &scr);
+  if (ss != SSD_OK) return ss;
+  // nothing in the forward scratch needs to start at zero: the chunk states
+  // are written before they are read, the padded step rows of a shorter last
+  // chunk are written whole by the padding launch and its y rows by the scan
+  return fwd_launch(s, x, dt, A, B, C, D, dt_bias, initial_state, y, final_state, saved_ws, saved_ws_bytes,
+                    saved_out, scr, stream, probe);
 }
 
 ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_state, void* dx, void* ddt, float* dA,

@@ -126,6 +126,33 @@ def test_fwd_rejects_before_launch(lib):
                        None, None) == INVALID
 
 
+def test_fwd_noalloc_rejects_before_launch(lib):
+    # the no-allocation forward checks its arguments like ssd_fwd, and a problem
+    # whose forward scratch exceeds the static buffer before it touches the GPU
+    def fwd_na(s, ws_bytes, **over):
+        a = dict(x=FAKE, y=FAKE, ws=FAKE, s0=None)
+        a.update(over)
+        return lib.ssd_fwd_noalloc(ctypes.byref(s) if s is not None else None, a["x"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, a["s0"], a["y"], FAKE, a["ws"], ws_bytes, None, None, None)
+
+    s = shape()
+    need_ws = lib.ssd_saved_bytes(ctypes.byref(s))
+    assert fwd_na(None, 0) == INVALID
+    assert fwd_na(shape(nheads=5), need_ws) == INVALID
+    assert fwd_na(shape(headdim=48), need_ws) == UNSUPPORTED
+    assert fwd_na(s, need_ws, x=None) == INVALID and fwd_na(s, need_ws, y=None) == INVALID
+    assert fwd_na(s, need_ws, x=FAKE + 8) == INVALID and fwd_na(s, need_ws, s0=FAKE + 4) == INVALID
+    assert fwd_na(s, need_ws - 1) == WORKSPACE and fwd_na(s, need_ws, ws=None) == WORKSPACE
+    # the long-context shape (1 x 65536 tokens, 80 heads of 64 x 128, bf16) needs 320 MiB of chunk states
+    big = shape(batch=1, seqlen=65536, nheads=80, ngroups=8)
+    assert lib.ssd_fwd_scratch_bytes(ctypes.byref(big)) > _lib.SSD_FWD_STATIC_SCRATCH_BYTES
+    assert fwd_na(big, lib.ssd_saved_bytes(ctypes.byref(big))) == _lib.SSD_ERR_TOO_LARGE
+    # the 2.7B shape fits (80 MiB)
+    fits = shape(batch=4, seqlen=4096, nheads=80, ngroups=1)
+    assert lib.ssd_fwd_scratch_bytes(ctypes.byref(fits)) <= _lib.SSD_FWD_STATIC_SCRATCH_BYTES
+    assert "static buffer" in _lib.status_string(_lib.SSD_ERR_TOO_LARGE)
+
+
 def test_bwd_rejects_before_launch(lib):
     s = shape()
     sv = _lib.Saved(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, lib.ssd_saved_bytes(ctypes.byref(s)))
@@ -153,7 +180,7 @@ def test_bwd_rejects_before_launch(lib):
 
 def test_strings(lib):
     assert lib.ssd_version().decode().count(".") == 2
-    for code in range(5):
+    for code in range(6):
         assert lib.ssd_status_string(code)
     for i, n in enumerate(_lib.KERNELS):
         assert lib.ssd_kernel_name(i).decode() == n
