@@ -96,7 +96,7 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   y.dapart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   y.ddpart_off = o; o += align_up((size_t)(y.b * y.K * y.H) * 4);
   const int64_t nsp = scan_bwd_splits((int)y.Q);
-  y.dlpart_off = o; o += align_up((size_t)(y.b * y.K * y.H * (nsp + 3) * y.Q) * 4);
+  y.dlpart_off = o; o += align_up((size_t)(y.b * y.K * y.H * dl_rows((int)y.Q) * y.Q) * 4);
   y.dlscal_off = o; o += align_up((size_t)(y.b * y.K * y.H * (nsp + 1)) * 4);
   y.bwd_bytes = o;
   return y;

@@ -14,8 +14,10 @@ namespace ssd {
 //   dl    = reverse cumsum of dcs inside the chunk
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dx_j = dt_j dxt_j + D dy_j
 // This kernel writes dx and, per token, the partial sums that dl is formed
-// from (row sums, column sums, q_j, <dxt_j, x_j>); k_dl_assemble finishes dl,
-// ddt and the chunk's dA / dD partials.
+// from (row sums, column sums, q_j, <dxt_j, x_j>); the state-to-output term
+// exp(cs_i) <dy_i, Hin^T C_i> comes from the chunk-state gradient kernel,
+// which has dy and C staged already, and k_dl_assemble finishes dl, ddt and
+// the chunk's dA / dD partials.
 //
 // Layout of the work.  NSPLIT workgroups of 4 waves share one (b, k, h);
 // the chunk's 16-token column tiles J are dealt to the 4 NSPLIT waves in a
@@ -24,13 +26,19 @@ namespace ssd {
 // as matrix-core accumulators (lane (q, c) holds dxt[16J + c][16tp + 4q + r]),
 // so every token's x and dxt values sit in the same lane and slot: <dxt_j, x_j>
 // and q_j need no second read of x.
-// This head's dy rows, the group's C rows and the owned C.B^T tiles stream
-// through LDS in 32-row slabs from the chunk end backwards (double-buffered:
-// the next slab is loaded into registers while the current one is used; C
-// and the tiles mostly hit in L2, which they share with the other heads of
-// the group).  Every use of dy falls in the slab being processed, so LDS
-// holds two slabs of it, not the whole chunk; the dy^T operands come from it
-// through transposing reads.  A column tile's dxt is complete once the slab holding its
+// This head's dy rows and the owned C.B^T tiles stream through LDS in 32-row
+// slabs from the chunk end backwards (the tiles mostly hit in L2, which they
+// share with the other heads of the group).  bf16 with headdim 64 copies the
+// slabs from global memory straight into LDS (global_load_lds, 16 bytes per
+// lane written at the wave's LDS base + 16 * lane: no registers, no LDS
+// stores) three slabs ahead of the one in use, into four buffers; every
+// other shape stages one slab ahead through registers.  The loop keeps its
+// global stores (dx and the per-token sums) until after its last slab, so
+// the only memory operations in flight in it are these copies and a slab is
+// known to have landed once at most the copies issued after it are
+// outstanding.  Every use of dy falls in the
+// slab being processed, so LDS holds two slabs of it, not the whole chunk;
+// the dy^T operands come from it through transposing reads.  A column tile's dxt is complete once the slab holding its
 // own rows has been used, so dx is written right there.
 // R is formed once per (I, J) tile pair on the matrix cores: lanes own a
 // column j, so column sums accumulate in-lane and row sums come from 16-lane
@@ -55,8 +63,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr int NSLOT = NT / NO;          // column tiles per wave
   constexpr int SR = 32;                  // rows per slab
   constexpr int VN = Vec16<T>::n;
-  constexpr int CUP = P / VN, CUN = N / VN;
-  constexpr int YPIECES = SR * CUP, CPIECES = SR * CUN;  // 16-byte pieces: dy slab, C slab
+  constexpr int CUP = P / VN;
+  constexpr int YPIECES = SR * CUP;       // 16-byte pieces of a dy slab
   // dy rows.  bf16 with headdim 64: unpadded, the 16-byte pieces of row r
   // XOR-permuted by f(r) = 2 ((r / 2) mod 4) + (r / 8) mod 2, so that the
   // transposing dy^T reads (per half-wave 8 rows x 32 bytes) and the row
@@ -64,7 +72,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   // pitch of 8 (mod 16) dwords, which serves the transposing reads.
   constexpr bool DSWZ = sizeof(T) == 2 && P == 64;
   constexpr int DPITCH = DSWZ ? P : sizeof(T) == 2 ? P + 2 * ((24 - (P / 2) % 16) % 16) : P + PADR;
-  constexpr int YPT = (YPIECES + NTH - 1) / NTH, CPT = (CPIECES + NTH - 1) / NTH;
+  constexpr bool DMA = DSWZ;               // slabs copied global -> LDS directly
+  constexpr int PF = DMA ? 3 : 1;          // slabs in flight ahead of the one in use
+  constexpr int NBUF = DMA ? PF + 1 : 2;   // slab buffers
+  constexpr int YPT = (YPIECES + NTH - 1) / NTH;
   // C.B^T tiles of a slab: rows I = 2s + half against every owned column tile
   // of this workgroup, slot (half, wave, sl); tiles with J > I stay unused
   constexpr int WT = 2 * NW * NSLOT;
@@ -78,9 +89,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   static_assert(NSPLIT == 1 || NSPLIT == 2, "a split owns one row tile of each slab");
   typedef typename Vec4<T>::type V4;
   typedef typename Vec16<T>::type V;
-  __shared__ __attribute__((aligned(16))) T DY[2][SR][DPITCH];     // slab rows of this head's dy
-  __shared__ __attribute__((aligned(16))) T Cs[2][SR][N + PADR];    // slab rows of C
-  __shared__ __attribute__((aligned(16))) T Ws[2][WT * 256];        // slab C.B^T tiles (lane order)
+  // slab buffers: this head's dy rows and the slab's C.B^T tiles (lane order).
+  // Each buffer is an array of its own, and the slab loop is unrolled over
+  // them, so the compiler can tell the buffer being read from the ones being
+  // filled by copies in flight (it does not wait for a copy before an LDS
+  // read of another array)
+  __shared__ __attribute__((aligned(16))) T DY0[SR][DPITCH], DY1[SR][DPITCH];
+  __shared__ __attribute__((aligned(16))) T DY2[DMA ? SR : 1][DPITCH], DY3[DMA ? SR : 1][DPITCH];
+  __shared__ __attribute__((aligned(16))) T W0[WT * 256], W1[WT * 256];
+  __shared__ __attribute__((aligned(16))) T W2[DMA ? WT * 256 : 1], W3[DMA ? WT * 256 : 1];
+  // Gk (DMA path): read by every wave, so it is copied into LDS once instead
+  // of each wave fetching all of it; 16-byte pieces of row r XOR-permuted by
+  // r mod (N / 8), so the 16 rows of a fragment read meet distinct banks
+  __shared__ __attribute__((aligned(16))) T GS[DMA ? P : 1][DMA ? N : 1];
+  static_assert(NBUF == 2 || NBUF == 4, "slab buffers");
   __shared__ __attribute__((aligned(16))) float cs[Q];
   __shared__ __attribute__((aligned(16))) float dts[Q];
   __shared__ __attribute__((aligned(16))) float ecs[Q];    // exp(cs_i)
@@ -104,17 +126,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   x = rows_in(rm, k, x, rm.x);
   const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   B = rows_in(rm, k, B, rm.B);
-  C = rows_in(rm, k, C, rm.C);
   dy = rows_in(rm, k, dy, rm.dy);
   dx = rows_out(rm, k, dx, rm.dx);
   const int64_t rs = (int64_t)H * P;      // row stride of x / dy / dx
   const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * rs
   const T* xh = x + (row0 * H + h) * P;
-  const T* ch = C + (row0 * G + g) * N;    // row i: ch + i * G * N
   const T* wbb = wb + (int64_t)((b * K + k) * G + g) * TILES * 256;
   const T* hinh = hin + (int64_t)bkh * P * N;
   const T* gsth = gst + (int64_t)bkh * P * N;
-  float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;  // rows: splits' row sums, column sums, q, <dxt, x>
+  float* part = dlpart + (int64_t)bkh * dl_rows(Q) * Q;  // rows: splits' row sums, column sums, q, <dxt, x>
 
   // column tile of wave w, slot sl, in this split
   auto tile_of = [&](int w, int sl) {
@@ -125,20 +145,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) Js[sl] = tile_of(wave, sl);
 
-  // ---- slab staging: registers <- global (next slab), LDS <- registers
-  V yv[YPT], cv[CPT], wv[WPT];
-  auto slab_load = [&](int s) {
+  // ---- slab staging: registers <- global (a slab ahead of the one next in
+  // LDS), LDS <- registers
+  struct SlabRegs { V yv[YPT], wv[WPT]; };
+  SlabRegs ra;
+  auto slab_load = [&](SlabRegs& R, int s) {
 #pragma unroll
     for (int n = 0; n < YPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (YPIECES % NTH == 0 || u < YPIECES)
-        yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * s + u / CUP) * rs + (u % CUP) * VN);
-    }
-#pragma unroll
-    for (int n = 0; n < CPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (CPIECES % NTH == 0 || u < CPIECES)
-        cv[n] = *reinterpret_cast<const V*>(ch + (int64_t)(SR * s + u / CUN) * G * N + (u % CUN) * VN);
+        R.yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * s + u / CUP) * rs + (u % CUP) * VN);
     }
 #pragma unroll
     for (int n = 0; n < WPT; ++n) {
@@ -149,24 +165,40 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       // tiles with J > I are never read: load the in-range tile (I, I) instead, so
       // the loads carry no branch
       if (WPIECES % NTH == 0 || u < WPIECES)
-        wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + piece * VN);
+        R.wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + piece * VN);
     }
   };
-  auto slab_store = [&](int bf) {
+  auto slab_store = [&](const SlabRegs& R, T (*dyb)[DPITCH], T* wtb) {
 #pragma unroll
     for (int n = 0; n < YPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (YPIECES % NTH == 0 || u < YPIECES) *reinterpret_cast<V*>(&DY[bf][u / CUP][dyc(u / CUP, (u % CUP) * VN)]) = yv[n];
-    }
-#pragma unroll
-    for (int n = 0; n < CPT; ++n) {
-      const int u = threadIdx.x + NTH * n;
-      if (CPIECES % NTH == 0 || u < CPIECES) *reinterpret_cast<V*>(&Cs[bf][u / CUN][(u % CUN) * VN]) = cv[n];
+      if (YPIECES % NTH == 0 || u < YPIECES)
+        *reinterpret_cast<V*>(&dyb[u / CUP][dyc(u / CUP, (u % CUP) * VN)]) = R.yv[n];
     }
 #pragma unroll
     for (int n = 0; n < WPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (WPIECES % NTH == 0 || u < WPIECES) *reinterpret_cast<V*>(&Ws[bf][u * VN]) = wv[n];
+      if (WPIECES % NTH == 0 || u < WPIECES) *reinterpret_cast<V*>(&wtb[u * VN]) = R.wv[n];
+    }
+  };
+  // global -> LDS copies of slab s into buffer (dyb, wtb): thread t's 16 bytes land at
+  // byte 16 t of the buffer, so it fetches the piece the swizzled layout keeps
+  // there (dy row t / 8, LDS piece t % 8 holds global piece (t % 8) ^ f(row))
+  constexpr int DPS = YPT + WPT;           // copies per thread and slab
+  static_assert(!DMA || (YPIECES == NTH && WPIECES % NTH == 0 && 2 * DPS <= 15), "slab copies");
+  auto slab_dma = [&](int s, T (*dyb)[DPITCH], T* wtb) {
+    const int t = threadIdx.x, r = t / CUP;
+    const int kp = (t % CUP) ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    lds_copy16(dyh + (int64_t)(SR * s + r) * rs + kp * VN, &dyb[0][0] + wave * kWave * VN);
+#pragma unroll
+    for (int n = 0; n < WPT; ++n) {
+      const int u = t + NTH * n;
+      const int tt = u / (256 / VN), piece = u % (256 / VN);
+      const int half = tt / (NW * NSLOT), w = (tt / NSLOT) % NW, sl = tt % NSLOT;
+      const int I = 2 * s + half, J = tile_of(w, sl);
+      // a slot with J > I is never read: its lanes all fetch the group's first
+      // tile, so they coalesce instead of moving a tile each
+      lds_copy16(wbb + (J <= I ? (int64_t)tri_index(I, J) * 256 : 0) + piece * VN, &wtb[(NTH * n + wave * kWave) * VN]);
     }
   };
 
@@ -184,26 +216,50 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       dtv[n] = dtc[i];
     }
   }
-  slab_load(NS - 1);
+  constexpr int NPC = N / VN;  // 16-byte pieces of a G row
+  if constexpr (DMA) {
+    static_assert((P * NPC) % NTH == 0 && (NPC & (NPC - 1)) == 0, "G copy");
+#pragma unroll
+    for (int n = 0; n < P * NPC / NTH; ++n) {
+      const int pp = n * NTH + threadIdx.x, r = pp / NPC, pc = (pp % NPC) ^ (r & (NPC - 1));
+      lds_copy16(gsth + r * N + pc * VN, &GS[0][0] + (n * NTH + wave * kWave) * VN);
+    }
+  } else {
+    slab_load(ra, NS - 1);
+  }
   Frag<T> xf[NSLOT][NKP];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl)
 #pragma unroll
     for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(xf[sl][kp], xh + (int64_t)(16 * Js[sl] + c) * rs, kp * 32, q);
-  // Hin rows 16 tw .. 16 tw + 15 (this wave's share of the C.Hin^T products)
-  const int tw = wave % TP;
+  // Hin rows 16 w .. 16 w + 15 (split 0, waves 0 .. TP-1: their share of <Gk, Hin>)
+  const bool gh_wave = split == 0 && wave < TP;
   Frag<T> hf[NK];
+  if (gh_wave) {
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(hf[ks], hinh + (16 * tw + c) * N, ks * 32 + 8 * q);
-  Frag<T> gf[NK][TP], bfr[NK][NSLOT];
+    for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(hf[ks], hinh + (16 * wave + c) * N, ks * 32 + 8 * q);
+  }
+  [[maybe_unused]] Frag<T> gf[DMA ? 1 : NK][TP];
+  Frag<T> bfr[NK][NSLOT];
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks) {
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) frag_load_k<N>(gf[ks][tp], gsth + (16 * tp + c) * N, ks * 32 + 8 * q);
+      for (int tp = 0; tp < TP; ++tp) frag_load_k<N>(gf[ks][tp], gsth + (16 * tp + c) * N, ks * 32 + 8 * q);
+    }
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl)
       frag_load_k<N>(bfr[ks][sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
   }
+  // fragment of Gk rows 16 tp .. 16 tp + 15, K-values ks * 32 + 8q .. (lane (q, c))
+  auto gfrag = [&](Frag<T>& f, int ks, int tp) {
+    if constexpr (DMA) {
+      const int r = 16 * tp + c;
+      frag_load(f, &GS[r][(((ks * 32 + 8 * q) / VN) ^ (r & (NPC - 1))) * VN]);
+    } else {
+      f = gf[ks][tp];
+    }
+  };
 
   // LDS stores of the per-token scalars (their loads were issued first) and
   // the row factors every slab uses, formed once here instead of by every
@@ -221,6 +277,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     }
   }
 
+  if constexpr (DMA) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this thread's copies of Gk have landed
+    __syncthreads();                     // everyone's, and the per-token scalars
+  }
   // state part of dxt^T: e_j (Gk B_j^T) with K = dstate
   f4 adx[NSLOT][TP];
 #pragma unroll
@@ -230,25 +290,34 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
   for (int ks = 0; ks < NK; ++ks)
 #pragma unroll
-    for (int sl = 0; sl < NSLOT; ++sl)
+    for (int tp = 0; tp < TP; ++tp) {
+      Frag<T> gk;
+      gfrag(gk, ks, tp);
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], gf[ks][tp], bfr[ks][sl]);
-  // <Gk, Hin>: waves 0 .. TP-1 of split 0 each cover Hin rows 16 tp .. 16 tp + 15
+      for (int sl = 0; sl < NSLOT; ++sl) mma(adx[sl][tp], gk, bfr[ks][sl]);
+    }
+  // <Gk, Hin>: waves 0 .. TP-1 of split 0 each cover Hin rows 16 w .. 16 w + 15
   float gh = 0.0f;
+  if (gh_wave) {
 #pragma unroll
-  for (int tp = 0; tp < TP; ++tp) {
-    if (split != 0 || tp != wave) continue;
+    for (int tp = 0; tp < TP; ++tp) {
+      if (tp != wave) continue;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks)
+      for (int ks = 0; ks < NK; ++ks) {
+        Frag<T> gk;
+        gfrag(gk, ks, tp);
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) gh += frag_get(gf[ks][tp], s8) * frag_get(hf[ks], s8);
+        for (int s8 = 0; s8 < 8; ++s8) gh += frag_get(gk, s8) * frag_get(hf[ks], s8);
+      }
+    }
   }
-  slab_store(0);
+  if constexpr (!DMA) slab_store(ra, DY0, W0);
   __syncthreads();
 
   const float cs_last = cs[Q - 1];
   const float Dh = Dp[h];
   // e_j scaling and q_j = dt_j <x_j, e_j B_j^T Gk>  (j = 16 J + c in this lane)
+  float qsv[NSLOT], csv2[NSLOT], xdv[NSLOT];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) {
     const int j = 16 * Js[sl] + c;
@@ -262,8 +331,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         qs += adx[sl][tp][r] * frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
       }
     }
-    qs = sum_q(qs) * dts[j];
-    if (q == 0) part[(NSPLIT + 1) * Q + j] = qs;
+    qsv[sl] = sum_q(qs) * dts[j];
   }
 
   float colsum[NSLOT];
@@ -271,9 +339,34 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   for (int sl = 0; sl < NSLOT; ++sl) colsum[sl] = 0.0f;
   float dd = 0.0f;
 
-  for (int it = 0; it < NS; ++it) {
-    const int s = NS - 1 - it, bf = it & 1;
-    if (it + 1 < NS) slab_load(s - 1);
+  if constexpr (DMA) {
+    slab_dma(NS - 1, DY0, W0);
+    if (NS >= 2) slab_dma(NS - 2, DY1, W1);
+    if (NS >= 3) slab_dma(NS - 3, DY2, W2);
+  }
+  // slab s = NS - 1 - it, read from (dys, wts); (dyn, wtn) is the buffer the
+  // slab PF ahead is copied into (DMA) or the next slab is stored into
+  auto slab_step = [&](int it, T (*dys)[DPITCH], const T* wts, T (*dyn)[DPITCH], T* wtn) {
+    const int s = NS - 1 - it;
+    if constexpr (DMA) {
+      // slab s has landed once at most the copies of the min(PF - 1, s) slabs
+      // issued after it are in flight (s_waitcnt vmcnt(n) lgkmcnt(0))
+      const int younger = min(PF - 1, s);
+      if (younger >= 2) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * DPS));
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(0x0070 | DPS);
+      else __builtin_amdgcn_s_waitcnt(0x0070);
+      // every thread's copies of slab s are in LDS, and the buffer copied into
+      // next was last read in the previous step.  A plain s_barrier: the
+      // workgroup fence of __syncthreads would also wait for the copies still
+      // in flight.  The signal fences keep the compiler from moving LDS
+      // accesses across it.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (s - PF >= 0) slab_dma(s - PF, dyn, wtn);
+    } else {
+      if (it + 1 < NS) slab_load(ra, s - 1);
+    }
     const int rb = 32 * s;  // first row of the slab
 
     // row sums of this slab's two row tiles (per lane: rows rb + 16 half + 4q + r)
@@ -283,46 +376,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
       for (int r = 0; r < 4; ++r) rowtot[half][r] = 0.0f;
 
-    // state -> output part: exp(cs_i) <dy_i, Hin^T C_i> over this wave's 16
-    // columns p.  Split sp takes the slab's row tile sp (all of them when
-    // there is one split); its TP output tiles are dealt over the waves.
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (NSPLIT == 2 && half != split) continue;
-      if (((NSPLIT == 2 ? 0 : half * TP) + tw) % NW != wave) continue;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NK; ++ks) {
-        Frag<T> fa;
-        frag_load_k<N>(fa, &Cs[bf][16 * half + c][0], ks * 32 + 8 * q);
-        mma(acc, fa, hf[ks]);
-      }
-      const f4 ei = *reinterpret_cast<const f4*>(&ecs[rb + 16 * half + 4 * q]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int yr = 16 * half + 4 * q + r;
-        rowtot[half][r] += ei[r] * (acc[r] * to_f(DY[bf][yr][dyc(yr, 16 * tw + c)]));
-      }
-    }
-
     // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
     Frag<T> fdt[TP];
 #pragma unroll
     for (int tp = 0; tp < TP; ++tp) {
       if constexpr (DSWZ) {  // rows 4q + c/4 and 16 below (same permutation)
         const int r0 = 4 * q + (c >> 2), col = 16 * tp + 4 * (c & 3);
-        frag_load_kmajor_at(fdt[tp], &DY[bf][r0][dyc(r0, col)], &DY[bf][r0 + 16][dyc(r0, col)]);
+        frag_load_kmajor_at(fdt[tp], &dys[r0][dyc(r0, col)], &dys[r0 + 16][dyc(r0, col)]);
       } else {
-        frag_load_kmajor<SR>(fdt[tp], &DY[bf][0][0], DPITCH, 0, 16 * tp, q, c);
+        frag_load_kmajor<SR>(fdt[tp], &dys[0][0], DPITCH, 0, 16 * tp, q, c);
       }
     }
     // dy row 16 half + c as a chained-K A fragment (K = headdim, from kp * 32)
     auto dy_row_frag = [&](Frag<T>& fd, int half, int kp) {
       const int yr = 16 * half + c;
       if constexpr (DSWZ)
-        frag_load2(fd, &DY[bf][yr][dyc(yr, kp * 32 + 4 * q)], &DY[bf][yr][dyc(yr, kp * 32 + 16 + 4 * q)]);
+        frag_load2(fd, &dys[yr][dyc(yr, kp * 32 + 4 * q)], &dys[yr][dyc(yr, kp * 32 + 16 + 4 * q)]);
       else
-        frag_load_chained<P>(fd, &DY[bf][yr][0], kp * 32, q);
+        frag_load_chained<P>(fd, &dys[yr][0], kp * 32, q);
     };
 
     // intra-chunk pairs (I in this slab, J owned), I >= J.
@@ -353,7 +424,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       Frag<T> fa;                            // P[i][j] as the B operand (col j, K = i)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const V4 wt = *reinterpret_cast<const V4*>(&Ws[bf][((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
+        const V4 wt = *reinterpret_cast<const V4*>(&wts[((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float t = to_f(wt[r]) * arow[half][r];
@@ -385,7 +456,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
           }
           const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
-          const V4 wt = *reinterpret_cast<const V4*>(&Ws[bf][((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
+          const V4 wt = *reinterpret_cast<const V4*>(&wts[((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
@@ -433,7 +504,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       rowacc[wave][rb + 16 * (c >> 3) + 4 * q + ((c >> 1) & 3)] = sum16_spread8(v8);
     }
     // next slab into the other buffer (its last readers passed the previous barrier)
-    if (it + 1 < NS) slab_store(bf ^ 1);
+    if constexpr (!DMA) {
+      if (it + 1 < NS) slab_store(ra, dyn, wtn);
+    }
 
     // column tiles whose rows are in this slab are complete: dx, <dxt_j, x_j>, column sums
 #pragma unroll
@@ -441,31 +514,61 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       const int J = Js[sl];
       if ((J >> 1) != s) continue;
       const int j = 16 * J + c;
-      const float csum = sum_q(colsum[sl]);
+      csv2[sl] = sum_q(colsum[sl]);
       const float dtj = dts[j];
-      T* dxr = dx + ((row0 + j) * H + h) * P;
       float xd = 0.0f;
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const V4 dv = *reinterpret_cast<const V4*>(&DY[bf][j - rb][dyc(j - rb, 16 * tp + 4 * q)]);
-        V4 o;
+        const V4 dv = *reinterpret_cast<const V4*>(&dys[j - rb][dyc(j - rb, 16 * tp + 4 * q)]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float xv = frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
           const float dyv = to_f(dv[r]);
           xd += adx[sl][tp][r] * xv;
           dd += dyv * xv;
-          o[r] = from_f<T>(dtj * adx[sl][tp][r] + Dh * dyv);
+          adx[sl][tp][r] = dtj * adx[sl][tp][r] + Dh * dyv;   // dx, stored after the loop
         }
-        *reinterpret_cast<V4*>(dxr + 16 * tp + 4 * q) = o;
       }
-      xd = sum_q(xd);
-      if (q == 0) {
-        part[NSPLIT * Q + j] = csum;
-        part[(NSPLIT + 2) * Q + j] = xd;
-      }
+      xdv[sl] = sum_q(xd);
     }
-    __syncthreads();
+    if constexpr (!DMA) __syncthreads();
+  };
+  if constexpr (DMA) {
+    // every slab is its own copy of the step (NS <= 8), so each step's buffers
+    // are fixed at compile time with no loop-carried state to merge
+    static_assert(NS <= 8, "unrolled slab steps");
+    slab_step(0, DY0, W0, DY3, W3);
+    if constexpr (NS > 1) slab_step(1, DY1, W1, DY0, W0);
+    if constexpr (NS > 2) slab_step(2, DY2, W2, DY1, W1);
+    if constexpr (NS > 3) slab_step(3, DY3, W3, DY2, W2);
+    if constexpr (NS > 4) slab_step(4, DY0, W0, DY3, W3);
+    if constexpr (NS > 5) slab_step(5, DY1, W1, DY0, W0);
+    if constexpr (NS > 6) slab_step(6, DY2, W2, DY1, W1);
+    if constexpr (NS > 7) slab_step(7, DY3, W3, DY2, W2);
+  } else {
+    for (int it = 0; it < NS; it += 2) {
+      slab_step(it, DY0, W0, DY1, W1);
+      if (it + 1 < NS) slab_step(it + 1, DY1, W1, DY0, W0);
+    }
+  }
+
+  // dx of the owned column tiles and their per-token sums
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int j = 16 * Js[sl] + c;
+    T* dxr = dx + ((row0 + j) * H + h) * P;
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) {
+      V4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = from_f<T>(adx[sl][tp][r]);
+      *reinterpret_cast<V4*>(dxr + 16 * tp + 4 * q) = o;
+    }
+    if (q == 0) {
+      part[NSPLIT * Q + j] = csv2[sl];
+      part[(NSPLIT + 1) * Q + j] = qsv[sl];
+      part[(NSPLIT + 2) * Q + j] = xdv[sl];
+    }
   }
 
   // this split's row sums (fixed wave order) and scalars
@@ -490,8 +593,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 }
 
 // dl, ddt and the chunk's dA / dD partials from the per-token partial sums of
-// k_chunk_scan_bwd:
-//   dl_j = sum_{i >= j} (row sum_i - column sum_i)  [suffix sum]
+// k_chunk_scan_bwd and (the state-to-output term t_i, in ntp headdim-tile
+// shares) of the chunk-state gradient:
+//   dl_j = sum_{i >= j} (row sum_i + t_i - column sum_i)  [suffix sum]
 //        + sum_{j' < j} q_j'                          [exclusive prefix sum]
 //        + exp(cs_{Q-1}) <Gk, Hin_k>
 // (the q terms, added at the chunk end and subtracted at each token, are
@@ -506,7 +610,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
                                                      float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
-                                                     int softplus) {
+                                                     int softplus, int ntp) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
   constexpr int HPB = 4;                      // heads (waves) per workgroup
   constexpr int TPL = Q / kWave;
@@ -521,7 +625,7 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   ddt = rows_out(rm, k, ddt, rm.ddt);
-  const float* part = dlpart + (int64_t)bkh * (NSPLIT + 3) * Q;
+  const float* part = dlpart + (int64_t)bkh * dl_rows(Q) * Q;
   const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
   const int j0 = jl * TPL;
   float v[TPL], qp[TPL];
@@ -530,7 +634,9 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
     float rs = part[j0 + t];
 #pragma unroll
     for (int sp = 1; sp < NSPLIT; ++sp) rs += part[sp * Q + j0 + t];
-    v[t] = rs - part[NSPLIT * Q + j0 + t];
+    float ts = part[(NSPLIT + 3) * Q + j0 + t];
+    for (int tp = 1; tp < ntp; ++tp) ts += part[(NSPLIT + 3 + tp) * Q + j0 + t];
+    v[t] = (rs + ts) - part[NSPLIT * Q + j0 + t];
     qp[t] = part[(NSPLIT + 1) * Q + j0 + t];
   }
 #pragma unroll
@@ -1096,7 +1202,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
-    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, static_cast<T*>(a.dhloc), a.rows, b, H, G, K, st);
+    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, static_cast<T*>(a.dhloc), hin, a.dlpart, a.rows, b, H, G,
+                                            K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
@@ -1109,7 +1216,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     k_chunk_scan_bwd<T, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     k_dl_assemble<T, Q><<<dim3(b * K * ((H + 3) / 4)), dim3(256), 0, st>>>(
-        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus);
+        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
+        P / 16);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int nbkg = b * K * G;

@@ -162,6 +162,15 @@ __device__ __forceinline__ void frag_load_kmajor(Frag<float>& f, const float* ti
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane l's bytes land at lds_wave_base + 16 l, where
+// lds_wave_base is the same for the whole wave (checked on gfx950 with an
+// in-bounds probe).  Counted by vmcnt like any vector-memory load; the caller
+// waits for it (s_waitcnt vmcnt) before a barrier that publishes the data.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 // ---- LDS staging --------------------------------------------------------------
 // 4 consecutive storage elements (one lane's share of an accumulator tile).
 template <typename T> struct Vec4;

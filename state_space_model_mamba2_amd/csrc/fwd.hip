@@ -256,7 +256,8 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, static_cast<T*>(a.S), a.rows, b, H, G, K, st);
+    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, static_cast<T*>(a.S), nullptr, nullptr, a.rows, b, H, G,
+                                              K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);

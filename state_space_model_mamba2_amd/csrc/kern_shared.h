@@ -227,6 +227,12 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
 // Chunk state: out[b][k][h][p][n] = sum_i w_i U[kQ+i][h][p] V[kQ+i][g][n]
 //   forward  (BWD = false): U = x,  V = B, w_i = dt_i exp(cs_{Q-1} - cs_i)
 //   backward (BWD = true) : U = dy, V = C, w_i = exp(cs_i)
+// The backward also forms, from the same staged rows, each token's
+// state-to-output term of the chunk-scan gradient
+//   t_i = exp(cs_i) <dy_i, Hin_k^T C_i>      (Hin_k: the chunk's entry state)
+// as (Hin C^T) tiles with K = dstate, one headdim tile per wave: wave w
+// writes its 16 headdim columns' share of t_i, and the chunk-scan gradient's
+// dl assembly adds the shares.
 // A (P x Q)(Q x N) product on the matrix cores with K = tokens.  Both
 // operands have K as their outer index in memory, so KB-token blocks of U
 // (rows scaled by w_i on the way) and V are staged row-major in LDS and both
@@ -238,7 +244,8 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
 template <typename T, typename TI, int Q, int P, int N, bool BWD, int HPW>
 __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
-                                                     T* __restrict__ out, const RowMap rm, int H, int G, int K,
+                                                     T* __restrict__ out, const T* __restrict__ hin,
+                                                     float* __restrict__ dlpart, const RowMap rm, int H, int G, int K,
                                                      int nitems) {
   constexpr int NTH = 256;
   constexpr int KB = 64;                           // tokens per block
@@ -270,6 +277,19 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
     csc[hh] = cs + (((int64_t)b * H + h0 + hh) * K + k) * Q;
     dtc[hh] = dt + (((int64_t)b * H + h0 + hh) * K + k) * Q;
     cs_last[hh] = csc[hh][Q - 1];
+  }
+
+  // backward: Hin rows 16 w .. 16 w + 15 of each head as A fragments (K = dstate)
+  constexpr int NKN = (N + 31) / 32, TPH = P / 16;
+  [[maybe_unused]] Frag<T> hfr[BWD ? HPW : 1][BWD ? NKN : 1];
+  if constexpr (BWD) {
+    if (wave < TPH) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+        for (int ks = 0; ks < NKN; ++ks)
+          frag_load_k<N>(hfr[hh][ks], hin + ((((int64_t)b * K + k) * H + h0 + hh) * P + 16 * wave + c) * N, ks * 32 + 8 * q);
+    }
   }
 
   V16 uv[HPW][UPT], vv[VPT];
@@ -346,6 +366,33 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
         }
       }
     }
+    if constexpr (BWD) {
+      // state-to-output term of the block's tokens, headdim tile `wave`:
+      // m[r] = (Hin C^T)[p = 16 wave + 4q + r][i = 16 rt + c], times the staged
+      // exp(cs_i) dy_i[p] and summed over p
+      if (wave < TPH) {
+        constexpr int NSP = scan_bwd_splits(Q);
+#pragma unroll
+        for (int rt = 0; rt < KB / 16; ++rt) {
+          Frag<T> fc[NKN];
+#pragma unroll
+          for (int ks = 0; ks < NKN; ++ks) frag_load_k<N>(fc[ks], &Vs[bf][16 * rt + c][0], ks * 32 + 8 * q);
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            f4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKN; ++ks) mma(m, hfr[hh][ks], fc[ks]);
+            const typename Vec4<T>::type u = *reinterpret_cast<const typename Vec4<T>::type*>(&Us[bf][hh][16 * rt + c][16 * wave + 4 * q]);
+            float t = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) t += m[r] * to_f(u[r]);
+            t = sum_q(t);
+            const int64_t bkhh = ((int64_t)b * K + k) * H + h0 + hh;
+            if (q == 0) dlpart[(bkhh * dl_rows(Q) + NSP + 3 + wave) * Q + KB * blk + 16 * rt + c] = t;
+          }
+        }
+      }
+    }
     if (blk + 1 < NB) store(bf ^ 1);
   }
 #pragma unroll
@@ -364,15 +411,17 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
 }
 
 // Launch of k_chunk_state: two heads per workgroup when a group's heads pair up.
+// hin / dlpart: the backward's chunk-entry states and dl partial sums (the
+// state-to-output term), unused (null) in the forward.
 template <typename T, typename TI, int Q, int P, int N, bool BWD>
-void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, T* out, const RowMap& rm,
-                        int b, int H, int G, int K, hipStream_t st) {
+void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, T* out, const T* hin,
+                        float* dlpart, const RowMap& rm, int b, int H, int G, int K, hipStream_t st) {
   if ((H / G) % 2 == 0)
-    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K,
-                                                                                            b * K * H / 2);
+    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(
+        U, V, dt, cs, out, hin, dlpart, rm, H, G, K, b * K * H / 2);
   else
-    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(U, V, dt, cs, out, rm, H, G, K,
-                                                                                        b * K * H);
+    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
+        U, V, dt, cs, out, hin, dlpart, rm, H, G, K, b * K * H);
 }
 
 // ---------------------------------------------------------------------------

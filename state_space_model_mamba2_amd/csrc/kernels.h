@@ -78,7 +78,7 @@ struct BwdArgs {
   float* dbpart;   // [nslice][b][K][Q][G][N] fp32 partials of dB (chunk rows)
   float* dapart;   // [b][K][H]
   float* ddpart;   // [b][K][H]
-  float* dlpart;   // [b][K][H][scan_bwd_splits(Q) + 3][Q]: per-token partial sums for dl
+  float* dlpart;   // [b][K][H][dl_rows(Q)][Q]: per-token partial sums for dl
   float* dlscal;   // [b][K][H][scan_bwd_splits(Q) + 1]: <Gk, Hin_k> and per-split sum <dy, x>
   RowMap rows;
 };
@@ -86,6 +86,11 @@ struct BwdArgs {
 // Workgroups that share one (batch, chunk, head) in the backward chunk kernel
 // (each owns an interleaved half of the chunk's 16-token column tiles).
 constexpr int scan_bwd_splits(int Q) { return Q >= 256 ? Q / 128 : 1; }
+// Rows of per-token partial sums that dl is formed from, per (b, k, h): the
+// splits' row sums of R, the column sums, q_j, <dxt_j, x_j> (chunk-scan
+// gradient) and up to four headdim tiles' shares of the state-to-output term
+// (chunk-state gradient).
+constexpr int dl_rows(int Q) { return scan_bwd_splits(Q) + 7; }
 
 // Kernel timing hook (see ssd_probe in the public header).
 struct ProbeScope {
