@@ -237,8 +237,9 @@ ssd_status ssd_conv1d_bwd(const ssd_conv_shape *shape, const void *x, const floa
                           const void *x_prev, const void *dy, void *dx, float *dw, float *dbias, void *dx_prev,
                           void *scratch, size_t scratch_bytes, hipStream_t stream);
 
-/* Static description of a status code. */
-const char *ssd_status_string(ssd_status status);
+/* Static description of a status code (an ssd_status value; any other
+ * value gives "unknown status"). */
+const char *ssd_status_string(int32_t status);
 
 /* Static name of a kernel id (NULL if out of range). */
 const char *ssd_kernel_name(int32_t kernel);

@@ -15,12 +15,16 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_LIB names another build of the same source (the sanitizer test
+# loads one built with AddressSanitizer); it is used as is, never rebuilt here.
+LIB_PATH = os.environ.get("SSD_ORACLE_LIB") or os.path.join(_HERE, "libssd_oracle.so")
 _lib = None
 
 
 def build(force: bool = False) -> str:
     """Compile the C oracle with gcc (float64, OpenMP)."""
+    if os.environ.get("SSD_ORACLE_LIB"):
+        return LIB_PATH
     if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
         tmp = LIB_PATH + ".tmp"
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",

@@ -36,10 +36,14 @@ ssd_status check_shape(const ssd_shape* s) {
     return SSD_ERR_INVALID_ARGUMENT;
   if (s->dtype != SSD_F32 && s->dtype != SSD_BF16 && s->dtype != SSD_FP8) return SSD_ERR_INVALID_ARGUMENT;
   if (s->nheads % s->ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
-  // Grid dimensions and 32-bit index products used inside the kernels.
+  // Grid dimensions and 32-bit index products used inside the kernels.  Every
+  // size is bounded first, so none of the products below can overflow.
+  const int64_t sizes[] = {s->batch, s->seqlen, s->nheads, s->headdim, s->dstate, s->ngroups, s->chunk};
+  for (int64_t v : sizes)
+    if (v > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
   const int64_t K = (s->seqlen + s->chunk - 1) / s->chunk;
-  if (s->batch * K * s->nheads > INT32_MAX || s->batch * s->nheads > 65535 ||
-      s->batch * s->seqlen > INT32_MAX / 4 || s->nheads > 65535)
+  if (s->nheads > 65535 || s->batch * s->nheads > 65535 || s->batch * s->seqlen > INT32_MAX / 4 ||
+      s->batch * K > INT32_MAX / s->nheads)
     return SSD_ERR_INVALID_ARGUMENT;
   if (!is_supported(s->dtype, s->chunk, s->headdim, s->dstate)) return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
@@ -328,7 +332,7 @@ extern "C" {
 
 const char* ssd_version(void) { return "0.1.0"; }
 
-const char* ssd_status_string(ssd_status st) {
+const char* ssd_status_string(int32_t st) {
   switch (st) {
     case SSD_OK: return "ok";
     case SSD_ERR_INVALID_ARGUMENT: return "invalid argument";
@@ -453,7 +457,7 @@ ssd_status conv_check(const ssd_conv_shape* s) {
   if (s->batch <= 0 || s->seqlen <= 0 || s->channels <= 0 || s->reserved != 0) return SSD_ERR_INVALID_ARGUMENT;
   if (s->dtype != SSD_F32 && s->dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
   if (s->silu != 0 && s->silu != 1) return SSD_ERR_INVALID_ARGUMENT;
-  if (s->batch * s->seqlen > INT32_MAX || s->channels > INT32_MAX / 8 || s->batch > 65535)
+  if (s->batch > 65535 || s->seqlen > INT32_MAX || s->channels > INT32_MAX / 8 || s->batch * s->seqlen > INT32_MAX)
     return SSD_ERR_INVALID_ARGUMENT;
   if (s->width < 2 || s->width > 4 || s->channels % 4 != 0) return SSD_ERR_UNSUPPORTED;
   // one workgroup row per block of run blocks (grid y)
