@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2_2p7b]
                     [--seqlen L] [--batch B] [--with-states] [--dt-softplus]
-                    [--dtype fp8 --fwd-only]
+                    [--dtype fp8] [--fwd-only]
     python bench.py --op conv1d [--workload mamba2_2p7b] [--batch B] [--seqlen L]
 
 A step is one ssd_fwd + ssd_bwd over one batch of the workload's seeded
@@ -13,8 +13,8 @@ seeded initial state and gives the backward a seeded final-state cotangent,
 returning the initial-state gradient as well (one GPU's share of a sequence
 split across GPUs); --dt-softplus passes the raw step and the per-head bias
 and lets the library apply softplus(dt_raw + dt_bias) (and return ddt_bias);
---dtype changes the storage mode (fp8: x, B, C as E4M3 codes, forward only, so
-it needs --fwd-only); --fwd-only times the forward pass alone.  Prints ONE JSON line on stdout;
+--dtype changes the storage mode (fp8: x, B, C as E4M3 codes, dy and the
+gradients bf16); --fwd-only times the forward pass alone.  Prints ONE JSON line on stdout;
 diagnostics (per-kernel times) go to stderr.
 
 Timing: W untimed warmup steps, then exactly K timed steps.  A 1 GiB write
@@ -78,6 +78,7 @@ def kernel_model(s, esz):
     nt = Q // 16
     tiles = nt * (nt + 1) // 2
     X = T * H * P * esz              # one x-sized tensor in the step dtype (y, dy, dx)
+    BCO = T * G * N * esz            # one of dB / dC (the step dtype)
     XI = T * H * P * eszx            # x as stored
     BC = T * G * N * eszx            # one of B / C
     DT = T * H * esz                 # dt / ddt in the caller's layout
@@ -90,17 +91,21 @@ def kernel_model(s, esz):
     tri = Q * (Q + 1) // 2
     bkh, bkg = b * K * H, b * K * G
     m = {
-        # dt in, cs and the float32 step out; B, C in, C.B^T tiles in both lane orders out
-        "cumsum_bmm": (DT + 2 * CS + 2 * BC + 2 * WT, 4 * bkg * tri * N),
+        # dt in, cs and the float32 step out; B, C in, C.B^T tiles out
+        "cumsum_bmm": (DT + 2 * CS + 2 * BC + WT, 2 * bkg * tri * N),
         "chunk_state": (XI + BC + 2 * CS + STe, 2 * bkh * Q * P * N),
         "state_passing": (2 * STe + b * H * P * N * 4, 0),
         "chunk_scan": (XI + X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
-        "chunk_state_bwd": (X + BC + CS + STe, 2 * bkh * Q * P * N),
+        # dy, C, cs, Hin in; dH_loc and the state-to-output term's headdim-tile shares out
+        "chunk_state_bwd": (X + BC + CS + 2 * STe + bkh * (P // 16) * Q * 4, 4 * bkh * Q * P * N),
         "state_passing_bwd": (2 * STe, 0),
-        "chunk_scan_bwd": (3 * X + DT + 2 * CS + 2 * BC + 2 * STe + WT, 2 * bkh * (2 * Q * N * P + 2 * tri * P)),
+        # x, dy, the step, cs, B, C, Gk, Hin (for <Gk, Hin>) in; dx out (+ dl assembly: ddt out).
+        # C.B^T is formed again per head in fp32 (the tri * N term)
+        "chunk_scan_bwd": (XI + 2 * X + DT + 2 * CS + 2 * BC + 2 * STe,
+                           2 * bkh * (Q * N * P + 2 * tri * P + tri * N)),
         # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in, dW out
-        "dw_heads": (2 * X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
-        "bc_final": (DW + 4 * BC, 4 * bkg * tri * N),  # dC and dB: dW, B, C in; dC, dB out
+        "dw_heads": (XI + X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
+        "bc_final": (DW + 2 * BC + 2 * BCO, 4 * bkg * tri * N),  # dC and dB: dW, B, C in; dC, dB out
         "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
     }
     return m
@@ -522,9 +527,6 @@ def main():
     over = {k: v for k, v in (("seqlen", args.seqlen), ("batch", args.batch), ("dtype", args.dtype))
             if v is not None}
     shape = inputs.workload(args.workload, **over)
-    if shape.dtype == "fp8" and not args.fwd_only:
-        print("fp8 storage is forward only: add --fwd-only", file=sys.stderr)
-        sys.exit(2)
     esz = 4 if shape.dtype == "f32" else 2
     log(f"[bench] workload {args.workload}: {shape}")
     t0 = time.perf_counter()

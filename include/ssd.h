@@ -33,12 +33,12 @@
  *                      [batch][nheads][headdim][dstate]    float32
  *                      (element [p][n] is the state's entry [n][p])
  * "dtype" is float32 (SSD_F32) or bfloat16 (SSD_BF16); accumulation is
- * always float32.  SSD_FP8 (forward only; ssd_bwd returns
- * SSD_ERR_UNSUPPORTED): x, B and C are OCP FP8 E4M3 codes (1 sign, 4
- * exponent bits with bias 7, 3 mantissa bits; one byte each, no scale),
- * every other dtype tensor bfloat16; C.B^T runs on the FP8 matrix cores and
- * the other products widen the codes to bfloat16 (exactly).  Every pointer is
- * a device pointer aligned to 16 bytes.
+ * always float32.  SSD_FP8: x, B and C are OCP FP8 E4M3 codes (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; one byte each, no scale) in
+ * both passes, every other dtype tensor (dt, y, dy, dx, ddt, dB, dC)
+ * bfloat16; the forward's C.B^T runs on the FP8 matrix cores and the other
+ * products widen the codes to bfloat16 (exactly).  Every pointer is a device pointer aligned
+ * to 16 bytes.
  *
  * Ownership: the caller allocates every buffer (inputs, outputs, the saved
  * workspace and the scratch workspaces); the library never allocates or frees
@@ -111,13 +111,14 @@ typedef struct {
 /* Kernel identifiers, for timing one kernel with an ssd_probe. */
 typedef enum {
     SSD_K_CUMSUM_BMM = 0,        /* one launch: per-chunk inclusive cumsum of dt*A, and C.B^T per chunk and
-                                    group in the forward and the backward lane order */
+                                    group for the forward chunk kernel */
     SSD_K_CHUNK_STATE = 1,       /* decay-weighted B^T x per chunk and head */
     SSD_K_STATE_PASSING = 2,     /* sequential inter-chunk state scan */
     SSD_K_CHUNK_SCAN = 3,        /* intra-chunk masked product + state-to-output + D x */
     SSD_K_CHUNK_STATE_BWD = 4,   /* exp(cs) C^T dy per chunk and head */
     SSD_K_STATE_PASSING_BWD = 5, /* reverse inter-chunk state scan */
-    SSD_K_CHUNK_SCAN_BWD = 6,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel + dl assembly) */
+    SSD_K_CHUNK_SCAN_BWD = 6,    /* dx, ddt and per-chunk dA/dD partials (chunk kernel, which forms C.B^T
+                                    again in fp32, + dl assembly) */
     SSD_K_DW_HEADS = 7,          /* one launch of the group-level head sums: masked dY.X^T (dW) and the
                                     dC / dB state terms, per chunk, group and head slice */
     SSD_K_BC_FINAL = 8,          /* dC and dB in one launch: slice sums + dW.B and dW^T.C */

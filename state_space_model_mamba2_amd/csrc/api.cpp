@@ -62,11 +62,10 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   size_t o = 0;
   y.cs_off = o;   o += align_up((size_t)(y.b * y.H * y.K * y.Q) * 4);
   y.hin_off = o;  o += align_up(states * y.esz);
-  y.wt_off = o;   o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
-  y.wtb_off = o;  o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.saved_bytes = o;
   o = 0;
   y.s_off = o;    o += align_up(states * y.esz);
+  y.wt_off = o;   o += align_up((size_t)(y.b * y.K * y.G * y.wtiles * 256) * y.esz);
   y.fwd_bytes = o;
   o = 0;
   y.dhloc_off = o;  o += align_up(states * y.esz);
@@ -136,7 +135,8 @@ Plan make_plan(const ssd_shape* s) {
   const size_t b = s->batch, H = s->nheads, P = s->headdim, N = s->dstate, G = s->ngroups, q = Q;
   const size_t xrows = tail ? align_up(b * q * H * P * eszx) : 0, trows = tail ? align_up(b * q * H * esz) : 0;
   const size_t yrows = tail ? align_up(b * q * H * P * esz) : 0;
-  const size_t brows = tail ? align_up(b * q * G * N * eszx) : 0;
+  const size_t brows = tail ? align_up(b * q * G * N * eszx) : 0;   // B, C rows as stored
+  const size_t grows = tail ? align_up(b * q * G * N * esz) : 0;    // dB, dC rows (bf16 also in FP8 mode)
   size_t o = p.lay.saved_bytes;
   p.sv_tx = o;   o += xrows;
   p.sv_tB = o;   o += brows;
@@ -152,8 +152,8 @@ Plan make_plan(const ssd_shape* s) {
   p.bw_tdy = o;  o += yrows;
   p.bw_tdx = o;  o += yrows;
   p.bw_tddt = o; o += trows;
-  p.bw_tdB = o;  o += brows;
-  p.bw_tdC = o;  o += brows;
+  p.bw_tdB = o;  o += grows;
+  p.bw_tdC = o;  o += grows;
   p.bw_dbias = o; if (sp) o += align_up(b * (size_t)p.lay.K * H * 4);
   p.bwd_bytes = o;
   return p;
@@ -171,15 +171,13 @@ const P* at(const void* base, size_t off) { return reinterpret_cast<const P*>(st
 void set_fwd_ws(FwdArgs& a, const Layout& lay, void* saved, void* scratch) {
   a.cs = at<float>(saved, lay.cs_off);
   a.hin = at<char>(saved, lay.hin_off);
-  a.wt = at<char>(saved, lay.wt_off);
-  a.wtb = at<char>(saved, lay.wtb_off);
+  a.wt = at<char>(scratch, lay.wt_off);
   a.S = at<char>(scratch, lay.s_off);
 }
 
 void set_bwd_ws(BwdArgs& a, const Layout& lay, const void* saved, void* scratch) {
   a.cs = at<float>(saved, lay.cs_off);
   a.hin = at<char>(saved, lay.hin_off);
-  a.w = at<char>(saved, lay.wtb_off);
   a.dhloc = at<char>(scratch, lay.dhloc_off);
   a.gst = at<char>(scratch, lay.g_off);
   a.dw = at<float>(scratch, lay.dw_off);
@@ -211,17 +209,20 @@ bool dispatch_fwd(int dtype, const Layout& lay, const FwdArgs& a, hipStream_t st
 }
 
 bool dispatch_bwd(int dtype, const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_probe* probe) {
-#define SSD_DISPATCH(TT, Q_, P_, N_)                        \
+#define SSD_DISPATCH(TT, TI, Q_, P_, N_)                    \
   if (lay.Q == Q_ && lay.P == P_ && lay.N == N_) {          \
-    run_bwd<TT, Q_, P_, N_>(lay, a, stream, probe);         \
+    run_bwd<TT, TI, Q_, P_, N_>(lay, a, stream, probe);     \
     return true;                                            \
   }
-#define SSD_DISPATCH_BF16(Q_, P_, N_) SSD_DISPATCH(bf16, Q_, P_, N_)
-#define SSD_DISPATCH_F32(Q_, P_, N_) SSD_DISPATCH(float, Q_, P_, N_)
+#define SSD_DISPATCH_BF16(Q_, P_, N_) SSD_DISPATCH(bf16, bf16, Q_, P_, N_)
+#define SSD_DISPATCH_FP8(Q_, P_, N_) SSD_DISPATCH(bf16, fp8, Q_, P_, N_)
+#define SSD_DISPATCH_F32(Q_, P_, N_) SSD_DISPATCH(float, float, Q_, P_, N_)
   if (dtype == SSD_BF16) { SSD_BF16_CONFIGS(SSD_DISPATCH_BF16) }
+  else if (dtype == SSD_FP8) { SSD_BF16_CONFIGS(SSD_DISPATCH_FP8) }
   else { SSD_F32_CONFIGS(SSD_DISPATCH_F32) }
 #undef SSD_DISPATCH
 #undef SSD_DISPATCH_BF16
+#undef SSD_DISPATCH_FP8
 #undef SSD_DISPATCH_F32
   return false;
 }
@@ -398,7 +399,6 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   const ssd_shape* s = &sv->shape;
   const ssd_status st = check_shape(s);
   if (st != SSD_OK) return st;
-  if (s->dtype == SSD_FP8) return SSD_ERR_UNSUPPORTED;  // FP8 operands: forward only
   if (!sv->x || !sv->dt || !sv->A || !sv->B || !sv->C || !sv->D || !dy || !dx || !ddt || !dA || !dB || !dC || !dD)
     return SSD_ERR_INVALID_ARGUMENT;
   const void* ptrs[] = {sv->x, sv->dt, sv->A, sv->B, sv->C, sv->D, dy, dx, ddt, dA, dB, dC, dD, sv->saved_ws, scratch,
@@ -409,7 +409,7 @@ ssd_status ssd_bwd(const ssd_saved* sv, const void* dy, const float* dfinal_stat
   if (!sv->saved_ws || sv->saved_ws_bytes < pl.saved_bytes) return SSD_ERR_WORKSPACE;
   if (!scratch || scratch_bytes < pl.bwd_bytes) return SSD_ERR_WORKSPACE;
 
-  const size_t esz = s->dtype == SSD_F32 ? 4 : 2;
+  const size_t esz = s->dtype == SSD_F32 ? 4 : 2;  // dy, dx, ddt, dB, dC (bf16 also in FP8 mode)
   const int64_t b = s->batch, L = s->seqlen, Q = s->chunk, H = s->nheads, G = s->ngroups;
   const int64_t P = s->headdim, N = s->dstate;
   BwdArgs a{};

@@ -26,9 +26,13 @@ namespace ssd {
 // as matrix-core accumulators (lane (q, c) holds dxt[16J + c][16tp + 4q + r]),
 // so every token's x and dxt values sit in the same lane and slot: <dxt_j, x_j>
 // and q_j need no second read of x.
-// This head's dy rows and the owned C.B^T tiles stream through LDS in 32-row
-// slabs from the chunk end backwards (the tiles mostly hit in L2, which they
-// share with the other heads of the group).  bf16 with headdim 64 copies the
+// This head's dy rows and the group's C rows stream through LDS in 32-row
+// slabs from the chunk end backwards (C mostly hits in L2, which it shares
+// with the other heads of the group).  W is formed per tile pair on the
+// matrix cores in fp32 from those C rows and the owned B_J fragments, which
+// stay in registers from the state term: dA sums R over the whole chunk with
+// much cancellation between row sums, column sums and the state terms, and
+// C.B^T rounded to bf16 moved dA by up to 3 % of its largest head.  bf16 with headdim 64 copies the
 // slabs from global memory straight into LDS (global_load_lds, 16 bytes per
 // lane written at the wave's LDS base + 16 * lane: no registers, no LDS
 // stores) three slabs ahead of the one in use, into four buffers; every
@@ -48,11 +52,32 @@ namespace ssd {
 // round-robin dispatch over the 8 XCDs runs them on one XCD (one L2) at
 // about the same time, and consecutive heads of a chunk (which share its C
 // and B rows and C.B^T tiles) run on the same XCD.
-template <typename T, int Q, int P, int N>
+// Piece swizzle of a staged C row r (NPC 16-byte pieces per row, CRPP rows
+// per 256 bytes of LDS): the 16 rows of one fragment read meet distinct banks.
+template <int NPC, int CRPP>
+__device__ __forceinline__ int cswz(int r) {
+  if constexpr (NPC == 1) return 0;
+  else return (r / CRPP) & ((NPC < 16 ? NPC : 16) - 1);
+}
+// Fragment of staged C row r with K-values k0 .. k0 + 7 (zero past N): one
+// piece for bf16 and FP8 (widened), two for fp32.
+template <int N, int NPC, int CRPP, typename T, typename TI>
+__device__ __forceinline__ void c_row_frag(Frag<T>& f, const TI* cb, int r, int k0) {
+  constexpr int EP = 16 / sizeof(TI);
+  auto at = [&](int kk) { return cb + r * N + ((kk / EP) ^ cswz<NPC, CRPP>(r)) * EP + kk % EP; };
+  if (N % 32 == 0 || k0 < N) {
+    if constexpr (sizeof(TI) == 4) frag_load2(f, at(k0), at(k0 + 4));
+    else frag_load(f, at(k0));
+  } else {
+    frag_zero(f);
+  }
+}
+
+template <typename T, typename TI, int Q, int P, int N>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
-    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
-    const T* __restrict__ B, const T* __restrict__ C, const T* __restrict__ hin, const T* __restrict__ gst,
-    const T* __restrict__ wb, const T* __restrict__ dy, T* __restrict__ dx, float* __restrict__ dlpart,
+    const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
+    const TI* __restrict__ B, const TI* __restrict__ C, const T* __restrict__ hin, const T* __restrict__ gst,
+    const T* __restrict__ dy, T* __restrict__ dx, float* __restrict__ dlpart,
     float* __restrict__ dlscal, int nitems, const RowMap rm, int H, int G, int K) {
   constexpr int NW = 4, NTH = NW * kWave;
   constexpr int NSPLIT = scan_bwd_splits(Q);
@@ -76,11 +101,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr int PF = DMA ? 3 : 1;          // slabs in flight ahead of the one in use
   constexpr int NBUF = DMA ? PF + 1 : 2;   // slab buffers
   constexpr int YPT = (YPIECES + NTH - 1) / NTH;
-  // C.B^T tiles of a slab: rows I = 2s + half against every owned column tile
-  // of this workgroup, slot (half, wave, sl); tiles with J > I stay unused
-  constexpr int WT = 2 * NW * NSLOT;
-  constexpr int WPIECES = WT * 256 / VN;
-  constexpr int WPT = (WPIECES + NTH - 1) / NTH;
+  // C rows of a slab, in their storage type: 16-byte pieces of EP elements,
+  // NPC per row, piece p of row r stored at p ^ cswz(r) so that the 16 rows
+  // of a fragment read meet distinct banks.  The last round of copies fills
+  // a spare tail of the buffer when a slab has fewer pieces than threads.
+  constexpr int EP = 16 / sizeof(TI);
+  constexpr int RBY = N * (int)sizeof(TI);  // bytes per C row
+  constexpr int NPC = RBY / 16;
+  constexpr int CRPP = RBY >= 256 ? 1 : 256 / RBY;  // C rows per 256 bytes
+  constexpr int CPIECES = SR * NPC;
+  constexpr int CPT = (CPIECES + NTH - 1) / NTH;
+  constexpr int CSLAB = CPT * NTH * EP;
+  static_assert(RBY % 16 == 0, "C rows are whole 16-byte pieces");
   static_assert(P == 16 || P % 32 == 0, "headdim");
   static_assert(N == 16 || N % 32 == 0, "dstate");
   static_assert(NT % NO == 0 && NSLOT >= 1 && NS >= 1, "chunk");
@@ -89,15 +121,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   static_assert(NSPLIT == 1 || NSPLIT == 2, "a split owns one row tile of each slab");
   typedef typename Vec4<T>::type V4;
   typedef typename Vec16<T>::type V;
-  // slab buffers: this head's dy rows and the slab's C.B^T tiles (lane order).
+  typedef uint4 CV;  // a 16-byte piece of C
+  // slab buffers: this head's dy rows and the group's C rows of the slab.
   // Each buffer is an array of its own, and the slab loop is unrolled over
   // them, so the compiler can tell the buffer being read from the ones being
   // filled by copies in flight (it does not wait for a copy before an LDS
   // read of another array)
   __shared__ __attribute__((aligned(16))) T DY0[SR][DPITCH], DY1[SR][DPITCH];
   __shared__ __attribute__((aligned(16))) T DY2[DMA ? SR : 1][DPITCH], DY3[DMA ? SR : 1][DPITCH];
-  __shared__ __attribute__((aligned(16))) T W0[WT * 256], W1[WT * 256];
-  __shared__ __attribute__((aligned(16))) T W2[DMA ? WT * 256 : 1], W3[DMA ? WT * 256 : 1];
+  __shared__ __attribute__((aligned(16))) TI W0[CSLAB], W1[CSLAB];
+  __shared__ __attribute__((aligned(16))) TI W2[DMA ? CSLAB : 1], W3[DMA ? CSLAB : 1];
   // Gk (DMA path): read by every wave, so it is copied into LDS once instead
   // of each wave fetching all of it; 16-byte pieces of row r XOR-permuted by
   // r mod (N / 8), so the 16 rows of a fragment read meet distinct banks
@@ -126,12 +159,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   x = rows_in(rm, k, x, rm.x);
   const float* dtc = dt + (((int64_t)b * H + h) * K + k) * Q;
   B = rows_in(rm, k, B, rm.B);
+  C = rows_in(rm, k, C, rm.C);
   dy = rows_in(rm, k, dy, rm.dy);
   dx = rows_out(rm, k, dx, rm.dx);
   const int64_t rs = (int64_t)H * P;      // row stride of x / dy / dx
   const T* dyh = dy + (row0 * H + h) * P;  // row i of this chunk and head: dyh + i * rs
-  const T* xh = x + (row0 * H + h) * P;
-  const T* wbb = wb + (int64_t)((b * K + k) * G + g) * TILES * 256;
+  const TI* xh = x + (row0 * H + h) * P;
+  const TI* cg = C + row0 * G * N + g * N;  // C row i of this chunk and group: cg + i * G * N
   const T* hinh = hin + (int64_t)bkh * P * N;
   const T* gsth = gst + (int64_t)bkh * P * N;
   float* part = dlpart + (int64_t)bkh * dl_rows(Q) * Q;  // rows: splits' row sums, column sums, q, <dxt, x>
@@ -147,7 +181,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 
   // ---- slab staging: registers <- global (a slab ahead of the one next in
   // LDS), LDS <- registers
-  struct SlabRegs { V yv[YPT], wv[WPT]; };
+  // global piece held at position u (< CPIECES) of a C slab buffer: row u / NPC
+  auto c_src = [&](int s, int u) {
+    const int r = u / NPC;
+    return cg + (int64_t)(SR * s + r) * G * N + ((u % NPC) ^ cswz<NPC, CRPP>(r)) * EP;
+  };
+  struct SlabRegs { V yv[YPT]; CV cv[CPT]; };
   SlabRegs ra;
   auto slab_load = [&](SlabRegs& R, int s) {
 #pragma unroll
@@ -157,18 +196,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         R.yv[n] = *reinterpret_cast<const V*>(dyh + (int64_t)(SR * s + u / CUP) * rs + (u % CUP) * VN);
     }
 #pragma unroll
-    for (int n = 0; n < WPT; ++n) {
+    for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      const int t = u / (256 / VN), piece = u % (256 / VN);
-      const int half = t / (NW * NSLOT), w = (t / NSLOT) % NW, sl = t % NSLOT;
-      const int I = 2 * s + half, J = tile_of(w, sl);
-      // tiles with J > I are never read: load the in-range tile (I, I) instead, so
-      // the loads carry no branch
-      if (WPIECES % NTH == 0 || u < WPIECES)
-        R.wv[n] = *reinterpret_cast<const V*>(wbb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + piece * VN);
+      if (CPIECES % NTH == 0 || u < CPIECES) R.cv[n] = *reinterpret_cast<const CV*>(c_src(s, u));
     }
   };
-  auto slab_store = [&](const SlabRegs& R, T (*dyb)[DPITCH], T* wtb) {
+  auto slab_store = [&](const SlabRegs& R, T (*dyb)[DPITCH], TI* cb) {
 #pragma unroll
     for (int n = 0; n < YPT; ++n) {
       const int u = threadIdx.x + NTH * n;
@@ -176,29 +209,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         *reinterpret_cast<V*>(&dyb[u / CUP][dyc(u / CUP, (u % CUP) * VN)]) = R.yv[n];
     }
 #pragma unroll
-    for (int n = 0; n < WPT; ++n) {
+    for (int n = 0; n < CPT; ++n) {
       const int u = threadIdx.x + NTH * n;
-      if (WPIECES % NTH == 0 || u < WPIECES) *reinterpret_cast<V*>(&wtb[u * VN]) = R.wv[n];
+      if (CPIECES % NTH == 0 || u < CPIECES) *reinterpret_cast<CV*>(&cb[u * EP]) = R.cv[n];
     }
   };
-  // global -> LDS copies of slab s into buffer (dyb, wtb): thread t's 16 bytes land at
+  // global -> LDS copies of slab s into buffer (dyb, cb): thread t's 16 bytes land at
   // byte 16 t of the buffer, so it fetches the piece the swizzled layout keeps
-  // there (dy row t / 8, LDS piece t % 8 holds global piece (t % 8) ^ f(row))
-  constexpr int DPS = YPT + WPT;           // copies per thread and slab
-  static_assert(!DMA || (YPIECES == NTH && WPIECES % NTH == 0 && 2 * DPS <= 15), "slab copies");
-  auto slab_dma = [&](int s, T (*dyb)[DPITCH], T* wtb) {
+  // there (dy row t / 8, LDS piece t % 8 holds global piece (t % 8) ^ f(row);
+  // C alike with cswz).  Every thread issues the same number of copies, so one
+  // vmcnt threshold fits every wave: positions past the slab's pieces fetch
+  // a copy of an earlier piece into the buffer's spare tail.
+  constexpr int DPS = YPT + CPT;           // copies per thread and slab
+  static_assert(!DMA || (YPIECES == NTH && 2 * DPS <= 15), "slab copies");
+  auto slab_dma = [&](int s, T (*dyb)[DPITCH], TI* cb) {
     const int t = threadIdx.x, r = t / CUP;
     const int kp = (t % CUP) ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
     lds_copy16(dyh + (int64_t)(SR * s + r) * rs + kp * VN, &dyb[0][0] + wave * kWave * VN);
 #pragma unroll
-    for (int n = 0; n < WPT; ++n) {
+    for (int n = 0; n < CPT; ++n) {
       const int u = t + NTH * n;
-      const int tt = u / (256 / VN), piece = u % (256 / VN);
-      const int half = tt / (NW * NSLOT), w = (tt / NSLOT) % NW, sl = tt % NSLOT;
-      const int I = 2 * s + half, J = tile_of(w, sl);
-      // a slot with J > I is never read: its lanes all fetch the group's first
-      // tile, so they coalesce instead of moving a tile each
-      lds_copy16(wbb + (J <= I ? (int64_t)tri_index(I, J) * 256 : 0) + piece * VN, &wtb[(NTH * n + wave * kWave) * VN]);
+      lds_copy16(c_src(s, u % CPIECES), &cb[(NTH * n + wave * kWave) * EP]);
     }
   };
 
@@ -216,12 +247,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       dtv[n] = dtc[i];
     }
   }
-  constexpr int NPC = N / VN;  // 16-byte pieces of a G row
+  constexpr int GPC = N / VN;  // 16-byte pieces of a G row
   if constexpr (DMA) {
-    static_assert((P * NPC) % NTH == 0 && (NPC & (NPC - 1)) == 0, "G copy");
+    static_assert((P * GPC) % NTH == 0 && (GPC & (GPC - 1)) == 0, "G copy");
 #pragma unroll
-    for (int n = 0; n < P * NPC / NTH; ++n) {
-      const int pp = n * NTH + threadIdx.x, r = pp / NPC, pc = (pp % NPC) ^ (r & (NPC - 1));
+    for (int n = 0; n < P * GPC / NTH; ++n) {
+      const int pp = n * NTH + threadIdx.x, r = pp / GPC, pc = (pp % GPC) ^ (r & (GPC - 1));
       lds_copy16(gsth + r * N + pc * VN, &GS[0][0] + (n * NTH + wave * kWave) * VN);
     }
   } else {
@@ -255,7 +286,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   auto gfrag = [&](Frag<T>& f, int ks, int tp) {
     if constexpr (DMA) {
       const int r = 16 * tp + c;
-      frag_load(f, &GS[r][(((ks * 32 + 8 * q) / VN) ^ (r & (NPC - 1))) * VN]);
+      frag_load(f, &GS[r][(((ks * 32 + 8 * q) / VN) ^ (r & (GPC - 1))) * VN]);
     } else {
       f = gf[ks][tp];
     }
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   }
   // slab s = NS - 1 - it, read from (dys, wts); (dyn, wtn) is the buffer the
   // slab PF ahead is copied into (DMA) or the next slab is stored into
-  auto slab_step = [&](int it, T (*dys)[DPITCH], const T* wts, T (*dyn)[DPITCH], T* wtn) {
+  auto slab_step = [&](int it, T (*dys)[DPITCH], const TI* cbs, T (*dyn)[DPITCH], TI* cbn) {
     const int s = NS - 1 - it;
     if constexpr (DMA) {
       // slab s has landed once at most the copies of the min(PF - 1, s) slabs
@@ -363,7 +394,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (s - PF >= 0) slab_dma(s - PF, dyn, wtn);
+      if (s - PF >= 0) slab_dma(s - PF, dyn, cbn);
     } else {
       if (it + 1 < NS) slab_load(ra, s - 1);
     }
@@ -376,17 +407,16 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
       for (int r = 0; r < 4; ++r) rowtot[half][r] = 0.0f;
 
-    // dy^T operands of the slab (row p, chained K over its 32 rows), shared by all pairs
-    Frag<T> fdt[TP];
-#pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
+    // dy^T operand tp of the slab (row p, chained K over its 32 rows), read
+    // where it is used so that it holds no registers across the pair products
+    auto fdt_load = [&](Frag<T>& f, int tp) {
       if constexpr (DSWZ) {  // rows 4q + c/4 and 16 below (same permutation)
         const int r0 = 4 * q + (c >> 2), col = 16 * tp + 4 * (c & 3);
-        frag_load_kmajor_at(fdt[tp], &dys[r0][dyc(r0, col)], &dys[r0 + 16][dyc(r0, col)]);
+        frag_load_kmajor_at(f, &dys[r0][dyc(r0, col)], &dys[r0 + 16][dyc(r0, col)]);
       } else {
-        frag_load_kmajor<SR>(fdt[tp], &dys[0][0], DPITCH, 0, 16 * tp, q, c);
+        frag_load_kmajor<SR>(f, &dys[0][0], DPITCH, 0, 16 * tp, q, c);
       }
-    }
+    };
     // dy row 16 half + c as a chained-K A fragment (K = headdim, from kp * 32)
     auto dy_row_frag = [&](Frag<T>& fd, int half, int kp) {
       const int yr = 16 * half + c;
@@ -406,6 +436,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     f4 arow[2];                              // exp(cs_i - cs_rb), rows of this lane
 #pragma unroll
     for (int half = 0; half < 2; ++half) arow[half] = *reinterpret_cast<const f4*>(&eslab[rb + 16 * half + 4 * q]);
+    // W_ij = C_i . B_j of row tile 2s + half and owned column tile sl, in fp32
+    // (lane (q, c): column j = 16 J + c, rows i = rb + 16 half + 4q + r)
+    auto wtile = [&](f4& w, int half, int sl) {
+      w = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        Frag<T> cf;
+        c_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
+        mma(w, cf, bfr[ks][sl]);
+      }
+    };
     auto full_pair = [&](int sl) {
       const int cj = 16 * Js[sl] + c;
       const float bj = __expf(cs[rb] - cs[cj]);
@@ -424,10 +465,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       Frag<T> fa;                            // P[i][j] as the B operand (col j, K = i)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const V4 wt = *reinterpret_cast<const V4*>(&wts[((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
+        f4 wt;
+        wtile(wt, half, sl);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float t = to_f(wt[r]) * arow[half][r];
+          const float t = wt[r] * arow[half][r];
           frag_set<T>(fa, half * 4 + r, t * bj);
           const float rv = dp[half][r] * t * bdt;   // the same value enters both sums
           colsum[sl] += rv;
@@ -435,7 +477,59 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         }
       }
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], fdt[tp], fa);
+      for (int tp = 0; tp < TP; ++tp) {
+        Frag<T> fdt;
+        fdt_load(fdt, tp);
+        mma(adx[sl][tp], fdt, fa);
+      }
+    };
+    // both owned column tiles full: every C and dy row fragment of the slab is
+    // read once for the two tiles, half by half
+    auto full_pairs2 = [&]() {
+      float bj[2], bdt[2];
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int cj = 16 * Js[sl] + c;
+        bj[sl] = __expf(cs[rb] - cs[cj]);
+        bdt[sl] = bj[sl] * dts[cj];
+      }
+      Frag<T> fa[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        f4 wt[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          Frag<T> cf;
+          c_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
+          mma(wt[0], cf, bfr[ks][0]);
+          mma(wt[1], cf, bfr[ks][1]);
+        }
+        f4 dp[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int kp = 0; kp < NKP; ++kp) {
+          Frag<T> fd;
+          dy_row_frag(fd, half, kp);
+          mma(dp[0], fd, xf[0][kp]);
+          mma(dp[1], fd, xf[1][kp]);
+        }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float t = wt[sl][r] * arow[half][r];
+            frag_set<T>(fa[sl], half * 4 + r, t * bj[sl]);
+            const float rv = dp[sl][r] * t * bdt[sl];
+            colsum[sl] += rv;
+            rowtot[half][r] += rv;
+          }
+      }
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        Frag<T> fdt;
+        fdt_load(fdt, tp);
+        mma(adx[0][tp], fdt, fa[0]);
+        mma(adx[1][tp], fdt, fa[1]);
+      }
     };
     auto diag_pair = [&](int sl) {
       const int J = Js[sl];
@@ -456,11 +550,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
           }
           const int i0 = 16 * I + 4 * q;
           const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
-          const V4 wt = *reinterpret_cast<const V4*>(&wts[((half * NW + wave) * NSLOT + sl) * 256 + l * 4]);
+          f4 wt;
+          wtile(wt, half, sl);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
-            const float pv = to_f(wt[r]) * lam;
+            const float pv = wt[r] * lam;
             frag_set<T>(fa, half * 4 + r, pv);
             // the diagonal R_jj enters a row sum and a column sum with opposite
             // signs and cancels exactly, so it is left out of both
@@ -474,18 +569,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
         }
       }
 #pragma unroll
-      for (int tp = 0; tp < TP; ++tp) mma(adx[sl][tp], fdt[tp], fa);
+      for (int tp = 0; tp < TP; ++tp) {
+        Frag<T> fdt;
+        fdt_load(fdt, tp);
+        mma(adx[sl][tp], fdt, fa);
+      }
     };
     if constexpr (NSLOT == 2) {
       const bool f0 = Js[0] < 2 * s, f1 = Js[1] < 2 * s;
-      if (f0 && f1) {                        // one straight-line block for both slots
-        full_pair(0);
-        full_pair(1);
-      } else if (f0) {
-        full_pair(0);
-      } else if (f1) {
-        full_pair(1);
-      }
+      if (f0 && f1) full_pairs2();
+      else if (f0) full_pair(0);
+      else if (f1) full_pair(1);
     } else {
       if (Js[0] < 2 * s) full_pair(0);
     }
@@ -505,7 +599,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     }
     // next slab into the other buffer (its last readers passed the previous barrier)
     if constexpr (!DMA) {
-      if (it + 1 < NS) slab_store(ra, dyn, wtn);
+      if (it + 1 < NS) slab_store(ra, dyn, cbn);
     }
 
     // column tiles whose rows are in this slab are complete: dx, <dxt_j, x_j>, column sums
@@ -718,8 +812,8 @@ struct DwLds {
   __attribute__((aligned(16))) float dtJ[2][64];
 };
 
-template <typename T, int Q, int P, bool DIAG>
-__device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* __restrict__ dt,
+template <typename T, typename TI, int Q, int P, bool DIAG>
+__device__ __forceinline__ void dw_block(const TI* __restrict__ x, const float* __restrict__ dt,
                                          const float* __restrict__ cs_g, const T* __restrict__ dy,
                                          float* __restrict__ dw, const RowMap& rm, int H, int G, int K, int hps,
                                          int bkg, int nbkg, int slice, int IB, int JB, DwLds<T, P>& sm, int dw_st) {
@@ -766,7 +860,7 @@ __device__ __forceinline__ void dw_block(const T* __restrict__ x, const float* _
       const int u = threadIdx.x + NTH * n;
       if (XPIECES % NTH == 0 || u < XPIECES) {
         const int r = u / (P / VN);
-        R.xv[n] = *reinterpret_cast<const V*>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
+        R.xv[n] = load_vec16<T, TI>(x + ((row0 + j0 + r) * H + h) * P + (u % (P / VN)) * VN);
         if (!DIAG) {
           R.dtv[n] = dtb[j0 + r];
           R.csv[n] = csb[j0 + r];
@@ -899,8 +993,8 @@ struct BcLds {
   __attribute__((aligned(16))) T Ss[2][P][SP];
 };
 
-template <typename T, int Q, int P, int N, bool DB>
-__device__ __forceinline__ void bc_heads_block(const T* __restrict__ x, const float* __restrict__ dt,
+template <typename T, typename TI, int Q, int P, int N, bool DB>
+__device__ __forceinline__ void bc_heads_block(const TI* __restrict__ x, const float* __restrict__ dt,
                                                const float* __restrict__ cs_g, const T* __restrict__ dy,
                                                const T* __restrict__ state, float* __restrict__ out,
                                                const RowMap& rm, int H, int G, int K, int hps, int bkg, int nbkg,
@@ -925,7 +1019,6 @@ __device__ __forceinline__ void bc_heads_block(const T* __restrict__ x, const fl
   const int h0 = g * hpg + slice * hps;
   const int nh = min(hps, hpg - slice * hps);
   const int i = 64 * RB + 16 * wave + c;     // this lane's row (A operand)
-  const T* U = DB ? x : dy;
 
   // registers of the head in flight
   V sv[SPT];
@@ -939,9 +1032,15 @@ __device__ __forceinline__ void bc_heads_block(const T* __restrict__ x, const fl
       const int u = threadIdx.x + NTH * n;
       if (SPIECES % NTH == 0 || u < SPIECES) sv[n] = *reinterpret_cast<const V*>(st + u * VN);
     }
-    const T* urow = U + ((row0 + i) * H + h) * P;
+    if constexpr (DB) {
+      const TI* urow = x + ((row0 + i) * H + h) * P;
 #pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], urow, kp * 32, q);
+      for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], urow, kp * 32, q);
+    } else {
+      const T* urow = dy + ((row0 + i) * H + h) * P;
+#pragma unroll
+      for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(av[kp], urow, kp * 32, q);
+    }
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
     ascale = DB ? __expf(csb[Q - 1] - csb[i]) * dt[(((int64_t)b * H + h) * K + k) * Q + i] : __expf(csb[i]);
   };
@@ -999,8 +1098,8 @@ __device__ __forceinline__ void bc_heads_block(const T* __restrict__ x, const fl
 // which the round-robin dispatch over the 8 XCDs places on one XCD at about
 // the same time: the rows come from HBM once and from that XCD's L2 for the
 // other blocks.  The heavier head-sum blocks come first in an item.
-template <typename T, int Q, int P, int N>
-__global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const float* __restrict__ dt,
+template <typename T, typename TI, int Q, int P, int N>
+__global__ __launch_bounds__(256) void k_dw_heads(const TI* __restrict__ x, const float* __restrict__ dt,
                                                   const float* __restrict__ cs_g, const T* __restrict__ dy,
                                                   const T* __restrict__ hin, const T* __restrict__ gst,
                                                   float* __restrict__ dw, float* __restrict__ dcpart,
@@ -1014,20 +1113,20 @@ __global__ __launch_bounds__(256) void k_dw_heads(const T* __restrict__ x, const
   if (item >= nitems) return;  // whole workgroup, before any barrier
   const int bkg = item % nbkg, slice = item / nbkg;
   if (blk < NB) {
-    bc_heads_block<T, Q, P, N, false>(x, dt, cs_g, dy, hin, dcpart, rm, H, G, K, hps, bkg, nbkg, slice, blk,
+    bc_heads_block<T, TI, Q, P, N, false>(x, dt, cs_g, dy, hin, dcpart, rm, H, G, K, hps, bkg, nbkg, slice, blk,
                                       *reinterpret_cast<BcLds<T, P, N>*>(smem));
   } else if (blk < 2 * NB) {
-    bc_heads_block<T, Q, P, N, true>(x, dt, cs_g, dy, gst, dbpart, rm, H, G, K, hps, bkg, nbkg, slice, blk - NB,
+    bc_heads_block<T, TI, Q, P, N, true>(x, dt, cs_g, dy, gst, dbpart, rm, H, G, K, hps, bkg, nbkg, slice, blk - NB,
                                      *reinterpret_cast<BcLds<T, P, N>*>(smem));
   } else if (blk < 3 * NB) {
     const int d = blk - 2 * NB;
-    dw_block<T, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, d, d,
+    dw_block<T, TI, Q, P, true>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, d, d,
                             *reinterpret_cast<DwLds<T, P>*>(smem), dw_st);
   } else {
     const int y = blk - 3 * NB;  // pairs IB > JB: y = IB (IB - 1) / 2 + JB
     int IB = 1;
     while ((IB + 1) * IB / 2 <= y) ++IB;
-    dw_block<T, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2,
+    dw_block<T, TI, Q, P, false>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, IB, y - IB * (IB - 1) / 2,
                              *reinterpret_cast<DwLds<T, P>*>(smem), dw_st);
   }
 }
@@ -1052,9 +1151,9 @@ struct BcFinalLds {
   __attribute__((aligned(16))) T Ms[64][MP];
 };
 
-template <typename T, int Q, int N, bool DB, int NH>
+template <typename T, typename TI, int Q, int N, bool DB, int NH>
 __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, const float* __restrict__ dw,
-                                               const T* __restrict__ M, T* __restrict__ out, const RowMap& rm,
+                                               const TI* __restrict__ M, T* __restrict__ out, const RowMap& rm,
                                                int G, int K, int nslice, int nslice_dw, int bkg, int nbkg, int RB,
                                                int zpart, BcFinalLds<T, Q, N, NH>& sm, int dw_st) {
   constexpr int NTH = 256;
@@ -1110,7 +1209,7 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
       if (MPIECES % NTH == 0 || u < MPIECES) {
         const int rr = u / (NP / VN), cu = u % (NP / VN);
         *reinterpret_cast<V*>(&Ms[rr][cu * VN]) =
-            *reinterpret_cast<const V*>(M + ((row0 + 64 * kb + rr) * G + g) * N + n0 + cu * VN);
+            load_vec16<T, TI>(M + ((row0 + 64 * kb + rr) * G + g) * N + n0 + cu * VN);
       }
     }
     __syncthreads();
@@ -1144,18 +1243,18 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
 
 // dC and dB in one launch (both read the same dW blocks): blockIdx.z < NH
 // takes dstate part z of dC, the rest the parts of dB.
-template <typename T, int Q, int N, int NH>
+template <typename T, typename TI, int Q, int N, int NH>
 __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ dcpart, const float* __restrict__ dbpart,
-                                                  const float* __restrict__ dw, const T* __restrict__ B,
-                                                  const T* __restrict__ C, T* __restrict__ dC, T* __restrict__ dB,
+                                                  const float* __restrict__ dw, const TI* __restrict__ B,
+                                                  const TI* __restrict__ C, T* __restrict__ dC, T* __restrict__ dB,
                                                   const RowMap rm, int G, int K, int nslice, int dw_st) {
   __shared__ BcFinalLds<T, Q, N, NH> sm;
   const int z = blockIdx.z;
   if (z < NH)
-    bc_final_block<T, Q, N, false, NH>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
+    bc_final_block<T, TI, Q, N, false, NH>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
                                        z, sm, dw_st);
   else
-    bc_final_block<T, Q, N, true, NH>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
+    bc_final_block<T, TI, Q, N, true, NH>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
                                       z - NH, sm, dw_st);
 }
 
@@ -1189,21 +1288,20 @@ __global__ __launch_bounds__(256) void k_da_dd(const float* __restrict__ dapart,
 // dstate parts of k_bc_final: 32 columns each
 template <int N> constexpr int kBcParts = N >= 32 ? N / 32 : 1;
 
-template <typename T, int Q, int P, int N>
+template <typename T, typename TI, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_probe* probe) {
   const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
-  const T* x = static_cast<const T*>(a.x);
+  const TI* x = static_cast<const TI*>(a.x);
   const float* dt = a.dtf;  // the step, float32, as the forward's cumsum wrote it
-  const T* B = static_cast<const T*>(a.B);
-  const T* C = static_cast<const T*>(a.C);
+  const TI* B = static_cast<const TI*>(a.B);
+  const TI* C = static_cast<const TI*>(a.C);
   const T* dy = static_cast<const T*>(a.dy);
   const T* hin = static_cast<const T*>(a.hin);
-  const T* w = static_cast<const T*>(a.w);
   T* gst = static_cast<T*>(a.gst);
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE_BWD, st);
-    launch_chunk_state<T, T, Q, P, N, true>(dy, C, dt, a.cs, static_cast<T*>(a.dhloc), hin, a.dlpart, a.rows, b, H, G,
-                                            K, st);
+    launch_chunk_state<T, T, TI, Q, P, N, true>(dy, C, dt, a.cs, static_cast<T*>(a.dhloc), hin, a.dlpart, a.rows, b, H,
+                                                G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
@@ -1213,8 +1311,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     const int nitems = b * K * H;
-    k_chunk_scan_bwd<T, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, B, C, hin, gst, w, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
+    k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
+        x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     k_dl_assemble<T, Q><<<dim3(b * K * ((H + 3) / 4)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
         P / 16);
@@ -1227,7 +1325,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_DW_HEADS, st);
     const int nb = Q / 64, nitems = nbkg * S;
-    k_dw_heads<T, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
+    k_dw_heads<T, TI, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
         x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems, dw_st);
   }
   {
@@ -1236,10 +1334,10 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     // workgroups, but every part stages and converts the whole dW block again;
     // once the row blocks alone make 2048 workgroups, one part takes all columns.
     if ((int64_t)nbkg * (Q / 64) * 2 >= 2048)
-      k_bc_final<T, Q, N, 1><<<dim3(nbkg, Q / 64, 2), dim3(256), 0, st>>>(
+      k_bc_final<T, TI, Q, N, 1><<<dim3(nbkg, Q / 64, 2), dim3(256), 0, st>>>(
           a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
     else
-      k_bc_final<T, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
+      k_bc_final<T, TI, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
           a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
   }
   {
@@ -1249,9 +1347,11 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
 }
 
-#define SSD_INST_BWD_BF16(Q_, P_, N_) template void run_bwd<bf16, Q_, P_, N_>(const Layout&, const BwdArgs&, hipStream_t, const ssd_probe*);
-#define SSD_INST_BWD_F32(Q_, P_, N_) template void run_bwd<float, Q_, P_, N_>(const Layout&, const BwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_BWD_BF16(Q_, P_, N_) template void run_bwd<bf16, bf16, Q_, P_, N_>(const Layout&, const BwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_BWD_FP8(Q_, P_, N_) template void run_bwd<bf16, fp8, Q_, P_, N_>(const Layout&, const BwdArgs&, hipStream_t, const ssd_probe*);
+#define SSD_INST_BWD_F32(Q_, P_, N_) template void run_bwd<float, float, Q_, P_, N_>(const Layout&, const BwdArgs&, hipStream_t, const ssd_probe*);
 SSD_BF16_CONFIGS(SSD_INST_BWD_BF16)
+SSD_BF16_CONFIGS(SSD_INST_BWD_FP8)
 SSD_F32_CONFIGS(SSD_INST_BWD_F32)
 
 }  // namespace ssd

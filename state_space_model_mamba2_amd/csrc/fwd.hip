@@ -247,17 +247,17 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
     // 16-byte load per token instead of four strided ones)
     if (H % 4 == 0)
       k_cumsum_bmm<T, TI, Q, N, 4><<<dim3(nbkg * ((TILES + 3) / 4) + (nbhk / 4 + 3) / 4), dim3(256), 0, st>>>(
-          static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, static_cast<T*>(a.wtb), a.rows, H, G,
+          static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, a.rows, H, G,
           K, a.softplus, nbkg, nbhk);
     else
       k_cumsum_bmm<T, TI, Q, N, 1><<<dim3(nbkg * ((TILES + 3) / 4) + (nbhk + 3) / 4), dim3(256), 0, st>>>(
-          static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, static_cast<T*>(a.wtb), a.rows, H, G,
+          static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, a.rows, H, G,
           K, a.softplus, nbkg, nbhk);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_STATE, st);
-    launch_chunk_state<T, TI, Q, P, N, false>(x, B, dt, a.cs, static_cast<T*>(a.S), nullptr, nullptr, a.rows, b, H, G,
-                                              K, st);
+    launch_chunk_state<T, TI, TI, Q, P, N, false>(x, B, dt, a.cs, static_cast<T*>(a.S), nullptr, nullptr, a.rows, b, H,
+                                                  G, K, st);
   }
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);

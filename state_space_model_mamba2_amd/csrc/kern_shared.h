@@ -44,6 +44,17 @@ __device__ __forceinline__ void frag_load_chained(Frag<T>& f, const T* row, int 
   }
 }
 
+// The same from eight OCP E4M3 codes (two runs of four bytes), widened to bf16
+// exactly (gfx950's packed conversion at scale 1).
+template <int KD>
+__device__ __forceinline__ void frag_load_chained(Frag<bf16>& f, const fp8* row, int k0, int q) {
+  const uint32_t a = *reinterpret_cast<const uint32_t*>(row + k0 + 4 * q);
+  uint32_t b = 0;  // E4M3 code 0 is +0
+  if constexpr (KD % 32 == 0) b = *reinterpret_cast<const uint32_t*>(row + k0 + 16 + 4 * q);
+  else static_assert(KD == 16, "K extent must be 16 or a multiple of 32");
+  f.v = e4m3x8_to_bf16(make_uint2(a, b));
+}
+
 // First row of chunk k of sequence b, and the tensor that holds it: the
 // caller's for whole chunks, the zero-padded copy for a shorter last chunk.
 __device__ __forceinline__ int64_t chunk_row0(const RowMap& rm, int b, int k, int Q) {
@@ -136,18 +147,17 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, cons
 
 // ---------------------------------------------------------------------------
 // W = C.B^T per (b, k, g), stored as lower-triangle 16x16 accumulator tiles in
-// the two lane orders the consumers read (4 elements per lane, 256 per tile):
-//   forward order  : tile (I, J) lane l holds W[16I + l%16][16J + 4q + r]
-//   backward order : tile (I, J) lane l holds W[16I + 4q + r][16J + l%16]
-// (q = l / 16, r = 0..3).  Both come from the same fragments of B rows J and
-// C rows I with the operands swapped; K of every product is dstate.  One
-// tile per wave: every load is issued before the first product.  With FP8
+// the lane order the forward chunk kernel reads (4 elements per lane, 256 per
+// tile): tile (I, J) lane l holds W[16I + l%16][16J + 4q + r] (q = l / 16,
+// r = 0..3), from fragments of B rows J and C rows I with K = dstate.  The
+// backward forms its tiles again in fp32 from C and B instead of reading
+// these.  One tile per wave: every load is issued before the first product.  With FP8
 // (E4M3) B and C the products run on the FP8 matrix cores, whose fragment is
 // the bf16 one with one byte per K-value (checked on gfx950: OCP E4M3
 // operands, lane (q, c) supplies row c, K-values 8q .. 8q + 7).
 template <typename T, typename TI, int Q, int N>
 __device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI* __restrict__ C, T* __restrict__ wf,
-                                              T* __restrict__ wb, const RowMap& rm, int G, int K, int bkg, int idx) {
+                                              const RowMap& rm, int G, int K, int bkg, int idx) {
   constexpr int NT = Q / 16;
   constexpr int TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32;
@@ -161,7 +171,7 @@ __device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI
   C = rows_in(rm, k, C, rm.C);
   const TI* brow = B + ((row0 + 16 * J + c) * G + g) * N;
   const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
-  f4 af = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+  f4 af = {0.f, 0.f, 0.f, 0.f};
   if constexpr (std::is_same<TI, fp8>::value) {
     long fb[NK], fc[NK];
 #pragma unroll
@@ -171,10 +181,7 @@ __device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI
       fc[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(crow + kk) : 0;
     }
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      af = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fb[ks], fc[ks], af, 0, 0, 0);
-      ab = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fc[ks], fb[ks], ab, 0, 0, 0);
-    }
+    for (int ks = 0; ks < NK; ++ks) af = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fb[ks], fc[ks], af, 0, 0, 0);
   } else {
     Frag<T> fb[NK], fc[NK];
 #pragma unroll
@@ -183,20 +190,12 @@ __device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI
       frag_load_k<N>(fc[ks], crow, ks * 32 + 8 * q);
     }
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
-      mma(ab, fc[ks], fb[ks]);  // [row i][col j] = C_i . B_j
-    }
+    for (int ks = 0; ks < NK; ++ks) mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
   }
-  typename Vec4<T>::type vf, vb;
+  typename Vec4<T>::type vf;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    vf[r] = from_f<T>(af[r]);
-    vb[r] = from_f<T>(ab[r]);
-  }
-  const int64_t o = ((int64_t)bkg * TILES + idx) * 256 + l * 4;
-  *reinterpret_cast<typename Vec4<T>::type*>(wf + o) = vf;
-  *reinterpret_cast<typename Vec4<T>::type*>(wb + o) = vb;
+  for (int r = 0; r < 4; ++r) vf[r] = from_f<T>(af[r]);
+  *reinterpret_cast<typename Vec4<T>::type*>(wf + ((int64_t)bkg * TILES + idx) * 256 + l * 4) = vf;
 }
 
 // The two independent first steps of the forward in one launch, one wave
@@ -208,7 +207,7 @@ template <typename T, typename TI, int Q, int N, int HW>
 __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, const float* __restrict__ A,
                                                     const float* __restrict__ dt_bias, float* __restrict__ dt_out,
                                                     float* __restrict__ cs, const TI* __restrict__ B,
-                                                    const TI* __restrict__ C, T* __restrict__ wf, T* __restrict__ wb,
+                                                    const TI* __restrict__ C, T* __restrict__ wf,
                                                     const RowMap rm, int H, int G, int K, int softplus, int nbkg,
                                                     int nbhk) {
   constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2, TB = (TILES + 3) / 4;
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
   const int nbmm = nbkg * TB;
   if ((int)blockIdx.x < nbmm) {
     const int idx = (blockIdx.x % TB) * 4 + wave;
-    if (idx < TILES) bmm_tile_wave<T, TI, Q, N>(B, C, wf, wb, rm, G, K, blockIdx.x / TB, idx);
+    if (idx < TILES) bmm_tile_wave<T, TI, Q, N>(B, C, wf, rm, G, K, blockIdx.x / TB, idx);
   } else {
     const int item = ((int)blockIdx.x - nbmm) * 4 + wave;
     if (item < nbhk / HW) chunk_cumsum_wave<T, Q, HW>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, item);
@@ -241,8 +240,8 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
 // current one is used.  One workgroup (4 waves) per (b, k) and HPW heads of
 // one group: V, the group's rows, is staged once for all of them, and their U
 // rows are one contiguous run per token.
-template <typename T, typename TI, int Q, int P, int N, bool BWD, int HPW>
-__global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, const TI* __restrict__ V,
+template <typename T, typename TU, typename TV, int Q, int P, int N, bool BWD, int HPW>
+__global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, const TV* __restrict__ V,
                                                      const float* __restrict__ dt, const float* __restrict__ cs,
                                                      T* __restrict__ out, const T* __restrict__ hin,
                                                      float* __restrict__ dlpart, const RowMap rm, int H, int G, int K,
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
         const int u = threadIdx.x + NTH * n;
         if (UPIECES % NTH == 0 || u < UPIECES) {
           const int i = KB * blk + u / (P / VN);
-          uv[hh][n] = load_vec16<T, TI>(U + ((row0 + i) * H + h0 + hh) * P + (u % (P / VN)) * VN);
+          uv[hh][n] = load_vec16<T, TU>(U + ((row0 + i) * H + h0 + hh) * P + (u % (P / VN)) * VN);
           uw[hh][n] = BWD ? __expf(csc[hh][i]) : dtc[hh][i] * __expf(cs_last[hh] - csc[hh][i]);
         }
       }
@@ -311,7 +310,7 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
     for (int n = 0; n < VPT; ++n) {
       const int u = threadIdx.x + NTH * n;
       if (VPIECES % NTH == 0 || u < VPIECES)
-        vv[n] = load_vec16<T, TI>(V + ((row0 + KB * blk + u / (N / VN)) * G + g) * N + (u % (N / VN)) * VN);
+        vv[n] = load_vec16<T, TV>(V + ((row0 + KB * blk + u / (N / VN)) * G + g) * N + (u % (N / VN)) * VN);
     }
   };
   auto store = [&](int bf) {
@@ -413,14 +412,14 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TI* __restrict__ U, c
 // Launch of k_chunk_state: two heads per workgroup when a group's heads pair up.
 // hin / dlpart: the backward's chunk-entry states and dl partial sums (the
 // state-to-output term), unused (null) in the forward.
-template <typename T, typename TI, int Q, int P, int N, bool BWD>
-void launch_chunk_state(const TI* U, const TI* V, const float* dt, const float* cs, T* out, const T* hin,
+template <typename T, typename TU, typename TV, int Q, int P, int N, bool BWD>
+void launch_chunk_state(const TU* U, const TV* V, const float* dt, const float* cs, T* out, const T* hin,
                         float* dlpart, const RowMap& rm, int b, int H, int G, int K, hipStream_t st) {
   if ((H / G) % 2 == 0)
-    k_chunk_state<T, TI, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(
+    k_chunk_state<T, TU, TV, Q, P, N, BWD, 2><<<dim3(xcd_grid(b * K * H / 2)), dim3(256), 0, st>>>(
         U, V, dt, cs, out, hin, dlpart, rm, H, G, K, b * K * H / 2);
   else
-    k_chunk_state<T, TI, Q, P, N, BWD, 1><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
+    k_chunk_state<T, TU, TV, Q, P, N, BWD, 1><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
         U, V, dt, cs, out, hin, dlpart, rm, H, G, K, b * K * H);
 }
 

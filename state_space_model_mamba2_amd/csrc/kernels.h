@@ -17,7 +17,7 @@ struct Layout {
   int64_t b, L, H, P, N, G, Q, K;
   size_t esz;  // bytes per storage element (2 for bf16, 4 for fp32)
   // saved workspace
-  size_t cs_off, hin_off, wt_off, wtb_off, saved_bytes;
+  size_t cs_off, hin_off, wt_off, saved_bytes;
   // forward scratch
   size_t s_off, fwd_bytes;
   // backward scratch
@@ -53,8 +53,7 @@ struct FwdArgs {
   float* cs;    // [b][H][K][Q]
   void* hin;    // [b][K][H][P][N]  storage dtype
   void* S;      // [b][K][H][P][N], storage dtype
-  void* wt;     // C.B^T tiles, forward lane order (kept in the saved workspace)
-  void* wtb;    // C.B^T tiles, backward lane order (kept in the saved workspace)
+  void* wt;     // C.B^T tiles, forward lane order (forward scratch)
 };
 
 struct BwdArgs {
@@ -70,7 +69,6 @@ struct BwdArgs {
   float* ddt_bias;      // [H] gradient of dt_bias, or null
   float* dbiaspart;     // [b][K][H] per-chunk partials of ddt_bias (softplus only)
   float* dinit;         // [b][H][P][N] initial-state gradient, or null
-  const void* w;   // C.B^T tiles, backward lane order (saved by the forward pass)
   void* dhloc;     // [b][K][H][P][N], storage dtype
   void* gst;       // [b][K][H][P][N]  storage dtype: dL/d(state leaving chunk k)
   float* dw;       // [nslice][b][K][G][Q][Q], per-slice partials
@@ -141,7 +139,7 @@ void run_conv_bwd(const ConvArgs& a, hipStream_t st);
 // x, B and C (T, or fp8 with T = bf16).
 template <typename T, typename TI, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t stream, const ssd_probe* probe);
-template <typename T, int Q, int P, int N>
+template <typename T, typename TI, int Q, int P, int N>
 void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t stream, const ssd_probe* probe);
 
 }  // namespace ssd

@@ -155,18 +155,17 @@ def bwd(dy, ctx: Context, *, dfinal_state: torch.Tensor | None = None, want_dini
     dt_softplus, ddt_bias (ddt is then the gradient of the raw step)."""
     lib = _lib.load()
     x, dt, A, B, C, D = ctx.tensors
-    if x.dtype == torch.float8_e4m3fn:
-        raise NotImplementedError("FP8 operands are forward only")
-    if dy.dtype != x.dtype or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
-        raise ValueError("dy must be a contiguous GPU tensor with x's shape and dtype")
+    gdt = _step_dtype(x.dtype)   # dy and the gradients: bfloat16 when x, B, C are FP8
+    if dy.dtype != gdt or dy.shape != x.shape or not dy.is_contiguous() or not dy.is_cuda:
+        raise ValueError(f"dy must be a contiguous GPU tensor with x's shape and dtype {gdt}")
     _check_state(dfinal_state, ctx.shape, "dfinal_state")
     scratch_bytes = lib.ssd_bwd_scratch_bytes(ctypes.byref(ctx.shape))
     if scratch is None or scratch.numel() < scratch_bytes:
         scratch = torch.empty(scratch_bytes, dtype=torch.uint8, device=x.device)
-    dx = torch.empty_like(x)
+    dx = torch.empty(x.shape, dtype=gdt, device=x.device)
     ddt = torch.empty_like(dt)
-    dB = torch.empty_like(B)
-    dC = torch.empty_like(C)
+    dB = torch.empty(B.shape, dtype=gdt, device=x.device)
+    dC = torch.empty(C.shape, dtype=gdt, device=x.device)
     dA = torch.empty_like(A)
     dD = torch.empty_like(D)
     s = ctx.shape

@@ -175,7 +175,9 @@ def test_bwd_rejects_before_launch(lib):
     bad = _lib.Saved(shape(nheads=5), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
     assert bwd(bad) == INVALID
     fp8 = _lib.Saved(shape(dtype=_lib.SSD_FP8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30)
-    assert bwd(fp8) == UNSUPPORTED                           # FP8 operands: forward only
+    need8 = lib.ssd_bwd_scratch_bytes(ctypes.byref(fp8.shape))
+    assert need8 > 0 and bwd(fp8, nbytes=need8 - 1) == WORKSPACE   # FP8 operands: checked like bf16
+    assert bwd(fp8, dy=None, nbytes=need8) == INVALID
 
 
 def test_strings(lib):

@@ -1,12 +1,13 @@
-"""FP8 (OCP E4M3) x, B, C in the forward pass, on the GPU.
+"""FP8 (OCP E4M3) x, B, C in the forward and backward passes, on the GPU.
 
-Parity: the library's forward on E4M3 inputs against the float64 oracle on
-exactly those E4M3 values (the kernels widen the codes exactly, so this
-measures the kernels' own arithmetic: bf16 products with fp32 accumulation,
-C.B^T on the FP8 matrix cores), tolerance 2e-2 as in bf16 mode.  The
-end-to-end cost of storing x, B, C in FP8 instead of bf16 is measured against
-the oracle on the bf16 values of the same draws and printed; it is bounded
-by the CPU study in tests/test_fp8_accuracy.py.
+Parity: the library's forward and backward on E4M3 inputs against the float64
+oracle on exactly those E4M3 values (the kernels widen the codes exactly, so
+this measures the kernels' own arithmetic: bf16 products with fp32
+accumulation, C.B^T on the FP8 matrix cores, dy and every gradient in bf16),
+tolerance 2e-2 as in bf16 mode.  The end-to-end cost of storing x, B, C in
+FP8 instead of bf16 is measured against the oracle on the bf16 values of the
+same draws and printed; it is bounded by the CPU study in
+tests/test_fp8_accuracy.py.
 """
 import numpy as np
 import pytest
@@ -74,12 +75,51 @@ def test_fp8_full_size_sampled():
     assert all(v <= TOL for v in e.values()), e
 
 
-def test_fp8_backward_is_refused():
+def run_fwd_bwd_gpu(inp, chunk, states=None):
     from state_space_model_mamba2_amd import ssd
 
-    shape = inputs.workload("mamba2_370m", batch=1, seqlen=256, nheads=2).replace(dtype="fp8")
-    inp = inputs.generate(shape, seed=32)
     dev = ssd.to_device(inp, "cuda")
-    _, _, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], shape.chunk)
-    with pytest.raises(NotImplementedError):
-        ssd.bwd(dev["dy"], ctx)
+    s0, dfs = ((torch.from_numpy(a).cuda() for a in states) if states is not None else (None, None))
+    y, fs, ctx = ssd.fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], chunk, initial_state=s0)
+    g = ssd.bwd(dev["dy"], ctx, dfinal_state=dfs, want_dinitial_state=states is not None)
+    torch.cuda.synchronize()
+    out = dict(y=to_np(y), final_state=to_np(fs))
+    out.update({k: to_np(v) for k, v in g.items()})
+    return out
+
+
+def oracle_fwd_bwd(inp, states=None):
+    from tests.util import run_oracle
+
+    return run_oracle(inp, states=states)
+
+
+@pytest.mark.parametrize("with_states", [False, True])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1].get('seqlen')}-Q{c[1].get('chunk', 256)}")
+def test_fp8_backward_parity(case, with_states):
+    shape = inputs.workload(case[0], **case[1]).replace(dtype="fp8")
+    print(f"[fp8 bwd] {shape} states={with_states}", flush=True)
+    inp = inputs.generate(shape, seed=33)
+    st = inputs.generate_states(shape, seed=33) if with_states else None
+    got = run_fwd_bwd_gpu(inp, shape.chunk, st)
+    ref = oracle_fwd_bwd(inp, st)
+    e = {k: max_rel(got[k], ref[k]) for k in ref}
+    ref16 = oracle_fwd_bwd(inputs.generate(shape.replace(dtype="bf16"), seed=33), st)
+    e16 = {k: max_rel(got[k], ref16[k]) for k in ref16}
+    print("  vs oracle on the E4M3 values: " + " ".join(f"{k}={v:.1e}" for k, v in e.items()), flush=True)
+    print("  vs oracle on the bf16 values: " + " ".join(f"{k}={v:.1e}" for k, v in e16.items()), flush=True)
+    bad = {k: v for k, v in e.items() if not v <= TOL}
+    assert not bad, bad
+
+
+def test_fp8_backward_full_size():
+    # the 2.7B shape, every element of every output against the oracle on the E4M3 values
+    shape = inputs.workload("mamba2_2p7b").replace(dtype="fp8")
+    print(f"[fp8 bwd full] {shape}", flush=True)
+    inp = inputs.generate(shape, seed=34)
+    got = run_fwd_bwd_gpu(inp, shape.chunk)
+    ref = oracle_fwd_bwd(inp)
+    e = {k: max_rel(got[k], ref[k]) for k in ref}
+    print("  " + " ".join(f"{k}={v:.1e}" for k, v in e.items()), flush=True)
+    bad = {k: v for k, v in e.items() if not v <= TOL}
+    assert not bad, bad
