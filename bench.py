@@ -283,10 +283,10 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
     rules = {
         "cumsum_bmm": "k_cumsum_bmm" in name,
         "chunk_state": "k_chunk_state" in name and fwd_flag,
-        "state_passing": "k_state_passing_fwd" in name,
+        "state_passing": "k_state_passing" in name and fwd_flag,
         "chunk_scan": "k_chunk_scan_fwd" in name,
         "chunk_state_bwd": "k_chunk_state" in name and bwd_flag,
-        "state_passing_bwd": "k_state_passing_bwd" in name,
+        "state_passing_bwd": "k_state_passing" in name and bwd_flag,
         "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,
         "dw_heads": "k_dw_heads" in name,
         "bc_final": "k_bc_final" in name,
@@ -365,7 +365,7 @@ def summarize_stats(csv_path: str, command: str, title: str) -> str:
         short = m.group(1) if m else n.split("(")[0].split("<")[0].replace("void ", "")[:40]
         # the kernels' bool template flag names the variant
         flag = re.search(r"L(b[01])E", n)
-        labels = {"k_chunk_state": ("forward", "backward")}
+        labels = {"k_chunk_state": ("forward", "backward"), "k_state_passing": ("forward", "backward")}
         if flag and short in labels:
             short += f" ({labels[short][int(flag.group(1)[1])]})"
         lines.append(f"| {short} | `{n[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "

@@ -52,27 +52,6 @@ namespace ssd {
 // round-robin dispatch over the 8 XCDs runs them on one XCD (one L2) at
 // about the same time, and consecutive heads of a chunk (which share its C
 // and B rows and C.B^T tiles) run on the same XCD.
-// Piece swizzle of a staged C row r (NPC 16-byte pieces per row, CRPP rows
-// per 256 bytes of LDS): the 16 rows of one fragment read meet distinct banks.
-template <int NPC, int CRPP>
-__device__ __forceinline__ int cswz(int r) {
-  if constexpr (NPC == 1) return 0;
-  else return (r / CRPP) & ((NPC < 16 ? NPC : 16) - 1);
-}
-// Fragment of staged C row r with K-values k0 .. k0 + 7 (zero past N): one
-// piece for bf16 and FP8 (widened), two for fp32.
-template <int N, int NPC, int CRPP, typename T, typename TI>
-__device__ __forceinline__ void c_row_frag(Frag<T>& f, const TI* cb, int r, int k0) {
-  constexpr int EP = 16 / sizeof(TI);
-  auto at = [&](int kk) { return cb + r * N + ((kk / EP) ^ cswz<NPC, CRPP>(r)) * EP + kk % EP; };
-  if (N % 32 == 0 || k0 < N) {
-    if constexpr (sizeof(TI) == 4) frag_load2(f, at(k0), at(k0 + 4));
-    else frag_load(f, at(k0));
-  } else {
-    frag_zero(f);
-  }
-}
-
 template <typename T, typename TI, int Q, int P, int N>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g, const float* __restrict__ Dp,
@@ -102,7 +81,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr int NBUF = DMA ? PF + 1 : 2;   // slab buffers
   constexpr int YPT = (YPIECES + NTH - 1) / NTH;
   // C rows of a slab, in their storage type: 16-byte pieces of EP elements,
-  // NPC per row, piece p of row r stored at p ^ cswz(r) so that the 16 rows
+  // NPC per row, piece p of row r stored at p ^ row_swz(r) so that the 16 rows
   // of a fragment read meet distinct banks.  The last round of copies fills
   // a spare tail of the buffer when a slab has fewer pieces than threads.
   constexpr int EP = 16 / sizeof(TI);
@@ -184,7 +163,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   // global piece held at position u (< CPIECES) of a C slab buffer: row u / NPC
   auto c_src = [&](int s, int u) {
     const int r = u / NPC;
-    return cg + (int64_t)(SR * s + r) * G * N + ((u % NPC) ^ cswz<NPC, CRPP>(r)) * EP;
+    return cg + (int64_t)(SR * s + r) * G * N + ((u % NPC) ^ row_swz<NPC, CRPP>(r)) * EP;
   };
   struct SlabRegs { V yv[YPT]; CV cv[CPT]; };
   SlabRegs ra;
@@ -217,7 +196,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   // global -> LDS copies of slab s into buffer (dyb, cb): thread t's 16 bytes land at
   // byte 16 t of the buffer, so it fetches the piece the swizzled layout keeps
   // there (dy row t / 8, LDS piece t % 8 holds global piece (t % 8) ^ f(row);
-  // C alike with cswz).  Every thread issues the same number of copies, so one
+  // C alike with row_swz).  Every thread issues the same number of copies, so one
   // vmcnt threshold fits every wave: positions past the slab's pieces fetch
   // a copy of an earlier piece into the buffer's spare tail.
   constexpr int DPS = YPT + CPT;           // copies per thread and slab
@@ -443,7 +422,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
       for (int ks = 0; ks < NK; ++ks) {
         Frag<T> cf;
-        c_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
+        staged_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
         mma(w, cf, bfr[ks][sl]);
       }
     };
@@ -500,7 +479,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
         for (int ks = 0; ks < NK; ++ks) {
           Frag<T> cf;
-          c_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
+          staged_row_frag<N, NPC, CRPP>(cf, cbs, 16 * half + c, ks * 32 + 8 * q);
           mma(wt[0], cf, bfr[ks][0]);
           mma(wt[1], cf, bfr[ks][1]);
         }
@@ -1306,7 +1285,7 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING_BWD, st);
     const int PN = P * N;
-    k_state_passing_bwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.dhloc), a.cs, a.dfinal, gst, a.dinit, H, K, PN);
+    k_state_passing<T, Q, true><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.dhloc), a.cs, a.dfinal, gst, a.dinit, H, K, PN);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);

@@ -241,16 +241,15 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   T* wt = static_cast<T*>(a.wt);
   {
     ProbeScope ps(probe, SSD_K_CUMSUM_BMM, st);
-    constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
-    const int nbkg = b * K * G, nbhk = b * H * K;
+    const int nbkg = b * K * G, nbhk = b * H * K, nbmm = nbkg * (Q / 64);
     // four adjacent heads per cumsum wave where the head count allows (one 8- or
     // 16-byte load per token instead of four strided ones)
     if (H % 4 == 0)
-      k_cumsum_bmm<T, TI, Q, N, 4><<<dim3(nbkg * ((TILES + 3) / 4) + (nbhk / 4 + 3) / 4), dim3(256), 0, st>>>(
+      k_cumsum_bmm<T, TI, Q, N, 4><<<dim3(nbmm + (nbhk / 4 + 3) / 4), dim3(256), 0, st>>>(
           static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, a.rows, H, G,
           K, a.softplus, nbkg, nbhk);
     else
-      k_cumsum_bmm<T, TI, Q, N, 1><<<dim3(nbkg * ((TILES + 3) / 4) + (nbhk + 3) / 4), dim3(256), 0, st>>>(
+      k_cumsum_bmm<T, TI, Q, N, 1><<<dim3(nbmm + (nbhk + 3) / 4), dim3(256), 0, st>>>(
           static_cast<const T*>(a.dt), a.A, a.dt_bias, a.dtf, a.cs, B, C, wt, a.rows, H, G,
           K, a.softplus, nbkg, nbhk);
   }
@@ -262,7 +261,7 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_STATE_PASSING, st);
     const int PN = P * N;
-    k_state_passing_fwd<T, Q><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.S), a.cs, a.init, hin, a.final_state, H, K, PN);
+    k_state_passing<T, Q, false><<<dim3((PN / 4 + 255) / 256, b * H), dim3(256), 0, st>>>(static_cast<const T*>(a.S), a.cs, a.init, hin, a.final_state, H, K, PN);
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);

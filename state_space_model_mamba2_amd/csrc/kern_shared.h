@@ -145,63 +145,122 @@ __device__ __forceinline__ void chunk_cumsum_wave(const T* __restrict__ dt, cons
   }
 }
 
+// Rows staged in LDS as 16-byte pieces (NPC pieces per row of N elements of
+// type TI, CRPP rows per 256 bytes of LDS): piece p of row r is stored at
+// p ^ row_swz(r), so that the 16 rows of one fragment read (lane (q, c) reads
+// row c) meet distinct banks.
+template <int NPC, int CRPP>
+__device__ __forceinline__ int row_swz(int r) {
+  if constexpr (NPC == 1) return 0;
+  else return (r / CRPP) & ((NPC < 16 ? NPC : 16) - 1);
+}
+// Element offset of K-value kk of staged row r.
+template <int N, int NPC, int CRPP, typename TI>
+__device__ __forceinline__ int staged_off(int r, int kk) {
+  constexpr int EP = 16 / sizeof(TI);
+  return r * N + ((kk / EP) ^ row_swz<NPC, CRPP>(r)) * EP + kk % EP;
+}
+// Fragment of staged row r with K-values k0 .. k0 + 7 (zero past N): one
+// piece for bf16 and FP8 (widened), two for fp32.
+template <int N, int NPC, int CRPP, typename T, typename TI>
+__device__ __forceinline__ void staged_row_frag(Frag<T>& f, const TI* rows, int r, int k0) {
+  if (N % 32 == 0 || k0 < N) {
+    if constexpr (sizeof(TI) == 4) frag_load2(f, rows + staged_off<N, NPC, CRPP, TI>(r, k0), rows + staged_off<N, NPC, CRPP, TI>(r, k0 + 4));
+    else frag_load(f, rows + staged_off<N, NPC, CRPP, TI>(r, k0));
+  } else {
+    frag_zero(f);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // W = C.B^T per (b, k, g), stored as lower-triangle 16x16 accumulator tiles in
 // the lane order the forward chunk kernel reads (4 elements per lane, 256 per
 // tile): tile (I, J) lane l holds W[16I + l%16][16J + 4q + r] (q = l / 16,
-// r = 0..3), from fragments of B rows J and C rows I with K = dstate.  The
-// backward forms its tiles again in fp32 from C and B instead of reading
-// these.  One tile per wave: every load is issued before the first product.  With FP8
-// (E4M3) B and C the products run on the FP8 matrix cores, whose fragment is
-// the bf16 one with one byte per K-value (checked on gfx950: OCP E4M3
-// operands, lane (q, c) supplies row c, K-values 8q .. 8q + 7).
+// r = 0..3), K = dstate.  The backward forms its tiles again in fp32 from C
+// and B instead of reading these.
+// One workgroup per (b, k, g) and four consecutive row tiles I = 4m + wave:
+// each wave holds the C fragments of its row tile in registers, and the B rows
+// stream through LDS in 64-row blocks (blocks 0 .. m), so every B and C row
+// is fetched once per workgroup instead of once per tile.  With FP8 (E4M3) B
+// and C the products run on the FP8 matrix cores, whose fragment is the bf16
+// one with one byte per K-value (checked on gfx950: OCP E4M3 operands, lane
+// (q, c) supplies row c, K-values 8q .. 8q + 7).
+template <typename TI, int N>
+struct BmmLds {
+  __attribute__((aligned(16))) TI Bs[64 * N];
+};
+
 template <typename T, typename TI, int Q, int N>
-__device__ __forceinline__ void bmm_tile_wave(const TI* __restrict__ B, const TI* __restrict__ C, T* __restrict__ wf,
-                                              const RowMap& rm, int G, int K, int bkg, int idx) {
-  constexpr int NT = Q / 16;
-  constexpr int TILES = NT * (NT + 1) / 2;
+__device__ __forceinline__ void bmm_rows_block(const TI* __restrict__ B, const TI* __restrict__ C, T* __restrict__ wf,
+                                               const RowMap& rm, int G, int K, int bkg, int m, BmmLds<TI, N>& sm) {
+  constexpr int NTH = 256;
+  constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = (N + 31) / 32;
+  constexpr bool F8 = std::is_same<TI, fp8>::value;
+  constexpr int EP = 16 / sizeof(TI);
+  constexpr int RBY = N * (int)sizeof(TI);
+  constexpr int NPC = RBY / 16, CRPP = RBY >= 256 ? 1 : 256 / RBY;
+  constexpr int PIECES = 64 * NPC, PPT = (PIECES + NTH - 1) / NTH;
+  static_assert(RBY % 16 == 0, "B rows are whole 16-byte pieces");
   const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
-  const int l = lane_id(), q = l >> 4, c = l & 15;
-  int I = 0;
-  while ((I + 1) * (I + 2) / 2 <= idx) ++I;
-  const int J = idx - I * (I + 1) / 2;
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int I = 4 * m + wave;
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   B = rows_in(rm, k, B, rm.B);
   C = rows_in(rm, k, C, rm.C);
-  const TI* brow = B + ((row0 + 16 * J + c) * G + g) * N;
   const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
-  f4 af = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (std::is_same<TI, fp8>::value) {
-    long fb[NK], fc[NK];
+  // C fragments of row tile I (the product's second operand: column c = row 16 I + c)
+  [[maybe_unused]] long c8[F8 ? NK : 1];
+  [[maybe_unused]] Frag<T> cf[F8 ? 1 : NK];
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      const int kk = ks * 32 + 8 * q;
-      fb[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(brow + kk) : 0;
-      fc[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(crow + kk) : 0;
-    }
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) af = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(fb[ks], fc[ks], af, 0, 0, 0);
-  } else {
-    Frag<T> fb[NK], fc[NK];
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-      frag_load_k<N>(fb[ks], brow, ks * 32 + 8 * q);
-      frag_load_k<N>(fc[ks], crow, ks * 32 + 8 * q);
-    }
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) mma(af, fb[ks], fc[ks]);  // [row j][col i] = B_j . C_i
+  for (int ks = 0; ks < NK; ++ks) {
+    const int kk = ks * 32 + 8 * q;
+    if constexpr (F8) c8[ks] = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(crow + kk) : 0;
+    else frag_load_k<N>(cf[ks], crow, kk);
   }
-  typename Vec4<T>::type vf;
+  T* out = wf + (int64_t)bkg * TILES * 256 + l * 4;
+  for (int jb = 0; jb <= m; ++jb) {
+    if (jb > 0) __syncthreads();  // the previous block's rows are no longer read
 #pragma unroll
-  for (int r = 0; r < 4; ++r) vf[r] = from_f<T>(af[r]);
-  *reinterpret_cast<typename Vec4<T>::type*>(wf + ((int64_t)bkg * TILES + idx) * 256 + l * 4) = vf;
+    for (int n = 0; n < PPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (PIECES % NTH == 0 || u < PIECES) {
+        const int r = u / NPC;
+        *reinterpret_cast<uint4*>(&sm.Bs[u * EP]) = *reinterpret_cast<const uint4*>(
+            B + ((row0 + 64 * jb + r) * G + g) * N + ((u % NPC) ^ row_swz<NPC, CRPP>(r)) * EP);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int J = 4 * jb + t;
+      if (J > I) break;  // wave-uniform
+      f4 af = {0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * t + c;  // B row 16 J + c of the staged block
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+        const int kk = ks * 32 + 8 * q;
+        if constexpr (F8) {
+          const long b8 = (N % 32 == 0 || kk < N) ? *reinterpret_cast<const long*>(&sm.Bs[staged_off<N, NPC, CRPP, TI>(r, kk)]) : 0;
+          af = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b8, c8[ks], af, 0, 0, 0);
+        } else {
+          Frag<T> fb;
+          staged_row_frag<N, NPC, CRPP>(fb, &sm.Bs[0], r, kk);
+          mma(af, fb, cf[ks]);  // [row j][col i] = B_j . C_i
+        }
+      }
+      typename Vec4<T>::type v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = from_f<T>(af[e]);
+      *reinterpret_cast<typename Vec4<T>::type*>(out + (int64_t)tri_index(I, J) * 256) = v;
+    }
+  }
 }
 
-// The two independent first steps of the forward in one launch, one wave
-// per work item and no barrier: workgroups [0, nbmm) compute C.B^T tiles
-// (workgroup = (b, k, g) and 4 consecutive tiles), the rest the chunk cumsum
-// of 4 consecutive (b, HW heads, k).  Both are small and latency-bound, so their
+// The two independent first steps of the forward in one launch:
+// workgroups [0, nbmm) compute C.B^T tiles (workgroup = (b, k, g) and four
+// consecutive row tiles, the heaviest first), the rest the chunk cumsum, one
+// wave per (b, HW heads, k).  Both are small and latency-bound, so their
 // waves overlap instead of running as two launches one after the other.
 template <typename T, typename TI, int Q, int N, int HW>
 __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, const float* __restrict__ A,
@@ -210,14 +269,14 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
                                                     const TI* __restrict__ C, T* __restrict__ wf,
                                                     const RowMap rm, int H, int G, int K, int softplus, int nbkg,
                                                     int nbhk) {
-  constexpr int NT = Q / 16, TILES = NT * (NT + 1) / 2, TB = (TILES + 3) / 4;
-  const int wave = threadIdx.x / kWave;
-  const int nbmm = nbkg * TB;
+  constexpr int NM = Q / 64;  // groups of four row tiles
+  static_assert(Q % 64 == 0, "chunk");
+  __shared__ BmmLds<TI, N> sm;
+  const int nbmm = nbkg * NM;
   if ((int)blockIdx.x < nbmm) {
-    const int idx = (blockIdx.x % TB) * 4 + wave;
-    if (idx < TILES) bmm_tile_wave<T, TI, Q, N>(B, C, wf, rm, G, K, blockIdx.x / TB, idx);
+    bmm_rows_block<T, TI, Q, N>(B, C, wf, rm, G, K, blockIdx.x / NM, NM - 1 - (int)blockIdx.x % NM, sm);
   } else {
-    const int item = ((int)blockIdx.x - nbmm) * 4 + wave;
+    const int item = ((int)blockIdx.x - nbmm) * 4 + threadIdx.x / kWave;
     if (item < nbhk / HW) chunk_cumsum_wave<T, Q, HW>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, item);
   }
 }
@@ -424,62 +483,79 @@ void launch_chunk_state(const TU* U, const TV* V, const float* dt, const float* 
 }
 
 // ---------------------------------------------------------------------------
-// Forward state passing, elementwise over the P*N state entries of each
-// (b, h) and sequential over chunks:
-//   h = init (zero if null);  hin[k] = h;  h = exp(cs_{Q-1}(k)) h + S[k];   final = h.
-// Each thread owns 4 consecutive entries.  S comes in the storage type (the
-// chunk states are rounded to it like every stored state); the scan itself
-// runs in float32.
-template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_state_passing_fwd(const T* __restrict__ S, const float* __restrict__ cs,
-                                                           const float* __restrict__ init, T* __restrict__ hin,
-                                                           float* __restrict__ final_state, int H, int K, int PN) {
+// Inter-chunk state passing, elementwise over the P*N state entries of each
+// (b, h) and sequential over chunks.
+//   forward:        h = init (zero if null); for k = 0 .. K-1:
+//                     out[k] = h;  h = exp(cs_{Q-1}(k)) h + in[k];      final = h
+//                   (in = the chunk states S, out = Hin)
+//   reverse (BWD):  g = dfinal (zero if null); for k = K-1 .. 0:
+//                     out[k] = g;  g = in[k] + exp(cs_{Q-1}(k)) g;      final = g
+//                   (in = dH_loc, out = G, the gradient w.r.t. the state
+//                   leaving chunk k; the final g is the initial-state gradient)
+// Each thread owns 4 consecutive entries; inputs and outputs are in the
+// storage type, the carry is float32.
+// The chain through the chunks is sequential, and a launch has only
+// b * H * P * N / 4 threads (2560 waves at 80 heads of 64 x 128 states), so a
+// wave that waited for each chunk's load before the next would leave HBM
+// mostly idle.  Loads run kScanAhead chunks ahead of the one being added,
+// through a ring of registers (the loop is unrolled by the ring length so
+// every slot is a fixed register set).  The log-decays of a block of
+// kScanAhead chunks arrive as one vector load, lane l holding chunk l of the
+// block, and are read with readlane: as scalar loads (which may return out
+// of order) every use would wait for all of them.
+constexpr int kScanAhead = 16;
+
+template <typename T, int Q, bool BWD>
+__global__ __launch_bounds__(256) void k_state_passing(const T* __restrict__ in, const float* __restrict__ cs,
+                                                       const float* __restrict__ init, T* __restrict__ out,
+                                                       float* __restrict__ fin, int H, int K, int PN) {
+  typedef typename Vec4<T>::type V;
+  constexpr int D = kScanAhead;
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (e >= PN) return;
-  const int bh = blockIdx.y, h = bh % H, b = bh / H;
+  const int bh = blockIdx.y, h = bh % H, b = bh / H, l = lane_id();
   const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
+  const int64_t stride = (int64_t)H * PN;  // one chunk further
+  const T* src = in + ((int64_t)b * K * H + h) * PN + e;
+  T* dst = out + ((int64_t)b * K * H + h) * PN + e;
+  auto chunk = [&](int i) { return BWD ? K - 1 - i : i; };  // chunk of step i
+  // log-decay of step i0 + l % D (clamped to the last step), lane l
+  auto lg_load = [&](int i0) { return csb[(int64_t)chunk(min(i0 + l % D, K - 1)) * Q]; };
   f4 st = {0.f, 0.f, 0.f, 0.f};
   if (init) st = *reinterpret_cast<const f4*>(init + (int64_t)bh * PN + e);
-  for (int k = 0; k < K; ++k) {
-    const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
-    const typename Vec4<T>::type s = *reinterpret_cast<const typename Vec4<T>::type*>(S + off);
-    const float alpha = __expf(csb[(int64_t)k * Q]);
-    typename Vec4<T>::type v;
+  // the slot is consumed before its refill is issued, so the refill can land
+  // in the same registers (no copy, which would wait for the load)
+  auto step = [&](V& slot, int i, float lgv, int u, bool refill) {
+    const float alpha = __expf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(lgv), u)));
+    V v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = from_f<T>(st[r]);
-    *reinterpret_cast<typename Vec4<T>::type*>(hin + off) = v;
+    *reinterpret_cast<V*>(dst + chunk(i) * stride) = v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st[r] = alpha * st[r] + to_f(s[r]);
+    for (int r = 0; r < 4; ++r) st[r] = alpha * st[r] + to_f(slot[r]);
+    if (refill) slot = *reinterpret_cast<const V*>(src + chunk(i + D) * stride);
+  };
+  V ring[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < K) ring[u] = *reinterpret_cast<const V*>(src + chunk(u) * stride);
+  float lgv = lg_load(0);
+  int i0 = 0;
+  // every refill of these blocks is in range
+  for (; i0 + 2 * D <= K; i0 += D) {
+    const float lgn = lg_load(i0 + D);
+#pragma unroll
+    for (int u = 0; u < D; ++u) step(ring[u], i0 + u, lgv, u, true);
+    lgv = lgn;
   }
-  if (final_state) *reinterpret_cast<f4*>(final_state + (int64_t)bh * PN + e) = st;
-}
-
-// Reverse state passing: g = dfinal (zero if null); for k = K-1..0:
-// gout[k] = g; g = dhloc[k] + exp(cs_{Q-1}(k)) g.  gout[k] is the gradient
-// w.r.t. the state leaving chunk k; the g left at the end is the gradient
-// w.r.t. the initial state, written to dinit if non-null.
-template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_state_passing_bwd(const T* __restrict__ dhloc, const float* __restrict__ cs,
-                                                           const float* __restrict__ dfinal, T* __restrict__ gout,
-                                                           float* __restrict__ dinit, int H, int K, int PN) {
-  const int e = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (e >= PN) return;
-  const int bh = blockIdx.y, h = bh % H, b = bh / H;
-  const float* csb = cs + (int64_t)bh * K * Q + (Q - 1);
-  f4 gs = {0.f, 0.f, 0.f, 0.f};
-  if (dfinal) gs = *reinterpret_cast<const f4*>(dfinal + (int64_t)bh * PN + e);
-  for (int k = K - 1; k >= 0; --k) {
-    const int64_t off = (((int64_t)b * K + k) * H + h) * PN + e;
-    typename Vec4<T>::type v;
+  for (; i0 < K; i0 += D) {
+    const float lgn = i0 + D < K ? lg_load(i0 + D) : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = from_f<T>(gs[r]);
-    *reinterpret_cast<typename Vec4<T>::type*>(gout + off) = v;
-    const typename Vec4<T>::type d = *reinterpret_cast<const typename Vec4<T>::type*>(dhloc + off);
-    const float alpha = __expf(csb[(int64_t)k * Q]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) gs[r] = to_f(d[r]) + alpha * gs[r];
+    for (int u = 0; u < D; ++u)
+      if (i0 + u < K) step(ring[u], i0 + u, lgv, u, i0 + u + D < K);
+    lgv = lgn;
   }
-  if (dinit) *reinterpret_cast<f4*>(dinit + (int64_t)bh * PN + e) = gs;
+  if (fin) *reinterpret_cast<f4*>(fin + (int64_t)bh * PN + e) = st;
 }
 
 }  // namespace ssd
