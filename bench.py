@@ -68,6 +68,17 @@ def log(*a):
 
 # ---------------------------------------------------------------------------
 # Algorithmic traffic and work per launch of each kernel.
+def head_slices(s) -> int:
+    """Head slices of the group-level backward launches, as the library plans
+    them: about 512 workgroups per kind of 64-row block, at most 4 slices, at
+    most one per head, every slice non-empty."""
+    base = s.batch * (-(-s.seqlen // s.chunk)) * s.ngroups * (s.chunk // 64)
+    hpg = s.nheads // s.ngroups
+    sl = max(1, min(-(-512 // base), 4, hpg))
+    per = -(-hpg // sl)
+    return -(-hpg // per)
+
+
 def kernel_model(s, esz):
     """Bytes and flops per launch over the whole chunks (a shorter last chunk
     runs as a separate launch of each kernel, which the probes do not time)."""
@@ -87,7 +98,10 @@ def kernel_model(s, esz):
     STe = b * K * H * P * N * esz    # chunk states, storage dtype
     WT = b * K * G * tiles * 256 * esz
     nbp = (Q // 64) * (Q // 64 + 1) // 2
-    DW = b * K * G * nbp * 64 * 64 * 4
+    S = head_slices(s)
+    # dW as the head-sum launch writes it: one slice in the storage dtype, else fp32 per slice
+    DW = b * K * G * nbp * 64 * 64 * (esz if S == 1 and esz == 2 else 4 * S)
+    PART = 2 * S * T * G * N * 4     # fp32 head-slice partials of dC and dB (written, then read once)
     tri = Q * (Q + 1) // 2
     bkh, bkg = b * K * H, b * K * G
     m = {
@@ -103,9 +117,11 @@ def kernel_model(s, esz):
         # C.B^T is formed again per head in fp32 (the tri * N term)
         "chunk_scan_bwd": (XI + 2 * X + DT + 2 * CS + 2 * BC + 2 * STe,
                            2 * bkh * (Q * N * P + 2 * tri * P + tri * N)),
-        # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in, dW out
-        "dw_heads": (XI + X + 2 * CS + 2 * STe + DW, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
-        "bc_final": (DW + 2 * BC + 2 * BCO, 4 * bkg * tri * N),  # dC and dB: dW, B, C in; dC, dB out
+        # dW, dC and dB head sums in one launch: x, dy, cs, the step, Hin and G in; dW and the
+        # dC / dB head-slice partials out
+        "dw_heads": (XI + X + 2 * CS + 2 * STe + DW + PART, 2 * bkh * tri * P + 4 * bkh * Q * P * N),
+        # dC and dB: dW, the partials, B, C in; dC, dB out
+        "bc_final": (DW + PART + 2 * BC + 2 * BCO, 4 * bkg * tri * N),
         "da_dd": (2 * b * K * H * 4 + 2 * H * 4, 0),
     }
     return m
@@ -364,10 +380,12 @@ def summarize_stats(csv_path: str, command: str, title: str) -> str:
         m = re.search(r"(k_[a-z_0-9]+)", n)
         short = m.group(1) if m else n.split("(")[0].split("<")[0].replace("void ", "")[:40]
         # the kernels' bool template flag names the variant
+        # (mangled Lb0E / Lb1E, or false / true in a demangled name)
         flag = re.search(r"L(b[01])E", n)
+        bit = int(flag.group(1)[1]) if flag else (1 if ", true" in n else 0 if ", false" in n else None)
         labels = {"k_chunk_state": ("forward", "backward"), "k_state_passing": ("forward", "backward")}
-        if flag and short in labels:
-            short += f" ({labels[short][int(flag.group(1)[1])]})"
+        if bit is not None and short in labels:
+            short += f" ({labels[short][bit]})"
         lines.append(f"| {short} | `{n[:70]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
     return "\n".join(lines) + "\n"
