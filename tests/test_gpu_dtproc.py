@@ -4,7 +4,7 @@ The library takes the raw step and the per-head bias, applies the softplus
 in the chunk cumsum and chains its gradient in the dl assembly; the oracle is
 the plain definition (oracle/dtproc.py) around the sequential recurrence.
 ddt is then the gradient w.r.t. dt_raw and ddt_bias the bias gradient.
-Tolerance as elsewhere (1e-4 fp32, 2e-2 bf16, max|gpu - ref| / max|ref|).
+Tolerance as elsewhere (1e-4 fp32, 2e-2 bf16 and FP8, max|gpu - ref| / max|ref|).
 """
 import numpy as np
 import pytest
@@ -15,7 +15,8 @@ from tests.util import NAMES_IN, max_rel, to_np
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+# fp8: against the oracle on the E4M3 values themselves (the kernels widen them exactly)
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 2e-2}
 
 
 def run_gpu_softplus(inp, chunk, states=None):
@@ -70,6 +71,9 @@ CASES = [
     ("mamba2_370m", dict(batch=2, seqlen=900, nheads=4)),
     ("zamba2_7b", dict(batch=1, seqlen=640, nheads=8, ngroups=2, chunk=128)),
     ("long_context", dict(seqlen=2048, nheads=16, ngroups=2)),
+    # E4M3 x, B, C with the fused step, both passes (a ragged tail and two groups)
+    ("mamba2_370m", dict(batch=2, seqlen=900, nheads=4, dtype="fp8")),
+    ("zamba2_7b", dict(batch=1, seqlen=640, nheads=8, ngroups=2, chunk=128, dtype="fp8")),
 ]
 
 
