@@ -144,6 +144,36 @@ size_t ssd_saved_bytes(const ssd_shape *shape);
 size_t ssd_fwd_scratch_bytes(const ssd_shape *shape);
 size_t ssd_bwd_scratch_bytes(const ssd_shape *shape);
 
+/* Where the chunked algorithm's intermediates sit, as byte offsets into the
+ * workspace each field names, so that they can be inspected and checked one
+ * kernel at a time (Mamba-2 SSD chunked algorithm: the in-chunk cumsum, the
+ * chunk states, state passing; and the reverse of each in the backward).
+ * With K = ceil(seqlen / chunk) chunks of Q = chunk rows, the last one
+ * zero-padded when Q does not divide seqlen, and "state" meaning float32
+ * for SSD_F32 and bf16 otherwise (SSD_FP8 included):
+ *   in saved_ws, written by ssd_fwd:
+ *     cs          float32 [b][H][K][Q]  sum_{j <= i} dt_j A_h within chunk k
+ *     step        float32 [b][H][K][Q]  the dt the scan used (softplus(dt + dt_bias)
+ *                                       with SSD_DT_SOFTPLUS; 0 on padded rows)
+ *     hin         state [b][K][H][P][N]  the state entering chunk k
+ *   in the forward scratch, written by ssd_fwd:
+ *     chunk_state state [b][K][H][P][N]  chunk k's contribution from a zero state:
+ *                                       sum_i exp(cs_{Q-1} - cs_i) dt_i x_i B_i^T
+ *   in the backward scratch, written by ssd_bwd:
+ *     dhloc       state [b][K][H][P][N]  sum_i exp(cs_i) dy_i C_i^T over chunk k
+ *     gstate      state [b][K][H][P][N]  the gradient with respect to the state
+ *                                       leaving chunk k
+ * The values stay until the workspace is next written; the library never
+ * reads them back from the caller except through ssd_bwd's saved context.
+ * Returns the ssd_check_shape error for an invalid or unsupported shape, and
+ * SSD_ERR_INVALID_ARGUMENT for a NULL pointer; *out is written on SSD_OK only. */
+typedef struct {
+    size_t cs, step, hin;
+    size_t chunk_state;
+    size_t dhloc, gstate;
+} ssd_regions;
+ssd_status ssd_workspace_regions(const ssd_shape *shape, ssd_regions *out);
+
 /* SSD_OK if the shape is valid and its (dtype, chunk, headdim, dstate) is
  * compiled in; otherwise the error ssd_fwd would return for it. */
 ssd_status ssd_check_shape(const ssd_shape *shape);

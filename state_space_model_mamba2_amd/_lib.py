@@ -30,6 +30,12 @@ class Saved(ctypes.Structure):
                 ("saved_ws", ctypes.c_void_p), ("saved_ws_bytes", ctypes.c_size_t)]
 
 
+class Regions(ctypes.Structure):
+    """Byte offsets of the chunked algorithm's intermediates (ssd_regions)."""
+    _fields_ = [("cs", ctypes.c_size_t), ("step", ctypes.c_size_t), ("hin", ctypes.c_size_t),
+                ("chunk_state", ctypes.c_size_t), ("dhloc", ctypes.c_size_t), ("gstate", ctypes.c_size_t)]
+
+
 class ConvShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("channels", ctypes.c_int64),
                 ("width", ctypes.c_int32), ("dtype", ctypes.c_int32), ("silu", ctypes.c_int32),
@@ -62,6 +68,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes, f.restype = [PShape], sz
     lib.ssd_check_shape.argtypes, lib.ssd_check_shape.restype = [PShape], st
+    lib.ssd_workspace_regions.argtypes = [PShape, ctypes.POINTER(Regions)]
+    lib.ssd_workspace_regions.restype = st
     lib.ssd_fwd.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, sz, vp, PProbe]
     lib.ssd_fwd.restype = st
     lib.ssd_fwd_noalloc.argtypes = [PShape, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, PSaved, vp, PProbe]

@@ -361,6 +361,20 @@ size_t ssd_saved_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? m
 size_t ssd_fwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).fwd_bytes : 0; }
 size_t ssd_bwd_scratch_bytes(const ssd_shape* s) { return check_shape(s) == SSD_OK ? make_plan(s).bwd_bytes : 0; }
 
+ssd_status ssd_workspace_regions(const ssd_shape* s, ssd_regions* out) {
+  if (!out) return SSD_ERR_INVALID_ARGUMENT;
+  const ssd_status st = check_shape(s);
+  if (st != SSD_OK) return st;
+  const Plan p = make_plan(s);
+  out->cs = p.lay.cs_off;
+  out->step = p.sv_dtf;
+  out->hin = p.lay.hin_off;
+  out->chunk_state = p.lay.s_off;
+  out->dhloc = p.lay.dhloc_off;
+  out->gstate = p.lay.g_off;
+  return SSD_OK;
+}
+
 ssd_status ssd_fwd(const ssd_shape* s, const void* x, const void* dt, const float* A, const void* B, const void* C,
                    const float* D, const float* dt_bias, const float* initial_state, void* y, float* final_state, void* saved_ws,
                    size_t saved_ws_bytes, ssd_saved* saved_out, void* scratch, size_t scratch_bytes,

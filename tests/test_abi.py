@@ -95,6 +95,32 @@ def test_workspace_sizes(lib):
     assert lib.ssd_saved_bytes(ctypes.byref(shape(batch=4))) > saved
 
 
+def test_workspace_regions(lib):
+    # each intermediate lies inside the workspace its field names, with room
+    # for its array, and no two arrays of one workspace overlap
+    for kw in [{}, dict(seqlen=500), dict(dtype=_lib.SSD_F32, chunk=64), dict(dtype=_lib.SSD_FP8, batch=3)]:
+        s = shape(**kw)
+        r = _lib.Regions()
+        assert lib.ssd_workspace_regions(ctypes.byref(s), ctypes.byref(r)) == OK
+        b, L, H, P, N, Q = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.chunk
+        K = -(-L // Q)
+        esz = 4 if s.dtype == _lib.SSD_F32 else 2
+        scal, states = b * H * K * Q * 4, b * K * H * P * N * esz
+        spans = {"saved": [(r.cs, scal), (r.step, scal), (r.hin, states)], "fwd": [(r.chunk_state, states)],
+                 "bwd": [(r.dhloc, states), (r.gstate, states)]}
+        size = {"saved": lib.ssd_saved_bytes(ctypes.byref(s)), "fwd": lib.ssd_fwd_scratch_bytes(ctypes.byref(s)),
+                "bwd": lib.ssd_bwd_scratch_bytes(ctypes.byref(s))}
+        for ws, sp in spans.items():
+            sp = sorted(sp)
+            assert all(o % 16 == 0 and o + n <= size[ws] for o, n in sp), (kw, ws, sp)
+            assert all(sp[i][0] + sp[i][1] <= sp[i + 1][0] for i in range(len(sp) - 1)), (kw, ws, sp)
+    r = _lib.Regions()
+    assert lib.ssd_workspace_regions(ctypes.byref(shape(nheads=5)), ctypes.byref(r)) == INVALID
+    assert lib.ssd_workspace_regions(ctypes.byref(shape(headdim=48)), ctypes.byref(r)) == UNSUPPORTED
+    assert lib.ssd_workspace_regions(ctypes.byref(shape()), None) == INVALID
+    assert lib.ssd_workspace_regions(None, ctypes.byref(r)) == INVALID
+
+
 FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
 
 
