@@ -73,17 +73,16 @@ Layout make_layout(const ssd_shape* s, int64_t L, int64_t K) {
   // Head slices of the group-level backward launch (dW and the dC / dB head
   // sums; each slice writes fp32 partials that are summed in a fixed order):
   // about `target` workgroups per kind of block, never finer than one head and
-  // never more than kMaxSlices.  Measured at the 2.7B shape
+  // never more than kMaxHeadSlices.  Measured at the 2.7B shape
   // (b*K*G*Q/64 = 256): two slices is fastest; more slices cost more in partial sums than the extra parallelism
   // gains, one slice starves dW.  Small problems (a one-chunk tail) would ask
   // for dozens of slices, whose serial partial sums on few workgroups cost far
   // more than the heads they spread.
-  constexpr int64_t kMaxSlices = 4;
   auto slices = [&](int64_t target) {
     const int64_t base = y.b * y.K * y.G * (y.Q / 64);
     const int64_t hpg = y.H / y.G;
     int64_t sl = (target + base - 1) / base;
-    if (sl > kMaxSlices) sl = kMaxSlices;
+    if (sl > kMaxHeadSlices) sl = kMaxHeadSlices;
     if (sl > hpg) sl = hpg;
     if (sl < 1) sl = 1;
     // the kernels give each slice ceil(hpg / sl) heads; take the slice count

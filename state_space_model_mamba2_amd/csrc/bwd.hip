@@ -1130,11 +1130,11 @@ struct BcFinalLds {
   __attribute__((aligned(16))) T Ms[64][MP];
 };
 
-template <typename T, typename TI, int Q, int N, bool DB, int NH>
+template <typename T, typename TI, int Q, int N, bool DB, int NH, bool DWST>
 __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, const float* __restrict__ dw,
                                                const TI* __restrict__ M, T* __restrict__ out, const RowMap& rm,
                                                int G, int K, int nslice, int nslice_dw, int bkg, int nbkg, int RB,
-                                               int zpart, BcFinalLds<T, Q, N, NH>& sm, int dw_st) {
+                                               int zpart, BcFinalLds<T, Q, N, NH>& sm) {
   constexpr int NTH = 256;
   constexpr int NP = N / NH;                 // dstate columns of this part
   constexpr int TN = NP / 16, NB = Q / 64;
@@ -1162,24 +1162,32 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) acc[tn] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // The operands of one block kb in registers: the dW block's 4-element runs
+  // and the M rows.  With dW in the storage type (DWST: a single head slice,
+  // the case of problems with many (b, k, g) items) block kb + 1 is loaded
+  // while block kb's products run; the fp32 head-slice partials (several
+  // slices: problems with few items, where the registers the prefetch takes
+  // cost more occupancy than it gains) are loaded, added and staged in turn.
+  constexpr int WRUNS = 64 * 64 / 4 / NTH;  // 4-element dW runs per thread
+  static_assert(64 * 64 % (4 * NTH) == 0, "dW runs");
+  typedef typename Vec4<T>::type W4;
+  [[maybe_unused]] W4 wst[WRUNS];
+  [[maybe_unused]] f4 wsl[WRUNS];
+  V mv[MPT];
   const int kb0 = DB ? RB : 0, kb1 = DB ? NB - 1 : RB;
-  for (int kb = kb0; kb <= kb1; ++kb) {
-    // dW block: rows i, columns j (dC: i in RB, j in kb; dB: i in kb, j in RB)
-    const int ib = DB ? kb : RB, jb = DB ? RB : kb;
-    for (int e = threadIdx.x * 4; e < 64 * 64; e += NTH * 4) {
-      const int il = e / 64, jl = e % 64;
-      const int64_t eo = (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
-      typename Vec4<T>::type w;
-      if (dw_st) {  // one slice, already in the storage dtype
-        w = *reinterpret_cast<const typename Vec4<T>::type*>(reinterpret_cast<const T*>(dw) + (int64_t)bkg * Q * Q + eo);
-      } else {
-        const float* src = dwb + eo;
-        f4 v = *reinterpret_cast<const f4*>(src);
-        for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(src + z * dws);
+  auto load_block = [&](int kb) {
+    const int ib = DB ? kb : RB, jb = DB ? RB : kb;  // dW rows i, columns j
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = from_f<T>(v[r]);
+    for (int it = 0; it < WRUNS; ++it) {
+      const int e = (threadIdx.x + NTH * it) * 4, il = e / 64, jl = e % 64;
+      const int64_t eo = (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
+      if constexpr (DWST) {  // one slice, already in the storage dtype
+        wst[it] = *reinterpret_cast<const W4*>(reinterpret_cast<const T*>(dw) + (int64_t)bkg * Q * Q + eo);
+      } else {
+        f4 v = *reinterpret_cast<const f4*>(dwb + eo);
+        for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(dwb + eo + z * dws);
+        wsl[it] = v;
       }
-      *reinterpret_cast<typename Vec4<T>::type*>(&Wb[il][jl]) = w;
     }
     // B rows j (dC) or C rows i (dB) of block kb
 #pragma unroll
@@ -1187,11 +1195,45 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
       const int u = threadIdx.x + NTH * n;
       if (MPIECES % NTH == 0 || u < MPIECES) {
         const int rr = u / (NP / VN), cu = u % (NP / VN);
-        *reinterpret_cast<V*>(&Ms[rr][cu * VN]) =
-            load_vec16<T, TI>(M + ((row0 + 64 * kb + rr) * G + g) * N + n0 + cu * VN);
+        mv[n] = load_vec16<T, TI>(M + ((row0 + 64 * kb + rr) * G + g) * N + n0 + cu * VN);
       }
     }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int it = 0; it < WRUNS; ++it) {
+      const int e = (threadIdx.x + NTH * it) * 4, il = e / 64, jl = e % 64;
+      W4 w;
+      if constexpr (DWST) {
+        w = wst[it];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = from_f<T>(wsl[it][r]);
+      }
+      *reinterpret_cast<W4*>(&Wb[il][jl]) = w;
+    }
+#pragma unroll
+    for (int n = 0; n < MPT; ++n) {
+      const int u = threadIdx.x + NTH * n;
+      if (MPIECES % NTH == 0 || u < MPIECES) {
+        const int rr = u / (NP / VN), cu = u % (NP / VN);
+        *reinterpret_cast<V*>(&Ms[rr][cu * VN]) = mv[n];
+      }
+    }
+  };
+  const int64_t ps = (int64_t)nbkg * Q * N;  // head-slice partial stride b*K*G*Q*N
+  auto pidx = [&](int tn, int r) {
+    return ((prow0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + n0 + 16 * tn + c;
+  };
+  if constexpr (DWST) load_block(kb0);
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    if (kb > kb0) __syncthreads();  // the previous block is no longer read
+    if constexpr (!DWST) load_block(kb);
+    store_block();
     __syncthreads();
+    if constexpr (DWST) {
+      if (kb < kb1) load_block(kb + 1);
+    }
 #pragma unroll
     for (int kp = 0; kp < 2; ++kp) {
       Frag<T> fa;
@@ -1204,37 +1246,34 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
         mma(acc[tn], fa, fb);
       }
     }
-    __syncthreads();
   }
-  const int64_t ps = (int64_t)nbkg * Q * N;  // head-slice partial stride b*K*G*Q*N
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int rr = r0 + 16 * wave + 4 * q + r;
-      const int64_t e = ((prow0 + rr) * G + g) * N + n0 + 16 * tn + c;
+      const int64_t e = pidx(tn, r);
       float v = part[e];
       for (int z = 1; z < nslice; ++z) v += part[z * ps + e];
-      out[((row0 + rr) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
+      out[((row0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
     }
   }
 }
 
 // dC and dB in one launch (both read the same dW blocks): blockIdx.z < NH
 // takes dstate part z of dC, the rest the parts of dB.
-template <typename T, typename TI, int Q, int N, int NH>
+template <typename T, typename TI, int Q, int N, int NH, bool DWST>
 __global__ __launch_bounds__(256) void k_bc_final(const float* __restrict__ dcpart, const float* __restrict__ dbpart,
                                                   const float* __restrict__ dw, const TI* __restrict__ B,
                                                   const TI* __restrict__ C, T* __restrict__ dC, T* __restrict__ dB,
-                                                  const RowMap rm, int G, int K, int nslice, int dw_st) {
+                                                  const RowMap rm, int G, int K, int nslice) {
   __shared__ BcFinalLds<T, Q, N, NH> sm;
   const int z = blockIdx.z;
   if (z < NH)
-    bc_final_block<T, TI, Q, N, false, NH>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
-                                       z, sm, dw_st);
+    bc_final_block<T, TI, Q, N, false, NH, DWST>(dcpart, dw, B, dC, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x,
+                                                 blockIdx.y, z, sm);
   else
-    bc_final_block<T, TI, Q, N, true, NH>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x, blockIdx.y,
-                                      z - NH, sm, dw_st);
+    bc_final_block<T, TI, Q, N, true, NH, DWST>(dbpart, dw, C, dB, rm, G, K, nslice, nslice, blockIdx.x, gridDim.x,
+                                                blockIdx.y, z - NH, sm);
 }
 
 // Fixed-order sums of the per-(b, k) partials (dA, dD and, when requested,
@@ -1312,12 +1351,21 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     // Splitting the dstate columns gives a launch with few (b, k, g) items enough
     // workgroups, but every part stages and converts the whole dW block again;
     // once the row blocks alone make 2048 workgroups, one part takes all columns.
-    if ((int64_t)nbkg * (Q / 64) * 2 >= 2048)
-      k_bc_final<T, TI, Q, N, 1><<<dim3(nbkg, Q / 64, 2), dim3(256), 0, st>>>(
-          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
-    else
-      k_bc_final<T, TI, Q, N, kBcParts<N>><<<dim3(nbkg, Q / 64, 2 * kBcParts<N>), dim3(256), 0, st>>>(
-          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S, dw_st);
+    auto launch = [&](auto nh, auto dwst) {
+      constexpr int NH = decltype(nh)::value;
+      k_bc_final<T, TI, Q, N, NH, decltype(dwst)::value><<<dim3(nbkg, Q / 64, 2 * NH), dim3(256), 0, st>>>(
+          a.dcpart, a.dbpart, a.dw, B, C, static_cast<T*>(a.dC), static_cast<T*>(a.dB), a.rows, G, K, S);
+    };
+    using one = std::integral_constant<int, 1>;
+    using parts = std::integral_constant<int, kBcParts<N>>;
+    using st1 = std::integral_constant<bool, sizeof(T) == 2>;  // dw_st: dW in the storage type
+    if ((int64_t)nbkg * (Q / 64) * 2 >= 2048) {
+      if (dw_st) launch(one{}, st1{});
+      else launch(one{}, std::false_type{});
+    } else {
+      if (dw_st) launch(parts{}, st1{});
+      else launch(parts{}, std::false_type{});
+    }
   }
   {
     ProbeScope ps(probe, SSD_K_DA_DD, st);

@@ -81,6 +81,10 @@ struct BwdArgs {
   RowMap rows;
 };
 
+// Most head slices the group-level head sums of the backward split a group's
+// heads into (each slice writes fp32 partials that are added in a fixed order).
+constexpr int kMaxHeadSlices = 4;
+
 // Workgroups that share one (batch, chunk, head) in the backward chunk kernel
 // (each owns an interleaved half of the chunk's 16-token column tiles).
 constexpr int scan_bwd_splits(int Q) { return Q >= 256 ? Q / 128 : 1; }
