@@ -241,7 +241,7 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   T* wt = static_cast<T*>(a.wt);
   {
     ProbeScope ps(probe, SSD_K_CUMSUM_BMM, st);
-    const int nbkg = b * K * G, nbhk = b * H * K, nbmm = nbkg * (Q / 64);
+    const int nbkg = b * K * G, nbhk = b * H * K, nbmm = (nbkg + 7) / 8 * 8 * (Q / 64);
     // four adjacent heads per cumsum wave where the head count allows (one 8- or
     // 16-byte load per token instead of four strided ones)
     if (H % 4 == 0)

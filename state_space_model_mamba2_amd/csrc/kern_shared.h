@@ -259,9 +259,12 @@ __device__ __forceinline__ void bmm_rows_block(const TI* __restrict__ B, const T
 
 // The two independent first steps of the forward in one launch:
 // workgroups [0, nbmm) compute C.B^T tiles (workgroup = (b, k, g) and four
-// consecutive row tiles, the heaviest first), the rest the chunk cumsum, one
-// wave per (b, HW heads, k).  Both are small and latency-bound, so their
-// waves overlap instead of running as two launches one after the other.
+// consecutive row tiles), the rest the chunk cumsum, one wave per (b, HW
+// heads, k).  Both are small and latency-bound, so their waves overlap
+// instead of running as two launches one after the other.  The Q/64 C.B^T
+// workgroups of one (b, k, g), which stage the same B rows, are dealt 8
+// dispatch slots apart (one XCD and its L2, about the same time; the
+// heaviest first), nbmm = Q/64 times the item count rounded up to 8.
 template <typename T, typename TI, int Q, int N, int HW>
 __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, const float* __restrict__ A,
                                                     const float* __restrict__ dt_bias, float* __restrict__ dt_out,
@@ -272,9 +275,12 @@ __global__ __launch_bounds__(256) void k_cumsum_bmm(const T* __restrict__ dt, co
   constexpr int NM = Q / 64;  // groups of four row tiles
   static_assert(Q % 64 == 0, "chunk");
   __shared__ BmmLds<TI, N> sm;
-  const int nbmm = nbkg * NM;
+  const int nbmm = (nbkg + 7) / 8 * 8 * NM;
   if ((int)blockIdx.x < nbmm) {
-    bmm_rows_block<T, TI, Q, N>(B, C, wf, rm, G, K, blockIdx.x / NM, NM - 1 - (int)blockIdx.x % NM, sm);
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int item = (j / NM) * 8 + xcd;
+    if (item >= nbkg) return;  // whole workgroup, before any barrier
+    bmm_rows_block<T, TI, Q, N>(B, C, wf, rm, G, K, item, NM - 1 - j % NM, sm);
   } else {
     const int item = ((int)blockIdx.x - nbmm) * 4 + threadIdx.x / kWave;
     if (item < nbhk / HW) chunk_cumsum_wave<T, Q, HW>(dt, A, dt_bias, dt_out, cs, rm, H, K, softplus, item);
