@@ -676,20 +676,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 //   ddt_j = A dl_j + <dxt_j, x_j>,  dA partial = sum_j dt_j dl_j.
 // One wave per (b, k, h) and 4 heads per workgroup (b K H / 4 workgroups, so
 // the launch fills the chip); lane l owns the Q / 64 consecutive tokens
-// starting at l Q / 64.
+// starting at l Q / 64.  A chunk's head groups share the token rows of ddt
+// (one step per head), so its workgroups are dealt 8 dispatch slots apart:
+// one XCD's L2 gathers each row's heads before it goes to memory.
 template <typename T, int Q>
 __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
                                                      const float* __restrict__ cs_g, const float* __restrict__ dt,
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
                                                      float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
-                                                     int softplus, int ntp) {
+                                                     int softplus, int ntp, int nbk) {
   constexpr int NSPLIT = scan_bwd_splits(Q);
   constexpr int HPB = 4;                      // heads (waves) per workgroup
   constexpr int TPL = Q / kWave;
   static_assert(Q % kWave == 0, "chunk");
   const int nhb = (H + HPB - 1) / HPB;
-  const int hb = blockIdx.x % nhb, bk = blockIdx.x / nhb;
+  const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+  const int hb = jb % nhb, bk = (jb / nhb) * 8 + xcd;
+  if (bk >= nbk) return;  // whole workgroup; no barrier in this kernel
   const int k = bk % K, b = bk / K;
   const int jl = lane_id();
   const int h = HPB * hb + threadIdx.x / kWave;
@@ -1352,9 +1356,9 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     const int nitems = b * K * H;
     k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
         x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
-    k_dl_assemble<T, Q><<<dim3(b * K * ((H + 3) / 4)), dim3(256), 0, st>>>(
+    k_dl_assemble<T, Q><<<dim3((b * K + 7) / 8 * 8 * ((H + 3) / 4)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
-        P / 16);
+        P / 16, b * K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int nbkg = b * K * G;
