@@ -312,7 +312,11 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
                                                      float* __restrict__ dlpart, const RowMap rm, int H, int G, int K,
                                                      int nitems) {
   constexpr int NTH = 256;
-  constexpr int KB = 64;                           // tokens per block
+  // tokens per block: the forward's smaller blocks at dstate 128 fit more
+  // workgroups on a CU (long context 0.268 -> 0.258 ms); the backward, which
+  // also forms the state-to-output rows per block, measured slower with them
+  // (0.38 -> 0.40 ms), and so did the forward at dstate 64
+  constexpr int KB = (!BWD && N >= 128) ? 32 : 64;
   constexpr int NB = Q / KB;
   constexpr int UP = P + 16, VP = N + 16;          // row pitches (8 mod 16 dwords for 64 / 128 wide rows)
   constexpr int TM = P / 16, TN = N / 16, NT = TM * TN, TPW = (NT + 3) / 4;
