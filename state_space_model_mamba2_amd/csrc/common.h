@@ -167,6 +167,10 @@ __device__ __forceinline__ void frag_load_kmajor(Frag<float>& f, const float* ti
 // lds_wave_base is the same for the whole wave (checked on gfx950 with an
 // in-bounds probe).  Counted by vmcnt like any vector-memory load; the caller
 // waits for it (s_waitcnt vmcnt) before a barrier that publishes the data.
+// s_waitcnt immediate for vmcnt(n) lgkmcnt(0) (expcnt not waited for):
+// vmcnt's low four bits at [3:0], its high two at [15:14].
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
 __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }

@@ -228,6 +228,235 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same chunk scan for bf16 with headdim 64, resident over heads: one
+// workgroup of 8 waves (one per CU, 2 waves per SIMD) per (b, k, g) and
+// slice of the group's heads.  Each wave keeps the C fragments and the C.B^T
+// tiles of its two row tiles in registers for the whole slice (the group's
+// operands, read once per slice instead of once per head), and the heads
+// stream through two LDS buffers: each head's x rows, entering state and step
+// / cumsum values are copied from global memory straight into LDS (no
+// registers) one head ahead, while the current head's products run.  Per
+// head a workgroup then reads only that head's rows, about 50 KB instead of
+// the 200 KB a per-head workgroup requests.  The products are those of
+// k_chunk_scan_fwd.  With one wave per SIMD (4 waves) the products' LDS and
+// exponential latencies stayed exposed (0.20 against 0.16 ms at the 2.7B
+// shape); with 8 waves the copy addresses are formed from 32-bit per-thread
+// offsets so the kernel stays within 256 registers without spilling.
+template <int Q, int N>
+struct FwdGroupLayout {
+  static constexpr int P = 64;
+  static constexpr int XPIECES = Q * P / 8, HPIECES = P * N / 8;  // 16-byte pieces
+  static constexpr int NW = 8, NTH = NW * 64;                     // 8 waves: 2 per SIMD
+  static constexpr int XPT = XPIECES / NTH, HPT = HPIECES / NTH;   // copies per thread and head
+  static constexpr int DPH = XPT + HPT + 1;                       // + the step / cumsum copy
+  static_assert(XPIECES % NTH == 0 && HPIECES % NTH == 0, "whole copies per thread");
+};
+
+template <int Q, int N>
+__global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
+    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
+    const float* __restrict__ Dp, const bf16* __restrict__ C, const bf16* __restrict__ hin,
+    const bf16* __restrict__ wt, bf16* __restrict__ y, const RowMap rm, int H, int G, int K, int hps, int nslice,
+    int nbkg) {
+  typedef bf16 T;
+  typedef FwdGroupLayout<Q, N> Ly;
+  constexpr int P = Ly::P;
+  constexpr int NTH = Ly::NTH, NW = Ly::NW;
+  constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
+  constexpr int NK = N / 32, NJ2 = NT / 2;
+  constexpr int NSLOT = NT / NW;  // row tiles per wave
+  constexpr int XPT = Ly::XPT, HPT = Ly::HPT, DPH = Ly::DPH;
+  constexpr int HPC = N / 8;      // 16-byte pieces of a state row
+  constexpr int YST = NSLOT * TP;  // y stores of one head per thread (8-byte, never merged)
+  static_assert(N % 32 == 0 && NT % NW == 0 && YST < 64, "shape");
+  typedef typename Vec4<T>::type V4;
+  // two head buffers, each its own set of arrays (see the head loop)
+  __shared__ __attribute__((aligned(16))) T X0[Q * P], X1[Q * P];      // x rows, xcol-permuted
+  __shared__ __attribute__((aligned(16))) T H0[P * N], H1[P * N];      // Hin, pieces XOR-permuted by row
+  __shared__ __attribute__((aligned(16))) float S0[4 * NTH], S1[4 * NTH];  // cs [0, Q), dt [Q, 2Q), spare
+  __shared__ __attribute__((aligned(16))) float F0[Q], F1[Q];          // bfac
+  __shared__ float Ds[64];                                             // D of the slice's heads
+
+  const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+  const int slice = jb % nslice, bkg = (jb / nslice) * 8 + xcd;
+  if (bkg >= nbkg) return;  // whole workgroup, before any barrier
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int hpg = H / G, h0 = g * hpg + slice * hps, nh = min(hps, hpg - slice * hps);
+  const int wave = threadIdx.x / kWave, l = lane_id(), q = l >> 4, c = l & 15;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  C = rows_in(rm, k, C, rm.C);
+  y = rows_out(rm, k, y, rm.y);
+  const T* wtb = wt + (int64_t)bkg * TILES * 256;
+
+  int Is[NSLOT];
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) Is[sl] = 2 * NW * (sl / 2) + ((sl & 1) ? 2 * NW - 1 - wave : wave);
+
+  // ---- the group's operands of this wave's row tiles, resident
+  Frag<T> cf[NSLOT][NK];
+  V4 wv[NSLOT][NT];
+  // slot sl's row tile never exceeds jm(sl) - 1 (zig-zag), so only its tiles
+  // J < jm(sl) are held (the rest are never referenced and take no registers)
+  auto jm = [&](int sl) { return 2 * NW * (sl / 2) + ((sl & 1) ? 2 * NW : NW); };
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int I = Is[sl];
+    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(cf[sl][ks], crow, ks * 32 + 8 * q);
+#pragma unroll
+    for (int J = 0; J < NT; ++J)  // tiles past the diagonal are never used: load (I, I) instead
+      if (J < jm(sl)) wv[sl][J] = *reinterpret_cast<const V4*>(wtb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + l * 4);
+  }
+  if (threadIdx.x < nh) Ds[threadIdx.x] = Dp[h0 + threadIdx.x];
+
+  // ---- one head's copies into a buffer: thread t's 16 bytes of copy n land
+  // at byte 16 (n NTH + t) of the array, so it fetches the piece the permuted
+  // layout keeps there.  Copy n of a thread reads 64 n / (P / 8) rows (x) or
+  // NTH / (N / 8) n rows (Hin) below copy 0, and the row permutations depend
+  // only on row bits the step does not change, so each source is a 32-bit
+  // per-thread offset plus a multiple of a uniform stride.  Every thread
+  // issues DPH copies per head.
+  static_assert(NTH % (P / 8) == 0 && NTH % HPC == 0 && (NTH / (P / 8)) % 16 == 0 && (NTH / HPC) % HPC == 0,
+                "copy steps keep the permutation bits");
+  const int t = threadIdx.x;
+  const int xr0 = t / (P / 8), xo0 = xr0 * H * P + ((t % (P / 8)) ^ (2 * ((xr0 ^ (xr0 >> 2)) & 3))) * 8;
+  const int xstep = (NTH / (P / 8)) * H * P;
+  const int hr0 = t / HPC, ho0 = hr0 * N + ((t % HPC) ^ (hr0 & (HPC - 1))) * 8;
+  const int su = t < Q / 2 ? t : 0;  // cs then dt (2 Q floats); threads past them copy cs again
+  auto head_dma = [&](int hh, T* Xb, T* Hb, float* Sb) {
+    const int h = h0 + hh;
+    const T* xh = x + (row0 * H + h) * P;
+#pragma unroll
+    for (int n = 0; n < XPT; ++n) lds_copy16(xh + xo0 + n * xstep, Xb + (n * NTH + wave * kWave) * 8);
+    const T* hs = hin + ((((int64_t)b * K + k) * H + h) * P) * N;
+#pragma unroll
+    for (int n = 0; n < HPT; ++n) lds_copy16(hs + ho0 + n * (NTH / HPC) * N, Hb + (n * NTH + wave * kWave) * 8);
+    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+    const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
+    lds_copy16(su < Q / 4 ? csb + 4 * su : dtb + 4 * (su - Q / 4), Sb + wave * kWave * 4);
+  };
+
+  int xoff[TP];
+#pragma unroll
+  for (int tp = 0; tp < TP; ++tp) {
+    const int r0 = 4 * q + (c >> 2);
+    xoff[tp] = r0 * P + xcol(r0, 16 * tp + 4 * (c & 3));
+  }
+
+  // one head from the buffer (Xb, Hb, Sb, Fb)
+  auto head = [&](int hh, const T* Xb, const T* Hb, const float* Sb, float* Fb) {
+    const int h = h0 + hh;
+    const float* csl = Sb;
+    const float* dtl = Sb + Q;
+    // bfac_j = dt_j exp(cs_r - cs_j), r the last token of j's 32-token step
+#pragma unroll
+    for (int i = threadIdx.x; i < Q; i += NTH) Fb[i] = __expf(csl[i | 31] - csl[i]) * dtl[i];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const float Dh = Ds[hh];
+    T* yh = y + h * P;
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) {
+      const int I = Is[sl];
+      f4 acc[TP];
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) acc[tp] = f4{0.f, 0.f, 0.f, 0.f};
+      // 1. state -> output: Hin . C_i (K = dstate); lane column i = 16I + c
+#pragma unroll
+      for (int ks = 0; ks < NK; ++ks) {
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          const int r = 16 * tp + c;
+          Frag<T> fh;
+          frag_load(fh, Hb + r * N + ((4 * ks + q) ^ (r & (HPC - 1))) * 8);
+          mma(acc[tp], fh, cf[sl][ks]);
+        }
+      }
+      const int ci = 16 * I + c;
+      const float cs_i = csl[ci];
+      {
+        const float e = __expf(cs_i);
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) acc[tp] *= e;
+      }
+      // 2. intra-chunk, steps of 32 source tokens (as in k_chunk_scan_fwd)
+#pragma unroll
+      for (int J2 = 0; J2 < NJ2; ++J2) {
+        if (2 * J2 >= jm(sl) || 2 * J2 > I) break;
+        Frag<T> fa;
+        if (2 * J2 + 1 < I) {
+          const float ai = __expf(cs_i - csl[32 * J2 + 31]);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int J = 2 * J2 + half;
+            const f4 bj = *reinterpret_cast<const f4*>(&Fb[16 * J + 4 * q]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, to_f(wv[sl][J][r]) * (ai * bj[r]));
+          }
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int J = 2 * J2 + half;
+            const int j0 = 16 * J + 4 * q;
+            const f4 csj = *reinterpret_cast<const f4*>(&csl[j0]);
+            const f4 dtj = *reinterpret_cast<const f4*>(&dtl[j0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float m = (J <= I && j0 + r <= ci) ? __expf(cs_i - csj[r]) * dtj[r] : 0.0f;
+              frag_set<T>(fa, half * 4 + r, to_f(wv[sl][J][r]) * m);
+            }
+          }
+        }
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          Frag<T> fx;
+          const T* a = Xb + 32 * J2 * P + xoff[tp];
+          frag_load_kmajor_at(fx, a, a + 16 * P);
+          mma(acc[tp], fx, fa);
+        }
+      }
+      // 3. + D x, store y[i][16tp + 4q + r]
+      T* yr = yh + (row0 + ci) * H * P;
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        const V4 xv = *reinterpret_cast<const V4*>(&Xb[ci * P + xcol(ci, 16 * tp + 4 * q)]);
+        V4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = from_f<T>(acc[tp][r] + Dh * to_f(xv[r]));
+        *reinterpret_cast<V4*>(yr + 16 * tp + 4 * q) = o;
+      }
+    }
+  };
+
+  // ---- heads.  Head hh lives in buffer hh & 1.  At the top of a head, its
+  // copies have landed once at most the previous head's y stores (issued
+  // after them) are in flight; after the barrier the other buffer is free
+  // (the previous head is done with it) and takes the next head's copies.
+  // The loop is unrolled by two so that every LDS access names its buffer's
+  // array, and the compiler does not wait for copies into the other one.
+  head_dma(0, X0, H0, S0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): resident operands and head 0
+  __syncthreads();                     // Ds, head 0's copies
+  auto step = [&](int hh, const T* Xb, const T* Hb, const float* Sb, float* Fb, T* Xn, T* Hn, float* Sn) {
+    if (hh > 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(YST));
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    if (hh + 1 < nh) head_dma(hh + 1, Xn, Hn, Sn);
+    head(hh, Xb, Hb, Sb, Fb);
+  };
+  for (int hh = 0; hh < nh; hh += 2) {
+    step(hh, X0, H0, S0, F0, X1, H1, S1);
+    if (hh + 1 < nh) step(hh + 1, X1, H1, S1, F1, X0, H0, S0);
+  }
+}
+
 template <typename T, typename TI, int Q, int P, int N>
 void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_probe* probe) {
   const int b = (int)lay.b, H = (int)lay.H, G = (int)lay.G, K = (int)lay.K;
@@ -265,8 +494,28 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
-    k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, b * K * H);
+    // The resident kernel: one workgroup per (b, k, g) and slice of at most 64
+    // of its heads, about one per CU where the items are few and one slice
+    // where they are many.  It pays when a slice has at least kMinHeads heads
+    // to spread the group operands' loads over: measured 20 heads (2.7B
+    // shape) 0.156 -> 0.130 ms, 14 (Zamba2-7B-like) 89 -> 82 us, 10 (long
+    // context) 0.583 -> 0.529 ms, but 8 (Mamba2-370M shape) 57 -> 59 us.
+    constexpr int kMinHeads = 10;
+    const int nbkg = b * K * G, hpg = H / G;
+    int S = (256 + nbkg - 1) / nbkg;
+    if (S > hpg) S = hpg;
+    int per = (hpg + S - 1) / S;
+    if (per > 64) per = 64;
+    S = (hpg + per - 1) / per;
+    if (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0 &&
+        per >= kMinHeads) {
+      if constexpr (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0)
+        k_chunk_scan_fwd_heads<Q, N><<<dim3((nbkg + 7) / 8 * 8 * S), dim3(FwdGroupLayout<Q, N>::NTH), 0, st>>>(
+            x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, per, S, nbkg);
+    } else {
+      k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
+          x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, b * K * H);
+    }
   }
 }
 
