@@ -494,21 +494,15 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
-    // The resident kernel: one workgroup per (b, k, g) and slice of at most 64
-    // of its heads, about one per CU where the items are few and one slice
-    // where they are many.  It pays when a slice has at least kMinHeads heads
-    // to spread the group operands' loads over: measured 20 heads (2.7B
-    // shape) 0.156 -> 0.130 ms, 14 (Zamba2-7B-like) 89 -> 82 us, 10 (long
-    // context) 0.583 -> 0.529 ms, but 8 (Mamba2-370M shape) 57 -> 59 us.
-    constexpr int kMinHeads = 10;
-    const int nbkg = b * K * G, hpg = H / G;
-    int S = (256 + nbkg - 1) / nbkg;
-    if (S > hpg) S = hpg;
-    int per = (hpg + S - 1) / S;
-    if (per > 64) per = 64;
-    S = (hpg + per - 1) / per;
+    // The resident kernel where a slice holds enough heads (resident_slices):
+    // measured 20 heads (2.7B shape) 0.156 -> 0.130 ms, 14 (Zamba2-7B-like)
+    // 89 -> 82 us, 10 (long context) 0.583 -> 0.529 ms, but 8 (Mamba2-370M
+    // shape) 57 -> 59 us.
+    const int nbkg = b * K * G;
+    int S;
+    const int per = resident_slices(nbkg, H / G, &S);
     if (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0 &&
-        per >= kMinHeads) {
+        per >= kMinResidentHeads) {
       if constexpr (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0)
         k_chunk_scan_fwd_heads<Q, N><<<dim3((nbkg + 7) / 8 * 8 * S), dim3(FwdGroupLayout<Q, N>::NTH), 0, st>>>(
             x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, per, S, nbkg);

@@ -478,6 +478,22 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
   }
 }
 
+// Head slices of a kernel resident over heads: about one workgroup per CU
+// where the (b, k, g) items are few, one slice per item where they are many,
+// at most 64 heads a slice.  Returns the heads per slice; *S the slice count.
+// Such a kernel pays when a slice holds at least kMinResidentHeads heads to
+// spread its group operands' staging over (measured on the forward chunk
+// scan: 20, 14 and 10 heads faster than one workgroup per head, 8 slower).
+constexpr int kMinResidentHeads = 10;
+inline int resident_slices(int nbkg, int hpg, int* S) {
+  int s = (256 + nbkg - 1) / nbkg;
+  if (s > hpg) s = hpg;
+  int per = (hpg + s - 1) / s;
+  if (per > 64) per = 64;
+  *S = (hpg + per - 1) / per;
+  return per;
+}
+
 // Launch of k_chunk_state: two heads per workgroup when a group's heads pair up.
 // hin / dlpart: the backward's chunk-entry states and dl partial sums (the
 // state-to-output term), unused (null) in the forward.
