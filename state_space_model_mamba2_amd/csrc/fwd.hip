@@ -246,17 +246,21 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 && P % 64 == 0) ? 3 : 2) void 
 template <int Q, int N>
 struct FwdGroupLayout {
   static constexpr int P = 64;
-  static constexpr int XPIECES = Q * P / 8, HPIECES = P * N / 8;  // 16-byte pieces
+  static constexpr int XPIECES = Q * P / 8, HPIECES = P * N / 8;  // 16-byte pieces (bf16)
   static constexpr int NW = 8, NTH = NW * 64;                     // 8 waves: 2 per SIMD
   static constexpr int XPT = XPIECES / NTH, HPT = HPIECES / NTH;   // copies per thread and head
-  static constexpr int DPH = XPT + HPT + 1;                       // + the step / cumsum copy
-  static_assert(XPIECES % NTH == 0 && HPIECES % NTH == 0, "whole copies per thread");
+  static constexpr int X8T = Q * P / 16 / NTH;                    // FP8 x: 16-code loads per thread
+  static_assert(XPIECES % NTH == 0 && HPIECES % NTH == 0 && (Q * P / 16) % NTH == 0, "whole copies per thread");
 };
 
-template <int Q, int N>
+// x in bf16 (TI = bf16) is copied into LDS directly; FP8 x, B and C (TI =
+// fp8): x is loaded into registers with the next head's copies, widened to
+// bf16 and stored into the other buffer after the current head's products,
+// and the resident C fragments are widened as they are loaded.
+template <typename TI, int Q, int N>
 __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
-    const bf16* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
-    const float* __restrict__ Dp, const bf16* __restrict__ C, const bf16* __restrict__ hin,
+    const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
+    const float* __restrict__ Dp, const TI* __restrict__ C, const bf16* __restrict__ hin,
     const bf16* __restrict__ wt, bf16* __restrict__ y, const RowMap rm, int H, int G, int K, int hps, int nslice,
     int nbkg) {
   typedef bf16 T;
@@ -266,7 +270,8 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
   constexpr int NK = N / 32, NJ2 = NT / 2;
   constexpr int NSLOT = NT / NW;  // row tiles per wave
-  constexpr int XPT = Ly::XPT, HPT = Ly::HPT, DPH = Ly::DPH;
+  constexpr int XPT = Ly::XPT, HPT = Ly::HPT, X8T = Ly::X8T;
+  constexpr bool F8 = std::is_same<TI, fp8>::value;
   constexpr int HPC = N / 8;      // 16-byte pieces of a state row
   constexpr int YST = NSLOT * TP;  // y stores of one head per thread (8-byte, never merged)
   static_assert(N % 32 == 0 && NT % NW == 0 && YST < 64, "shape");
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) {
     const int I = Is[sl];
-    const T* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+    const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(cf[sl][ks], crow, ks * 32 + 8 * q);
 #pragma unroll
@@ -328,15 +333,35 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   const int su = t < Q / 2 ? t : 0;  // cs then dt (2 Q floats); threads past them copy cs again
   auto head_dma = [&](int hh, T* Xb, T* Hb, float* Sb) {
     const int h = h0 + hh;
-    const T* xh = x + (row0 * H + h) * P;
+    if constexpr (!F8) {
+      const TI* xh = x + (row0 * H + h) * P;
 #pragma unroll
-    for (int n = 0; n < XPT; ++n) lds_copy16(xh + xo0 + n * xstep, Xb + (n * NTH + wave * kWave) * 8);
+      for (int n = 0; n < XPT; ++n) lds_copy16(xh + xo0 + n * xstep, Xb + (n * NTH + wave * kWave) * 8);
+    }
     const T* hs = hin + ((((int64_t)b * K + k) * H + h) * P) * N;
 #pragma unroll
     for (int n = 0; n < HPT; ++n) lds_copy16(hs + ho0 + n * (NTH / HPC) * N, Hb + (n * NTH + wave * kWave) * 8);
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
     const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
     lds_copy16(su < Q / 4 ? csb + 4 * su : dtb + 4 * (su - Q / 4), Sb + wave * kWave * 4);
+  };
+  // FP8 x: 16 codes (a quarter row) per load, widened into the xcol-permuted rows
+  [[maybe_unused]] uint4 x8[F8 ? X8T : 1];
+  auto x8_load = [&](int hh) {
+    const int h = h0 + hh;
+#pragma unroll
+    for (int n = 0; n < X8T; ++n) {
+      const int u = t + NTH * n, r = u / (P / 16), cq = (u % (P / 16)) * 16;
+      x8[n] = *reinterpret_cast<const uint4*>(x + ((row0 + r) * H + h) * P + cq);
+    }
+  };
+  auto x8_store = [&](T* Xb) {
+#pragma unroll
+    for (int n = 0; n < X8T; ++n) {
+      const int u = t + NTH * n, r = u / (P / 16), cq = (u % (P / 16)) * 16;
+      *reinterpret_cast<bf16x8*>(&Xb[r * P + xcol(r, cq)]) = e4m3x8_to_bf16(make_uint2(x8[n].x, x8[n].y));
+      *reinterpret_cast<bf16x8*>(&Xb[r * P + xcol(r, cq + 8)]) = e4m3x8_to_bf16(make_uint2(x8[n].z, x8[n].w));
+    }
   };
 
   int xoff[TP];
@@ -439,6 +464,10 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   // The loop is unrolled by two so that every LDS access names its buffer's
   // array, and the compiler does not wait for copies into the other one.
   head_dma(0, X0, H0, S0);
+  if constexpr (F8) {
+    x8_load(0);
+    x8_store(X0);
+  }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): resident operands and head 0
   __syncthreads();                     // Ds, head 0's copies
   auto step = [&](int hh, const T* Xb, const T* Hb, const float* Sb, float* Fb, T* Xn, T* Hn, float* Sn) {
@@ -448,8 +477,18 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
-    if (hh + 1 < nh) head_dma(hh + 1, Xn, Hn, Sn);
+    if (hh + 1 < nh) {
+      head_dma(hh + 1, Xn, Hn, Sn);
+      if constexpr (F8) x8_load(hh + 1);
+    }
     head(hh, Xb, Hb, Sb, Fb);
+    // FP8: head hh + 1's x rows into the other buffer, free since the
+    // barrier above; the next barrier publishes them.  Their loads, issued
+    // after head hh + 1's copies, are waited for here, and with them those
+    // copies (vmcnt counts in order), so the next wait stays correct.
+    if constexpr (F8) {
+      if (hh + 1 < nh) x8_store(Xn);
+    }
   };
   for (int hh = 0; hh < nh; hh += 2) {
     step(hh, X0, H0, S0, F0, X1, H1, S1);
@@ -501,10 +540,9 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
     const int nbkg = b * K * G;
     int S;
     const int per = resident_slices(nbkg, H / G, &S);
-    if (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0 &&
-        per >= kMinResidentHeads) {
-      if constexpr (std::is_same<T, bf16>::value && std::is_same<TI, bf16>::value && P == 64 && N % 32 == 0)
-        k_chunk_scan_fwd_heads<Q, N><<<dim3((nbkg + 7) / 8 * 8 * S), dim3(FwdGroupLayout<Q, N>::NTH), 0, st>>>(
+    if (std::is_same<T, bf16>::value && P == 64 && N % 32 == 0 && per >= kMinResidentHeads) {
+      if constexpr (std::is_same<T, bf16>::value && P == 64 && N % 32 == 0)
+        k_chunk_scan_fwd_heads<TI, Q, N><<<dim3((nbkg + 7) / 8 * 8 * S), dim3(FwdGroupLayout<Q, N>::NTH), 0, st>>>(
             x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, per, S, nbkg);
     } else {
       k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
