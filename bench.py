@@ -304,7 +304,7 @@ def kernel_matches(bench_kernel: str, name: str) -> bool:
         "chunk_state_bwd": "k_chunk_state" in name and bwd_flag,
         "state_passing_bwd": "k_state_passing" in name and bwd_flag,
         "chunk_scan_bwd": "k_chunk_scan_bwd" in name or "k_dl_assemble" in name,
-        "dw_heads": "k_dw_heads" in name,
+        "dw_heads": "k_dw_heads" in name or "k_head_sums" in name,
         "bc_final": "k_bc_final" in name,
         "da_dd": "k_da_dd" in name,
     }

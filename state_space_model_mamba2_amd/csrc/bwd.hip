@@ -1115,6 +1115,369 @@ __global__ __launch_bounds__(256) void k_dw_heads(const TI* __restrict__ x, cons
 }
 
 // ---------------------------------------------------------------------------
+// The same head sums with a whole chunk per workgroup (bf16 storage, chunk
+// 256, headdim 64).  Per ((b, k, g), head slice) two workgroups of 8 waves:
+//   kind 0: the dC and dB partials of all Q rows (the sums of bc_heads_block)
+//   kind 1: the lower triangle of dW (the sums of dw_block)
+// The 64-row blocks of k_dw_heads read every head's dy and x rows and states
+// once per block: about 352 KB of requests per head and item at dstate 128
+// against 96 KB of distinct data.  Here each workgroup reads what it uses
+// once (kind 0: dy, x, Hin, Gk; kind 1: dy, x), and the two workgroups of an
+// item are dealt 8 dispatch slots apart, so they run on one XCD and the rows
+// the second reads come from its L2.  The states (kind 0) and the x rows
+// with the head's cs and dt (kind 1) travel global -> LDS by direct copies,
+// one head ahead, into two buffers; each wave loads the row fragments of
+// its own rows into registers one head ahead.  Kind 1 takes each head's
+// 16x16 products of raw operands and applies the head's decay
+// dt_j exp(cs_i - cs_j) and the causal mask to the product before adding
+// it, so no operand is rescaled and rounded again.
+template <typename TI, int N>
+struct HsLayout {
+  static constexpr int Q = 256, P = 64, NW = 8, NTH = NW * 64;
+  static constexpr int SPC = P * N / 8;                  // 16-byte pieces of one state
+  static constexpr int SPT = 2 * SPC / NTH;              // state copies per thread and head (Hin, Gk)
+  static constexpr int XPR = P * (int)sizeof(TI) / 16;   // 16-byte pieces of an x row
+  static constexpr int XPT = Q * XPR / NTH;              // x copies per thread and head
+  static constexpr int XBYTES = Q * P * (int)sizeof(TI);
+  static constexpr int BUF = (2 * P * N * 2 > XBYTES + 2 * Q * 4) ? 2 * P * N * 2 : XBYTES + 2 * Q * 4;
+  static_assert(SPC % NTH == 0 && (Q * XPR) % NTH == 0, "whole copies per thread");
+  static_assert(NTH % (N / 8) == 0 && (NTH / (N / 8)) % 16 == 0, "state copies keep the swizzle bits");
+};
+
+// State rows in LDS: row r's 32-byte segments (16 columns) are XOR-permuted
+// by hs_key(r), so that the 16 rows one transposing read touches (rows
+// 8q + t and 8q + 4 + t of a 32-row K step, t < 4) fall on distinct banks.
+template <int N>
+__device__ __forceinline__ int hs_key(int r) {
+  return N >= 128 ? ((r & 3) | ((r >> 1) & 4)) : ((r & 3) ^ ((r >> 3) & 1));
+}
+// x rows in LDS: row r's 16-byte pieces are XOR-permuted by hs_xkey(r), so
+// that the 16 rows a fragment read touches (a 16-aligned group) fall on
+// distinct banks.  The key depends on r % 16 only, so a tile's rows share
+// one per-lane offset.
+template <typename TI>
+__device__ __forceinline__ int hs_xkey(int r) {
+  return sizeof(TI) == 2 ? ((r ^ ((r >> 3) & 1)) & 7) : ((r >> 2) & 3);
+}
+
+template <typename TI, int N>
+__device__ __forceinline__ void hs_bc(const TI* __restrict__ x, const float* __restrict__ dt,
+                                      const float* __restrict__ cs_g, const bf16* __restrict__ dy,
+                                      const bf16* __restrict__ hin, const bf16* __restrict__ gst,
+                                      float* __restrict__ dcpart, float* __restrict__ dbpart, const RowMap& rm,
+                                      int H, int G, int K, int hps, int bkg, int nbkg, int slice, bf16* S0,
+                                      bf16* S1) {
+  typedef bf16 T;
+  typedef HsLayout<TI, N> Ly;
+  constexpr int Q = Ly::Q, P = Ly::P, NTH = Ly::NTH, SPT = Ly::SPT, SPC = Ly::SPC;
+  constexpr int TN = N / 16, RPC = N / 8;
+  constexpr bool F8 = std::is_same<TI, fp8>::value;
+  typedef typename std::conditional<F8, uint2, bf16x8>::type XR;  // raw x piece of a fragment
+
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id(), q = l >> 4, c = l & 15;
+  const int t = threadIdx.x;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dy = rows_in(rm, k, dy, rm.dy);
+  const int hpg = H / G, h0 = g * hpg + slice * hps, nh = min(hps, hpg - slice * hps);
+
+  // copy n of thread t fills LDS piece n NTH + t: state (n NTH) / SPC, row
+  // ((n NTH) % SPC) / RPC + t / RPC; rows advance by multiples of 16 between
+  // copies, which keeps the key
+  const int sr = t / RPC, sp = t % RPC;
+  const int so0 = sr * N + ((((sp >> 1) ^ hs_key<N>(sr)) << 1) | (sp & 1)) * 8;
+  auto dma = [&](int hh, T* Sb) {
+    const int64_t st = (((int64_t)b * K + k) * H + h0 + hh) * P * N;
+#pragma unroll
+    for (int n = 0; n < SPT; ++n) {
+      const T* src = ((n * NTH) / SPC == 0 ? hin : gst) + st + ((n * NTH) % SPC) * 8 + so0;
+      lds_copy16(src, Sb + (n * NTH + wave * kWave) * 8);
+    }
+  };
+  struct Regs {
+    bf16x8 ad[2][2];  // dy rows 32 wave + 16 tt + c, K = 32 kp + 8 q ..
+    XR ax[2][2];      // x rows, the same pieces
+    float cs[2], dt[2], cl;
+  };
+  const int ioff = (32 * wave + c) * H * P + 8 * q;  // this lane's first row, its K piece
+  auto load_regs = [&](Regs& R, int hh) {
+    const int h = h0 + hh;
+    const T* dyh = dy + (row0 * H + h) * P + ioff;
+    const TI* xh = x + (row0 * H + h) * P + ioff;
+    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+    const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        R.ad[tt][kp] = *reinterpret_cast<const bf16x8*>(dyh + 16 * tt * H * P + 32 * kp);
+        R.ax[tt][kp] = *reinterpret_cast<const XR*>(xh + 16 * tt * H * P + 32 * kp);
+      }
+      R.cs[tt] = csb[32 * wave + 16 * tt + c];
+      R.dt[tt] = dtb[32 * wave + 16 * tt + c];
+    }
+    R.cl = csb[Q - 1];
+  };
+
+  f4 accC[2][TN], accB[2][TN];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) accC[tt][tn] = accB[tt][tn] = f4{0.f, 0.f, 0.f, 0.f};
+  // transposing reads: lane (q, c) addresses row 32 kp + 8 q + c / 4 (and 4
+  // rows below), columns 16 tn + 4 (c % 4) .. of its segment
+  const int kr = 8 * q + (c >> 2), key = hs_key<N>(kr);
+  const int roff = kr * N + 4 * (c & 3);
+  auto compute = [&](Regs& R, const T* Sb) {
+    // the row fragments, scaled in place: dC rows by exp(cs_i), dB rows by
+    // exp(cs_last - cs_j) dt_j
+    Frag<T> fc[2][2], fb[2][2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const float sc = __expf(R.cs[tt]);
+      const float sb = __expf(R.cl - R.cs[tt]) * R.dt[tt];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        bf16x8 xr;
+        if constexpr (F8) xr = e4m3x8_to_bf16(R.ax[tt][kp]);
+        else xr = R.ax[tt][kp];
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+          R.ad[tt][kp][s8] = (bf16)((float)R.ad[tt][kp][s8] * sc);
+          xr[s8] = (bf16)((float)xr[s8] * sb);
+        }
+        fc[tt][kp].v = R.ad[tt][kp];
+        fb[tt][kp].v = xr;
+      }
+    }
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const T* a = Sb + 32 * kp * N + roff + ((tn ^ key) << 4);
+        Frag<T> bh, bg;
+        frag_load_kmajor_at(bh, a, a + 4 * N);
+        frag_load_kmajor_at(bg, a + P * N, a + P * N + 4 * N);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          mma(accC[tt][tn], fc[tt][kp], bh);
+          mma(accB[tt][tn], fb[tt][kp], bg);
+        }
+      }
+    }
+  };
+
+  // Head hh lives in buffer hh & 1.  At the top of a head its copies and row
+  // loads (issued one head earlier) are waited for; after the barrier the
+  // other buffer is free (the previous head is done with it) and takes the
+  // next head's copies.  Unrolled by two so that every LDS access names its
+  // buffer's array.
+  Regs R0, R1;
+  dma(0, S0);
+  load_regs(R0, 0);
+  auto step = [&](int hh, Regs& Rc, Regs& Rn, const T* Sb, T* Sn) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (hh + 1 < nh) {
+      dma(hh + 1, Sn);
+      load_regs(Rn, hh + 1);
+    }
+    compute(Rc, Sb);
+  };
+  for (int hh = 0; hh < nh; hh += 2) {
+    step(hh, R0, R1, S0, S1);
+    if (hh + 1 < nh) step(hh + 1, R1, R0, S1, S0);
+  }
+
+  const int64_t prow0 = ((int64_t)b * K + k) * Q;
+  float* oc = dcpart + (int64_t)slice * nbkg * Q * N;
+  float* ob = dbpart + (int64_t)slice * nbkg * Q * N;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t o = ((prow0 + 32 * wave + 16 * tt + 4 * q + r) * G + g) * N + c;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        oc[o + 16 * tn] = accC[tt][tn][r];
+        ob[o + 16 * tn] = accB[tt][tn][r];
+      }
+    }
+}
+
+template <typename TI, int N>
+__device__ __forceinline__ void hs_dw(const TI* __restrict__ x, const float* __restrict__ dt,
+                                      const float* __restrict__ cs_g, const bf16* __restrict__ dy,
+                                      float* __restrict__ dw, const RowMap& rm, int H, int G, int K, int hps, int bkg,
+                                      int nbkg, int slice, TI* X0, TI* X1, float* C0, float* C1, int dw_st) {
+  typedef bf16 T;
+  typedef HsLayout<TI, N> Ly;
+  constexpr int Q = Ly::Q, P = Ly::P, NTH = Ly::NTH, XPR = Ly::XPR, XPT = Ly::XPT;
+  constexpr int NT = Q / 16, EPP = 16 / (int)sizeof(TI);
+  constexpr int NS = NT + 1;  // tiles per wave: row tiles NT - 1 - wave and wave
+  constexpr bool F8 = std::is_same<TI, fp8>::value;
+  static_assert(NT == 2 * Ly::NW, "two row tiles per wave");
+
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), l = lane_id(), q = l >> 4, c = l & 15;
+  const int t = threadIdx.x;
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  dy = rows_in(rm, k, dy, rm.dy);
+  const int hpg = H / G, h0 = g * hpg + slice * hps, nh = min(hps, hpg - slice * hps);
+  // slot s < NT - wave: tile (ti1, s); else (ti0, NT - s).  The first NT / 2
+  // slots always belong to ti1 (wave < NT / 2).
+  const int ti1 = NT - 1 - wave, ti0 = wave;
+
+  // copy n of thread t fills LDS piece n NTH + t: row n NTH / XPR + t / XPR
+  // (the step keeps the key); the head's cs and dt come with waves 0 and 1
+  const int xr0 = t / XPR;
+  const int xo0 = xr0 * H * P + ((t % XPR) ^ hs_xkey<TI>(xr0)) * EPP;
+  auto dma = [&](int hh, TI* Xb, float* Cb) {
+    const int h = h0 + hh;
+    const TI* xh = x + (row0 * H + h) * P + xo0;
+#pragma unroll
+    for (int n = 0; n < XPT; ++n) lds_copy16(xh + n * (NTH / XPR) * H * P, Xb + (n * NTH + wave * kWave) * EPP);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? cs_g : dt) + (((int64_t)b * H + h) * K + k) * Q + 4 * l;
+      lds_copy16(src, Cb + wave * kWave * 4);
+    }
+  };
+  struct Regs {
+    bf16x8 ad[2][2];  // dy rows 16 ti + c of the row tiles (ti0, ti1), K = 32 kp + 8 q ..
+  };
+  auto load_regs = [&](Regs& R, int hh) {
+    const T* dyh = dy + (row0 * H + h0 + hh) * P + c * H * P + 8 * q;
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      R.ad[0][kp] = *reinterpret_cast<const bf16x8*>(dyh + 16 * ti0 * H * P + 32 * kp);
+      R.ad[1][kp] = *reinterpret_cast<const bf16x8*>(dyh + 16 * ti1 * H * P + 32 * kp);
+    }
+  };
+  auto slot = [&](int s, int& ti, int& tj) {
+    const bool first = s < NT / 2 || s < NT - wave;
+    ti = first ? ti1 : ti0;
+    tj = first ? s : NT - s;
+    return first;
+  };
+
+  f4 acc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc[s] = f4{0.f, 0.f, 0.f, 0.f};
+  // per-lane parts of the fragment reads of x row 16 tj + c (K = 32 kp + 8 q ..)
+  int xl[2];
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp)
+    xl[kp] = F8 ? c * P + ((2 * kp + (q >> 1)) ^ hs_xkey<TI>(c)) * EPP + 8 * (q & 1)
+                : c * P + ((4 * kp + q) ^ hs_xkey<TI>(c)) * EPP;
+  auto compute = [&](const Regs& R, const TI* Xb, const float* Cb) {
+    // The per-lane offsets pass through an empty asm at every head, so the
+    // 17 slots' addresses and masks are formed here instead of being hoisted
+    // out of the head loop (where they took more registers than there are).
+    int xo[2] = {xl[0], xl[1]}, cl = c, mb = 4 * q - c;
+    asm volatile("" : "+v"(xo[0]), "+v"(xo[1]), "+v"(cl), "+v"(mb));
+    const f4 cs0 = *reinterpret_cast<const f4*>(&Cb[16 * ti0 + 4 * q]);
+    const f4 cs1 = *reinterpret_cast<const f4*>(&Cb[16 * ti1 + 4 * q]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      int ti, tj;
+      const bool first = slot(s, ti, tj);
+      const TI* xt = Xb + 16 * tj * P;
+      Frag<T> fb[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        if constexpr (F8) fb[kp].v = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(xt + xo[kp]));
+        else fb[kp].v = *reinterpret_cast<const bf16x8*>(xt + xo[kp]);
+      }
+      f4 dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        Frag<T> fa;
+        fa.v = first ? R.ad[1][kp] : R.ad[0][kp];
+        mma(dp, fa, fb[kp]);
+      }
+      const float csj = Cb[16 * tj + cl], dtj = Cb[Q + 16 * tj + cl];
+      const f4 csi = first ? cs1 : cs0;
+      const int d = 16 * (ti - tj) + mb;  // row i - column j = d + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = dp[r] * (dtj * __expf(csi[r] - csj));
+        acc[s][r] += (d + r >= 0) ? v : 0.0f;
+      }
+    }
+  };
+
+  Regs R0, R1;
+  dma(0, X0, C0);
+  load_regs(R0, 0);
+  auto step = [&](int hh, const Regs& Rc, Regs& Rn, const TI* Xb, const float* Cb, TI* Xn, float* Cn) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (hh + 1 < nh) {
+      dma(hh + 1, Xn, Cn);
+      load_regs(Rn, hh + 1);
+    }
+    compute(Rc, Xb, Cb);
+  };
+  for (int hh = 0; hh < nh; hh += 2) {
+    step(hh, R0, R1, X0, C0, X1, C1);
+    if (hh + 1 < nh) step(hh + 1, R1, R0, X1, C1, X0, C0);
+  }
+
+  // the tiles, then zeros above the diagonal inside the 64-row diagonal
+  // blocks (the dC / dB finalisation reads whole 64 x 64 blocks)
+  auto store = [&](auto* o) {  // o: this item's Q x Q dW
+    typedef typename std::remove_pointer<decltype(o)>::type O;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      int ti, tj;
+      slot(s, ti, tj);
+      O* p = o + (16 * ti + 4 * q) * Q + 16 * tj + c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r * Q] = from_f<O>(acc[s][r]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ti = u ? ti1 : ti0;
+      O* p = o + (16 * ti + 4 * q) * Q + c;
+      for (int tj = ti + 1; tj <= (ti | 3); ++tj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r * Q + 16 * tj] = from_f<O>(0.0f);
+    }
+  };
+  if (dw_st) store(reinterpret_cast<T*>(dw) + (int64_t)bkg * Q * Q);
+  else store(dw + ((int64_t)slice * nbkg + bkg) * Q * Q);
+}
+
+template <typename TI, int N>
+__global__ __launch_bounds__(512, 1) void k_head_sums(const TI* __restrict__ x, const float* __restrict__ dt,
+                                                      const float* __restrict__ cs_g, const bf16* __restrict__ dy,
+                                                      const bf16* __restrict__ hin, const bf16* __restrict__ gst,
+                                                      float* __restrict__ dw, float* __restrict__ dcpart,
+                                                      float* __restrict__ dbpart, const RowMap rm, int H, int G,
+                                                      int K, int hps, int nbkg, int nitems, int dw_st) {
+  typedef HsLayout<TI, N> Ly;
+  // two head buffers, each its own array (see the head loops)
+  __shared__ __attribute__((aligned(16))) unsigned char B0[Ly::BUF], B1[Ly::BUF];
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int item = (j >> 1) * 8 + xcd;
+  if (item >= nitems) return;  // whole workgroup, before any barrier
+  const int bkg = item % nbkg, slice = item / nbkg;
+  if ((j & 1) == 0)
+    hs_bc<TI, N>(x, dt, cs_g, dy, hin, gst, dcpart, dbpart, rm, H, G, K, hps, bkg, nbkg, slice,
+                 reinterpret_cast<bf16*>(B0), reinterpret_cast<bf16*>(B1));
+  else
+    hs_dw<TI, N>(x, dt, cs_g, dy, dw, rm, H, G, K, hps, bkg, nbkg, slice, reinterpret_cast<TI*>(B0),
+                 reinterpret_cast<TI*>(B1), reinterpret_cast<float*>(B0 + Ly::XBYTES),
+                 reinterpret_cast<float*>(B1 + Ly::XBYTES), dw_st);
+}
+
+// ---------------------------------------------------------------------------
 // dC / dB for one (b, k, g) and one 64-row block RB: the head-slice partials
 // summed in slice order, plus the dW part
 //   dC_i = ... + sum_{j <= i} dW_ij B_j        dB_j = ... + sum_{i >= j} dW_ij C_i
@@ -1368,8 +1731,13 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_DW_HEADS, st);
     const int nb = Q / 64, nitems = nbkg * S;
-    k_dw_heads<T, TI, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
-        x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems, dw_st);
+    if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {
+      k_head_sums<TI, N><<<dim3((nitems + 7) / 8 * 8 * 2), dim3(HsLayout<TI, N>::NTH), 0, st>>>(
+          x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems, dw_st);
+    } else {
+      k_dw_heads<T, TI, Q, P, N><<<dim3((nitems + 7) / 8 * 8 * (2 * nb + nb * (nb + 1) / 2)), dim3(256), 0, st>>>(
+          x, dt, a.cs, dy, hin, gst, a.dw, a.dcpart, a.dbpart, a.rows, H, G, K, hps, nbkg, nitems, dw_st);
+    }
   }
   {
     ProbeScope ps(probe, SSD_K_BC_FINAL, st);
