@@ -22,10 +22,12 @@ namespace ssd {
 // Layout of the work.  NSPLIT workgroups of 4 waves share one (b, k, h);
 // the chunk's 16-token column tiles J are dealt to the 4 NSPLIT waves in a
 // zig-zag (owner o gets J = o and 2 NO - 1 - o), so the triangular work is
-// even.  A wave keeps, per owned tile, x_J as chained-K fragments and dxt_J^T
-// as matrix-core accumulators (lane (q, c) holds dxt[16J + c][16tp + 4q + r]),
-// so every token's x and dxt values sit in the same lane and slot: <dxt_j, x_j>
-// and q_j need no second read of x.
+// even.  A wave keeps, per owned tile, x_J as fragments and dxt_J^T as
+// matrix-core accumulators whose rows are the same headdim entries (lane
+// (q, c) holds dxt[16J + c][16tp + 4q + r], or with bf16 and headdim 64 the
+// permuted rows 32 (tp / 2) + 8q + 4 (tp % 2) + r, which makes x one 16-byte
+// load), so every token's x and dxt values sit in the same lane and slot:
+// <dxt_j, x_j> and q_j need no second read of x.
 // This head's dy rows and the group's C rows stream through LDS in 32-row
 // slabs from the chunk end backwards (C mostly hits in L2, which it shares
 // with the other heads of the group).  W is formed per tile pair on the
@@ -77,6 +79,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   constexpr bool DSWZ = sizeof(T) == 2 && P == 64;
   constexpr int DPITCH = DSWZ ? P : sizeof(T) == 2 ? P + 2 * ((24 - (P / 2) % 16) % 16) : P + PADR;
   constexpr bool DMA = DSWZ;               // slabs copied global -> LDS directly
+  // XC (bf16, headdim 64): the rows of dxt^T tile tp are permuted so that lane
+  // (q, c) holds headdim entries 32 (tp / 2) + 8 q + 4 (tp % 2) + r, r < 4: the
+  // two tiles of a 32-wide K step give each lane 8 consecutive entries, so
+  // x is one 16-byte load per fragment (instead of two 8-byte pieces), a dy
+  // row fragment one 16-byte LDS read and dx one 16-byte store.  Row m of
+  // tile tp is headdim entry xrow(tp, m).
+  constexpr bool XC = DSWZ;
+  auto xrow = [](int tp, int m) { return 32 * (tp >> 1) + 8 * (m >> 2) + 4 * (tp & 1) + (m & 3); };
   constexpr int PF = DMA ? 3 : 1;          // slabs in flight ahead of the one in use
   constexpr int NBUF = DMA ? PF + 1 : 2;   // slab buffers
   constexpr int YPT = (YPIECES + NTH - 1) / NTH;
@@ -241,13 +251,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl)
 #pragma unroll
-    for (int kp = 0; kp < NKP; ++kp) frag_load_chained<P>(xf[sl][kp], xh + (int64_t)(16 * Js[sl] + c) * rs, kp * 32, q);
+    for (int kp = 0; kp < NKP; ++kp) {
+      if constexpr (XC) frag_load(xf[sl][kp], xh + (int64_t)(16 * Js[sl] + c) * rs + kp * 32 + 8 * q);
+      else frag_load_chained<P>(xf[sl][kp], xh + (int64_t)(16 * Js[sl] + c) * rs, kp * 32, q);
+    }
   // Hin rows 16 w .. 16 w + 15 (split 0, waves 0 .. TP-1: their share of <Gk, Hin>)
   const bool gh_wave = split == 0 && wave < TP;
   Frag<T> hf[NK];
   if (gh_wave) {
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(hf[ks], hinh + (16 * wave + c) * N, ks * 32 + 8 * q);
+    for (int ks = 0; ks < NK; ++ks)
+      frag_load_k<N>(hf[ks], hinh + (XC ? xrow(wave, c) : 16 * wave + c) * N, ks * 32 + 8 * q);
   }
   [[maybe_unused]] Frag<T> gf[DMA ? 1 : NK][TP];
   Frag<T> bfr[NK][NSLOT];
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   // fragment of Gk rows 16 tp .. 16 tp + 15, K-values ks * 32 + 8q .. (lane (q, c))
   auto gfrag = [&](Frag<T>& f, int ks, int tp) {
     if constexpr (DMA) {
-      const int r = 16 * tp + c;
+      const int r = XC ? xrow(tp, c) : 16 * tp + c;
       frag_load(f, &GS[r][(((ks * 32 + 8 * q) / VN) ^ (r & (GPC - 1))) * VN]);
     } else {
       f = gf[ks][tp];
@@ -390,7 +404,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     // where it is used so that it holds no registers across the pair products
     auto fdt_load = [&](Frag<T>& f, int tp) {
       if constexpr (DSWZ) {  // rows 4q + c/4 and 16 below (same permutation)
-        const int r0 = 4 * q + (c >> 2), col = 16 * tp + 4 * (c & 3);
+        // lane c of a group receives headdim entry xrow(tp, c): the 4 lanes
+        // addressing a row fetch the runs of 4 entries those columns need
+        const int r0 = 4 * q + (c >> 2), col = XC ? 32 * (tp >> 1) + 8 * (c & 3) + 4 * (tp & 1) : 16 * tp + 4 * (c & 3);
         frag_load_kmajor_at(f, &dys[r0][dyc(r0, col)], &dys[r0 + 16][dyc(r0, col)]);
       } else {
         frag_load_kmajor<SR>(f, &dys[0][0], DPITCH, 0, 16 * tp, q, c);
@@ -399,7 +415,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
     // dy row 16 half + c as a chained-K A fragment (K = headdim, from kp * 32)
     auto dy_row_frag = [&](Frag<T>& fd, int half, int kp) {
       const int yr = 16 * half + c;
-      if constexpr (DSWZ)
+      if constexpr (XC)
+        frag_load(fd, &dys[yr][dyc(yr, kp * 32 + 8 * q)]);
+      else if constexpr (DSWZ)
         frag_load2(fd, &dys[yr][dyc(yr, kp * 32 + 4 * q)], &dys[yr][dyc(yr, kp * 32 + 16 + 4 * q)]);
       else
         frag_load_chained<P>(fd, &dys[yr][0], kp * 32, q);
@@ -592,7 +610,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
       float xd = 0.0f;
 #pragma unroll
       for (int tp = 0; tp < TP; ++tp) {
-        const V4 dv = *reinterpret_cast<const V4*>(&dys[j - rb][dyc(j - rb, 16 * tp + 4 * q)]);
+        const V4 dv = *reinterpret_cast<const V4*>(
+            &dys[j - rb][dyc(j - rb, XC ? 32 * (tp >> 1) + 8 * q + 4 * (tp & 1) : 16 * tp + 4 * q)]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float xv = frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
@@ -630,12 +649,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   for (int sl = 0; sl < NSLOT; ++sl) {
     const int j = 16 * Js[sl] + c;
     T* dxr = dx + ((row0 + j) * H + h) * P;
+    if constexpr (XC) {
 #pragma unroll
-    for (int tp = 0; tp < TP; ++tp) {
-      V4 o;
+      for (int kp = 0; kp < TP / 2; ++kp) {
+        V o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = from_f<T>(adx[sl][tp][r]);
-      *reinterpret_cast<V4*>(dxr + 16 * tp + 4 * q) = o;
+        for (int r = 0; r < 8; ++r) o[r] = from_f<T>(adx[sl][2 * kp + r / 4][r % 4]);
+        *reinterpret_cast<V*>(dxr + 32 * kp + 8 * q) = o;
+      }
+    } else {
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        V4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = from_f<T>(adx[sl][tp][r]);
+        *reinterpret_cast<V4*>(dxr + 16 * tp + 4 * q) = o;
+      }
     }
     if (q == 0) {
       part[NSPLIT * Q + j] = csv2[sl];
