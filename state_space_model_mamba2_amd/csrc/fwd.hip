@@ -276,12 +276,15 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   constexpr int YST = NSLOT * TP;  // y stores of one head per thread (8-byte, never merged)
   static_assert(N % 32 == 0 && NT % NW == 0 && YST < 64, "shape");
   typedef typename Vec4<T>::type V4;
-  // two head buffers, each its own set of arrays (see the head loop)
-  __shared__ __attribute__((aligned(16))) T X0[Q * P], X1[Q * P];      // x rows, xcol-permuted
-  __shared__ __attribute__((aligned(16))) T H0[P * N], H1[P * N];      // Hin, pieces XOR-permuted by row
-  __shared__ __attribute__((aligned(16))) float S0[4 * NTH], S1[4 * NTH];  // cs [0, Q), dt [Q, 2Q), spare
-  __shared__ __attribute__((aligned(16))) float F0[Q], F1[Q];          // bfac
-  __shared__ float Ds[64];                                             // D of the slice's heads
+  // Two head buffers, each one object (see the head loop).
+  struct alignas(16) Buf {
+    T X[Q * P];             // x rows, xcol-permuted
+    T H[P * N];             // Hin, pieces XOR-permuted by row
+    float S[2 * Q + 4 * kWave];  // cs [0, Q), dt [Q, 2Q); the other waves' copies land past them, unread
+    float F[Q];                  // bfac
+  };
+  __shared__ Buf B0, B1;
+  __shared__ float Ds[64];  // D of the slice's heads
 
   const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
   const int slice = jb % nslice, bkg = (jb / nslice) * 8 + xcd;
@@ -330,7 +333,11 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   const int xr0 = t / (P / 8), xo0 = xr0 * H * P + ((t % (P / 8)) ^ (2 * ((xr0 ^ (xr0 >> 2)) & 3))) * 8;
   const int xstep = (NTH / (P / 8)) * H * P;
   const int hr0 = t / HPC, ho0 = hr0 * N + ((t % HPC) ^ (hr0 & (HPC - 1))) * 8;
-  const int su = t < Q / 2 ? t : 0;  // cs then dt (2 Q floats); threads past them copy cs again
+  // cs then dt (2 Q floats) from the first Q / 128 waves; every other wave
+  // issues the same copy (so all waves count the same copies per head) into
+  // the spare tail of the buffer's S, which nothing reads
+  const int su = t < Q / 2 ? t : 0;
+  static_assert(Q / 2 % kWave == 0, "whole waves copy cs and dt");
   auto head_dma = [&](int hh, T* Xb, T* Hb, float* Sb) {
     const int h = h0 + hh;
     if constexpr (!F8) {
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
     for (int n = 0; n < HPT; ++n) lds_copy16(hs + ho0 + n * (NTH / HPC) * N, Hb + (n * NTH + wave * kWave) * 8);
     const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
     const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
-    lds_copy16(su < Q / 4 ? csb + 4 * su : dtb + 4 * (su - Q / 4), Sb + wave * kWave * 4);
+    lds_copy16(su < Q / 4 ? csb + 4 * su : dtb + 4 * (su - Q / 4), Sb + min(wave, Q / 128) * kWave * 4);
   };
   // FP8 x: 16 codes (a quarter row) per load, widened into the xcol-permuted rows
   [[maybe_unused]] uint4 x8[F8 ? X8T : 1];
@@ -384,6 +391,16 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const float Dh = Ds[hh];
     T* yh = y + h * P;
+    // The per-lane values pass through an empty asm at every head, so the
+    // addresses formed from them are formed here instead of being hoisted
+    // out of the head loop, one set per buffer (hoisted, they spilled, and
+    // the spill reloads in the loop waited for every copy)
+    int c = lane_id() & 15, q = lane_id() >> 4, xo[TP];
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) xo[tp] = xoff[tp];
+    asm volatile("" : "+v"(c), "+v"(q));
+#pragma unroll
+    for (int tp = 0; tp < TP; ++tp) asm volatile("" : "+v"(xo[tp]));
 #pragma unroll
     for (int sl = 0; sl < NSLOT; ++sl) {
       const int I = Is[sl];
@@ -439,7 +456,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
 #pragma unroll
         for (int tp = 0; tp < TP; ++tp) {
           Frag<T> fx;
-          const T* a = Xb + 32 * J2 * P + xoff[tp];
+          const T* a = Xb + 32 * J2 * P + xo[tp];
           frag_load_kmajor_at(fx, a, a + 16 * P);
           mma(acc[tp], fx, fa);
         }
@@ -461,16 +478,18 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   // copies have landed once at most the previous head's y stores (issued
   // after them) are in flight; after the barrier the other buffer is free
   // (the previous head is done with it) and takes the next head's copies.
-  // The loop is unrolled by two so that every LDS access names its buffer's
-  // array, and the compiler does not wait for copies into the other one.
-  head_dma(0, X0, H0, S0);
+  // The loop is unrolled by two so that every LDS access names its buffer,
+  // and the compiler does not wait for copies into the other one.  (Three
+  // buffers, the copies two heads ahead, measured slower: 0.128 -> 0.138 ms
+  // at the 2.7B shape.)
+  head_dma(0, B0.X, B0.H, B0.S);
   if constexpr (F8) {
     x8_load(0);
-    x8_store(X0);
+    x8_store(B0.X);
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): resident operands and head 0
   __syncthreads();                     // Ds, head 0's copies
-  auto step = [&](int hh, const T* Xb, const T* Hb, const float* Sb, float* Fb, T* Xn, T* Hn, float* Sn) {
+  auto step = [&](int hh, Buf& Bc, Buf& Bn) {
     if (hh > 0) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(YST));
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -478,21 +497,21 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
     if (hh + 1 < nh) {
-      head_dma(hh + 1, Xn, Hn, Sn);
+      head_dma(hh + 1, Bn.X, Bn.H, Bn.S);
       if constexpr (F8) x8_load(hh + 1);
     }
-    head(hh, Xb, Hb, Sb, Fb);
+    head(hh, Bc.X, Bc.H, Bc.S, Bc.F);
     // FP8: head hh + 1's x rows into the other buffer, free since the
     // barrier above; the next barrier publishes them.  Their loads, issued
     // after head hh + 1's copies, are waited for here, and with them those
     // copies (vmcnt counts in order), so the next wait stays correct.
     if constexpr (F8) {
-      if (hh + 1 < nh) x8_store(Xn);
+      if (hh + 1 < nh) x8_store(Bn.X);
     }
   };
   for (int hh = 0; hh < nh; hh += 2) {
-    step(hh, X0, H0, S0, F0, X1, H1, S1);
-    if (hh + 1 < nh) step(hh + 1, X1, H1, S1, F1, X0, H0, S0);
+    step(hh, B0, B1);
+    if (hh + 1 < nh) step(hh + 1, B1, B0);
   }
 }
 
