@@ -36,8 +36,9 @@
  * always float32.  SSD_FP8: x, B and C are OCP FP8 E4M3 codes (1 sign, 4
  * exponent bits with bias 7, 3 mantissa bits; one byte each, no scale) in
  * both passes, every other dtype tensor (dt, y, dy, dx, ddt, dB, dC)
- * bfloat16; the forward's C.B^T runs on the FP8 matrix cores and the other
- * products widen the codes to bfloat16 (exactly).  Every pointer is a device pointer aligned
+ * bfloat16; every product widens the codes to bfloat16 exactly (the
+ * forward's C.B^T runs on the FP8 matrix cores where a launch of its own
+ * forms it).  Every pointer is a device pointer aligned
  * to 16 bytes.
  *
  * Ownership: the caller allocates every buffer (inputs, outputs, the saved

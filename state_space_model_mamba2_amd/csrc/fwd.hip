@@ -260,14 +260,13 @@ struct FwdGroupLayout {
 template <typename TI, int Q, int N>
 __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
     const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
-    const float* __restrict__ Dp, const TI* __restrict__ C, const bf16* __restrict__ hin,
-    const bf16* __restrict__ wt, bf16* __restrict__ y, const RowMap rm, int H, int G, int K, int hps, int nslice,
-    int nbkg) {
+    const float* __restrict__ Dp, const TI* __restrict__ C, const TI* __restrict__ B, const bf16* __restrict__ hin,
+    bf16* __restrict__ y, const RowMap rm, int H, int G, int K, int hps, int nslice, int nbkg) {
   typedef bf16 T;
   typedef FwdGroupLayout<Q, N> Ly;
   constexpr int P = Ly::P;
   constexpr int NTH = Ly::NTH, NW = Ly::NW;
-  constexpr int NT = Q / 16, TP = P / 16, TILES = NT * (NT + 1) / 2;
+  constexpr int NT = Q / 16, TP = P / 16;
   constexpr int NK = N / 32, NJ2 = NT / 2;
   constexpr int NSLOT = NT / NW;  // row tiles per wave
   constexpr int XPT = Ly::XPT, HPT = Ly::HPT, X8T = Ly::X8T;
@@ -295,14 +294,21 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   const int64_t row0 = chunk_row0(rm, b, k, Q);
   x = rows_in(rm, k, x, rm.x);
   C = rows_in(rm, k, C, rm.C);
+  B = rows_in(rm, k, B, rm.B);
   y = rows_out(rm, k, y, rm.y);
-  const T* wtb = wt + (int64_t)bkg * TILES * 256;
 
   int Is[NSLOT];
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) Is[sl] = 2 * NW * (sl / 2) + ((sl & 1) ? 2 * NW - 1 - wave : wave);
 
-  // ---- the group's operands of this wave's row tiles, resident
+  // ---- the group's operands of this wave's row tiles, resident: the C
+  // fragments, and the tiles W = C.B^T of its row tiles, formed here from
+  // the chunk's B rows staged in the two x buffers (the products, their
+  // order and the rounding to bf16 of the C.B^T tile kernel)
+  constexpr int RBY = N * (int)sizeof(TI), NPC = RBY / 16, EPC = 16 / (int)sizeof(TI);
+  constexpr int XBP = Q * P * 2 / 16, BPT = Q * NPC / NTH;  // 16-byte pieces of an x buffer; B copies per thread
+  static_assert(Q * RBY <= 2 * Q * P * 2 && XBP % NTH == 0 && BPT * NTH == Q * NPC && (NTH / NPC) % NPC == 0,
+                "B rows fit the two x buffers");
   Frag<T> cf[NSLOT][NK];
   V4 wv[NSLOT][NT];
   // slot sl's row tile never exceeds jm(sl) - 1 (zig-zag), so only its tiles
@@ -310,14 +316,53 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_fwd_heads(
   auto jm = [&](int sl) { return 2 * NW * (sl / 2) + ((sl & 1) ? 2 * NW : NW); };
 #pragma unroll
   for (int sl = 0; sl < NSLOT; ++sl) {
-    const int I = Is[sl];
-    const TI* crow = C + ((row0 + 16 * I + c) * G + g) * N;
+    const TI* crow = C + ((row0 + 16 * Is[sl] + c) * G + g) * N;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) frag_load_k<N>(cf[sl][ks], crow, ks * 32 + 8 * q);
-#pragma unroll
-    for (int J = 0; J < NT; ++J)  // tiles past the diagonal are never used: load (I, I) instead
-      if (J < jm(sl)) wv[sl][J] = *reinterpret_cast<const V4*>(wtb + (int64_t)tri_index(I, J <= I ? J : I) * 256 + l * 4);
   }
+  {
+    // B row j, piece pl at LDS piece pl ^ (j mod NPC): rows of the first
+    // XBP pieces in B0.X, the rest in B1.X
+    const int t = threadIdx.x, bj0 = t / NPC, bo0 = bj0 * G * N + ((t % NPC) ^ (bj0 & (NPC - 1))) * EPC;
+    const TI* bg = B + (row0 * G + g) * N;
+#pragma unroll
+    for (int n = 0; n < BPT; ++n) {
+      const int u0 = n * NTH;
+      unsigned char* dst = (u0 < XBP ? reinterpret_cast<unsigned char*>(B0.X) : reinterpret_cast<unsigned char*>(B1.X)) +
+                           ((u0 % XBP) + wave * kWave) * 16;
+      lds_copy16(bg + bo0 + (int64_t)(u0 / NPC) * G * N, dst);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+#pragma unroll
+  for (int sl = 0; sl < NSLOT; ++sl) {
+    const int I = Is[sl];
+#pragma unroll
+    for (int J = 0; J < NT; ++J) {
+      if (J >= jm(sl)) continue;
+      f4 af = {0.f, 0.f, 0.f, 0.f};
+      if (J <= I) {  // tiles past the diagonal are never used
+        const int r = 16 * J + c, u = r * NPC;
+        const unsigned char* rowp = (u < XBP ? reinterpret_cast<const unsigned char*>(B0.X)
+                                             : reinterpret_cast<const unsigned char*>(B1.X)) + (u % XBP) * 16;
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          Frag<T> fb;
+          if constexpr (F8) {
+            const int pc = (2 * ks + (q >> 1)) ^ (r & (NPC - 1));
+            fb.v = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(rowp + pc * 16 + 8 * (q & 1)));
+          } else {
+            fb.v = *reinterpret_cast<const bf16x8*>(rowp + (((4 * ks + q) ^ (r & (NPC - 1))) * 16));
+          }
+          mma(af, fb, cf[sl][ks]);  // [row j][col i] = B_j . C_i
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wv[sl][J][e] = from_f<T>(af[e]);
+    }
+  }
+  __syncthreads();  // the B rows are no longer read: the x buffers take the heads
   if (threadIdx.x < nh) Ds[threadIdx.x] = Dp[h0 + threadIdx.x];
 
   // ---- one head's copies into a buffer: thread t's 16 bytes of copy n land
@@ -526,9 +571,17 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   const TI* C = static_cast<const TI*>(a.C);
   T* hin = static_cast<T*>(a.hin);
   T* wt = static_cast<T*>(a.wt);
+  // The chunk scan resident over heads where a slice holds enough heads
+  // (resident_slices): measured 20 heads (2.7B shape) 0.156 -> 0.130 ms, 14
+  // (Zamba2-7B-like) 89 -> 82 us, 10 (long context) 0.583 -> 0.529 ms, but 8
+  // (Mamba2-370M shape) 57 -> 59 us.  It forms its C.B^T tiles itself, so
+  // the first launch then computes the cumsum only.
+  int S = 1;
+  const int per = resident_slices(b * K * G, H / G, &S);
+  const bool resident = std::is_same<T, bf16>::value && P == 64 && N % 32 == 0 && per >= kMinResidentHeads;
   {
     ProbeScope ps(probe, SSD_K_CUMSUM_BMM, st);
-    const int nbkg = b * K * G, nbhk = b * H * K, nbmm = (nbkg + 7) / 8 * 8 * (Q / 64);
+    const int nbkg = resident ? 0 : b * K * G, nbhk = b * H * K, nbmm = (nbkg + 7) / 8 * 8 * (Q / 64);
     // four adjacent heads per cumsum wave where the head count allows (one 8- or
     // 16-byte load per token instead of four strided ones)
     if (H % 4 == 0)
@@ -552,17 +605,11 @@ void run_fwd(const Layout& lay, const FwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN, st);
-    // The resident kernel where a slice holds enough heads (resident_slices):
-    // measured 20 heads (2.7B shape) 0.156 -> 0.130 ms, 14 (Zamba2-7B-like)
-    // 89 -> 82 us, 10 (long context) 0.583 -> 0.529 ms, but 8 (Mamba2-370M
-    // shape) 57 -> 59 us.
     const int nbkg = b * K * G;
-    int S;
-    const int per = resident_slices(nbkg, H / G, &S);
-    if (std::is_same<T, bf16>::value && P == 64 && N % 32 == 0 && per >= kMinResidentHeads) {
+    if (resident) {
       if constexpr (std::is_same<T, bf16>::value && P == 64 && N % 32 == 0)
         k_chunk_scan_fwd_heads<TI, Q, N><<<dim3((nbkg + 7) / 8 * 8 * S), dim3(FwdGroupLayout<Q, N>::NTH), 0, st>>>(
-            x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, per, S, nbkg);
+            x, dt, a.cs, a.D, C, B, hin, static_cast<T*>(a.y), a.rows, H, G, K, per, S, nbkg);
     } else {
       k_chunk_scan_fwd<T, TI, Q, P, N><<<dim3(xcd_grid(b * K * H)), dim3(256), 0, st>>>(
           x, dt, a.cs, a.D, C, hin, wt, static_cast<T*>(a.y), a.rows, H, G, K, b * K * H);
