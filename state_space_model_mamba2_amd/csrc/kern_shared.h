@@ -176,8 +176,9 @@ __device__ __forceinline__ void staged_row_frag(Frag<T>& f, const TI* rows, int 
 // W = C.B^T per (b, k, g), stored as lower-triangle 16x16 accumulator tiles in
 // the lane order the forward chunk kernel reads (4 elements per lane, 256 per
 // tile): tile (I, J) lane l holds W[16I + l%16][16J + 4q + r] (q = l / 16,
-// r = 0..3), K = dstate.  The backward forms its tiles again in fp32 from C
-// and B instead of reading these.
+// r = 0..3), K = dstate.  Only k_chunk_scan_fwd reads these: the chunk scan
+// resident over heads forms the same tiles itself, and the backward forms
+// its tiles again in fp32 from C and B.
 // One workgroup per (b, k, g) and four consecutive row tiles I = 4m + wave:
 // each wave holds the C fragments of its row tile in registers, and the B rows
 // stream through LDS in 64-row blocks (blocks 0 .. m), so every B and C row
