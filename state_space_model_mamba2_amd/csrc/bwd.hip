@@ -694,6 +694,510 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The chunk-scan backward resident over heads (bf16 dy, chunk 256, headdim
+// 64): one workgroup of 8 waves per (b, k, g) and slice of its heads, where
+// k_chunk_scan_bwd takes one (b, k, h) per two workgroups and fetches the
+// group's C rows (twice, as slabs) and the owned B rows again for every
+// head.  Here the chunk's C rows stay in LDS and each wave's owned B_J
+// fragments in registers for the whole slice; wave w owns the column tiles
+// w and 15 - w (the zig-zag of k_chunk_scan_bwd, two per wave).  A head's
+// dy rows and cs/dt travel global -> LDS by direct copies one head ahead
+// (two buffers), its Gk into one buffer once every wave has formed the
+// head's state term, and Hin (for <Gk, Hin>) and the owned x rows straight
+// into registers.  With the whole of dy in LDS the slab loop has no
+// barrier; it runs from the chunk start, so a column tile is complete (and
+// dx written) after the last slab.  The products are those of
+// k_chunk_scan_bwd (W formed per slab in fp32 from the staged C rows), and
+// so are the outputs: dx, and per token the row sums (all of them in the
+// first split's row, zeros in the others), column sums, q_j and
+// <dxt_j, x_j>, and per head <Gk, Hin> and <dy, x> (the first split's).
+// Memory waits are explicit: the compiler takes copies into LDS and loads
+// into registers for unordered on vmcnt and would wait for every copy in
+// flight before a register's first use or an LDS store it cannot tell
+// apart from a copy's destination.  So x and Hin are waited for by count
+// right after the next head's copies are issued, and the per-slab row sums
+// go to LDS through an asm store (the head's top wait, lgkmcnt(0) with its
+// barrier, publishes them).
+template <typename TI, int N>
+__global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
+    const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
+    const float* __restrict__ Dp, const TI* __restrict__ B, const TI* __restrict__ C, const bf16* __restrict__ hin,
+    const bf16* __restrict__ gst, const bf16* __restrict__ dy, bf16* __restrict__ dx, float* __restrict__ dlpart,
+    float* __restrict__ dlscal, const RowMap rm, int H, int G, int K, int hps, int nslice, int nbkg) {
+  typedef bf16 T;
+  constexpr int Q = 256, P = 64, NW = 8, NTH = NW * kWave;
+  constexpr int NT = Q / 16, NS = NT / 2, TP = P / 16, NK = N / 32;
+  constexpr int NSPLIT = scan_bwd_splits(Q);
+  constexpr int EP = 16 / (int)sizeof(TI);
+  constexpr int RBY = N * (int)sizeof(TI);
+  constexpr int NPC = RBY / 16, CRPP = RBY >= 256 ? 1 : 256 / RBY;
+  constexpr int GPC = N / 8;                        // 16-byte pieces of a Gk row
+  constexpr int CPT = Q * NPC / NTH, DYPT = Q * P / 8 / NTH, GPT = P * N / 8 / NTH;
+  constexpr int YST = 2 * (P / 32) + 3 * 2;         // dx stores and per-token writes per thread and head
+  static_assert(NT == 2 * NW && CPT * NTH == Q * NPC && DYPT * NTH * 8 == Q * P && GPT * NTH * 8 == P * N,
+                "whole copies per thread");
+  static_assert((NTH / NPC) % (CRPP * (NPC < 16 ? NPC : 16)) == 0 && (NTH / GPC) % GPC == 0 && (NTH / 8) % 16 == 0,
+                "copy steps keep the row permutations");
+  typedef typename Vec16<T>::type V;
+  struct alignas(16) Buf {
+    T DY[Q * P];                 // dy rows, pieces XOR-permuted by dyc
+    float S[2 * Q + 4 * kWave];  // cs [0, Q), dt [Q, 2Q); the other waves' copies land past them, unread
+  };
+  __shared__ Buf B0, B1;
+  __shared__ __attribute__((aligned(16))) TI CS[Q * N];  // the chunk's C rows, pieces XOR-permuted by row_swz
+  __shared__ __attribute__((aligned(16))) T GS[P * N];   // Gk of the head, pieces of row r XOR-permuted by r mod GPC
+  __shared__ float RA[NW][Q];                            // per-wave row sums of R
+  __shared__ float RED[2 * NW];                          // per-wave <Gk, Hin> and <dy, x>
+  // storage column of dy element (r, col): the slab layout of k_chunk_scan_bwd
+  auto dyc = [](int r, int col) { return col ^ (8 * ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))); };
+  // headdim entry of row m of dxt^T tile tp (as in k_chunk_scan_bwd with bf16 and headdim 64)
+  auto xrow = [](int tp, int m) { return 32 * (tp >> 1) + 8 * (m >> 2) + 4 * (tp & 1) + (m & 3); };
+
+  const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+  const int slice = jb % nslice, bkg = (jb / nslice) * 8 + xcd;
+  if (bkg >= nbkg) return;  // whole workgroup, before any barrier
+  const int g = bkg % G, bk = bkg / G, k = bk % K, b = bk / K;
+  const int hpg = H / G, h0 = g * hpg + slice * hps, nh = min(hps, hpg - slice * hps);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t row0 = chunk_row0(rm, b, k, Q);
+  x = rows_in(rm, k, x, rm.x);
+  B = rows_in(rm, k, B, rm.B);
+  C = rows_in(rm, k, C, rm.C);
+  dy = rows_in(rm, k, dy, rm.dy);
+  dx = rows_out(rm, k, dx, rm.dx);
+  const int Js[2] = {wave, NT - 1 - wave};
+  const int64_t rs = (int64_t)H * P;  // row stride of x / dy / dx
+
+  // ---- the owned B fragments (K = dstate), and the chunk's C rows into LDS
+  Frag<T> bfr[NK][2];
+  {
+    const int l = lane_id(), q = l >> 4, c = l & 15;
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        frag_load_k<N>(bfr[ks][sl], B + ((row0 + 16 * Js[sl] + c) * G + g) * N, ks * 32 + 8 * q);
+    const int t = threadIdx.x, cr0 = t / NPC;
+    const TI* cs0 = C + ((row0 + cr0) * G + g) * N + ((t % NPC) ^ row_swz<NPC, CRPP>(cr0)) * EP;
+#pragma unroll
+    for (int n = 0; n < CPT; ++n) lds_copy16(cs0 + (int64_t)n * (NTH / NPC) * G * N, &CS[(n * NTH + wave * kWave) * EP]);
+  }
+  // ---- one head's copies: dy and cs/dt into a buffer, Gk into GS.  Every
+  // per-thread offset here and below is formed from a thread index passed
+  // through an empty asm at each use, so the compiler forms it where it is
+  // used instead of keeping it (as a 64-bit address) live over the head loop.
+  auto tid = []() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  auto dma_dy = [&](int hh, Buf& Bn) {
+    const int t = tid(), r = t / 8;
+    const int h = h0 + hh;
+    const T* dyh = dy + (row0 * H + h) * P;
+    const uint32_t o = r * H * P + ((t % 8) ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) * 8;
+#pragma unroll
+    for (int n = 0; n < DYPT; ++n)
+      lds_copy16(dyh + (o + (uint32_t)(n * (NTH / 8) * H * P)), Bn.DY + (n * NTH + wave * kWave) * 8);
+    const float* csb = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+    const float* dtb = dt + (((int64_t)b * H + h) * K + k) * Q;
+    // wave 0 copies cs, wave 1 dt (a wave's 64 x 16 bytes each); the other
+    // waves copy dt again into the spare tail, so every wave issues the
+    // same copies
+    static_assert(Q == 4 * kWave, "cs / dt: one wave's copy each");
+    lds_copy16((wave == 0 ? csb : dtb) + 4 * (t % kWave), Bn.S + min(wave, 2) * kWave * 4);
+  };
+  auto dma_gk = [&](int hh) {
+    const int t = tid(), r = t / GPC;
+    const T* gh = gst + ((((int64_t)b * K + k) * H + h0 + hh) * P) * N;
+    const uint32_t o = r * N + ((t % GPC) ^ (r & (GPC - 1))) * 8;
+#pragma unroll
+    for (int n = 0; n < GPT; ++n) lds_copy16(gh + (o + (uint32_t)(n * (NTH / GPC) * N)), &GS[(n * NTH + wave * kWave) * 8]);
+  };
+
+  // ---- row sums and scalars of head hh from the waves' shares (after a barrier)
+  auto finish = [&](int hh) {
+    const int t = tid();
+    const int64_t bkh = ((int64_t)b * K + k) * H + h0 + hh;
+    float* part = dlpart + bkh * dl_rows(Q) * Q;
+    if (t < Q) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += RA[w][t];
+      part[t] = v;
+#pragma unroll
+      for (int sp = 1; sp < NSPLIT; ++sp) part[sp * Q + t] = 0.0f;
+    }
+    if (t == 0) {
+      float ghs = 0.0f, dds = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { ghs += RED[w]; dds += RED[NW + w]; }
+      float* sc = dlscal + bkh * (NSPLIT + 1);
+      sc[0] = ghs;
+      sc[1] = dds;
+#pragma unroll
+      for (int sp = 1; sp < NSPLIT; ++sp) sc[1 + sp] = 0.0f;
+    }
+  };
+  auto barrier = [&]() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // ---- head hh's register operands: x of the owned columns (lane (q, c): 8
+  // consecutive headdim entries) and this thread's Hin pieces, matching the
+  // GS pieces it reads for <Gk, Hin>.  Issued before the next head's copies,
+  // so that waiting for them does not wait for those.
+  typedef Frag<T> XF[2][2];
+  typedef V HV[GPT];
+  auto load_regs = [&](int hh, XF& xf, HV& hv) {
+    int c = lane_id() & 15, q = lane_id() >> 4;
+    asm volatile("" : "+v"(c), "+v"(q));
+    const int t = tid();
+    const int h = h0 + hh;
+    const TI* xh = x + (row0 * H + h) * P;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp)
+        frag_load(xf[sl][kp], xh + (uint32_t)((16 * Js[sl] + c) * H * P + kp * 32 + 8 * q));
+    const T* hh0 = hin + (((int64_t)b * K + k) * H + h) * P * N;
+#pragma unroll
+    for (int n = 0; n < GPT; ++n) {
+      const int u = n * NTH + t, r = u / GPC;
+      hv[n] = *reinterpret_cast<const V*>(hh0 + (uint32_t)(r * N + ((u % GPC) ^ (r & (GPC - 1))) * 8));
+    }
+  };
+
+  // ---- one head from buffer Bc
+  auto head = [&](int hh, const Buf& Bc, const XF& xf, const HV& hv) {
+    // The lane indices pass through an empty asm at every head, so the
+    // addresses formed from them are formed here instead of being hoisted
+    // out of the head loop.
+    int c = lane_id() & 15, q = lane_id() >> 4;
+    asm volatile("" : "+v"(c), "+v"(q));
+    const int t = tid();
+    const int h = h0 + hh;
+    const float* cs = Bc.S;
+    const float* dts = Bc.S + Q;
+    const int64_t bkh = ((int64_t)b * K + k) * H + h;
+    float* part = dlpart + bkh * dl_rows(Q) * Q;
+
+    // state part of dxt^T: e_j (Gk B_j^T) with K = dstate (rows xrow(tp, .))
+    f4 adx[2][TP];
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) adx[sl][tp] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        const int r = xrow(tp, c);
+        Frag<T> gk;
+        frag_load(gk, &GS[r * N + ((((ks * 32 + 8 * q) / 8) ^ (r & (GPC - 1))) * 8)]);
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) mma(adx[sl][tp], gk, bfr[ks][sl]);
+      }
+    float gh = 0.0f;
+#pragma unroll
+    for (int n = 0; n < GPT; ++n) {
+      const V a = *reinterpret_cast<const V*>(&GS[(n * NTH + t) * 8]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gh += to_f(a[e]) * to_f(hv[n][e]);
+    }
+    barrier();  // every wave is done with GS: it takes the next head's Gk
+    dma_gk(min(hh + 1, nh - 1));
+
+    const float cs_last = cs[Q - 1];
+    const float Dh = Dp[h];
+    // e_j scaling and q_j = dt_j <x_j, e_j B_j^T Gk>  (j = 16 J + c in this lane)
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int j = 16 * Js[sl] + c;
+      const float e = __expf(cs_last - cs[j]);
+      float qs = 0.0f;
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          adx[sl][tp][r] *= e;
+          qs += adx[sl][tp][r] * frag_get(xf[sl][tp / 2], 4 * (tp & 1) + r);
+        }
+      qs = sum_q(qs) * dts[j];
+      if (q == 0) part[(NSPLIT + 1) * Q + j] = qs;
+    }
+
+    float colsum[2] = {0.0f, 0.0f};
+#pragma unroll 1
+    for (int s = 0; s < NS; ++s) {
+      const int rb = 32 * s;  // first row of the slab
+      float rowtot[2][4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rowtot[half][r] = 0.0f;
+      // dy^T operand tp of the slab (rows xrow(tp, .), chained K over its 32 rows)
+      auto fdt_load = [&](Frag<T>& f, int tp) {
+        const int r0 = rb + 4 * q + (c >> 2), col = 32 * (tp >> 1) + 8 * (c & 3) + 4 * (tp & 1);
+        frag_load_kmajor_at(f, &Bc.DY[r0 * P + dyc(r0, col)], &Bc.DY[(r0 + 16) * P + dyc(r0, col)]);
+      };
+      // dy row rb + 16 half + c as an A fragment (K = headdim from kp * 32)
+      auto dy_row_frag = [&](Frag<T>& fd, int half, int kp) {
+        const int yr = rb + 16 * half + c;
+        frag_load(fd, &Bc.DY[yr * P + dyc(yr, kp * 32 + 8 * q)]);
+      };
+      f4 arow[2];  // exp(cs_i - cs_rb), rows rb + 16 half + 4q + r of this lane
+      {
+        const float csr = cs[rb];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const f4 ci = *reinterpret_cast<const f4*>(&cs[rb + 16 * half + 4 * q]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) arow[half][r] = __expf(ci[r] - csr);
+        }
+      }
+      // W_ij = C_i . B_j of row tile 2s + half and owned column tile sl, in fp32
+      auto wtile = [&](f4& w, int half, int sl) {
+        w = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) {
+          Frag<T> cf;
+          staged_row_frag<N, NPC, CRPP>(cf, CS, rb + 16 * half + c, ks * 32 + 8 * q);
+          mma(w, cf, bfr[ks][sl]);
+        }
+      };
+      // column tiles wholly before the slab: the decay factors at the slab's first row
+      auto full_pair = [&](int sl) {
+        const int cj = 16 * Js[sl] + c;
+        const float bj = __expf(cs[rb] - cs[cj]);
+        const float bdt = bj * dts[cj];
+        f4 dp[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          dp[half] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            Frag<T> fd;
+            dy_row_frag(fd, half, kp);
+            mma(dp[half], fd, xf[sl][kp]);
+          }
+        }
+        Frag<T> fa;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f4 wt;
+          wtile(wt, half, sl);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float tv = wt[r] * arow[half][r];
+            frag_set<T>(fa, half * 4 + r, tv * bj);
+            const float rv = dp[half][r] * tv * bdt;
+            colsum[sl] += rv;
+            rowtot[half][r] += rv;
+          }
+        }
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          Frag<T> fdt;
+          fdt_load(fdt, tp);
+          mma(adx[sl][tp], fdt, fa);
+        }
+      };
+      auto full_pairs2 = [&]() {
+        float bj[2], bdt[2];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int cj = 16 * Js[sl] + c;
+          bj[sl] = __expf(cs[rb] - cs[cj]);
+          bdt[sl] = bj[sl] * dts[cj];
+        }
+        Frag<T> fa[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f4 wt[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int ks = 0; ks < NK; ++ks) {
+            Frag<T> cf;
+            staged_row_frag<N, NPC, CRPP>(cf, CS, rb + 16 * half + c, ks * 32 + 8 * q);
+            mma(wt[0], cf, bfr[ks][0]);
+            mma(wt[1], cf, bfr[ks][1]);
+          }
+          f4 dp[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            Frag<T> fd;
+            dy_row_frag(fd, half, kp);
+            mma(dp[0], fd, xf[0][kp]);
+            mma(dp[1], fd, xf[1][kp]);
+          }
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float tv = wt[sl][r] * arow[half][r];
+              frag_set<T>(fa[sl], half * 4 + r, tv * bj[sl]);
+              const float rv = dp[sl][r] * tv * bdt[sl];
+              colsum[sl] += rv;
+              rowtot[half][r] += rv;
+            }
+        }
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          Frag<T> fdt;
+          fdt_load(fdt, tp);
+          mma(adx[0][tp], fdt, fa[0]);
+          mma(adx[1][tp], fdt, fa[1]);
+        }
+      };
+      // the slab holding column tile J's own rows: the masked direct form
+      auto diag_pair = [&](int sl) {
+        const int J = Js[sl];
+        const int cj = 16 * J + c;
+        const float cs_cj = cs[cj];
+        const float dt_cj = dts[cj];
+        Frag<T> fa;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int I = 2 * s + half;
+          if (I >= J) {
+            f4 dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+              Frag<T> fd;
+              dy_row_frag(fd, half, kp);
+              mma(dp, fd, xf[sl][kp]);
+            }
+            const int i0 = 16 * I + 4 * q;
+            const f4 csi = *reinterpret_cast<const f4*>(&cs[i0]);
+            f4 wt;
+            wtile(wt, half, sl);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float lam = (i0 + r >= cj) ? __expf(csi[r] - cs_cj) : 0.0f;
+              const float pv = wt[r] * lam;
+              frag_set<T>(fa, half * 4 + r, pv);
+              // the diagonal R_jj cancels between the row and column sums and is left out of both
+              const float rv = (i0 + r > cj) ? dp[r] * pv * dt_cj : 0.0f;
+              colsum[sl] += rv;
+              rowtot[half][r] += rv;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) frag_set<T>(fa, half * 4 + r, 0.0f);
+          }
+        }
+#pragma unroll
+        for (int tp = 0; tp < TP; ++tp) {
+          Frag<T> fdt;
+          fdt_load(fdt, tp);
+          mma(adx[sl][tp], fdt, fa);
+        }
+      };
+      {
+        const bool f0 = Js[0] < 2 * s, f1 = Js[1] < 2 * s;
+        if (f0 && f1) full_pairs2();
+        else if (f0) full_pair(0);
+        else if (f1) full_pair(1);
+      }
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        if ((Js[sl] >> 1) == s) diag_pair(sl);
+      // the slab's 32 row totals of this wave: lane (q, c) ends with row
+      // rb + 16 half + 4q + r, half = c / 8, r = (c / 2) % 4 (lanes c, c ^ 1 alike)
+      float v8[8];
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v8[4 * half + r] = rowtot[half][r];
+      {
+        const float v = sum16_spread8(v8);
+        const uint32_t a = (uint32_t)(uintptr_t)&RA[wave][rb + 16 * (c >> 3) + 4 * q + ((c >> 1) & 3)];
+        asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+      }
+    }
+
+    // the owned columns are complete: <dxt_j, x_j>, <dy_j, x_j>, dx, the per-token sums
+    float dd = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      // x passes through an empty asm here, so that its fp32 values for q_j
+      // are converted again instead of being held over the slab loop
+      Frag<T> xe[2] = {xf[sl][0], xf[sl][1]};
+      asm volatile("" : "+v"(xe[0].v), "+v"(xe[1].v));
+      const int j = 16 * Js[sl] + c;
+      const float dtj = dts[j];
+      float xd = 0.0f;
+#pragma unroll
+      for (int tp = 0; tp < TP; ++tp) {
+        const typename Vec4<T>::type dv = *reinterpret_cast<const typename Vec4<T>::type*>(
+            &Bc.DY[j * P + dyc(j, 32 * (tp >> 1) + 8 * q + 4 * (tp & 1))]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float xv = frag_get(xe[tp / 2], 4 * (tp & 1) + r);
+          const float dyv = to_f(dv[r]);
+          xd += adx[sl][tp][r] * xv;
+          dd += dyv * xv;
+          adx[sl][tp][r] = dtj * adx[sl][tp][r] + Dh * dyv;
+        }
+      }
+      const float csv = sum_q(colsum[sl]);
+      const float xdv = sum_q(xd);
+      T* dxr = dx + ((row0 + j) * H + h) * P;
+#pragma unroll
+      for (int kp = 0; kp < TP / 2; ++kp) {
+        V o;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) o[r] = from_f<T>(adx[sl][2 * kp + r / 4][r % 4]);
+        *reinterpret_cast<V*>(dxr + 32 * kp + 8 * q) = o;
+      }
+      if (q == 0) {
+        part[NSPLIT * Q + j] = csv;
+        part[(NSPLIT + 2) * Q + j] = xdv;
+      }
+    }
+    gh = wave_sum(gh);
+    dd = wave_sum(dd);
+    if (lane_id() == 0) {
+      RED[wave] = gh;
+      RED[NW + wave] = dd;
+    }
+  };
+
+  // ---- heads.  Head hh's dy and cs/dt live in buffer hh & 1, its Gk in GS.
+  // At the top of a head its copies have landed once at most the previous
+  // head's dx and per-token stores (issued after the last of them, the Gk
+  // copy) are in flight; after the barrier the other buffer is free, and
+  // the previous head's row sums are complete.  Unrolled by two so that
+  // every LDS access names its buffer.
+  dma_dy(0, B0);
+  dma_gk(0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // C rows, B fragments, head 0
+  __syncthreads();
+  auto step = [&](int hh, const Buf& Bc, Buf& Bn) {
+    if (hh > 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(YST));
+      barrier();
+      finish(hh - 1);
+    }
+    XF xf;
+    HV hv;
+    load_regs(hh, xf, hv);
+    dma_dy(min(hh + 1, nh - 1), Bn);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DYPT + 1));  // x and Hin (the copies after them stay in flight)
+    head(hh, Bc, xf, hv);
+  };
+  for (int hh = 0; hh < nh; hh += 2) {
+    step(hh, B0, B1);
+    if (hh + 1 < nh) step(hh + 1, B1, B0);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the last head's spare copies too
+  __syncthreads();
+  finish(nh - 1);
+}
+
 // dl, ddt and the chunk's dA / dD partials from the per-token partial sums of
 // k_chunk_scan_bwd and (the state-to-output term t_i, in ntp headdim-tile
 // shares) of the chunk-state gradient:
@@ -1745,9 +2249,24 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
-    const int nitems = b * K * H;
-    k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
-        x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
+    // resident over heads where a slice holds enough heads (resident_slices):
+    // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.333 ms,
+    // 14 (Zamba2-7B-like) 0.222 -> 0.215 ms, 10 (long context) 1.34 -> 1.32 ms
+    int RS = 1;
+    const int rper = resident_slices(b * K * G, H / G, &RS);
+    if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {
+      if (rper >= kMinResidentHeads) {
+        const int nbkg = b * K * G;
+        k_chunk_scan_bwd_heads<TI, N><<<dim3((nbkg + 7) / 8 * 8 * RS), dim3(512), 0, st>>>(
+            x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, a.rows, H, G, K, rper, RS,
+            nbkg);
+      }
+    }
+    if (!(std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) || rper < kMinResidentHeads) {
+      const int nitems = b * K * H;
+      k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
+          x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
+    }
     k_dl_assemble<T, Q><<<dim3((b * K + 7) / 8 * 8 * ((H + 3) / 4)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
         P / 16, b * K);

@@ -170,6 +170,14 @@ __device__ __forceinline__ void frag_load_kmajor(Frag<float>& f, const float* ti
 // s_waitcnt immediate for vmcnt(n) lgkmcnt(0) (expcnt not waited for):
 // vmcnt's low four bits at [3:0], its high two at [15:14].
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+// vmcnt(n) alone (lgkmcnt field at its maximum, 15).  Vector-memory loads,
+// copies into LDS and stores leave this counter in the order they were
+// issued; the compiler assumes no such order between copies into LDS and
+// loads into registers and, with both in flight, waits for vmcnt(0) before
+// a register's first use.  A kernel that keeps copies in flight over such a
+// use waits for the register itself with this count (everything issued
+// after it) before that use.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);

@@ -1,7 +1,8 @@
-"""The forward chunk scan resident over heads, on the shapes that reach its
-edge paths, against the float64 oracle on every output.
+"""The chunk scans resident over heads (forward, and backward at chunk 256
+with dstate a multiple of 64), on the shapes that reach their edge paths,
+against the float64 oracle on every output.
 
-The kernel takes a (b, k, g) item and a slice of its heads per workgroup
+The kernels take a (b, k, g) item and a slice of its heads per workgroup
 when a slice holds at least 10 heads (bf16 or FP8, headdim 64).  Slices
 are planned as about 256 workgroups: s = ceil(256 / items) slices of
 per = ceil(heads per group / s) heads (at most 64), so the last slice may
@@ -9,7 +10,8 @@ hold fewer.  The shapes below are chosen to land on:
 
   * an odd head count per slice (the head loop's unpaired last step) and a
     shorter last chunk: 1 x (256 x 128 + 77) tokens, 11 heads, chunk 128
-    -> 257 items, one slice of 11 heads;
+    -> 257 items, one slice of 11 heads (forward only), and the same at
+    chunk 256: 1 x (256 x 256 + 77) tokens -> 257 items (both scans);
   * a shorter last slice: 4 x 4096 tokens, 42 heads, chunk 256 -> 64 items,
     slices of 11, 11, 11 and 9 heads (also with FP8 x, B, C, and with an
     initial state and a final-state cotangent);
@@ -51,6 +53,8 @@ def _slice_plan(shape):
 
 CASES = [
     ("odd_heads_ragged", inputs.workload("mamba2_370m", batch=1, seqlen=256 * 128 + 77, nheads=11, chunk=128),
+     dict(), (11, 1)),
+    ("odd_heads_ragged_q256", inputs.workload("mamba2_370m", batch=1, seqlen=256 * 256 + 77, nheads=11, chunk=256),
      dict(), (11, 1)),
     ("short_last_slice", inputs.workload("mamba2_2p7b", batch=4, seqlen=4096, nheads=42), dict(), (11, 4)),
     ("short_last_slice_fp8", inputs.workload("mamba2_2p7b", batch=4, seqlen=4096, nheads=42, dtype="fp8"),
