@@ -734,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
   constexpr int NPC = RBY / 16, CRPP = RBY >= 256 ? 1 : 256 / RBY;
   constexpr int GPC = N / 8;                        // 16-byte pieces of a Gk row
   constexpr int CPT = Q * NPC / NTH, DYPT = Q * P / 8 / NTH, GPT = P * N / 8 / NTH;
-  constexpr int YST = 2 * (P / 32) + 3 * 2;         // dx stores and per-token writes per thread and head
+  constexpr int YST = 2 * (P / 32) + 2 * 2;         // dx stores and per-token writes per thread after the x loads
   static_assert(NT == 2 * NW && CPT * NTH == Q * NPC && DYPT * NTH * 8 == Q * P && GPT * NTH * 8 == P * N,
                 "whole copies per thread");
   static_assert((NTH / NPC) % (CRPP * (NPC < 16 ? NPC : 16)) == 0 && (NTH / GPC) % GPC == 0 && (NTH / 8) % 16 == 0,
@@ -749,6 +749,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
   __shared__ __attribute__((aligned(16))) T GS[P * N];   // Gk of the head, pieces of row r XOR-permuted by r mod GPC
   __shared__ float RA[NW][Q];                            // per-wave row sums of R
   __shared__ float RED[2 * NW];                          // per-wave <Gk, Hin> and <dy, x>
+  __shared__ __attribute__((aligned(16))) float ES[Q];   // exp(cs_i - cs_rb) of the head, rb = first row of i's slab
   // storage column of dy element (r, col): the slab layout of k_chunk_scan_bwd
   auto dyc = [](int r, int col) { return col ^ (8 * ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))); };
   // headdim entry of row m of dxt^T tile tp (as in k_chunk_scan_bwd with bf16 and headdim 64)
@@ -872,7 +873,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
   };
 
   // ---- one head from buffer Bc
-  auto head = [&](int hh, const Buf& Bc, const XF& xf, const HV& hv) {
+  auto head = [&](int hh, const Buf& Bc, const XF& xf, const HV& hv, XF& xn, HV& hn) {
     // The lane indices pass through an empty asm at every head, so the
     // addresses formed from them are formed here instead of being hoisted
     // out of the head loop.
@@ -908,7 +909,15 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
 #pragma unroll
       for (int e = 0; e < 8; ++e) gh += to_f(a[e]) * to_f(hv[n][e]);
     }
-    barrier();  // every wave is done with GS: it takes the next head's Gk
+    // the slab row factors of this head (the previous head's slab loops are
+    // done: they were before the last barrier)
+    if (t < Q) {
+      const float v = __expf(cs[t] - cs[t & ~31]);
+      const uint32_t a = (uint32_t)(uintptr_t)&ES[t];
+      asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier();  // every wave is done with GS (it takes the next head's Gk), ES is complete
     dma_gk(min(hh + 1, nh - 1));
 
     const float cs_last = cs[Q - 1];
@@ -950,15 +959,8 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
         frag_load(fd, &Bc.DY[yr * P + dyc(yr, kp * 32 + 8 * q)]);
       };
       f4 arow[2];  // exp(cs_i - cs_rb), rows rb + 16 half + 4q + r of this lane
-      {
-        const float csr = cs[rb];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const f4 ci = *reinterpret_cast<const f4*>(&cs[rb + 16 * half + 4 * q]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) arow[half][r] = __expf(ci[r] - csr);
-        }
-      }
+      for (int half = 0; half < 2; ++half) arow[half] = *reinterpret_cast<const f4*>(&ES[rb + 16 * half + 4 * q]);
       // W_ij = C_i . B_j of row tile 2s + half and owned column tile sl, in fp32
       auto wtile = [&](f4& w, int half, int sl) {
         w = f4{0.f, 0.f, 0.f, 0.f};
@@ -1119,6 +1121,10 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
       }
     }
 
+    // the next head's x and Hin, in flight over this head's epilogue and the
+    // head switch (the last head reloads its own)
+    load_regs(min(hh + 1, nh - 1), xn, hn);
+
     // the owned columns are complete: <dxt_j, x_j>, <dy_j, x_j>, dx, the per-token sums
     float dd = 0.0f;
 #pragma unroll
@@ -1153,10 +1159,11 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
         for (int r = 0; r < 8; ++r) o[r] = from_f<T>(adx[sl][2 * kp + r / 4][r % 4]);
         *reinterpret_cast<V*>(dxr + 32 * kp + 8 * q) = o;
       }
-      if (q == 0) {
-        part[NSPLIT * Q + j] = csv;
-        part[(NSPLIT + 2) * Q + j] = xdv;
-      }
+      // the four lanes of column j hold the same sums and all store them:
+      // no branch, so every path from the x loads above to the next head's
+      // wait issues the same stores
+      part[NSPLIT * Q + j] = csv;
+      part[(NSPLIT + 2) * Q + j] = xdv;
     }
     gh = wave_sum(gh);
     dd = wave_sum(dd);
@@ -1166,32 +1173,39 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
     }
   };
 
-  // ---- heads.  Head hh's dy and cs/dt live in buffer hh & 1, its Gk in GS.
-  // At the top of a head its copies have landed once at most the previous
-  // head's dx and per-token stores (issued after the last of them, the Gk
-  // copy) are in flight; after the barrier the other buffer is free, and
-  // the previous head's row sums are complete.  Unrolled by two so that
-  // every LDS access names its buffer.
+  // ---- heads.  Head hh's dy and cs/dt live in buffer hh & 1, its Gk in GS,
+  // its x and Hin in registers loaded during the previous head.  At the top
+  // of a head its copies and loads have landed once at most the previous
+  // head's dx and per-token stores (issued after the last of them, the x and
+  // Hin loads) are in flight; after the barrier the other buffer is free,
+  // and the previous head's row sums are complete.  The wait and barrier
+  // are unconditional (the first head has nothing in flight), so that every
+  // path into a head has waited the same.  Unrolled by two so that every
+  // LDS access names its buffer.
+  XF xa, xb;
+  HV ha, hb;
+  load_regs(0, xa, ha);
   dma_dy(0, B0);
   dma_gk(0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // C rows, B fragments, head 0
   __syncthreads();
-  auto step = [&](int hh, const Buf& Bc, Buf& Bn) {
-    if (hh > 0) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(YST));
-      barrier();
-      finish(hh - 1);
-    }
-    XF xf;
-    HV hv;
-    load_regs(hh, xf, hv);
+  // head 0's registers pass through an empty asm here, so their loads are
+  // issued (and waited for) before this point: the loop's first wait then
+  // finds them complete on every path into it
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) asm volatile("" : "+v"(xa[sl][0].v), "+v"(xa[sl][1].v));
+#pragma unroll
+  for (int n = 0; n < GPT; ++n) asm volatile("" : "+v"(ha[n]));
+  auto step = [&](int hh, const Buf& Bc, Buf& Bn, const XF& xc, const HV& hc, XF& xn, HV& hn) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(YST));
+    barrier();
+    if (hh > 0) finish(hh - 1);
     dma_dy(min(hh + 1, nh - 1), Bn);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(DYPT + 1));  // x and Hin (the copies after them stay in flight)
-    head(hh, Bc, xf, hv);
+    head(hh, Bc, xc, hc, xn, hn);
   };
   for (int hh = 0; hh < nh; hh += 2) {
-    step(hh, B0, B1);
-    if (hh + 1 < nh) step(hh + 1, B1, B0);
+    step(hh, B0, B1, xa, ha, xb, hb);
+    if (hh + 1 < nh) step(hh + 1, B1, B0, xb, hb, xa, ha);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));  // the last head's spare copies too
   __syncthreads();
@@ -2250,8 +2264,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     // resident over heads where a slice holds enough heads (resident_slices):
-    // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.333 ms,
-    // 14 (Zamba2-7B-like) 0.222 -> 0.215 ms, 10 (long context) 1.34 -> 1.32 ms
+    // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.285 ms,
+    // 14 (Zamba2-7B-like) 0.222 -> 0.181 ms, 10 (long context) 1.34 -> 1.15 ms
     int RS = 1;
     const int rper = resident_slices(b * K * G, H / G, &RS);
     if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {

@@ -178,6 +178,9 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0
 // use waits for the register itself with this count (everything issued
 // after it) before that use.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+// lgkmcnt(0) alone (vmcnt and expcnt fields at their maxima): LDS stores
+// written in asm, which the compiler does not count, have completed.
+constexpr int kWaitLgkm0 = 0xC07F;
 
 __device__ __forceinline__ void lds_copy16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
