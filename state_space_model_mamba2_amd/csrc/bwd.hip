@@ -940,7 +940,10 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
     }
 
     float colsum[2] = {0.0f, 0.0f};
-#pragma unroll 1
+    // two slabs per iteration: their LDS addresses are one set of registers
+    // with immediate offsets (measured 0.285 -> 0.276 ms on the 2.7B shape;
+    // by four 0.280 ms, not unrolled 0.285 ms)
+#pragma unroll 2
     for (int s = 0; s < NS; ++s) {
       const int rb = 32 * s;  // first row of the slab
       float rowtot[2][4];
@@ -2264,8 +2267,8 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     // resident over heads where a slice holds enough heads (resident_slices):
-    // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.285 ms,
-    // 14 (Zamba2-7B-like) 0.222 -> 0.181 ms, 10 (long context) 1.34 -> 1.15 ms
+    // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.276 ms,
+    // 14 (Zamba2-7B-like) 0.222 -> 0.178 ms, 10 (long context) 1.34 -> 1.15 ms
     int RS = 1;
     const int rper = resident_slices(b * K * G, H / G, &RS);
     if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {
