@@ -2268,18 +2268,19 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
     // resident over heads where a slice holds enough heads (resident_slices):
     // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.276 ms,
-    // 14 (Zamba2-7B-like) 0.222 -> 0.178 ms, 10 (long context) 1.34 -> 1.15 ms
+    // 14 (Zamba2-7B-like) 0.222 -> 0.178 ms, 10 (long context) 1.34 -> 1.15 ms,
+    // 8 (Mamba2-370M shape) 0.154 -> 0.122 ms
     int RS = 1;
     const int rper = resident_slices(b * K * G, H / G, &RS);
     if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {
-      if (rper >= kMinResidentHeads) {
+      if (rper >= kMinResidentHeadsBwd) {
         const int nbkg = b * K * G;
         k_chunk_scan_bwd_heads<TI, N><<<dim3((nbkg + 7) / 8 * 8 * RS), dim3(512), 0, st>>>(
             x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, a.rows, H, G, K, rper, RS,
             nbkg);
       }
     }
-    if (!(std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) || rper < kMinResidentHeads) {
+    if (!(std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) || rper < kMinResidentHeadsBwd) {
       const int nitems = b * K * H;
       k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
           x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);

@@ -486,6 +486,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
 // spread its group operands' staging over (measured on the forward chunk
 // scan: 20, 14 and 10 heads faster than one workgroup per head, 8 slower).
 constexpr int kMinResidentHeads = 10;
+// The chunk-scan backward resident over heads pays from fewer heads: 8 (the
+// Mamba2-370M shape) measured 0.154 -> 0.122 ms; fewer were not measured.
+constexpr int kMinResidentHeadsBwd = 8;
 inline int resident_slices(int nbkg, int hpg, int* S) {
   int s = (256 + nbkg - 1) / nbkg;
   if (s > hpg) s = hpg;

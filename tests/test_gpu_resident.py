@@ -3,7 +3,8 @@ with dstate a multiple of 64), on the shapes that reach their edge paths,
 against the float64 oracle on every output.
 
 The kernels take a (b, k, g) item and a slice of its heads per workgroup
-when a slice holds at least 10 heads (bf16 or FP8, headdim 64).  Slices
+when a slice holds at least 10 heads (the backward from 8; bf16 or FP8,
+headdim 64).  Slices
 are planned as about 256 workgroups: s = ceil(256 / items) slices of
 per = ceil(heads per group / s) heads (at most 64), so the last slice may
 hold fewer.  The shapes below are chosen to land on:
@@ -18,8 +19,8 @@ hold fewer.  The shapes below are chosen to land on:
   * dstate 64 and two groups: 1 x 16384 tokens, 40 heads in 2 groups ->
     128 items, two slices of 10 heads.
 
-The full-size workload tests reach the same kernel with 20, 14 and 10
-heads per slice.  Tolerance 2e-2 (max|gpu - oracle| / max|oracle|, bf16
+The full-size workload tests reach the same kernels with 20, 14 and 10
+heads per slice, and the backward one also with 8 (Mamba2-370M shape).  Tolerance 2e-2 (max|gpu - oracle| / max|oracle|, bf16
 storage; FP8 against the oracle on the E4M3 values).
 """
 import os
