@@ -710,8 +710,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 // dx written) after the last slab.  The products are those of
 // k_chunk_scan_bwd (W formed per slab in fp32 from the staged C rows), and
 // so are the outputs: dx, and per token the row sums (all of them in the
-// first split's row, zeros in the others), column sums, q_j and
-// <dxt_j, x_j>, and per head <Gk, Hin> and <dy, x> (the first split's).
+// first split's row; k_dl_assemble then reads that row only), column sums,
+// q_j and <dxt_j, x_j>, and per head <Gk, Hin> and <dy, x> (the first
+// split's).
 // Memory waits are explicit: the compiler takes copies into LDS and loads
 // into registers for unordered on vmcnt and would wait for every copy in
 // flight before a register's first use or an LDS store it cannot tell
@@ -826,9 +827,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
       float v = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) v += RA[w][t];
-      part[t] = v;
-#pragma unroll
-      for (int sp = 1; sp < NSPLIT; ++sp) part[sp * Q + t] = 0.0f;
+      part[t] = v;  // the other split rows are not read after this kernel
     }
     if (t == 0) {
       float ghs = 0.0f, dds = 0.0f;
@@ -837,8 +836,6 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
       float* sc = dlscal + bkh * (NSPLIT + 1);
       sc[0] = ghs;
       sc[1] = dds;
-#pragma unroll
-      for (int sp = 1; sp < NSPLIT; ++sp) sc[1 + sp] = 0.0f;
     }
   };
   auto barrier = [&]() {
@@ -1235,8 +1232,8 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
                                                      float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
-                                                     int softplus, int ntp, int nbk) {
-  constexpr int NSPLIT = scan_bwd_splits(Q);
+                                                     int softplus, int ntp, int nbk, int nsplit) {
+  constexpr int NSPLIT = scan_bwd_splits(Q);  // the layout's split rows; the first nsplit hold sums
   constexpr int HPB = 4;                      // heads (waves) per workgroup
   constexpr int TPL = Q / kWave;
   static_assert(Q % kWave == 0, "chunk");
@@ -1260,7 +1257,8 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   for (int t = 0; t < TPL; ++t) {
     float rs = part[j0 + t];
 #pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp) rs += part[sp * Q + j0 + t];
+    for (int sp = 1; sp < NSPLIT; ++sp)
+      if (sp < nsplit) rs += part[sp * Q + j0 + t];
     float ts = part[(NSPLIT + 3) * Q + j0 + t];
     for (int tp = 1; tp < ntp; ++tp) ts += part[(NSPLIT + 3 + tp) * Q + j0 + t];
     v[t] = (rs + ts) - part[NSPLIT * Q + j0 + t];
@@ -1311,7 +1309,8 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   if (jl == 0) {
     float dds = 0.0f;
 #pragma unroll
-    for (int sp = 0; sp < NSPLIT; ++sp) dds += sc[1 + sp];
+    for (int sp = 0; sp < NSPLIT; ++sp)
+      if (sp < nsplit) dds += sc[1 + sp];
     dapart[bkh] = da;
     ddpart[bkh] = dds;
     if (softplus) dbiaspart[bkh] = dbias;
@@ -2266,28 +2265,30 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
   }
   {
     ProbeScope ps(probe, SSD_K_CHUNK_SCAN_BWD, st);
-    // resident over heads where a slice holds enough heads (resident_slices):
+    // resident over heads where a slice holds enough heads (resident_slices);
+    // it writes the row sums of every split into the first split's row
     // measured with k_dl_assemble, 20 heads (2.7B shape) 0.352 -> 0.276 ms,
     // 14 (Zamba2-7B-like) 0.222 -> 0.178 ms, 10 (long context) 1.34 -> 1.15 ms,
     // 8 (Mamba2-370M shape) 0.154 -> 0.122 ms
     int RS = 1;
     const int rper = resident_slices(b * K * G, H / G, &RS);
+    const bool res_bwd = std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0 && rper >= kMinResidentHeadsBwd;
     if constexpr (std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) {
-      if (rper >= kMinResidentHeadsBwd) {
+      if (res_bwd) {
         const int nbkg = b * K * G;
         k_chunk_scan_bwd_heads<TI, N><<<dim3((nbkg + 7) / 8 * 8 * RS), dim3(512), 0, st>>>(
             x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, a.rows, H, G, K, rper, RS,
             nbkg);
       }
     }
-    if (!(std::is_same<T, bf16>::value && Q == 256 && P == 64 && N % 64 == 0) || rper < kMinResidentHeadsBwd) {
+    if (!res_bwd) {
       const int nitems = b * K * H;
       k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
           x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     }
     k_dl_assemble<T, Q><<<dim3((b * K + 7) / 8 * 8 * ((H + 3) / 4)), dim3(256), 0, st>>>(
         a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
-        P / 16, b * K);
+        P / 16, b * K, res_bwd ? 1 : scan_bwd_splits(Q));
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int nbkg = b * K * G;
