@@ -1930,6 +1930,17 @@ __device__ __forceinline__ void hs_dw(const TI* __restrict__ x, const float* __r
     asm volatile("" : "+v"(xo[0]), "+v"(xo[1]), "+v"(cl), "+v"(mb));
     const f4 cs0 = *reinterpret_cast<const f4*>(&Cb[16 * ti0 + 4 * q]);
     const f4 cs1 = *reinterpret_cast<const f4*>(&Cb[16 * ti1 + 4 * q]);
+    // Below the diagonal tile (every i after every j) the decay splits at the
+    // row tile's first token r: exp(cs_i - cs_r) exp(cs_r - cs_j), both
+    // factors <= 1, so a lane forms its 4 row factors per row tile once per
+    // head and one column factor per tile instead of 4 exponentials per tile.
+    const float cr0 = Cb[16 * ti0], cr1 = Cb[16 * ti1];
+    f4 rf0, rf1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rf0[r] = __expf(cs0[r] - cr0);
+      rf1[r] = __expf(cs1[r] - cr1);
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       int ti, tj;
@@ -1949,12 +1960,19 @@ __device__ __forceinline__ void hs_dw(const TI* __restrict__ x, const float* __r
         mma(dp, fa, fb[kp]);
       }
       const float csj = Cb[16 * tj + cl], dtj = Cb[Q + 16 * tj + cl];
-      const f4 csi = first ? cs1 : cs0;
-      const int d = 16 * (ti - tj) + mb;  // row i - column j = d + r
+      if (ti != tj) {  // wave-uniform
+        const f4 rf = first ? rf1 : rf0;
+        const float cf = dtj * __expf((first ? cr1 : cr0) - csj);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = dp[r] * (dtj * __expf(csi[r] - csj));
-        acc[s][r] += (d + r >= 0) ? v : 0.0f;
+        for (int r = 0; r < 4; ++r) acc[s][r] += dp[r] * (rf[r] * cf);
+      } else {  // the diagonal tile: masked, one exponential per element
+        const f4 csi = first ? cs1 : cs0;
+        const int d = mb;  // row i - column j = d + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = dp[r] * (dtj * __expf(csi[r] - csj));
+          acc[s][r] += (d + r >= 0) ? v : 0.0f;
+        }
       }
     }
   };
