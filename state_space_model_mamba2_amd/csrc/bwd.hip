@@ -751,8 +751,15 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
   __shared__ float RA[NW][Q];                            // per-wave row sums of R
   __shared__ float RED[2 * NW];                          // per-wave <Gk, Hin> and <dy, x>
   __shared__ __attribute__((aligned(16))) float ES[Q];   // exp(cs_i - cs_rb) of the head, rb = first row of i's slab
-  // storage column of dy element (r, col): the slab layout of k_chunk_scan_bwd
-  auto dyc = [](int r, int col) { return col ^ (8 * ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))); };
+  // dy rows in LDS: the 16-byte pieces of row r XOR-permuted by
+  // f(r) = 4 (u mod 2) + u / 2, u = (r / 2) mod 8.  Within each row parity f
+  // takes every value once over 16 rows, so a row fragment read (16
+  // consecutive rows, one piece each) meets every bank once; and f(r) ^
+  // f(r + 2) has bit 2 set, so the transposing dy^T reads (4 consecutive
+  // rows, 4 pieces each) put rows r and r + 2 on disjoint pieces.
+  auto dyf = [](int r) { return 4 * ((r >> 1) & 1) + ((r >> 2) & 3); };
+  // storage column of dy element (r, col)
+  auto dyc = [dyf](int r, int col) { return col ^ (8 * dyf(r)); };
   // headdim entry of row m of dxt^T tile tp (as in k_chunk_scan_bwd with bf16 and headdim 64)
   auto xrow = [](int tp, int m) { return 32 * (tp >> 1) + 8 * (m >> 2) + 4 * (tp & 1) + (m & 3); };
 
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
     const int t = tid(), r = t / 8;
     const int h = h0 + hh;
     const T* dyh = dy + (row0 * H + h) * P;
-    const uint32_t o = r * H * P + ((t % 8) ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))) * 8;
+    const uint32_t o = r * H * P + ((t % 8) ^ dyf(r)) * 8;
 #pragma unroll
     for (int n = 0; n < DYPT; ++n)
       lds_copy16(dyh + (o + (uint32_t)(n * (NTH / 8) * H * P)), Bn.DY + (n * NTH + wave * kWave) * 8);
