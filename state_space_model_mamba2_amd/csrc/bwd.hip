@@ -1233,14 +1233,18 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
 // starting at l Q / 64.  A chunk's head groups share the token rows of ddt
 // (one step per head), so its workgroups are dealt 8 dispatch slots apart:
 // one XCD's L2 gathers each row's heads before it goes to memory.
-template <typename T, int Q>
+template <typename T, int Q, int NTP, int NSP>
 __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ dlpart, const float* __restrict__ dlscal,
                                                      const float* __restrict__ cs_g, const float* __restrict__ dt,
                                                      const float* __restrict__ Ap, T* __restrict__ ddt,
                                                      float* __restrict__ dapart, float* __restrict__ ddpart,
                                                      float* __restrict__ dbiaspart, const RowMap rm, int H, int K,
-                                                     int softplus, int ntp, int nbk, int nsplit) {
-  constexpr int NSPLIT = scan_bwd_splits(Q);  // the layout's split rows; the first nsplit hold sums
+                                                     int softplus, int nbk) {
+  // NTP: headdim-tile shares of the state-to-output term; NSP: split rows
+  // holding row sums (the layout has NSPLIT).  Both fixed at compile time,
+  // so every load of a lane is issued before the first wait.
+  constexpr int NSPLIT = scan_bwd_splits(Q);
+  static_assert(NSP >= 1 && NSP <= NSPLIT && NTP >= 1, "rows");
   constexpr int HPB = 4;                      // heads (waves) per workgroup
   constexpr int TPL = Q / kWave;
   static_assert(Q % kWave == 0, "chunk");
@@ -1258,16 +1262,24 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   ddt = rows_out(rm, k, ddt, rm.ddt);
   const float* part = dlpart + (int64_t)bkh * dl_rows(Q) * Q;
   const float* sc = dlscal + (int64_t)bkh * (NSPLIT + 1);
+  const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
+  // the per-head values first (uniform: scalar loads), with the lane's rows below
+  const float cs_last = csc[Q - 1], ghin = sc[0], Ah = Ap[h];
+  float dds = 0.0f;
+#pragma unroll
+  for (int sp = 0; sp < NSP; ++sp) dds += sc[1 + sp];
   const int j0 = jl * TPL;
-  float v[TPL], qp[TPL];
+  float v[TPL], qp[TPL], dtv[TPL], xdv[TPL];
 #pragma unroll
   for (int t = 0; t < TPL; ++t) {
+    dtv[t] = dtc[j0 + t];
+    xdv[t] = part[(NSPLIT + 2) * Q + j0 + t];
     float rs = part[j0 + t];
 #pragma unroll
-    for (int sp = 1; sp < NSPLIT; ++sp)
-      if (sp < nsplit) rs += part[sp * Q + j0 + t];
+    for (int sp = 1; sp < NSP; ++sp) rs += part[sp * Q + j0 + t];
     float ts = part[(NSPLIT + 3) * Q + j0 + t];
-    for (int tp = 1; tp < ntp; ++tp) ts += part[(NSPLIT + 3 + tp) * Q + j0 + t];
+#pragma unroll
+    for (int tp = 1; tp < NTP; ++tp) ts += part[(NSPLIT + 3 + tp) * Q + j0 + t];
     v[t] = (rs + ts) - part[NSPLIT * Q + j0 + t];
     qp[t] = part[(NSPLIT + 1) * Q + j0 + t];
   }
@@ -1292,21 +1304,17 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   float excl = __shfl_down(incl, 1, kWave);
   if (jl == kWave - 1) excl = 0.0f;
   const float qexcl = qincl - qrun;
-  const float* csc = cs_g + (((int64_t)b * H + h) * K + k) * Q;
-  const float tail = __expf(csc[Q - 1]) * sc[0];
-  const float Ah = Ap[h];
-  const float* xd = part + (NSPLIT + 2) * Q + j0;
+  const float tail = __expf(cs_last) * ghin;
   float da = 0.0f, dbias = 0.0f;
 #pragma unroll
   for (int t = 0; t < TPL; ++t) {
     const int j = j0 + t;
     const float dl = v[t] + excl + (qp[t] + qexcl) + tail;
-    const float dtv = dtc[j];
-    da += dtv * dl;
-    float g = Ah * dl + xd[t];
+    da += dtv[t] * dl;
+    float g = Ah * dl + xdv[t];
     if (softplus) {
       // the step was softplus(z): d dt / dz = sigmoid(z) = 1 - exp(-dt)
-      g *= -expm1f(-dtv);
+      g *= -expm1f(-dtv[t]);
       dbias += g;
     }
     ddt[(row0 + j) * H + h] = from_f<T>(g);
@@ -1314,10 +1322,6 @@ __global__ __launch_bounds__(256) void k_dl_assemble(const float* __restrict__ d
   da = wave_sum(da);
   if (softplus) dbias = wave_sum(dbias);
   if (jl == 0) {
-    float dds = 0.0f;
-#pragma unroll
-    for (int sp = 0; sp < NSPLIT; ++sp)
-      if (sp < nsplit) dds += sc[1 + sp];
     dapart[bkh] = da;
     ddpart[bkh] = dds;
     if (softplus) dbiaspart[bkh] = dbias;
@@ -2311,9 +2315,15 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
       k_chunk_scan_bwd<T, TI, Q, P, N><<<dim3(xcd_grid(nitems) * scan_bwd_splits(Q)), dim3(256), 0, st>>>(
           x, dt, a.cs, a.D, B, C, hin, gst, dy, static_cast<T*>(a.dx), a.dlpart, a.dlscal, nitems, a.rows, H, G, K);
     }
-    k_dl_assemble<T, Q><<<dim3((b * K + 7) / 8 * 8 * ((H + 3) / 4)), dim3(256), 0, st>>>(
-        a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K, a.softplus,
-        P / 16, b * K, res_bwd ? 1 : scan_bwd_splits(Q));
+    const dim3 dlg((b * K + 7) / 8 * 8 * ((H + 3) / 4));
+    if (res_bwd)
+      k_dl_assemble<T, Q, P / 16, 1><<<dlg, dim3(256), 0, st>>>(
+          a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K,
+          a.softplus, b * K);
+    else
+      k_dl_assemble<T, Q, P / 16, scan_bwd_splits(Q)><<<dlg, dim3(256), 0, st>>>(
+          a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K,
+          a.softplus, b * K);
   }
   const int hpg = H / G, S = (int)lay.nslice, hps = (hpg + S - 1) / S;
   const int nbkg = b * K * G;
