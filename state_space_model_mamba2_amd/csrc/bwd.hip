@@ -2122,17 +2122,22 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
   const int kb0 = DB ? RB : 0, kb1 = DB ? NB - 1 : RB;
   auto load_block = [&](int kb) {
     const int ib = DB ? kb : RB, jb = DB ? RB : kb;  // dW rows i, columns j
-#pragma unroll
-    for (int it = 0; it < WRUNS; ++it) {
+    auto eo_of = [&](int it) {
       const int e = (threadIdx.x + NTH * it) * 4, il = e / 64, jl = e % 64;
-      const int64_t eo = (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
-      if constexpr (DWST) {  // one slice, already in the storage dtype
-        wst[it] = *reinterpret_cast<const W4*>(reinterpret_cast<const T*>(dw) + (int64_t)bkg * Q * Q + eo);
-      } else {
-        f4 v = *reinterpret_cast<const f4*>(dwb + eo);
-        for (int z = 1; z < nslice_dw; ++z) v += *reinterpret_cast<const f4*>(dwb + eo + z * dws);
-        wsl[it] = v;
-      }
+      return (int64_t)(64 * ib + il) * Q + 64 * jb + jl;
+    };
+    if constexpr (DWST) {  // one slice, already in the storage dtype
+#pragma unroll
+      for (int it = 0; it < WRUNS; ++it)
+        wst[it] = *reinterpret_cast<const W4*>(reinterpret_cast<const T*>(dw) + (int64_t)bkg * Q * Q + eo_of(it));
+    } else {
+      // slice by slice, each slice's loads issued together (the sum per
+      // element runs over the slices in order either way)
+#pragma unroll
+      for (int it = 0; it < WRUNS; ++it) wsl[it] = *reinterpret_cast<const f4*>(dwb + eo_of(it));
+      for (int z = 1; z < nslice_dw; ++z)
+#pragma unroll
+        for (int it = 0; it < WRUNS; ++it) wsl[it] += *reinterpret_cast<const f4*>(dwb + eo_of(it) + z * dws);
     }
     // B rows j (dC) or C rows i (dB) of block kb
 #pragma unroll
@@ -2192,15 +2197,22 @@ __device__ __forceinline__ void bc_final_block(const float* __restrict__ part, c
       }
     }
   }
+  // the head-slice partials slice by slice, each slice's loads issued together
+  float pv[TN][4];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[tn][r] = part[pidx(tn, r)];
+  for (int z = 1; z < nslice; ++z)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[tn][r] += part[z * ps + pidx(tn, r)];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t e = pidx(tn, r);
-      float v = part[e];
-      for (int z = 1; z < nslice; ++z) v += part[z * ps + e];
-      out[((row0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(v + acc[tn][r]);
-    }
+    for (int r = 0; r < 4; ++r)
+      out[((row0 + r0 + 16 * wave + 4 * q + r) * G + g) * N + n0 + 16 * tn + c] = from_f<T>(pv[tn][r] + acc[tn][r]);
   }
 }
 
