@@ -2329,11 +2329,11 @@ void run_bwd(const Layout& lay, const BwdArgs& a, hipStream_t st, const ssd_prob
     }
     const dim3 dlg((b * K + 7) / 8 * 8 * ((H + 3) / 4));
     if (res_bwd)
-      k_dl_assemble<T, Q, P / 16, 1><<<dlg, dim3(256), 0, st>>>(
+      k_dl_assemble<T, Q, 1, 1><<<dlg, dim3(256), 0, st>>>(
           a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K,
           a.softplus, b * K);
     else
-      k_dl_assemble<T, Q, P / 16, scan_bwd_splits(Q)><<<dlg, dim3(256), 0, st>>>(
+      k_dl_assemble<T, Q, 1, scan_bwd_splits(Q)><<<dlg, dim3(256), 0, st>>>(
           a.dlpart, a.dlscal, a.cs, dt, a.A, static_cast<T*>(a.ddt), a.dapart, a.ddpart, a.dbiaspart, a.rows, H, K,
           a.softplus, b * K);
   }

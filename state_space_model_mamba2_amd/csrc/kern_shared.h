@@ -327,6 +327,10 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
   typedef typename Vec16<T>::type V16;
   __shared__ __attribute__((aligned(16))) T Us[2][HPW][KB][UP];
   __shared__ __attribute__((aligned(16))) T Vs[2][KB][VP];
+  // backward: the state-to-output term's headdim-tile shares of a block,
+  // summed over the tiles after the next barrier and written as one row
+  constexpr int TPHS = BWD ? P / 16 : 1;
+  __shared__ float TS[BWD ? 2 : 1][BWD ? HPW : 1][TPHS][BWD ? KB : 1];
 
   const int bkhp = xcd_item(blockIdx.x, nitems);
   if (bkhp >= nitems) return;  // whole workgroup, before any barrier
@@ -411,11 +415,27 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc[hh][t] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // the shares of block sblk (in TS[sblk & 1]) summed over the headdim tiles
+  // in tile order and written (after a barrier that follows their writes)
+  auto ts_write = [&](int sblk) {
+    if constexpr (BWD) {
+      constexpr int NSP = scan_bwd_splits(Q);
+      const int hh = threadIdx.x / KB, i = threadIdx.x % KB;
+      if (hh < HPW) {
+        float v = TS[sblk & 1][hh][0][i];
+#pragma unroll
+        for (int w = 1; w < TPHS; ++w) v += TS[sblk & 1][hh][w][i];
+        const int64_t bkhh = ((int64_t)b * K + k) * H + h0 + hh;
+        dlpart[(bkhh * dl_rows(Q) + NSP + 3) * Q + KB * sblk + i] = v;
+      }
+    }
+  };
   load(0);
   store(0);
   for (int blk = 0; blk < NB; ++blk) {
     const int bf = blk & 1;
     __syncthreads();  // block blk is in buffer bf; buffer bf ^ 1 is no longer read
+    if (blk > 0) ts_write(blk - 1);
     if (blk + 1 < NB) load(blk + 1);
 #pragma unroll
     for (int ks = 0; ks < KB / 32; ++ks) {
@@ -438,9 +458,9 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
     if constexpr (BWD) {
       // state-to-output term of the block's tokens, headdim tile `wave`:
       // m[r] = (Hin C^T)[p = 16 wave + 4q + r][i = 16 rt + c], times the staged
-      // exp(cs_i) dy_i[p] and summed over p
+      // exp(cs_i) dy_i[p] and summed over p; the tile's share goes to TS
+      static_assert(TPH == TPHS && HPW * KB <= NTH, "shares summed by one thread per token and head");
       if (wave < TPH) {
-        constexpr int NSP = scan_bwd_splits(Q);
 #pragma unroll
         for (int rt = 0; rt < KB / 16; ++rt) {
           Frag<T> fc[NKN];
@@ -456,13 +476,16 @@ __global__ __launch_bounds__(256) void k_chunk_state(const TU* __restrict__ U, c
 #pragma unroll
             for (int r = 0; r < 4; ++r) t += m[r] * to_f(u[r]);
             t = sum_q(t);
-            const int64_t bkhh = ((int64_t)b * K + k) * H + h0 + hh;
-            if (q == 0) dlpart[(bkhh * dl_rows(Q) + NSP + 3 + wave) * Q + KB * blk + 16 * rt + c] = t;
+            if (q == 0) TS[bf][hh][wave][16 * rt + c] = t;
           }
         }
       }
     }
     if (blk + 1 < NB) store(bf ^ 1);
+  }
+  if constexpr (BWD) {
+    __syncthreads();
+    ts_write(NB - 1);
   }
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
