@@ -110,8 +110,8 @@ def kernel_model(s, esz):
         "chunk_state": (XI + BC + 2 * CS + STe, 2 * bkh * Q * P * N),
         "state_passing": (2 * STe + b * H * P * N * 4, 0),
         "chunk_scan": (XI + X + 2 * CS + BC + STe + WT, 2 * bkh * (Q * N * P + tri * P)),
-        # dy, C, cs, Hin in; dH_loc and the state-to-output term's headdim-tile shares out
-        "chunk_state_bwd": (X + BC + CS + 2 * STe + bkh * (P // 16) * Q * 4, 4 * bkh * Q * P * N),
+        # dy, C, cs, Hin in; dH_loc and the state-to-output term (one fp32 row per unit) out
+        "chunk_state_bwd": (X + BC + CS + 2 * STe + bkh * Q * 4, 4 * bkh * Q * P * N),
         "state_passing_bwd": (2 * STe, 0),
         # x, dy, the step, cs, B, C, Gk, Hin (for <Gk, Hin>) in; dx out (+ dl assembly: ddt out).
         # C.B^T is formed again per head in fp32 (the tri * N term)
