@@ -705,7 +705,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 // dy rows and cs/dt travel global -> LDS by direct copies one head ahead
 // (two buffers), its Gk into one buffer once every wave has formed the
 // head's state term, and Hin (for <Gk, Hin>) and the owned x rows straight
-// into registers.  With the whole of dy in LDS the slab loop has no
+// into registers during the previous head's epilogue.  The slab row
+// factors exp(cs_i - cs_rb) are formed once per head into a small LDS
+// table.  With the whole of dy in LDS the slab loop has no
 // barrier; it runs from the chunk start, so a column tile is complete (and
 // dx written) after the last slab.  The products are those of
 // k_chunk_scan_bwd (W formed per slab in fp32 from the staged C rows), and
@@ -716,10 +718,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void k_chunk_scan_bwd(
 // Memory waits are explicit: the compiler takes copies into LDS and loads
 // into registers for unordered on vmcnt and would wait for every copy in
 // flight before a register's first use or an LDS store it cannot tell
-// apart from a copy's destination.  So x and Hin are waited for by count
-// right after the next head's copies are issued, and the per-slab row sums
-// go to LDS through an asm store (the head's top wait, lgkmcnt(0) with its
-// barrier, publishes them).
+// apart from a copy's destination.  So the head's top wait (vmcnt of the
+// previous head's last stores) covers its copies, x and Hin, every path
+// into it has issued the same stores, and the per-slab row sums and the
+// row factors go to LDS through asm stores (published by an lgkmcnt(0)
+// wait before the barrier that precedes their readers).
 template <typename TI, int N>
 __global__ __launch_bounds__(512, 1) void k_chunk_scan_bwd_heads(
     const TI* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ cs_g,
